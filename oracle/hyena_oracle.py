@@ -1,0 +1,249 @@
+"""Float64 CPU oracle for the Hyena order-N operator forward pass.
+
+THIS IS TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the test suite,
+the smoke check and the benchmark's CPU-baseline leg may import it.  It shares
+no code with the HIP path (no kernels, helpers, tables or constants) and it
+imports nothing from this repository.
+
+Everything here is plain, slow and meant to be checked by eye against the
+pages it follows.  Floating point is float64 throughout; fp32 or bf16 inputs
+are upcast exactly before use.
+
+Sources (web pages; cited below by key, page title and section):
+  [P1] abeam-guide-lp.pages.dev, explainer of "Hyena Hierarchy: Towards Larger
+       Convolutional Language Models" (Japanese).
+  [P2] jisaku.com glossary entry "Hyena（ハイエナ）".
+  [P3] imamachi-n.github.io homemade-llm, "02. 3つの Hyena 演算子"
+       (StripedHyena 2 operators).
+  [P4] irregular6612.github.io paper digest "Hyena Hierarchy - Towards Larger
+       Convolutional Language Models" (Korean).
+  [P5] gist.science summary of "Native Multi-Dimensional Subquadratic Operators
+       via Input Dependent Long Convolutions" (HyenaND / nSubQ).
+
+What the operator computes (restated):
+  * [P1] section "Hyena 演算子の形" and [P4] section "방법 (Method)", framework
+    figure: start from z_1 = v; for n = 1..N the next state is the elementwise
+    product of the gate x_n with the long convolution of filter h_n and z_n;
+    the output is y = z_{N+1}.
+  * [P3] section 4 "FIR フィルタと効率的な生成", its causal-convolution equation:
+    output sample t depends only on input samples at or before t, with the
+    filter tap k weighting the input k steps back.  Here the filter spans the
+    whole sequence (length L) and the output keeps the first L samples.
+  * [P2] section "暗黙的畳み込みフィルタ": the filter is a window in t times an
+    FFN evaluated on the normalised position t/L and sin/cos features of t;
+    the window is an exponential decay and the FFN is a small MLP.
+  * [P2] section "計算効率" and [P5] section "手法: HyenaND" (boundary handling):
+    the long convolution is evaluated as FFT, pointwise product, inverse FFT,
+    with the signals zero-padded to twice their length so that the circular
+    convolution equals the linear one.  Any FFT length >= 2L-1 gives the same
+    exact result; the oracle uses the next power of two >= 2L.
+
+Readings where the pages are silent (each listed in the design notes):
+  positional features e(t) = [t/L, sin(2*pi*k*t/L) for k=1..K,
+  cos(2*pi*k*t/L) for k=1..K]; FFN = affine -> sin -> affine -> sin -> affine
+  (sin with unit frequency, "2-layer" counting hidden layers); output column
+  j = n*D + d feeds filter h_n of channel d; window exp(-alpha_d * t / L) is
+  the same for every order; no bias/skip term, no normalisation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "positional_features",
+    "filter_ffn",
+    "filter_gen",
+    "causal_conv_direct",
+    "fft",
+    "causal_conv_fft",
+    "causal_conv",
+    "hyena_forward",
+    "filter_spectrum",
+    "DIRECT_MAX_L",
+]
+
+# Up to this length the convolution is the brute-force sum; beyond it the
+# oracle's own radix-2 FFT is used (same exact result, O(L log L)).
+DIRECT_MAX_L = 8192
+
+
+# ---------------------------------------------------------------------------
+# Implicit filter  ([P2] section "暗黙的畳み込みフィルタ"; [P1] section
+# "フィルタの作り方"; [P4] framework figure, HyenaFilter node:
+# positional encoding -> FFN -> window)
+# ---------------------------------------------------------------------------
+
+def positional_features(L: int, K: int = 8) -> np.ndarray:
+    """e(t) for t = 0..L-1, shape [L, 1 + 2K], float64.
+
+    Column 0 is the normalised position t/L; columns 1..K are sin(2*pi*k*t/L)
+    and columns K+1..2K are cos(2*pi*k*t/L), k = 1..K ([P2] "暗黙的畳み込み
+    フィルタ": t/L plus sin/cos frequency features).  The phase k*t/L is
+    reduced modulo 1 with exact integer arithmetic before taking sin/cos.
+    """
+    t = np.arange(L, dtype=np.int64)
+    feats = np.empty((L, 1 + 2 * K), dtype=np.float64)
+    feats[:, 0] = t / L
+    for k in range(1, K + 1):
+        frac = np.mod(k * t, L) / L  # exact integer reduction, then one division
+        feats[:, k] = np.sin(2.0 * np.pi * frac)
+        feats[:, K + k] = np.cos(2.0 * np.pi * frac)
+    return feats
+
+
+def filter_ffn(e: np.ndarray, W1, b1, W2, b2, W3, b3, cols=None) -> np.ndarray:
+    """FFN(e(t)) for every t: sin(W1 e + b1) -> sin(W2 . + b2) -> W3 . + b3.
+
+    Weights are row-major [out][in] (W1 [H][1+2K], W2 [H][H], W3 [N*D][H]).
+    Returns [L, len(cols)] (all N*D outputs when cols is None).  ``cols``
+    selects output columns j = n*D + d so large shapes only evaluate the
+    columns a test needs.
+    """
+    W1 = np.asarray(W1, np.float64); b1 = np.asarray(b1, np.float64)
+    W2 = np.asarray(W2, np.float64); b2 = np.asarray(b2, np.float64)
+    W3 = np.asarray(W3, np.float64); b3 = np.asarray(b3, np.float64)
+    a1 = np.sin(e @ W1.T + b1)
+    a2 = np.sin(a1 @ W2.T + b2)
+    if cols is None:
+        return a2 @ W3.T + b3
+    cols = np.asarray(cols, dtype=np.int64)
+    return a2 @ W3[cols].T + b3[cols]
+
+
+def filter_gen(params: dict, L: int, channels=None) -> np.ndarray:
+    """Filters h[n, d, t] = exp(-alpha_d * t / L) * FFN(e(t))[n*D + d].
+
+    ``params`` holds D, N, K and the arrays W1, b1, W2, b2, W3, b3, alpha (any
+    float dtype; upcast to float64).  Returns [N, D, L] float64, or
+    [N, len(channels), L] when ``channels`` (a list of d) is given.
+    """
+    D, N, K = int(params["D"]), int(params["N"]), int(params.get("K", 8))
+    chans = list(range(D)) if channels is None else [int(c) for c in channels]
+    cols = [n * D + d for n in range(N) for d in chans]
+    e = positional_features(L, K)
+    o = filter_ffn(e, params["W1"], params["b1"], params["W2"], params["b2"],
+                   params["W3"], params["b3"], cols=cols)          # [L, N*len(chans)]
+    alpha = np.asarray(params["alpha"], np.float64)
+    t = np.arange(L, dtype=np.float64)
+    h = np.empty((N, len(chans), L), dtype=np.float64)
+    for n in range(N):
+        for i, d in enumerate(chans):
+            window = np.exp(-alpha[d] * t / L)                      # exponential decay
+            h[n, i] = window * o[:, n * len(chans) + i]
+    return h
+
+
+# ---------------------------------------------------------------------------
+# Causal long convolution ([P3] section 4, causal FIR equation; [P1] section
+# "なぜ attention っぽい表現力を持てるのか": a Toeplitz matrix)
+# ---------------------------------------------------------------------------
+
+def causal_conv_direct(h: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """c[..., t] = sum_{k=0..t} h[..., k] * z[..., t-k]  for t = 0..L-1.
+
+    Brute force over the lag k.  ``h`` broadcasts against ``z`` on the
+    leading axes; the last axis is time.
+    """
+    h = np.asarray(h, np.float64)
+    z = np.asarray(z, np.float64)
+    L = z.shape[-1]
+    assert h.shape[-1] == L
+    shape = np.broadcast_shapes(h.shape, z.shape)
+    c = np.zeros(shape, dtype=np.float64)
+    for k in range(L):
+        c[..., k:] += h[..., k:k + 1] * z[..., :L - k]
+    return c
+
+
+def _bit_reverse_indices(n: int) -> np.ndarray:
+    bits = n.bit_length() - 1
+    idx = np.arange(n, dtype=np.int64)
+    rev = np.zeros(n, dtype=np.int64)
+    for b in range(bits):
+        rev |= ((idx >> b) & 1) << (bits - 1 - b)
+    return rev
+
+
+def fft(x: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """The oracle's own iterative radix-2 Cooley-Tukey DFT along the last axis.
+
+    Forward: X[k] = sum_n x[n] exp(-2*pi*i*n*k/P).  Inverse uses the opposite
+    sign and divides by P.  P must be a power of two.  Decimation in time:
+    bit-reverse the input, then merge sub-transforms of size m into 2m with
+    X[k] = E[k] + w^k O[k], X[k+m] = E[k] - w^k O[k], w = exp(-+2*pi*i/(2m)).
+    """
+    a = np.asarray(x, dtype=np.complex128)
+    P = a.shape[-1]
+    assert P >= 1 and (P & (P - 1)) == 0, "power-of-two length required"
+    lead = a.shape[:-1]
+    a = a[..., _bit_reverse_indices(P)].copy()
+    sign = 1.0 if inverse else -1.0
+    m = 1
+    while m < P:
+        k = np.arange(m, dtype=np.float64)
+        w = np.cos(np.pi * k / m) + sign * 1j * np.sin(np.pi * k / m)
+        blocks = a.reshape(*lead, P // (2 * m), 2, m)
+        even = blocks[..., 0, :]
+        odd = blocks[..., 1, :] * w
+        a = np.stack([even + odd, even - odd], axis=-2).reshape(*lead, P)
+        m *= 2
+    if inverse:
+        a = a / P
+    return a
+
+
+def causal_conv_fft(h: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Same result as causal_conv_direct, by zero-padded FFT ([P2] "計算効率":
+    transform, pointwise product, inverse transform; [P5] "手法: HyenaND":
+    pad to twice the length so no circular wrap reaches the kept samples).
+    """
+    h = np.asarray(h, np.float64)
+    z = np.asarray(z, np.float64)
+    L = z.shape[-1]
+    P = 1
+    while P < 2 * L:
+        P *= 2
+    hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
+    zp = np.zeros(z.shape[:-1] + (P,)); zp[..., :L] = z
+    c = fft(fft(hp) * fft(zp), inverse=True)
+    return c[..., :L].real
+
+
+def causal_conv(h: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Direct sum for L <= DIRECT_MAX_L, FFT path beyond."""
+    if np.asarray(z).shape[-1] <= DIRECT_MAX_L:
+        return causal_conv_direct(h, z)
+    return causal_conv_fft(h, z)
+
+
+# ---------------------------------------------------------------------------
+# The order-N recurrence ([P1] "Hyena 演算子の形"; [P4] framework figure)
+# ---------------------------------------------------------------------------
+
+def hyena_forward(v: np.ndarray, xs, h: np.ndarray, conv=causal_conv) -> np.ndarray:
+    """y = z_{N+1} with z_1 = v and z_{n+1} = x_n * (h_n conv z_n).
+
+    v: [..., D, L]; xs: sequence of N arrays shaped like v; h: [N, D, L].
+    Gate x_n pairs with filter h_n at step n (figure of [P4]: the step that
+    produces z2 uses x1 and h1).  Returns float64 with v's shape.
+    """
+    z = np.asarray(v, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    N = h.shape[0]
+    assert len(xs) == N
+    for n in range(N):
+        c = conv(h[n], z)
+        z = np.asarray(xs[n], dtype=np.float64) * c
+    return z
+
+
+def filter_spectrum(h: np.ndarray, P: int) -> np.ndarray:
+    """Half spectrum H[..., k] = sum_{t<L} h[..., t] exp(-2*pi*i*k*t/P),
+    k = 0..P/2, of the filter zero-padded to P points ([P2] "計算効率", first
+    step applied to the filter).  P must be a power of two >= 2L.
+    """
+    h = np.asarray(h, np.float64)
+    L = h.shape[-1]
+    assert P >= 2 * L
+    hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
+    return fft(hp)[..., : P // 2 + 1]

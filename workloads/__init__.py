@@ -1,0 +1,134 @@
+"""Seeded synthetic workloads for the Hyena order-N forward.
+
+This module only draws random inputs; it holds none of the operator's
+arithmetic, so both the HIP path and the float64 oracle can take their inputs
+from it.  Every value is reproducible from (config seed, tensor id).
+
+Workload shapes follow the five operator configurations the project measures
+(orders 2 and 3, lengths 256 .. 1,048,576, fp32 or bf16 I/O).  The pages'
+own workloads (language modelling at 2K context, the 64K speed point of the
+Hyena Hierarchy explainer, the 1M-token DNA setting of the jisaku.com
+glossary entry, order-3 at ~128K) need datasets and trained weights that are
+not available, so seeded random tensors of the same shape and dtype stand in
+for them:
+
+  * v, x_1..x_N ~ N(0, 1) (torch generator seeded per tensor), rounded to
+    bf16 (round-to-nearest-even) where the I/O dtype is bf16;
+  * DNA-style v: tokens i.i.d. uniform over a 4-symbol alphabet, looked up in
+    a 4 x D embedding table drawn from N(0, 1);
+  * filter FFN weights ~ N(0, 1/fan_in) (numpy PCG64 per layer), biases 0,
+    window rates alpha_d linearly spaced in [1, 10].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+__all__ = ["Config", "CONFIGS", "make_filter_params", "make_activations",
+           "config_by_name"]
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    N: int          # order
+    B: int          # batch
+    D: int          # channels
+    L: int          # sequence length
+    io: str         # "fp32" or "bf16"
+    H: int          # FFN hidden width
+    seed: int
+    K: int = 8      # sin/cos frequencies in the positional features (dim 1+2K)
+    v_kind: str = "normal"   # "normal" or "dna"
+    desc: str = ""
+
+    def with_(self, **kw) -> "Config":
+        return replace(self, **kw)
+
+
+CONFIGS = {
+    "C1": Config("C1", 2, 1, 16, 256, "fp32", 32, 1,
+                 desc="order-2, B=1, D=16, L=256, fp32 (small parity case)"),
+    "C2": Config("C2", 2, 4, 768, 2048, "fp32", 64, 2,
+                 desc="order-2, B=4, D=768, L=2048, fp32 (2K-context LM shape)"),
+    "C3": Config("C3", 2, 1, 768, 65536, "bf16", 64, 3,
+                 desc="order-2, B=1, D=768, L=65536, bf16 I/O (64K long-context shape)"),
+    "C4": Config("C4", 2, 1, 256, 1048576, "fp32", 64, 4, v_kind="dna",
+                 desc="order-2, B=1, D=256, L=1048576, fp32, DNA-token v (1M-token shape)"),
+    "C5a": Config("C5a", 3, 2, 1024, 131072, "bf16", 64, 5,
+                  desc="order-3, B=2, D=1024, L=131072, bf16 I/O"),
+    "C5b": Config("C5b", 3, 2, 1024, 100000, "bf16", 64, 6,
+                  desc="order-3, B=2, D=1024, L=100000, bf16 I/O (non-power-of-two L)"),
+}
+
+
+def config_by_name(name: str) -> Config:
+    return CONFIGS[name]
+
+
+def _np_rng(seed: int, tid: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid])))
+
+
+def make_filter_params(cfg: Config, bias_scale: float = 0.0) -> dict:
+    """FFN weights (float32, row-major [out][in]) and window rates.
+
+    W1 [H][1+2K] ~ N(0, 1/(1+2K)), W2 [H][H] ~ N(0, 1/H), W3 [N*D][H] ~ N(0, 1/H).
+    Biases are zero unless ``bias_scale`` > 0 (tests use nonzero biases too).
+    alpha_d = linspace(1, 10, D) (alpha = 1 when D = 1).
+    """
+    F = 1 + 2 * cfg.K
+    H, ND = cfg.H, cfg.N * cfg.D
+    r1, r2, r3, rb = (_np_rng(cfg.seed, 101), _np_rng(cfg.seed, 102),
+                      _np_rng(cfg.seed, 103), _np_rng(cfg.seed, 104))
+    W1 = (r1.standard_normal((H, F)) / np.sqrt(F)).astype(np.float32)
+    W2 = (r2.standard_normal((H, H)) / np.sqrt(H)).astype(np.float32)
+    W3 = (r3.standard_normal((ND, H)) / np.sqrt(H)).astype(np.float32)
+    if bias_scale > 0:
+        b1 = (bias_scale * rb.standard_normal(H)).astype(np.float32)
+        b2 = (bias_scale * rb.standard_normal(H)).astype(np.float32)
+        b3 = (bias_scale * rb.standard_normal(ND)).astype(np.float32)
+    else:
+        b1 = np.zeros(H, np.float32); b2 = np.zeros(H, np.float32); b3 = np.zeros(ND, np.float32)
+    if cfg.D == 1:
+        alpha = np.ones(1, np.float32)
+    else:
+        alpha = np.linspace(1.0, 10.0, cfg.D).astype(np.float32)
+    return dict(D=cfg.D, N=cfg.N, K=cfg.K, H=H, W1=W1, b1=b1, W2=W2, b2=b2,
+                W3=W3, b3=b3, alpha=alpha)
+
+
+def make_activations(cfg: Config, device="cpu", B: int | None = None):
+    """(v, [x_1..x_N]) as torch tensors [B][D][L] in the config's I/O dtype.
+
+    Drawn with a torch generator on ``device`` (seeded per tensor), so large
+    shapes are generated where they are used.  Values for a given device are
+    reproducible; CPU and GPU generators give different streams.
+    """
+    import torch
+
+    B = cfg.B if B is None else B
+    dt = torch.float32 if cfg.io == "fp32" else torch.bfloat16
+    dev = torch.device(device)
+
+    def gen(tid: int):
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed * 1000 + tid)
+        return g
+
+    shape = (B, cfg.D, cfg.L)
+    if cfg.v_kind == "dna":
+        table = torch.from_numpy(_np_rng(cfg.seed, 200).standard_normal((4, cfg.D))
+                                 .astype(np.float32)).to(dev)
+        tokens = torch.randint(0, 4, (B, cfg.L), generator=gen(0), device=dev)
+        # v[b, d, t] = table[tokens[b, t], d]  (embedding lookup, done upstream)
+        v = table.t()[:, tokens].permute(1, 0, 2).contiguous()
+    else:
+        v = torch.randn(shape, generator=gen(0), device=dev, dtype=torch.float32)
+    xs = [torch.randn(shape, generator=gen(1 + n), device=dev, dtype=torch.float32)
+          for n in range(cfg.N)]
+    v = v.to(dt).contiguous()
+    xs = [x.to(dt).contiguous() for x in xs]
+    return v, xs
+
