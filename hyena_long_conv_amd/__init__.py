@@ -1,0 +1,205 @@
+"""Hyena order-N forward on MI355X: Python binding of the C ABI in include/hyena.h.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of libhyena_mi355x.so.  Tensors are torch CUDA (ROCm) tensors; work is
+enqueued on torch's current stream of the tensors' device.  There is no CPU
+fallback: without the built library every call raises.
+
+    h    = filter_gen(params, L)          # [N, D, L] fp32
+    spec = filter_spectrum(h)             # opaque spectrum, reused across calls
+    y    = forward(v, [x1, ..., xN], spec)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectrum_export",
+           "forward", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
+           "LIB_PATH", "HEADER_PATH", "header_functions"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
+
+HYENA_FP32, HYENA_BF16 = 0, 1
+STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_NULL", 2: "HYENA_ERR_SHAPE", 3: "HYENA_ERR_UNSUPPORTED",
+          4: "HYENA_ERR_ALIGN", 5: "HYENA_ERR_WORKSPACE", 6: "HYENA_ERR_ALIAS", 7: "HYENA_ERR_HIP"}
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+
+
+class FilterParams(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("b3", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int64), ("M", ctypes.c_int64), ("path", ctypes.c_int32),
+                ("n1", ctypes.c_int32), ("n2", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("spec_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhyena_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hyena_long_conv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    L.hyena_plan.argtypes = [i64, ctypes.POINTER(PlanInfo)]
+    L.hyena_plan.restype = i32
+    L.hyena_filter_gen.argtypes = [ctypes.POINTER(FilterParams), i64, vp, vp]
+    L.hyena_filter_gen.restype = i32
+    L.hyena_spectrum_bytes.argtypes = [i32, i32, i64]
+    L.hyena_spectrum_bytes.restype = i64
+    L.hyena_spectrum_workspace_bytes.argtypes = [i32, i32, i64]
+    L.hyena_spectrum_workspace_bytes.restype = i64
+    L.hyena_filter_spectrum.argtypes = [vp, i32, i32, i64, vp, vp, i64, vp]
+    L.hyena_filter_spectrum.restype = i32
+    L.hyena_spectrum_export.argtypes = [vp, i32, i32, i64, vp, vp]
+    L.hyena_spectrum_export.restype = i32
+    L.hyena_forward_workspace_bytes.argtypes = [i64, i32, i32, i64, i32]
+    L.hyena_forward_workspace_bytes.restype = i64
+    L.hyena_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, vp, i64, vp]
+    L.hyena_forward.restype = i32
+    L.hyena_status_str.argtypes = [i32]
+    L.hyena_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/hyena.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyena_[a-z_]+)\s*\(", text)))
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise HyenaError(code, what)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (ROCm) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def plan(L: int) -> dict:
+    info = PlanInfo()
+    _check(lib().hyena_plan(int(L), ctypes.byref(info)), "hyena_plan")
+    return dict(L=info.L, M=info.M, path=("single" if info.path == 1 else "fourstep"),
+                n1=info.n1, n2=info.n2, spec_stride=info.spec_stride)
+
+
+def spectrum_bytes(D: int, N: int, L: int) -> int:
+    return int(lib().hyena_spectrum_bytes(D, N, L))
+
+
+def spectrum_workspace_bytes(D: int, N: int, L: int) -> int:
+    return int(lib().hyena_spectrum_workspace_bytes(D, N, L))
+
+
+def forward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32") -> int:
+    return int(lib().hyena_forward_workspace_bytes(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16))
+
+
+def filter_gen(params: dict, L: int, out=None):
+    """h[n, d, t] from the implicit-filter weights (torch CUDA fp32 tensors
+    W1, W2, W3, alpha and optional b1, b2, b3; ints D, N, K, H)."""
+    import torch
+    W1 = params["W1"]
+    _need_cuda(W1, "W1", torch.float32)
+    D, N, K, H = int(params["D"]), int(params["N"]), int(params["K"]), int(params["H"])
+    keep = {}
+    for k in ("W1", "b1", "W2", "b2", "W3", "b3", "alpha"):
+        t = params.get(k)
+        if t is not None:
+            _need_cuda(t, k, torch.float32)
+        keep[k] = t
+    p = FilterParams(D, N, K, H, *[_ptr(keep[k]).value for k in ("W1", "b1", "W2", "b2", "W3", "b3", "alpha")])
+    h = out if out is not None else torch.empty((N, D, L), dtype=torch.float32, device=W1.device)
+    _need_cuda(h, "h", torch.float32)
+    _check(lib().hyena_filter_gen(ctypes.byref(p), int(L), _ptr(h), _stream(h)), "hyena_filter_gen")
+    return h
+
+
+def filter_spectrum(h, out=None, workspace=None):
+    """Spectrum of the filters h [N, D, L] (fp32), as an opaque uint8 buffer."""
+    import torch
+    _need_cuda(h, "h", torch.float32)
+    N, D, L = h.shape
+    nbytes = spectrum_bytes(D, N, L)
+    if nbytes < 0:
+        raise HyenaError(2, "hyena_spectrum_bytes")
+    spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=h.device)
+    wsb = spectrum_workspace_bytes(D, N, L)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=h.device)
+    _check(lib().hyena_filter_spectrum(_ptr(h), D, N, L, _ptr(spec), _ptr(workspace),
+                                       workspace.numel() if workspace is not None else 0, _stream(h)),
+           "hyena_filter_spectrum")
+    spec._hyena_shape = (D, N, L)
+    return spec
+
+
+def spectrum_export(spec, D: int, N: int, L: int):
+    """Natural-order spectrum [N, D, M/2+1] complex64 (unscaled DFT of each
+    filter zero-padded to M points)."""
+    import torch
+    M = plan(L)["M"]
+    out = torch.empty((N, D, M // 2 + 1, 2), dtype=torch.float32, device=spec.device)
+    _check(lib().hyena_spectrum_export(_ptr(spec), D, N, L, _ptr(out), _stream(out)), "hyena_spectrum_export")
+    return torch.view_as_complex(out)
+
+
+def forward(v, xs, spec, out=None, workspace=None):
+    """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16)."""
+    import torch
+    if v.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("v must be float32 or bfloat16")
+    _need_cuda(v, "v", v.dtype)
+    B, D, L = v.shape
+    N = len(xs)
+    for i, x in enumerate(xs):
+        _need_cuda(x, f"x[{i}]", v.dtype)
+        if tuple(x.shape) != (B, D, L):
+            raise ValueError(f"x[{i}] shape {tuple(x.shape)} != {(B, D, L)}")
+    io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
+    y = out if out is not None else torch.empty_like(v)
+    _need_cuda(y, "y", v.dtype)
+    wsb = int(lib().hyena_forward_workspace_bytes(B, D, N, L, io))
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
+    xp = (ctypes.c_void_p * N)(*[x.data_ptr() for x in xs])
+    _check(lib().hyena_forward(_ptr(v), xp, _ptr(spec), _ptr(y), B, D, N, L, io, _ptr(workspace),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(v)),
+           "hyena_forward")
+    return y

@@ -1,0 +1,217 @@
+// api.cpp -- the extern "C" entry points declared in include/hyena.h.
+//
+// Every entry point validates its arguments on the host before it enqueues
+// anything, so argument errors never reach the GPU.  The library allocates
+// nothing: spectrum, workspace and outputs come from the caller.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "hyena.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace hyena;
+
+namespace {
+
+int plan_env(int64_t L, PlanInfo* p) {
+  return make_plan(L, std::getenv("HYENA_FORCE_PATH"), std::getenv("HYENA_FOURSTEP_N1"), p);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+hyena_status from_plan_code(int c) {
+  return c == 0 ? HYENA_OK : (c == 2 ? HYENA_ERR_SHAPE : HYENA_ERR_UNSUPPORTED);
+}
+
+int64_t spec_bytes(const PlanInfo& p, int64_t NF) { return NF * p.spec_stride * 8; }
+
+int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
+  if (p.path == PATH_SINGLE) return 0;
+  const int64_t pairs = (NF + 1) / 2;
+  return (int64_t)pairs_per_group(p.M, pairs) * p.M * 8;
+}
+
+int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
+  if (p.path == PATH_SINGLE) return 0;
+  const Pairing pr = make_pairing(B, D);
+  return (int64_t)pairs_per_group(p.M, pr.n_pairs) * p.M * 8;
+}
+
+bool sizes_ok(int64_t D, int64_t N, int64_t L) {
+  return D >= 1 && D <= (1 << 20) && N >= 1 && L >= 1 && L <= kMaxL;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hyena_status_str(hyena_status s) {
+  switch (s) {
+    case HYENA_OK: return "ok";
+    case HYENA_ERR_NULL: return "a required pointer is NULL";
+    case HYENA_ERR_SHAPE: return "a size is out of range";
+    case HYENA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HYENA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case HYENA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HYENA_ERR_ALIAS: return "the output overlaps an input";
+    case HYENA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+hyena_status hyena_plan(int64_t L, hyena_plan_info* out) {
+  if (!out) return HYENA_ERR_NULL;
+  PlanInfo p;
+  const int c = plan_env(L, &p);
+  if (c) return from_plan_code(c);
+  out->L = p.L;
+  out->M = p.M;
+  out->path = p.path;
+  out->n1 = p.n1;
+  out->n2 = p.n2;
+  out->reserved = 0;
+  out->spec_stride = p.spec_stride;
+  return HYENA_OK;
+}
+
+hyena_status hyena_filter_gen(const hyena_filter_params* p, int64_t L, float* h, void* stream) {
+  if (!p || !h || !p->W1 || !p->W2 || !p->W3 || !p->alpha) return HYENA_ERR_NULL;
+  if (!sizes_ok(p->D, p->N, L) || p->K < 0 || p->K > kMaxFreq) return HYENA_ERR_SHAPE;
+  if (p->N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (p->H != 8 && p->H != 16 && p->H != 32 && p->H != 64 && p->H != 128) return HYENA_ERR_UNSUPPORTED;
+  if ((int64_t)p->N * p->D > 65535LL * 64) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(h)) return HYENA_ERR_ALIGN;
+  FilterGenArgs a{};
+  a.D = p->D; a.N = p->N; a.K = p->K; a.H = p->H;
+  a.W1 = p->W1; a.b1 = p->b1; a.W2 = p->W2; a.b2 = p->b2; a.W3 = p->W3; a.b3 = p->b3;
+  a.alpha = p->alpha; a.L = L; a.h = h;
+  return filter_gen(a, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+int64_t hyena_spectrum_bytes(int32_t D, int32_t N, int64_t L) {
+  if (!sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  PlanInfo p;
+  if (plan_env(L, &p)) return -1;
+  return spec_bytes(p, (int64_t)N * D);
+}
+
+int64_t hyena_spectrum_workspace_bytes(int32_t D, int32_t N, int64_t L) {
+  if (!sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  PlanInfo p;
+  if (plan_env(L, &p)) return -1;
+  return spectrum_ws(p, (int64_t)N * D);
+}
+
+hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t L, void* spec,
+                                   void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!h || !spec) return HYENA_ERR_NULL;
+  if (!sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  PlanInfo p;
+  const int c = plan_env(L, &p);
+  if (c) return from_plan_code(c);
+  const int64_t NF = (int64_t)N * D;
+  if (!aligned16(h) || !aligned16(spec) || (workspace && !aligned16(workspace))) return HYENA_ERR_ALIGN;
+  const int64_t need = spectrum_ws(p, NF);
+  if (need > 0 && (!workspace || workspace_bytes < p.M * 8)) return HYENA_ERR_WORKSPACE;
+  if (overlap(spec, spec_bytes(p, NF), h, NF * L * 4)) return HYENA_ERR_ALIAS;
+  if (workspace && need > 0 && (overlap(workspace, workspace_bytes, h, NF * L * 4) ||
+                                overlap(workspace, workspace_bytes, spec, spec_bytes(p, NF))))
+    return HYENA_ERR_ALIAS;
+  SpectrumArgs a{};
+  a.h = h; a.spec = spec; a.NF = (int)NF; a.L = L; a.spec_stride = p.spec_stride;
+  a.work = workspace;
+  hipError_t e;
+  if (p.path == PATH_SINGLE) {
+    e = single_spectrum(a, p.M, (hipStream_t)stream);
+  } else {
+    int64_t g = pairs_per_group(p.M, (NF + 1) / 2);
+    if (g * p.M * 8 > workspace_bytes) g = workspace_bytes / (p.M * 8);
+    a.pairs_per_group = (int)g;
+    e = fourstep_spectrum(a, p, (hipStream_t)stream);
+  }
+  return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+hyena_status hyena_spectrum_export(const void* spec, int32_t D, int32_t N, int64_t L, float* out,
+                                   void* stream) {
+  if (!spec || !out) return HYENA_ERR_NULL;
+  if (!sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  PlanInfo p;
+  const int c = plan_env(L, &p);
+  if (c) return from_plan_code(c);
+  if (!aligned16(spec) || !aligned16(out)) return HYENA_ERR_ALIGN;
+  const int64_t NF = (int64_t)N * D;
+  if (overlap(out, NF * (p.M / 2 + 1) * 8, spec, spec_bytes(p, NF))) return HYENA_ERR_ALIAS;
+  return spectrum_export(spec, (int)NF, p, out, (hipStream_t)stream) == hipSuccess ? HYENA_OK
+                                                                                   : HYENA_ERR_HIP;
+}
+
+int64_t hyena_forward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io) {
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
+  PlanInfo p;
+  if (plan_env(L, &p)) return -1;
+  return forward_ws(p, B, D);
+}
+
+hyena_status hyena_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                           int32_t D, int32_t N, int64_t L, hyena_dtype io, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  if (!v || !x || !spec || !y) return HYENA_ERR_NULL;
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  for (int n = 0; n < N; ++n)
+    if (!x[n]) return HYENA_ERR_NULL;
+  const Pairing pr = make_pairing(B, D);
+  if ((int64_t)pr.n_pairs > (int64_t)1 << 30) return HYENA_ERR_UNSUPPORTED;
+  PlanInfo p;
+  const int c = plan_env(L, &p);
+  if (c) return from_plan_code(c);
+  if (!aligned16(v) || !aligned16(y) || !aligned16(spec) || (workspace && !aligned16(workspace)))
+    return HYENA_ERR_ALIGN;
+  for (int n = 0; n < N; ++n)
+    if (!aligned16(x[n])) return HYENA_ERR_ALIGN;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * D * L * esz;
+  const int64_t sb = spec_bytes(p, (int64_t)N * D);
+  if (overlap(y, act, v, act) || overlap(y, act, spec, sb)) return HYENA_ERR_ALIAS;
+  for (int n = 0; n < N; ++n)
+    if (overlap(y, act, x[n], act)) return HYENA_ERR_ALIAS;
+  ForwardArgs a{};
+  a.v = v;
+  for (int n = 0; n < N; ++n) a.x.p[n] = x[n];
+  a.spec = spec; a.y = y; a.B = (int)B; a.D = D; a.N = N; a.L = L;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  a.spec_stride = p.spec_stride;
+  a.n_pairs = pr.n_pairs; a.n_batch_pairs = pr.n_batch_pairs; a.half_b = pr.half_b;
+  hipError_t e;
+  if (p.path == PATH_SINGLE) {
+    e = single_forward(a, p.M, (hipStream_t)stream);
+  } else {
+    if (!workspace || workspace_bytes < p.M * 8) return HYENA_ERR_WORKSPACE;
+    if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
+        overlap(workspace, workspace_bytes, spec, sb))
+      return HYENA_ERR_ALIAS;
+    for (int n = 0; n < N; ++n)
+      if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
+    int64_t g = pairs_per_group(p.M, pr.n_pairs);
+    if (g * p.M * 8 > workspace_bytes) g = workspace_bytes / (p.M * 8);
+    a.work = workspace;
+    a.pairs_per_group = (int)g;
+    e = fourstep_forward(a, p, (hipStream_t)stream);
+  }
+  return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+}  // extern "C"

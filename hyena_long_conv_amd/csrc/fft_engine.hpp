@@ -1,0 +1,464 @@
+// fft_engine.hpp -- workgroup-level complex FFT building blocks for gfx950.
+//
+// A workgroup computes one or more complex FFTs of NPT points.  Each thread
+// owns E = (a multiple of every radix used) points in registers.  Stages are
+// Stockham autosort (decimation in time, twiddle on the inputs): a radix-R
+// stage that follows stages of total size NS reads leg r of butterfly beta
+// from index beta + r*NPT/R, multiplies it by W_{R*NS}^{(beta mod NS)*r},
+// applies an R-point DFT and writes output q to (beta/NS)*NS*R + beta mod NS
+// + q*NS.  The output comes out in natural order with no bit reversal.
+//
+// Thread j handles butterflies beta = j + m*(NPT/E), m < E/R.  With that
+// assignment the thread's register set is {j + i*(NPT/E) : i < E} both at the
+// input of the first stage and at the output of the last stage, for any
+// radix sequence.  Consequences used throughout the kernels:
+//   * a forward FFT leaves bin k = j + i*NPT/E in reg[i];
+//   * an inverse FFT started from those registers needs no data exchange and
+//     leaves time sample t = j + i*NPT/E in reg[i];
+//   * the next forward FFT starts from those same registers.
+// Only the stages in between go through LDS.
+//
+// The math is the textbook Cooley-Tukey factorisation of the DFT; the
+// Stockham ordering avoids a separate bit-reversal pass.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "plan.hpp"
+
+namespace hyena {
+
+typedef float2 cf;
+
+__device__ __forceinline__ cf cadd(cf a, cf b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ cf csub(cf a, cf b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ cf cscale(cf a, float s) { return make_float2(a.x * s, a.y * s); }
+__device__ __forceinline__ cf cconj(cf a) { return make_float2(a.x, -a.y); }
+__device__ __forceinline__ cf cmul(cf a, cf b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+// a * conj(b)
+__device__ __forceinline__ cf cmulc(cf a, cf b) {
+  return make_float2(fmaf(a.x, b.x, a.y * b.y), fmaf(a.y, b.x, -a.x * b.y));
+}
+
+// Multiply by -i (forward transform) or +i (inverse transform).
+template <bool INV>
+__device__ __forceinline__ cf rot90(cf a) {
+  return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x);
+}
+
+// exp(-2 pi i k / n) (forward) or its conjugate (inverse), for 0 <= k < n.
+// The argument 2k/n is formed exactly for power-of-two n.
+template <bool INV>
+__device__ __forceinline__ cf twiddle(uint32_t k, uint32_t n) {
+  float s, c;
+  sincospif(2.0f * (float)k / (float)n, &s, &c);
+  return INV ? make_float2(c, s) : make_float2(c, -s);
+}
+
+// ---------------------------------------------------------------- small DFTs
+
+template <bool INV>
+__device__ __forceinline__ void dft2(cf& a0, cf& a1) {
+  cf t = a0;
+  a0 = cadd(t, a1);
+  a1 = csub(t, a1);
+}
+
+template <bool INV>
+__device__ __forceinline__ void dft4(cf& a0, cf& a1, cf& a2, cf& a3) {
+  cf t0 = cadd(a0, a2), t1 = csub(a0, a2);
+  cf t2 = cadd(a1, a3), t3 = rot90<INV>(csub(a1, a3));
+  a0 = cadd(t0, t2);
+  a2 = csub(t0, t2);
+  a1 = cadd(t1, t3);
+  a3 = csub(t1, t3);
+}
+
+// times exp(-+ i pi / 4)
+template <bool INV>
+__device__ __forceinline__ cf mul_w8(cf a) {
+  const float r = 0.70710678118654752440f;
+  return INV ? make_float2((a.x - a.y) * r, (a.x + a.y) * r)
+             : make_float2((a.x + a.y) * r, (a.y - a.x) * r);
+}
+
+template <bool INV>
+__device__ __forceinline__ void dft8(cf* a) {
+  // even / odd halves, then combine with W8^k
+  cf e0 = a[0], e1 = a[2], e2 = a[4], e3 = a[6];
+  cf o0 = a[1], o1 = a[3], o2 = a[5], o3 = a[7];
+  dft4<INV>(e0, e1, e2, e3);
+  dft4<INV>(o0, o1, o2, o3);
+  o1 = mul_w8<INV>(o1);
+  o2 = rot90<INV>(o2);
+  o3 = rot90<INV>(mul_w8<INV>(o3));
+  a[0] = cadd(e0, o0); a[4] = csub(e0, o0);
+  a[1] = cadd(e1, o1); a[5] = csub(e1, o1);
+  a[2] = cadd(e2, o2); a[6] = csub(e2, o2);
+  a[3] = cadd(e3, o3); a[7] = csub(e3, o3);
+}
+
+template <bool INV>
+__device__ __forceinline__ void dft16(cf* a) {
+  // 4 x 4: inner DFT4 over n1 for each n2, twiddle W16^{n2 k1}, outer DFT4.
+  const float c1 = 0.92387953251128675613f;  // cos(pi/8)
+  const float s1 = 0.38268343236508977173f;  // sin(pi/8)
+#pragma unroll
+  for (int n2 = 0; n2 < 4; ++n2) dft4<INV>(a[n2], a[n2 + 4], a[n2 + 8], a[n2 + 12]);
+  // a[n2 + 4*k1] now holds b[n2][k1]
+  const cf w1 = INV ? make_float2(c1, s1) : make_float2(c1, -s1);   // W16^1
+  const cf w3 = INV ? make_float2(s1, c1) : make_float2(s1, -c1);   // W16^3
+  a[1 + 4 * 1] = cmul(a[1 + 4 * 1], w1);
+  a[1 + 4 * 2] = mul_w8<INV>(a[1 + 4 * 2]);
+  a[1 + 4 * 3] = cmul(a[1 + 4 * 3], w3);
+  a[2 + 4 * 1] = mul_w8<INV>(a[2 + 4 * 1]);
+  a[2 + 4 * 2] = rot90<INV>(a[2 + 4 * 2]);
+  a[2 + 4 * 3] = rot90<INV>(mul_w8<INV>(a[2 + 4 * 3]));
+  a[3 + 4 * 1] = cmul(a[3 + 4 * 1], w3);
+  a[3 + 4 * 2] = rot90<INV>(mul_w8<INV>(a[3 + 4 * 2]));
+  a[3 + 4 * 3] = cmul(a[3 + 4 * 3], make_float2(-w1.x, -w1.y));     // W16^9 = -W16^1
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1) dft4<INV>(a[4 * k1 + 0], a[4 * k1 + 1], a[4 * k1 + 2], a[4 * k1 + 3]);
+  // a[4*k1 + k2] holds X[k1 + 4*k2]; transpose the 4x4 index into natural order
+  cf t[16];
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1)
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) t[k1 + 4 * k2] = a[4 * k1 + k2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = t[i];
+}
+
+template <int R, bool INV>
+__device__ __forceinline__ void dft(cf* a) {
+  if constexpr (R == 2) dft2<INV>(a[0], a[1]);
+  else if constexpr (R == 4) dft4<INV>(a[0], a[1], a[2], a[3]);
+  else if constexpr (R == 8) dft8<INV>(a);
+  else if constexpr (R == 16) dft16<INV>(a);
+  else static_assert(R == 2, "unsupported radix");
+}
+
+// ------------------------------------------------- twiddled DIT butterflies
+//
+// A Stockham stage after stages of total size NS evaluates, for butterfly
+// beta with p = beta mod NS and w = W_{R*NS}^p,
+//     X_q = sum_r a_r (w W_R^q)^r,   q = 0..R-1,
+// i.e. the polynomial sum_r a_r z^r at the R points w W_R^q.  Splitting r
+// into even and odd terms gives X_q = E_q + w W_R^q O_q and
+// X_{q+R/2} = E_q - w W_R^q O_q, where E and O are the same problem of size
+// R/2 for base w^2.  Each radix-2 step below costs six FMAs; the only
+// twiddles needed are powers w^(2^k) (squarings) times the constants W_R^q.
+
+// Hide a value from loop-invariant code motion: derived twiddles are cheaper
+// to recompute per use than to keep live across a whole FFT pair.
+__device__ __forceinline__ cf opaque(cf w) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y));
+  return w;
+}
+
+__device__ __forceinline__ cf csq(cf w) {
+  return make_float2(fmaf(w.x, w.x, -w.y * w.y), 2.0f * w.x * w.y);
+}
+
+// (a, b) <- (a + t b, a - t b) with six FMAs.
+__device__ __forceinline__ void bfly2(cf& a, cf& b, cf t) {
+  const float rx = fmaf(-b.y, t.y, fmaf(b.x, t.x, a.x));
+  const float ry = fmaf(b.x, t.y, fmaf(b.y, t.x, a.y));
+  b = make_float2(fmaf(2.0f, a.x, -rx), fmaf(2.0f, a.y, -ry));
+  a = make_float2(rx, ry);
+}
+
+// w * W_R^q (W_R = exp(-2 pi i / R) forward, its conjugate inverse).
+template <int R, int Q, bool INV>
+__device__ __forceinline__ cf tw_const(cf w) {
+  constexpr int q = Q % R;
+  if constexpr (q == 0) return w;
+  else if constexpr (4 * q == R) return rot90<INV>(w);
+  else if constexpr (4 * q > R) return rot90<INV>(tw_const<R, q - R / 4, INV>(w));
+  else if constexpr (8 * q == R) return mul_w8<INV>(w);
+  else {
+    static_assert(R == 16 && (q == 1 || q == 3), "unsupported constant twiddle");
+    const float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f;
+    const cf k = (q == 1) ? make_float2(c1, INV ? s1 : -s1) : make_float2(s1, INV ? c1 : -c1);
+    return cmul(w, k);
+  }
+}
+
+template <int R, bool INV>
+struct Dit {
+  static __device__ __forceinline__ void run(cf* a, cf w) {
+    if constexpr (R == 1) {
+      return;
+    } else {
+      cf e[R / 2], o[R / 2];
+#pragma unroll
+      for (int r = 0; r < R / 2; ++r) { e[r] = a[2 * r]; o[r] = a[2 * r + 1]; }
+      if constexpr (R > 2) {
+        const cf w2 = csq(w);
+        Dit<R / 2, INV>::run(e, w2);
+        Dit<R / 2, INV>::run(o, w2);
+      }
+      twiddle_combine(e, o, w, std::make_integer_sequence<int, R / 2>{});
+#pragma unroll
+      for (int q = 0; q < R / 2; ++q) { a[q] = e[q]; a[q + R / 2] = o[q]; }
+    }
+  }
+  template <int... Q>
+  static __device__ __forceinline__ void twiddle_combine(cf* e, cf* o, cf w, std::integer_sequence<int, Q...>) {
+    (bfly2(e[Q], o[Q], tw_const<R, Q, INV>(w)), ...);
+  }
+};
+
+// One butterfly of a twiddled stage: a[r] in, X_q out (natural order).
+template <int R, bool INV>
+__device__ __forceinline__ void bfly_tw(cf* a, cf w) {
+  Dit<R, INV>::run(a, INV ? cconj(w) : w);
+}
+
+// b * s^i for a compile-time i < E (binary powers of s, CSE'd across i).
+template <int E>
+__device__ __forceinline__ cf step_power(cf b, cf s, int i) {
+  cf p = b, sp = s;
+#pragma unroll
+  for (int bit = 1; bit < E; bit <<= 1) {
+    if (i & bit) p = cmul(p, sp);
+    if ((bit << 1) < E) sp = csq(sp);
+  }
+  return p;
+}
+
+// ---------------------------------------------------------------- LDS layouts
+
+// One FFT per row, point index fastest, one pad slot per 16 points (spreads
+// the strided Stockham writes over the banks).
+struct RowLds {
+  cf* base;
+  static constexpr __host__ __device__ int padded(int npt) { return npt + npt / 16; }
+  __device__ __forceinline__ cf& operator()(int i) const { return base[i + (i >> 4)]; }
+};
+
+// Many FFTs side by side, FFT instance fastest: element i of instance c sits
+// at i*NB + c.  Lanes that differ in c touch consecutive words.
+template <int NB>
+struct ColLds {
+  cf* base;  // already offset by the instance index c
+  __device__ __forceinline__ cf& operator()(int i) const { return base[i * NB]; }
+};
+
+// ---------------------------------------------------------------- stages
+
+template <int... Rs>
+struct Radices {};
+
+// Butterflies of the first stage (NS = 1: no twiddles).  u[m + r*BPT] holds
+// leg r of butterfly m on entry and output q at u[m + q*BPT] on exit.
+template <int E, int R, bool INV>
+__device__ __forceinline__ void stage_first(cf (&u)[E]) {
+  constexpr int BPT = E / R;
+  static_assert(E % R == 0, "radix must divide the per-thread count");
+#pragma unroll
+  for (int m = 0; m < BPT; ++m) {
+    cf a[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) a[r] = u[m + r * BPT];
+    dft<R, INV>(a);
+#pragma unroll
+    for (int q = 0; q < R; ++q) u[m + q * BPT] = a[q];
+  }
+}
+
+template <int E, int R, bool INV>
+__device__ __forceinline__ void stage_twiddled(cf (&u)[E], const cf* tw) {
+  constexpr int BPT = E / R;
+  static_assert(E % R == 0, "radix must divide the per-thread count");
+#pragma unroll
+  for (int m = 0; m < BPT; ++m) {
+    cf a[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) a[r] = u[m + r * BPT];
+    bfly_tw<R, INV>(a, opaque(tw[m]));
+#pragma unroll
+    for (int q = 0; q < R; ++q) u[m + q * BPT] = a[q];
+  }
+}
+
+template <int NPT, int E, int R, int NS, class Lds>
+__device__ __forceinline__ void stage_store(const cf (&u)[E], const Lds& lds, int j) {
+  constexpr int BPT = E / R;
+#pragma unroll
+  for (int m = 0; m < BPT; ++m) {
+    const int beta = j + m * (NPT / E);
+    const int base = (beta / NS) * NS * R + (beta & (NS - 1));
+#pragma unroll
+    for (int q = 0; q < R; ++q) lds(base + q * NS) = u[m + q * BPT];
+  }
+}
+
+template <int NPT, int E, int R, class Lds>
+__device__ __forceinline__ void stage_load(cf (&u)[E], const Lds& lds, int j) {
+  constexpr int BPT = E / R;
+#pragma unroll
+  for (int m = 0; m < BPT; ++m) {
+    const int beta = j + m * (NPT / E);
+#pragma unroll
+    for (int r = 0; r < R; ++r) u[m + r * BPT] = lds(beta + r * (NPT / R));
+  }
+}
+
+// Base twiddles w = W_{R*NS}^{beta mod NS} of every later stage, in stage order.
+template <int NPT, int E, int NS, int OFF, int R, int... Rest>
+__device__ __forceinline__ void tw_init(cf* tw, int j) {
+  constexpr int BPT = E / R;
+#pragma unroll
+  for (int m = 0; m < BPT; ++m) {
+    const uint32_t beta = (uint32_t)j + (uint32_t)m * (NPT / E);
+    tw[OFF + m] = twiddle<false>(beta & (NS - 1), (uint32_t)(R * NS));
+  }
+  if constexpr (sizeof...(Rest) > 0) tw_init<NPT, E, NS * R, OFF + BPT, Rest...>(tw, j);
+}
+
+template <int NPT, int E, bool INV, int NS, int OFF, class Lds, int R, int... Rest>
+__device__ __forceinline__ void fft_tail(cf (&u)[E], const Lds& lds, int j, const cf* tw) {
+  stage_load<NPT, E, R>(u, lds, j);
+  stage_twiddled<E, R, INV>(u, tw + OFF);
+  if constexpr (sizeof...(Rest) > 0) {
+    __syncthreads();                       // all reads of this stage done
+    stage_store<NPT, E, R, NS>(u, lds, j);
+    __syncthreads();                       // writes visible to the next stage
+    fft_tail<NPT, E, INV, NS * R, OFF + E / R, Lds, Rest...>(u, lds, j, tw);
+  }
+}
+
+template <int NPT, int E, class Rad> struct BlockFFT;
+
+// Complex FFT of NPT points by the threads of a workgroup, E points each,
+// radix sequence R0, Rs...  Registers in and out in the invariant layout.
+// Every thread of the workgroup must call run() (it has barriers when there
+// is more than one stage).  On return other threads may still read LDS:
+// callers put a barrier before their next LDS write.
+template <int NPT, int E, int R0, int... Rs>
+struct BlockFFT<NPT, E, Radices<R0, Rs...>> {
+  static constexpr int NTW = (0 + ... + (E / Rs));
+  cf tw[NTW > 0 ? NTW : 1];
+
+  __device__ __forceinline__ void init(int j) {
+    if constexpr (NTW > 0) tw_init<NPT, E, R0, 0, Rs...>(tw, j);
+  }
+
+  template <bool INV, class Lds>
+  __device__ __forceinline__ void run(cf (&u)[E], const Lds& lds, int j) const {
+    stage_first<E, R0, INV>(u);
+    if constexpr (sizeof...(Rs) > 0) {
+      __syncthreads();
+      stage_store<NPT, E, R0, 1>(u, lds, j);
+      __syncthreads();
+      fft_tail<NPT, E, INV, R0, 0, Lds, Rs...>(u, lds, j, tw);
+    }
+  }
+};
+
+// Radix sequences per FFT length for 16 (or 8) points per thread.  First and
+// last radix equal E so a thread's register set stays put.
+template <int NPT> struct Plan16;
+template <> struct Plan16<16> { using R = Radices<16>; };
+template <> struct Plan16<32> { using R = Radices<16, 2>; };
+template <> struct Plan16<64> { using R = Radices<16, 4>; };
+template <> struct Plan16<128> { using R = Radices<16, 8>; };
+template <> struct Plan16<256> { using R = Radices<16, 16>; };
+template <> struct Plan16<512> { using R = Radices<16, 2, 16>; };
+template <> struct Plan16<1024> { using R = Radices<16, 4, 16>; };
+template <> struct Plan16<2048> { using R = Radices<16, 8, 16>; };
+template <> struct Plan16<4096> { using R = Radices<16, 16, 16>; };
+template <> struct Plan16<8192> { using R = Radices<16, 2, 16, 16>; };
+template <> struct Plan16<16384> { using R = Radices<16, 4, 16, 16>; };
+
+template <int NPT> struct Plan8;
+template <> struct Plan8<64> { using R = Radices<8, 8>; };
+template <> struct Plan8<128> { using R = Radices<8, 2, 8>; };
+template <> struct Plan8<256> { using R = Radices<8, 4, 8>; };
+template <> struct Plan8<512> { using R = Radices<8, 8, 8>; };
+
+// ---------------------------------------------------------------- I/O types
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays NaN (quieted).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int IOT> struct IO;
+template <> struct IO<0> {  // fp32
+  static __device__ __forceinline__ float ld(const void* p, int64_t i) {
+    return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+  }
+  static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    __builtin_nontemporal_store(v, static_cast<float*>(p) + i);
+  }
+};
+template <> struct IO<1> {  // bf16
+  static __device__ __forceinline__ float ld(const void* p, int64_t i) {
+    return bf16_bits_to_f32(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i));
+  }
+  static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    __builtin_nontemporal_store(f32_to_bf16_bits(v), static_cast<uint16_t*>(p) + i);
+  }
+};
+
+// ---------------------------------------------------------------- pairing
+
+// Two real sequences travel as one complex signal (real part a, imaginary
+// part b).  Pairs are either two batch rows of one channel (same filter) or,
+// for a leftover odd batch row, two channels of that row (different filters;
+// the spectra are separated with the conjugate-symmetry identity).
+struct Pair {
+  int64_t off_a, off_b;  // element offsets of the two [L] rows in [B][D][L]
+  int da, db;            // channels (filter index within an order)
+  bool has_b;            // false: the imaginary part is an all-zero row
+  bool same;             // both halves use the filter of channel da
+};
+
+__device__ __forceinline__ Pair decode_pair(int p, int B, int D, int64_t L, int n_batch_pairs,
+                                            int half_b) {
+  Pair r;
+  if (p < n_batch_pairs) {
+    const int d = p / half_b, q = p - d * half_b;
+    r.da = r.db = d;
+    r.off_a = ((int64_t)(2 * q) * D + d) * L;
+    r.off_b = ((int64_t)(2 * q + 1) * D + d) * L;
+    r.has_b = true;
+    r.same = true;
+  } else {
+    const int pc = p - n_batch_pairs;
+    r.da = 2 * pc;
+    r.db = 2 * pc + 1;
+    r.has_b = r.db < D;
+    if (!r.has_b) r.db = r.da;
+    r.same = !r.has_b;
+    r.off_a = ((int64_t)(B - 1) * D + r.da) * L;
+    r.off_b = ((int64_t)(B - 1) * D + r.db) * L;
+  }
+  return r;
+}
+
+// Y = Ga*A + i*Gb*B where Z = A + iB, A and B being spectra of real rows:
+// with Zm = Z(M-k): A = (Z + conj Zm)/2, iB = (Z - conj Zm)/2.
+__device__ __forceinline__ cf pair_multiply(cf z, cf zm, cf ga, cf gb) {
+  const cf s = make_float2(z.x + zm.x, z.y - zm.y);
+  const cf d = make_float2(z.x - zm.x, z.y + zm.y);
+  const cf y = cadd(cmul(ga, s), cmul(gb, d));
+  return cscale(y, 0.5f);
+}
+
+using XPtrs = XPtrsHost;
+
+}  // namespace hyena

@@ -1,0 +1,114 @@
+// kernels_filter.hip -- implicit filter generation and spectrum export.
+//
+// h_n[d](t) = Window_d(t) * FFN(e(t))[n*D + d] with the positional features
+// e(t) = [t/L, sin(2 pi k t/L), cos(2 pi k t/L)] and an exponential-decay
+// window exp(-alpha_d t / L) (jisaku.com glossary "Hyena（ハイエナ）", section
+// "暗黙的畳み込みフィルタ"; paper digest of Hyena Hierarchy, framework figure,
+// HyenaFilter node: positional encoding -> FFN -> window).  The FFN is
+// affine -> sin -> affine -> sin -> affine.
+#include "fft_engine.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+constexpr int kFgThreads = 256;
+constexpr int kFgChunk = 64;   // filter rows per block (layer 1-2 recomputed per chunk)
+
+template <int H>
+__global__ void __launch_bounds__(kFgThreads) k_filter_gen(FilterGenArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * kFgThreads + threadIdx.x;
+  if (t >= a.L) return;
+  const int K = a.K;
+  const float tl = (float)t / (float)a.L;
+  float es[kMaxFreq + 1], ec[kMaxFreq + 1];
+#pragma unroll
+  for (int k = 1; k <= kMaxFreq; ++k) {
+    es[k] = 0.f; ec[k] = 0.f;
+    if (k <= K) {
+      // phase k t / L reduced modulo 1 exactly in integers
+      const int64_t m = ((int64_t)k * t) % a.L;
+      sincospif(2.0f * (float)m / (float)a.L, &es[k], &ec[k]);
+    }
+  }
+  const int F = 1 + 2 * K;
+  float a1[H];
+#pragma unroll
+  for (int q = 0; q < H; ++q) {
+    const float* w = a.W1 + q * F;
+    float acc = a.b1 ? a.b1[q] : 0.f;
+    acc = fmaf(w[0], tl, acc);
+#pragma unroll
+    for (int k = 1; k <= kMaxFreq; ++k) {
+      if (k <= K) {
+        acc = fmaf(w[k], es[k], acc);
+        acc = fmaf(w[K + k], ec[k], acc);
+      }
+    }
+    a1[q] = sinf(acc);
+  }
+  float a2[H];
+#pragma unroll
+  for (int q = 0; q < H; ++q) {
+    const float* w = a.W2 + q * H;
+    float acc = a.b2 ? a.b2[q] : 0.f;
+#pragma unroll
+    for (int m = 0; m < H; ++m) acc = fmaf(w[m], a1[m], acc);
+    a2[q] = sinf(acc);
+  }
+  const int NF = a.N * a.D;
+  const int f0 = blockIdx.y * kFgChunk;
+  const int f1 = (f0 + kFgChunk < NF) ? f0 + kFgChunk : NF;
+  for (int f = f0; f < f1; ++f) {
+    const float* w = a.W3 + (int64_t)f * H;
+    float acc = a.b3 ? a.b3[f] : 0.f;
+#pragma unroll
+    for (int m = 0; m < H; ++m) acc = fmaf(w[m], a2[m], acc);
+    const int d = f % a.D;
+    const float win = expf(-a.alpha[d] * tl);
+    a.h[(int64_t)f * a.L + t] = win * acc;
+  }
+}
+
+hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s) {
+  const int NF = a.N * a.D;
+  const dim3 grid((unsigned)((a.L + kFgThreads - 1) / kFgThreads), (unsigned)((NF + kFgChunk - 1) / kFgChunk));
+  const dim3 block(kFgThreads);
+  switch (a.H) {
+    case 8: hipLaunchKernelGGL((k_filter_gen<8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_filter_gen<16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_filter_gen<32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_filter_gen<64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_filter_gen<128>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Library spectrum layout -> natural order, undoing the 1/M scale.
+__global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict__ out, int NF, int64_t M,
+                                  int path, int n1, int n2, int64_t stride) {
+  const int64_t half = M / 2 + 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)NF * half) return;
+  const int64_t f = idx / half, k = idx - f * half;
+  int64_t src;
+  if (path == PATH_SINGLE) {
+    src = k;
+  } else {
+    const int64_t k1 = k % n1, k2 = k / n1;
+    src = k1 * (n2 / 2 + 1) + k2;
+  }
+  const cf g = spec[f * stride + src];
+  out[2 * idx] = g.x * (float)M;
+  out[2 * idx + 1] = g.y * (float)M;
+}
+
+hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s) {
+  const int64_t total = (int64_t)NF * (p.M / 2 + 1);
+  const int threads = 256;
+  hipLaunchKernelGGL(k_spectrum_export, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s,
+                     (const cf*)spec, out, NF, p.M, p.path, p.n1, p.n2, p.spec_stride);
+  return hipGetLastError();
+}
+
+}  // namespace hyena

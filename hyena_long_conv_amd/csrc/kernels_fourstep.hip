@@ -1,0 +1,348 @@
+// kernels_fourstep.hip -- multi-pass Hyena forward and filter spectrum for
+// FFT lengths too long for one workgroup's LDS.
+//
+// The M-point DFT is factored as M = n1 * n2 (Bailey's four-step): with time
+// index t = n2*i1 + i2 and frequency index k = k1 + n1*k2,
+//   A[k1][i2]  = sum_{i1} z[n2*i1 + i2] W_{n1}^{i1 k1}          (column pass)
+//   X[k1+n1 k2] = sum_{i2} A[k1][i2] W_M^{i2 k1} W_{n2}^{i2 k2}  (row pass)
+// and the inverse runs the same steps backwards with conjugate twiddles.
+// Per order the row pass does row FFT -> spectral product -> inverse row
+// FFT in one kernel, and the column pass does inverse column FFT -> gate with
+// x_n -> forward column FFT of the next order in one kernel, so each order
+// costs two passes over an M-point intermediate per row pair.  Row k1 and
+// row n1-k1 hold mirror bins (k and M-k), so each row workgroup takes such a
+// pair of rows; rows 0 and n1/2 are their own mirrors and go together.
+//
+// Long convolution by FFT with zero padding (jisaku.com glossary
+// "Hyena（ハイエナ）", section "計算効率"; gist.science HyenaND summary, section
+// "手法: HyenaND", boundary handling); gating recurrence of the Hyena
+// Hierarchy explainer, section "Hyena 演算子の形".
+#include "fft_engine.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+
+template <int N1> struct ColCfg {
+  static constexpr int E = 16;
+  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 512 ? 32 : 16;
+  static constexpr int T = W * N1 / E;
+  static constexpr bool LDS = N1 > E;
+  using R = typename Plan16<N1>::R;
+};
+
+template <int N2> struct RowCfg {
+  static constexpr int E = 16;
+  static constexpr int TPR = N2 / E;  // threads per row
+  static constexpr int T = 2 * TPR;
+  using R = typename Plan16<N2>::R;
+};
+
+enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3 };
+enum { ROW_CONV = 0, ROW_SPEC = 1 };
+
+struct ColArgs {
+  const void* v;       // FIRST: z_1 rows
+  const void* xg;      // MID/LAST: gate x_n
+  void* y;             // LAST: output
+  const float* h;      // SPEC: filters [NF][L]
+  cf* work;            // [group][n1][n2]
+  int B, D, NF;
+  int64_t L;
+  int n2;
+  int p0;              // first pair of this launch
+  int n_batch_pairs, half_b;
+  int n_col_blocks;
+};
+
+template <int N1, int IOT, int KIND>
+__global__ void __launch_bounds__(ColCfg<N1>::T) k_col(ColArgs a) {
+  using C = ColCfg<N1>;
+  constexpr int E = C::E, W = C::W, S1 = N1 / E;
+  __shared__ cf smem[C::LDS ? N1 * W : 1];
+  const int c = threadIdx.x % W, j = threadIdx.x / W;
+  const int g = blockIdx.x / a.n_col_blocks, cb = blockIdx.x - g * a.n_col_blocks;
+  const int col = cb * W + c;
+  const bool valid = col < a.n2;
+  const int64_t M = (int64_t)N1 * a.n2;
+  cf* buf = a.work + (int64_t)g * M;
+  const ColLds<W> lds{smem + c};
+  BlockFFT<N1, E, typename C::R> fft;
+  fft.init(j);
+  cf u[E];
+
+  int64_t off_a, off_b;
+  bool has_b;
+  if constexpr (KIND == COL_SPEC) {
+    const int fa = 2 * (a.p0 + g);
+    has_b = fa + 1 < a.NF;
+    off_a = (int64_t)fa * a.L;
+    off_b = off_a + a.L;
+  } else {
+    const Pair pr = decode_pair(a.p0 + g, a.B, a.D, a.L, a.n_batch_pairs, a.half_b);
+    off_a = pr.off_a; off_b = pr.off_b; has_b = pr.has_b;
+  }
+
+  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t t = (int64_t)a.n2 * (j + i * S1) + col;
+      u[i] = make_float2(0.f, 0.f);
+      if (valid && t < a.L) {
+        if constexpr (KIND == COL_SPEC) {
+          u[i].x = a.h[off_a + t];
+          if (has_b) u[i].y = a.h[off_b + t];
+        } else {
+          u[i].x = IO<IOT>::ld(a.v, off_a + t);
+          if (has_b) u[i].y = IO<IOT>::ld(a.v, off_b + t);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      u[i] = valid ? buf[(int64_t)(j + i * S1) * a.n2 + col] : make_float2(0.f, 0.f);
+    fft.template run<true>(u, lds, j);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t t = (int64_t)a.n2 * (j + i * S1) + col;
+      float za = 0.f, zb = 0.f;
+      if (valid && t < a.L) {
+        za = IO<IOT>::ld(a.xg, off_a + t) * u[i].x;
+        if (has_b) zb = IO<IOT>::ld(a.xg, off_b + t) * u[i].y;
+        if constexpr (KIND == COL_LAST) {
+          IO<IOT>::st(a.y, off_a + t, za);
+          if (has_b) IO<IOT>::st(a.y, off_b + t, zb);
+        }
+      }
+      u[i] = make_float2(za, zb);
+    }
+  }
+  if constexpr (KIND != COL_LAST) {
+    fft.template run<false>(u, lds, j);
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) buf[(int64_t)(j + i * S1) * a.n2 + col] = u[i];
+    }
+  }
+}
+
+struct RowArgs {
+  cf* work;
+  const cf* spec;      // CONV: spectrum (read)
+  cf* spec_out;        // SPEC: spectrum (written)
+  int n1;
+  int64_t spec_stride;
+  int order;           // CONV: order n (filters n*D + d)
+  int B, D, NF;
+  int64_t L;
+  int p0;
+  int n_batch_pairs, half_b;
+  int n_row_pairs;     // n1 / 2
+};
+
+template <int N2, int KIND>
+__global__ void __launch_bounds__(RowCfg<N2>::T) k_row(RowArgs a) {
+  using C = RowCfg<N2>;
+  constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E, HALF = N2 / 2 + 1;
+  constexpr int PADN = RowLds::padded(N2);
+  __shared__ cf smem[2 * PADN];
+  const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
+  const int g = blockIdx.x / a.n_row_pairs, w = blockIdx.x - g * a.n_row_pairs;
+  const int n1 = a.n1;
+  const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
+  const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
+  const int mb = self_mirror ? b : 1 - b;          // row holding the mirror bins
+  const int k1m = (k1 == 0) ? 0 : n1 - k1;         // its k1
+  const uint32_t M = (uint32_t)n1 * (uint32_t)N2;
+  cf* row = a.work + (int64_t)g * M + (int64_t)k1 * N2;
+  const RowLds lds{smem + b * PADN};
+  const RowLds ldsm{smem + mb * PADN};
+  BlockFFT<N2, E, typename C::R> fft;
+  fft.init(j);
+  cf u[E];
+
+  // four-step twiddle W_M^{k1 i2} for i2 = j + i*S2: base W_M^{k1 j} times
+  // powers of the step W_M^{k1 S2}
+  const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, M);
+  const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, M);
+#pragma unroll
+  for (int i = 0; i < E; ++i) u[i] = cmul(row[j + i * S2], step_power<E>(tb, ts, i));
+  fft.template run<false>(u, lds, j);
+
+  if constexpr (KIND == ROW_SPEC) {
+    const int fa = 2 * (a.p0 + g);
+    const bool has_b = fa + 1 < a.NF;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+    __syncthreads();
+    const float sc = 0.5f / (float)M;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k2 = j + i * S2;
+      if (k2 < HALF) {
+        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+        const cf zm = ldsm(k2m), z = u[i];
+        const int64_t o = (int64_t)k1 * HALF + k2;
+        a.spec_out[(int64_t)fa * a.spec_stride + o] = make_float2((z.x + zm.x) * sc, (z.y - zm.y) * sc);
+        if (has_b)
+          a.spec_out[(int64_t)(fa + 1) * a.spec_stride + o] = make_float2((z.y + zm.y) * sc, (zm.x - z.x) * sc);
+      }
+    }
+  } else {
+    const Pair pr = decode_pair(a.p0 + g, a.B, a.D, a.L, a.n_batch_pairs, a.half_b);
+    const cf* ga = a.spec + (int64_t)(a.order * a.D + pr.da) * a.spec_stride;
+    const cf* gb = a.spec + (int64_t)(a.order * a.D + pr.db) * a.spec_stride;
+    if (pr.same) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int k2 = j + i * S2;
+        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+        const cf g0 = (k2 < HALF) ? ga[(int64_t)k1 * HALF + k2] : cconj(ga[(int64_t)k1m * HALF + k2m]);
+        u[i] = cmul(g0, u[i]);
+      }
+    } else {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int k2 = j + i * S2;
+        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+        const cf zm = ldsm(k2m);
+        cf gak, gbk;
+        if (k2 < HALF) {
+          gak = ga[(int64_t)k1 * HALF + k2];
+          gbk = gb[(int64_t)k1 * HALF + k2];
+        } else {
+          gak = cconj(ga[(int64_t)k1m * HALF + k2m]);
+          gbk = cconj(gb[(int64_t)k1m * HALF + k2m]);
+        }
+        u[i] = pair_multiply(u[i], zm, gak, gbk);
+      }
+    }
+    fft.template run<true>(u, lds, j);
+#pragma unroll
+    for (int i = 0; i < E; ++i) row[j + i * S2] = cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i));
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int N1>
+static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+  const dim3 grid(groups * c.n_col_blocks), block(ColCfg<N1>::T);
+  if (kind == COL_SPEC) {
+    hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC>), grid, block, 0, s, c);
+  } else if (io == 0) {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST>), grid, block, 0, s, c);
+  } else {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST>), grid, block, 0, s, c);
+  }
+  return hipGetLastError();
+}
+
+static int col_width(int n1) {
+  switch (n1) {
+    case 16: return ColCfg<16>::W;
+    case 32: return ColCfg<32>::W;
+    case 64: return ColCfg<64>::W;
+    case 128: return ColCfg<128>::W;
+    case 256: return ColCfg<256>::W;
+    case 512: return ColCfg<512>::W;
+    case 1024: return ColCfg<1024>::W;
+  }
+  return 0;
+}
+
+static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+  switch (n1) {
+    case 16: return launch_col<16>(kind, io, c, groups, s);
+    case 32: return launch_col<32>(kind, io, c, groups, s);
+    case 64: return launch_col<64>(kind, io, c, groups, s);
+    case 128: return launch_col<128>(kind, io, c, groups, s);
+    case 256: return launch_col<256>(kind, io, c, groups, s);
+    case 512: return launch_col<512>(kind, io, c, groups, s);
+    case 1024: return launch_col<1024>(kind, io, c, groups, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int N2>
+static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t s) {
+  const dim3 grid(groups * r.n_row_pairs), block(RowCfg<N2>::T);
+  if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, block, 0, s, r);
+  else hipLaunchKernelGGL((k_row<N2, ROW_CONV>), grid, block, 0, s, r);
+  return hipGetLastError();
+}
+
+static hipError_t dispatch_row(int n2, int kind, const RowArgs& r, int groups, hipStream_t s) {
+  switch (n2) {
+    case 64: return launch_row<64>(kind, r, groups, s);
+    case 128: return launch_row<128>(kind, r, groups, s);
+    case 256: return launch_row<256>(kind, r, groups, s);
+    case 512: return launch_row<512>(kind, r, groups, s);
+    case 1024: return launch_row<1024>(kind, r, groups, s);
+    case 2048: return launch_row<2048>(kind, r, groups, s);
+    case 4096: return launch_row<4096>(kind, r, groups, s);
+    case 8192: return launch_row<8192>(kind, r, groups, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s) {
+  const int W = col_width(p.n1);
+  if (W == 0) return hipErrorInvalidValue;
+  ColArgs c{};
+  c.v = a.v; c.y = a.y; c.h = nullptr; c.work = (cf*)a.work;
+  c.B = a.B; c.D = a.D; c.NF = a.N * a.D; c.L = a.L; c.n2 = p.n2;
+  c.n_batch_pairs = a.n_batch_pairs; c.half_b = a.half_b;
+  c.n_col_blocks = (p.n2 + W - 1) / W;
+  RowArgs r{};
+  r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
+  r.n1 = p.n1; r.spec_stride = a.spec_stride; r.B = a.B; r.D = a.D; r.NF = a.N * a.D; r.L = a.L;
+  r.n_batch_pairs = a.n_batch_pairs; r.half_b = a.half_b; r.n_row_pairs = p.n1 / 2;
+  for (int p0 = 0; p0 < a.n_pairs; p0 += a.pairs_per_group) {
+    const int groups = (a.n_pairs - p0 < a.pairs_per_group) ? a.n_pairs - p0 : a.pairs_per_group;
+    c.p0 = p0; r.p0 = p0;
+    hipError_t e = dispatch_col(p.n1, COL_FIRST, a.io, c, groups, s);
+    if (e != hipSuccess) return e;
+    for (int n = 0; n < a.N; ++n) {
+      r.order = n;
+      e = dispatch_row(p.n2, ROW_CONV, r, groups, s);
+      if (e != hipSuccess) return e;
+      c.xg = a.x.p[n];
+      e = dispatch_col(p.n1, n == a.N - 1 ? COL_LAST : COL_MID, a.io, c, groups, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s) {
+  const int W = col_width(p.n1);
+  if (W == 0) return hipErrorInvalidValue;
+  const int n_fpairs = (a.NF + 1) / 2;
+  ColArgs c{};
+  c.h = a.h; c.work = (cf*)a.work; c.NF = a.NF; c.L = a.L; c.n2 = p.n2;
+  c.n_col_blocks = (p.n2 + W - 1) / W;
+  RowArgs r{};
+  r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = p.n1; r.spec_stride = a.spec_stride;
+  r.NF = a.NF; r.L = a.L; r.n_row_pairs = p.n1 / 2;
+  for (int p0 = 0; p0 < n_fpairs; p0 += a.pairs_per_group) {
+    const int groups = (n_fpairs - p0 < a.pairs_per_group) ? n_fpairs - p0 : a.pairs_per_group;
+    c.p0 = p0; r.p0 = p0;
+    hipError_t e = dispatch_col(p.n1, COL_SPEC, 0, c, groups, s);
+    if (e != hipSuccess) return e;
+    e = dispatch_row(p.n2, ROW_SPEC, r, groups, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace hyena

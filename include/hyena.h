@@ -1,0 +1,161 @@
+/*
+ * hyena.h -- C ABI of the MI355X (gfx950) Hyena order-N forward library.
+ *
+ * The operator (Hyena Hierarchy explainer, abeam-guide-lp.pages.dev, section
+ * "Hyena 演算子の形"; paper digest, irregular6612.github.io, section
+ * "방법 (Method)", framework figure):
+ *
+ *     z_1 = v,   z_{n+1} = x_n * (h_n conv z_n)  (n = 1..N),   y = z_{N+1}
+ *
+ * where "*" is the elementwise product and "conv" the causal long
+ * convolution c[t] = sum_{k<=t} h[k] z[t-k] over the full length L
+ * (homemade-llm "02. 3つの Hyena 演算子", section 4, causal FIR equation).
+ * The convolution is evaluated by FFT with zero padding to at least 2L
+ * (jisaku.com glossary "Hyena（ハイエナ）", section "計算効率"; gist.science
+ * HyenaND summary, section "手法: HyenaND", boundary handling).  The filters
+ * are generated implicitly as Window(t) * FFN(t/L, sin, cos) (jisaku.com
+ * glossary, section "暗黙的畳み込みフィルタ").
+ *
+ * Conventions shared by every call:
+ *   - Device pointers point to memory of the current HIP device; the caller
+ *     allocates and frees all of it.  The library never allocates device
+ *     memory, keeps no global state, and is reentrant.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns; results are ready after the stream syncs.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and returned as a status; nothing is written in that case.  A failed
+ *     kernel launch returns HYENA_ERR_HIP.  Device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *   - Activations v, x_n and y are contiguous [B][D][L] arrays (time
+ *     fastest) in the I/O dtype; device pointers must be 16-byte aligned.
+ *   - Test hook: the environment variable HYENA_FORCE_PATH ("single" or
+ *     "fourstep") and HYENA_FOURSTEP_N1 (a power of two) override the
+ *     planner.  Both the spectrum and the forward read them at each call,
+ *     so set them identically for both.
+ */
+#ifndef HYENA_MI355X_H
+#define HYENA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HYENA_OK = 0,
+  HYENA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  HYENA_ERR_SHAPE = 2,       /* a size is <= 0 or out of the supported range     */
+  HYENA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement    */
+  HYENA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned          */
+  HYENA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  HYENA_ERR_ALIAS = 6,       /* the output overlaps an input                     */
+  HYENA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed       */
+} hyena_status;
+
+typedef enum { HYENA_FP32 = 0, HYENA_BF16 = 1 } hyena_dtype;
+
+typedef enum { HYENA_PATH_SINGLE = 1, HYENA_PATH_FOURSTEP = 2 } hyena_path;
+
+/* Limits of this build. */
+#define HYENA_MAX_ORDER 8          /* N in 1..8                                 */
+#define HYENA_MAX_L (1LL << 22)    /* L in 1..2^22                              */
+#define HYENA_MAX_FREQ 16          /* K in 0..16 (positional features 1+2K)     */
+
+/*
+ * Implicit filter generator weights (jisaku.com glossary, section
+ * "暗黙的畳み込みフィルタ"; paper digest figure, HyenaFilter node).  All device
+ * pointers, fp32, row-major [out][in]:
+ *   W1 [H][1+2K], b1 [H]; W2 [H][H], b2 [H]; W3 [N*D][H], b3 [N*D]; alpha [D].
+ * b1, b2, b3 may be NULL (zero bias).  H must be one of 8, 16, 32, 64, 128.
+ */
+typedef struct {
+  int32_t D;      /* channels                                   */
+  int32_t N;      /* order (number of filters per channel)      */
+  int32_t K;      /* sin/cos frequencies; feature dim is 1+2K   */
+  int32_t H;      /* FFN hidden width                           */
+  const float* W1;
+  const float* b1;
+  const float* W2;
+  const float* b2;
+  const float* W3;
+  const float* b3;
+  const float* alpha;
+} hyena_filter_params;
+
+/* Planner result for a sequence length (host only, no GPU needed). */
+typedef struct {
+  int64_t L;            /* sequence length                                        */
+  int64_t M;            /* FFT length in complex points; M >= 2L                  */
+  int32_t path;         /* hyena_path                                             */
+  int32_t n1;           /* four-step: column FFT length (0 on the single path)    */
+  int32_t n2;           /* four-step: row FFT length (0 on the single path)       */
+  int32_t reserved;
+  int64_t spec_stride;  /* complex64 elements per (n, d) filter in the spectrum   */
+} hyena_plan_info;
+
+/* Fill *out with the plan the library uses for length L.
+ * Errors: NULL out -> HYENA_ERR_NULL; L outside 1..HYENA_MAX_L -> HYENA_ERR_SHAPE. */
+hyena_status hyena_plan(int64_t L, hyena_plan_info* out);
+
+/*
+ * hyena_filter_gen: h[n][d][t] = exp(-alpha_d * t / L) * o_{n*D+d}(t),
+ *   o(t) = W3 sin(W2 sin(W1 e(t) + b1) + b2) + b3,
+ *   e(t) = [t/L, sin(2 pi k t/L) (k=1..K), cos(2 pi k t/L) (k=1..K)].
+ * Output h: device fp32 [N][D][L], written completely.
+ * Errors: NULL p/h/weights -> NULL; bad D, N, K, H or L -> SHAPE / UNSUPPORTED.
+ */
+hyena_status hyena_filter_gen(const hyena_filter_params* p, int64_t L, float* h, void* stream);
+
+/* Bytes of the spectrum buffer for (D, N, L): N*D*spec_stride*8. -1 on bad sizes. */
+int64_t hyena_spectrum_bytes(int32_t D, int32_t N, int64_t L);
+
+/* Bytes of scratch hyena_filter_spectrum needs (0 on the single path). -1 on bad sizes. */
+int64_t hyena_spectrum_workspace_bytes(int32_t D, int32_t N, int64_t L);
+
+/*
+ * hyena_filter_spectrum: the DFT of each filter zero-padded to M points
+ * (first step of the FFT convolution applied to h; jisaku.com glossary,
+ * section "計算効率"), computed once and reused for any batch.
+ * In: h, device fp32 [N][D][L].  Out: spec, device, hyena_spectrum_bytes()
+ * bytes, in a library-defined order and scale (read it back in natural order
+ * with hyena_spectrum_export).  workspace: device scratch of at least
+ * hyena_spectrum_workspace_bytes() bytes (may be NULL when that is 0).
+ * Errors: NULL -> NULL; sizes -> SHAPE; alignment -> ALIGN; small workspace
+ * -> WORKSPACE; spec overlapping h -> ALIAS.
+ */
+hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t L, void* spec,
+                                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Natural-order copy of the spectrum: out[n][d][k][re,im] = sum_{t<L} h[n][d][t]
+ * exp(-2 pi i k t / M) for k = 0..M/2 (device fp32, N*D*(M/2+1)*2 floats).  For tests. */
+hyena_status hyena_spectrum_export(const void* spec, int32_t D, int32_t N, int64_t L, float* out,
+                                   void* stream);
+
+/* Bytes of scratch hyena_forward needs for this shape (0 on the single path). -1 on bad sizes. */
+int64_t hyena_forward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
+
+/*
+ * hyena_forward: y = z_{N+1} of the order-N recurrence above.
+ *   v        device [B][D][L], I/O dtype
+ *   x        HOST array of N device pointers, each [B][D][L], I/O dtype
+ *   spec     the spectrum hyena_filter_spectrum wrote for the same (D, N, L)
+ *   y        device [B][D][L], I/O dtype; must not overlap v, any x_n or spec
+ *   io       HYENA_FP32, or HYENA_BF16 (bf16 loads widened exactly, all
+ *            arithmetic fp32, y rounded to nearest even)
+ *   workspace device scratch of hyena_forward_workspace_bytes() bytes
+ * Errors: NULL -> NULL; sizes -> SHAPE; N > HYENA_MAX_ORDER -> UNSUPPORTED;
+ * alignment -> ALIGN; workspace -> WORKSPACE; y overlapping an input -> ALIAS.
+ */
+hyena_status hyena_forward(const void* v, const void* const* x, const void* spec, void* y,
+                           int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
+                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* hyena_status_str(hyena_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_MI355X_H */

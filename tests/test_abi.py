@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/hyena.h declares, plans lengths as documented, and rejects bad
+arguments with status codes before anything touches a GPU.  Runs on CPU."""
+import ctypes
+import os
+
+import pytest
+
+import hyena_long_conv_amd as H
+
+pytestmark = pytest.mark.skipif(not os.path.exists(H.LIB_PATH), reason="library not built")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+vp = ctypes.c_void_p
+
+
+def test_exports_every_header_symbol():
+    names = H.header_functions()
+    assert {"hyena_forward", "hyena_filter_gen", "hyena_filter_spectrum", "hyena_plan"} <= set(names)
+    lib = ctypes.CDLL(H.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = H.lib()
+    for code in range(8):
+        assert lib.hyena_status_str(code)
+    assert lib.hyena_status_str(0) == b"ok"
+
+
+@pytest.mark.parametrize("L,M,path", [(1, 64, "single"), (17, 64, "single"), (32, 64, "single"),
+                                      (33, 128, "single"), (256, 512, "single"), (1000, 2048, "single"),
+                                      (2048, 4096, "single"), (8192, 16384, "single"),
+                                      (8193, 32768, "fourstep"), (65536, 131072, "fourstep"),
+                                      (100000, 262144, "fourstep"), (131072, 262144, "fourstep"),
+                                      (1 << 20, 1 << 21, "fourstep"), (1 << 22, 1 << 23, "fourstep")])
+def test_plan_lengths(L, M, path):
+    p = H.plan(L)
+    assert p["M"] == M and p["path"] == path
+    assert p["M"] >= 2 * L - 1
+    if path == "fourstep":
+        assert p["n1"] * p["n2"] == M and 16 <= p["n1"] <= 1024 and 64 <= p["n2"] <= 8192
+        assert p["spec_stride"] >= p["n1"] * (p["n2"] // 2 + 1)
+    else:
+        assert p["spec_stride"] >= M // 2 + 1
+    assert p["spec_stride"] % 16 == 0
+
+
+def test_plan_forced_paths(monkeypatch):
+    monkeypatch.setenv("HYENA_FORCE_PATH", "fourstep")
+    p = H.plan(300)
+    assert p["path"] == "fourstep" and p["M"] >= 600 and p["n1"] * p["n2"] == p["M"]
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "64")
+    p = H.plan(300)
+    assert p["n1"] == 64 and p["n2"] >= 64
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "48")          # not a power of two
+    with pytest.raises(H.HyenaError):
+        H.plan(300)
+    monkeypatch.delenv("HYENA_FOURSTEP_N1")
+    monkeypatch.setenv("HYENA_FORCE_PATH", "single")
+    assert H.plan(8192)["path"] == "single"
+    with pytest.raises(H.HyenaError):                       # too long for one workgroup
+        H.plan(8193)
+
+
+def test_plan_bad_lengths():
+    for L in (0, -1, (1 << 22) + 1):
+        with pytest.raises(H.HyenaError) as e:
+            H.plan(L)
+        assert e.value.code == SHAPE
+    assert H.lib().hyena_plan(16, None) == NULL
+
+
+def test_size_queries():
+    assert H.spectrum_bytes(768, 2, 2048) == 2 * 768 * H.plan(2048)["spec_stride"] * 8
+    assert H.spectrum_workspace_bytes(768, 2, 2048) == 0
+    assert H.forward_workspace_bytes(4, 768, 2, 2048) == 0
+    ws = H.forward_workspace_bytes(1, 768, 2, 65536, "bf16")
+    assert ws > 0 and ws % (H.plan(65536)["M"] * 8) == 0
+    assert H.spectrum_bytes(0, 2, 16) == -1 and H.spectrum_bytes(4, 9, 16) == -1
+    assert H.forward_workspace_bytes(0, 4, 2, 16) == -1
+
+
+# Fake, well-aligned, non-overlapping device addresses: every call below must
+# fail validation on the host, so none of them is ever dereferenced.
+A, Bp, C, Dp, Y, W = (0x10000000 * k for k in range(1, 7))
+
+
+def _fwd(v=A, x=(Bp, C), spec=Dp, y=Y, B=1, D=4, N=2, L=64, io=0, ws=0, wsb=0):
+    xs = None if x is None else (vp * max(1, len(x)))(*x)
+    return H.lib().hyena_forward(vp(v), xs, vp(spec), vp(y), B, D, N, L, io, vp(ws), wsb, None)
+
+
+def test_forward_rejects_bad_arguments():
+    assert _fwd(v=0) == NULL
+    assert _fwd(x=None) == NULL
+    assert _fwd(x=(Bp, 0)) == NULL
+    assert _fwd(spec=0) == NULL
+    assert _fwd(y=0) == NULL
+    assert _fwd(B=0) == SHAPE
+    assert _fwd(D=0) == SHAPE
+    assert _fwd(N=0, x=(Bp,)) == SHAPE
+    assert _fwd(L=0) == SHAPE
+    assert _fwd(L=(1 << 22) + 1) == SHAPE
+    assert _fwd(N=9, x=tuple(Bp + 0x1000000 * i for i in range(9))) == UNSUP
+    assert _fwd(io=7) == UNSUP
+    assert _fwd(v=A + 4) == ALIGN
+    assert _fwd(x=(Bp, C + 8)) == ALIGN
+    assert _fwd(y=Y + 2) == ALIGN
+    assert _fwd(spec=Dp + 4) == ALIGN
+    assert _fwd(y=A) == ALIAS                       # y == v
+    assert _fwd(y=C + 64) == ALIAS                  # y inside x_2
+    assert _fwd(y=Dp + 16) == ALIAS                 # y inside the spectrum
+    # four-step path needs a workspace
+    assert _fwd(L=65536, ws=0, wsb=0) == WS
+    assert _fwd(L=65536, ws=W, wsb=1024) == WS
+    assert _fwd(L=65536, ws=A, wsb=1 << 24, y=Y) == ALIAS
+
+
+def test_spectrum_and_filter_gen_reject_bad_arguments():
+    lib = H.lib()
+    assert lib.hyena_filter_spectrum(None, 4, 2, 64, vp(Dp), None, 0, None) == NULL
+    assert lib.hyena_filter_spectrum(vp(A), 4, 2, 64, None, None, 0, None) == NULL
+    assert lib.hyena_filter_spectrum(vp(A), 0, 2, 64, vp(Dp), None, 0, None) == SHAPE
+    assert lib.hyena_filter_spectrum(vp(A), 4, 9, 64, vp(Dp), None, 0, None) == UNSUP
+    assert lib.hyena_filter_spectrum(vp(A + 4), 4, 2, 64, vp(Dp), None, 0, None) == ALIGN
+    assert lib.hyena_filter_spectrum(vp(A), 4, 2, 64, vp(A + 256), None, 0, None) == ALIAS
+    assert lib.hyena_filter_spectrum(vp(A), 4, 2, 65536, vp(Dp), None, 0, None) == WS
+    assert lib.hyena_spectrum_export(None, 4, 2, 64, vp(Y), None) == NULL
+    assert lib.hyena_spectrum_export(vp(Dp), 4, 2, 64, vp(Dp), None) == ALIAS
+    p = H.FilterParams(4, 2, 8, 64, A, 0, Bp, 0, C, 0, Dp)
+    assert lib.hyena_filter_gen(ctypes.byref(p), 64, None, None) == NULL
+    assert lib.hyena_filter_gen(None, 64, vp(Y), None) == NULL
+    assert lib.hyena_filter_gen(ctypes.byref(H.FilterParams(4, 2, 8, 64, 0, 0, Bp, 0, C, 0, Dp)), 64, vp(Y), None) == NULL
+    assert lib.hyena_filter_gen(ctypes.byref(H.FilterParams(4, 2, 8, 48, A, 0, Bp, 0, C, 0, Dp)), 64, vp(Y), None) == UNSUP
+    assert lib.hyena_filter_gen(ctypes.byref(H.FilterParams(4, 2, 17, 64, A, 0, Bp, 0, C, 0, Dp)), 64, vp(Y), None) == SHAPE
+    assert lib.hyena_filter_gen(ctypes.byref(p), 0, vp(Y), None) == SHAPE
+    assert lib.hyena_filter_gen(ctypes.byref(p), 64, vp(Y + 4), None) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(H, "_lib", None)
+    monkeypatch.setattr(H, "LIB_PATH", "/nonexistent/libhyena_mi355x.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        H.lib()
