@@ -1,0 +1,235 @@
+"""Benchmark of the Hyena order-N forward (hyena_forward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
+
+A step is one hyena_forward over one batch of synthetic inputs already
+resident in HBM (v, x_1..x_N and the precomputed filter spectrum).  Inputs
+rotate over several independent sets so the working set exceeds the 256 MB
+Infinity Cache and every step reads from HBM.  Prints one JSON line with
+channel-tokens/s (B*D*L per second), the roofline of the forward kernel and
+the float64 CPU oracle timed on a bounded sample on the host cores.
+
+The default workload is the 2K-context shape (order 2, B=4, D=768, L=2048,
+fp32); --config selects the other shapes (C1, C3, C4, C5a, C5b).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12                  # B/s, MI355X HBM3E
+# Non-packed FP32 VALU: 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz.
+ALU_PEAK = 256 * 4 * 16 * 2 * 2.4e9
+ALU_PEAK_PACKED = 157.3e12        # vendor figure, needs packed-FP32 instructions (not used)
+MALL_BYTES = 256 << 20
+
+
+def min_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one forward: v, x_1..x_N, y in the I/O dtype
+    plus the spectrum read once as complex64 with L+1 bins per (n, d)."""
+    s = 4 if cfg.io == "fp32" else 2
+    return (cfg.N + 2) * cfg.B * cfg.D * cfg.L * s + cfg.N * cfg.D * (cfg.L + 1) * 8
+
+
+def algo_flops(cfg) -> float:
+    """N * (10 log2(2L) + 7) flops per channel-token: forward and inverse real
+    FFT of 2L points at 2.5 M log2 M each, one complex product per bin, gate."""
+    return cfg.N * cfg.B * cfg.D * cfg.L * (10.0 * math.log2(2 * cfg.L) + 7.0)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "hyena_long_conv_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_name: str):
+    """HBM bytes per forward from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_step")
+
+
+def cpu_baseline(cfg, budget_s: float = 12.0):
+    """Time the float64 oracle on a bounded sample of (b, d) rows of the same
+    workload on the host cores (one single-threaded worker per core)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    # calibrate on one row, then size the sample to about budget_s of wall time
+    t0 = time.perf_counter()
+    _oracle_rows(cfg, [0])
+    one = time.perf_counter() - t0
+    rows_total = cfg.B * cfg.D
+    n = int(max(cores, min(rows_total, budget_s * cores / max(one, 1e-3))))
+    n = max(1, min(n, rows_total))
+    rng = np.random.default_rng(cfg.seed)
+    sample = sorted(rng.choice(rows_total, size=n, replace=False).tolist())
+    chunks = [sample[i::cores] for i in range(cores) if sample[i::cores]]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(chunks), initializer=_pin_threads) as pool:
+        pool.starmap(_oracle_rows, [(cfg, c) for c in chunks])
+    wall = time.perf_counter() - t0
+    return {"value": n * cfg.L / wall, "unit": "channel-tokens/s", "cores": len(chunks), "kind": "oracle",
+            "sample": f"{n} of {rows_total} (b,d) rows of {cfg.name} (float64 oracle, direct conv for "
+                      f"L<=8192 else its radix-2 FFT), {wall:.1f} s wall",
+            "extrapolated_full_s": wall * rows_total / n}
+
+
+def _pin_threads():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+
+
+def _oracle_rows(cfg, rows):
+    """Oracle forward for flat row indices b*D + d: filters from the same
+    seeded FFN weights, activation rows drawn from N(0, 1) on the CPU (the
+    oracle's cost does not depend on the values)."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import make_filter_params
+    p = make_filter_params(cfg)
+    ds = sorted({r % cfg.D for r in rows})
+    h = O.filter_gen(p, cfg.L, channels=ds)
+    col = {d: i for i, d in enumerate(ds)}
+    rs = np.random.default_rng([cfg.seed, len(rows), rows[0]])
+    v = rs.standard_normal((len(rows), cfg.L))
+    xs = [rs.standard_normal((len(rows), cfg.L)) for _ in range(cfg.N)]
+    hh = np.stack([h[:, col[r % cfg.D]] for r in rows], axis=1)  # [N, rows, L]
+    return O.hyena_forward(v, xs, hh).shape
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run one 1 GiB device copy first (reference dispatch for counter scaling)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (the operator shards by channel with no communication); "
+              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import hyena_long_conv_amd as H
+    from workloads import CONFIGS, make_activations, make_filter_params
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H.lib()
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    per_set = min_bytes(cfg)
+    sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / per_set))
+    p = make_filter_params(cfg)
+    pd = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    h = H.filter_gen(pd, cfg.L)
+    spec0 = H.filter_spectrum(h)
+    del h
+    data = []
+    for s in range(sets):
+        c = cfg.with_(seed=cfg.seed * 100 + s)
+        v, xs = make_activations(c, dev)
+        spec = spec0 if s == 0 else spec0.clone()
+        data.append((v, xs, spec, torch.empty_like(v)))
+    wsb = H.forward_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        v, xs, spec, y = data[i % sets]
+        H.forward(v, xs, spec, out=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    t = ms / 1e3
+    tokens = cfg.B * cfg.D * cfg.L
+    value = tokens / t
+    mb, fl = min_bytes(cfg), algo_flops(cfg)
+    hbm_frac = mb / t / HBM_PEAK
+    alu_frac = fl / t / ALU_PEAK
+    plan = H.plan(cfg.L)
+    traffic = measured_traffic(cfg.name)
+    bound = "alu" if fl / mb > ALU_PEAK / HBM_PEAK else "hbm"
+    if bound == "alu":
+        roof = {"bound": "alu", "achieved": fl / t / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": alu_frac}
+    else:
+        roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": hbm_frac}
+    roof.update({"traffic": traffic, "kernel": ("k_single_forward" if plan["path"] == "single"
+                                                 else f"four-step forward ({2 * cfg.N + 1} passes per pair group)"),
+                 "launches_per_step": 1 if plan["path"] == "single" else None,
+                 "hbm_frac": hbm_frac, "hbm_GBps": mb / t / 1e9, "alu_frac": alu_frac,
+                 "alu_TFLOPs": fl / t / 1e12, "alu_frac_vs_packed_peak": fl / t / ALU_PEAK_PACKED,
+                 "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl})
+    out = {
+        "metric": "Hyena order-N fwd channel-tokens/sec (B*D*L/s) + % of HBM roofline",
+        "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations, random-init filter FFN)",
+        "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D, "L": cfg.L,
+                   "io": cfg.io, "ffn_hidden": cfg.H, "fft_len": plan["M"], "path": plan["path"],
+                   "input_sets": sets, "wall_s": wall},
+        "roofline": roof,
+    }
+    del data
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -38,30 +38,35 @@ def _common_flags():
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, tag + os.path.basename(src) + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [_hipcc(), *(["-x", "hip"] if src.endswith(".hip") else []), *_common_flags(), "-c", path, "-o", obj]
+    cmd = [_hipcc(), *(["-x", "hip"] if src.endswith(".hip") else []), *_common_flags(),
+           *[f"-D{d}" for d in defines], "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, defines=(), out: str | None = None) -> str:
+    """Compile and link; ``defines`` (NAME=VALUE strings) and ``out`` serve
+    tuning builds of the same sources."""
     os.makedirs(BUILD, exist_ok=True)
+    out = out or LIB
+    tag = "" if out == LIB else os.path.basename(out) + "."
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -35,14 +35,12 @@ int64_t spec_bytes(const PlanInfo& p, int64_t NF) { return NF * p.spec_stride * 
 
 int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
   if (p.path == PATH_SINGLE) return 0;
-  const int64_t pairs = (NF + 1) / 2;
-  return (int64_t)pairs_per_group(p.M, pairs) * p.M * 8;
+  return (int64_t)rows_per_group(p.N, NF) * p.N * 8;
 }
 
 int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
   if (p.path == PATH_SINGLE) return 0;
-  const Pairing pr = make_pairing(B, D);
-  return (int64_t)pairs_per_group(p.M, pr.n_pairs) * p.M * 8;
+  return (int64_t)rows_per_group(p.N, B * D) * p.N * 8;
 }
 
 bool sizes_ok(int64_t D, int64_t N, int64_t L) {
@@ -121,7 +119,7 @@ hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t
   const int64_t NF = (int64_t)N * D;
   if (!aligned16(h) || !aligned16(spec) || (workspace && !aligned16(workspace))) return HYENA_ERR_ALIGN;
   const int64_t need = spectrum_ws(p, NF);
-  if (need > 0 && (!workspace || workspace_bytes < p.M * 8)) return HYENA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < p.N * 8)) return HYENA_ERR_WORKSPACE;
   if (overlap(spec, spec_bytes(p, NF), h, NF * L * 4)) return HYENA_ERR_ALIAS;
   if (workspace && need > 0 && (overlap(workspace, workspace_bytes, h, NF * L * 4) ||
                                 overlap(workspace, workspace_bytes, spec, spec_bytes(p, NF))))
@@ -131,11 +129,11 @@ hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t
   a.work = workspace;
   hipError_t e;
   if (p.path == PATH_SINGLE) {
-    e = single_spectrum(a, p.M, (hipStream_t)stream);
+    e = single_spectrum(a, p.N, (hipStream_t)stream);
   } else {
-    int64_t g = pairs_per_group(p.M, (NF + 1) / 2);
-    if (g * p.M * 8 > workspace_bytes) g = workspace_bytes / (p.M * 8);
-    a.pairs_per_group = (int)g;
+    int64_t g = rows_per_group(p.N, NF);
+    if (g * p.N * 8 > workspace_bytes) g = workspace_bytes / (p.N * 8);
+    a.rows_per_group = (int)g;
     e = fourstep_spectrum(a, p, (hipStream_t)stream);
   }
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
@@ -151,7 +149,7 @@ hyena_status hyena_spectrum_export(const void* spec, int32_t D, int32_t N, int64
   if (c) return from_plan_code(c);
   if (!aligned16(spec) || !aligned16(out)) return HYENA_ERR_ALIGN;
   const int64_t NF = (int64_t)N * D;
-  if (overlap(out, NF * (p.M / 2 + 1) * 8, spec, spec_bytes(p, NF))) return HYENA_ERR_ALIAS;
+  if (overlap(out, NF * (p.N + 1) * 8, spec, spec_bytes(p, NF))) return HYENA_ERR_ALIAS;
   return spectrum_export(spec, (int)NF, p, out, (hipStream_t)stream) == hipSuccess ? HYENA_OK
                                                                                    : HYENA_ERR_HIP;
 }
@@ -173,8 +171,7 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
   for (int n = 0; n < N; ++n)
     if (!x[n]) return HYENA_ERR_NULL;
-  const Pairing pr = make_pairing(B, D);
-  if ((int64_t)pr.n_pairs > (int64_t)1 << 30) return HYENA_ERR_UNSUPPORTED;
+  if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
   PlanInfo p;
   const int c = plan_env(L, &p);
   if (c) return from_plan_code(c);
@@ -191,24 +188,24 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   ForwardArgs a{};
   a.v = v;
   for (int n = 0; n < N; ++n) a.x.p[n] = x[n];
-  a.spec = spec; a.y = y; a.B = (int)B; a.D = D; a.N = N; a.L = L;
+  a.spec = spec; a.y = y; a.B = (int)B; a.D = D; a.NORD = N; a.L = L;
   a.io = (io == HYENA_FP32) ? 0 : 1;
   a.spec_stride = p.spec_stride;
-  a.n_pairs = pr.n_pairs; a.n_batch_pairs = pr.n_batch_pairs; a.half_b = pr.half_b;
+  a.n_rows = (int)(B * D);
   hipError_t e;
   if (p.path == PATH_SINGLE) {
-    e = single_forward(a, p.M, (hipStream_t)stream);
+    e = single_forward(a, p.N, (hipStream_t)stream);
   } else {
-    if (!workspace || workspace_bytes < p.M * 8) return HYENA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < p.N * 8) return HYENA_ERR_WORKSPACE;
     if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
         overlap(workspace, workspace_bytes, spec, sb))
       return HYENA_ERR_ALIAS;
     for (int n = 0; n < N; ++n)
       if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
-    int64_t g = pairs_per_group(p.M, pr.n_pairs);
-    if (g * p.M * 8 > workspace_bytes) g = workspace_bytes / (p.M * 8);
+    int64_t g = rows_per_group(p.N, B * D);
+    if (g * p.N * 8 > workspace_bytes) g = workspace_bytes / (p.N * 8);
     a.work = workspace;
-    a.pairs_per_group = (int)g;
+    a.rows_per_group = (int)g;
     e = fourstep_forward(a, p, (hipStream_t)stream);
   }
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;

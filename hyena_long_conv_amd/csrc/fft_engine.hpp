@@ -383,6 +383,10 @@ template <> struct Plan8<64> { using R = Radices<8, 8>; };
 template <> struct Plan8<128> { using R = Radices<8, 2, 8>; };
 template <> struct Plan8<256> { using R = Radices<8, 4, 8>; };
 template <> struct Plan8<512> { using R = Radices<8, 8, 8>; };
+template <> struct Plan8<1024> { using R = Radices<8, 2, 8, 8>; };
+template <> struct Plan8<2048> { using R = Radices<8, 4, 8, 8>; };
+template <> struct Plan8<4096> { using R = Radices<8, 8, 8, 8>; };
+template <> struct Plan8<8192> { using R = Radices<8, 2, 8, 8, 8>; };
 
 // ---------------------------------------------------------------- I/O types
 
@@ -414,49 +418,52 @@ template <> struct IO<1> {  // bf16
   }
 };
 
-// ---------------------------------------------------------------- pairing
+// ------------------------------------------------- real rows as half-size FFTs
+//
+// A real row x of M = 2N samples (zero-padded) travels as the complex signal
+// c[m] = x[2m] + i x[2m+1] of N points.  With C = DFT_N(c) and W = W_M^k:
+//   even part E(k) = (C(k) + conj C(N-k)) / 2, odd part O(k) = (C(k) - conj C(N-k)) / (2i),
+//   X(k) = E(k) + W O(k) is the M-point real DFT (k = 0..N; C(N) means C(0)).
+// For the filtered row Y = H X the inverse needs C'(k) = E'(k) + i O'(k) with
+// E' = (Y(k) + conj Y(N-k))/2, O' = (Y(k) - conj Y(N-k)) conj(W) / 2.  Folding
+// the two steps gives, with s = sin(2 pi k/M), c = cos(2 pi k/M), G = H/(2N),
+// G' = conj G(N-k):
+//   C'(k) = C(k) [(G + G') + s (G' - G)] + conj C(N-k) [i c (G - G')]
+// and the inverse N-point DFT of C' (unnormalised) returns y[2m] + i y[2m+1].
+// Each row is processed on its own, so rounding never mixes two rows.
 
-// Two real sequences travel as one complex signal (real part a, imaginary
-// part b).  Pairs are either two batch rows of one channel (same filter) or,
-// for a leftover odd batch row, two channels of that row (different filters;
-// the spectra are separated with the conjugate-symmetry identity).
-struct Pair {
-  int64_t off_a, off_b;  // element offsets of the two [L] rows in [B][D][L]
-  int da, db;            // channels (filter index within an order)
-  bool has_b;            // false: the imaginary part is an all-zero row
-  bool same;             // both halves use the filter of channel da
-};
+// cos(2 pi q / 32), q = 0..31
+__device__ constexpr float kCos32[32] = {1.00000000000000000000f, 0.98078528040323043058f, 0.92387953251128673848f, 0.83146961230254523567f, 0.70710678118654757274f, 0.55557023301960228867f, 0.38268343236508983729f, 0.19509032201612833135f, 0.00000000000000006123f, -0.19509032201612819257f, -0.38268343236508972627f, -0.55557023301960195560f, -0.70710678118654746172f, -0.83146961230254534669f, -0.92387953251128673848f, -0.98078528040323043058f, -1.00000000000000000000f, -0.98078528040323043058f, -0.92387953251128684951f, -0.83146961230254545772f, -0.70710678118654768376f, -0.55557023301960217765f, -0.38268343236509033689f, -0.19509032201612866442f, -0.00000000000000018370f, 0.19509032201612830359f, 0.38268343236509000382f, 0.55557023301960184458f, 0.70710678118654735069f, 0.83146961230254523567f, 0.92387953251128651644f, 0.98078528040323031956f};
 
-__device__ __forceinline__ Pair decode_pair(int p, int B, int D, int64_t L, int n_batch_pairs,
-                                            int half_b) {
-  Pair r;
-  if (p < n_batch_pairs) {
-    const int d = p / half_b, q = p - d * half_b;
-    r.da = r.db = d;
-    r.off_a = ((int64_t)(2 * q) * D + d) * L;
-    r.off_b = ((int64_t)(2 * q + 1) * D + d) * L;
-    r.has_b = true;
-    r.same = true;
-  } else {
-    const int pc = p - n_batch_pairs;
-    r.da = 2 * pc;
-    r.db = 2 * pc + 1;
-    r.has_b = r.db < D;
-    if (!r.has_b) r.db = r.da;
-    r.same = !r.has_b;
-    r.off_a = ((int64_t)(B - 1) * D + r.da) * L;
-    r.off_b = ((int64_t)(B - 1) * D + r.db) * L;
-  }
-  return r;
+// W_{2E}^i = exp(-2 pi i * i / (2E)) for compile-time i < 2E, E in {8, 16}.
+template <int E>
+__device__ __forceinline__ cf w2e(int i) {
+  const int q = i * (16 / E);
+  return make_float2(kCos32[q & 31], -kCos32[(q + 24) & 31]);
 }
 
-// Y = Ga*A + i*Gb*B where Z = A + iB, A and B being spectra of real rows:
-// with Zm = Z(M-k): A = (Z + conj Zm)/2, iB = (Z - conj Zm)/2.
-__device__ __forceinline__ cf pair_multiply(cf z, cf zm, cf ga, cf gb) {
-  const cf s = make_float2(z.x + zm.x, z.y - zm.y);
-  const cf d = make_float2(z.x - zm.x, z.y + zm.y);
-  const cf y = cadd(cmul(ga, s), cmul(gb, d));
-  return cscale(y, 0.5f);
+__device__ __forceinline__ cf realconv_bin(cf a, cf am, cf g, cf gm, cf w) {
+  const float co = w.x, si = -w.y;
+  const float sx = g.x + gm.x, sy = g.y - gm.y;      // G + G'
+  const float dx = gm.x - g.x, dy = -gm.y - g.y;     // G' - G
+  const cf U = make_float2(fmaf(si, dx, sx), fmaf(si, dy, sy));
+  const cf V = make_float2(co * dy, -co * dx);       // i c (G - G')
+  // a U + conj(am) V
+  return make_float2(fmaf(am.y, V.y, fmaf(am.x, V.x, fmaf(a.x, U.x, -a.y * U.y))),
+                     fmaf(-am.y, V.x, fmaf(am.x, V.y, fmaf(a.x, U.y, a.y * U.x))));
+}
+
+// X(k) / (2N) of the real row from C(k), C(N-k) and W = W_M^k.
+__device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
+  const cf e = make_float2(a.x + am.x, a.y - am.y);          // 2 E
+  const cf o = make_float2(a.y + am.y, am.x - a.x);          // 2 O
+  return cscale(cadd(e, cmul(w, o)), 0.5f * scale);
+}
+
+// x[t] with zero padding beyond L.
+template <int IOT>
+__device__ __forceinline__ float ld_masked(const void* p, int64_t row_off, int64_t t, int64_t L) {
+  return t < L ? IO<IOT>::ld(p, row_off + t) : 0.f;
 }
 
 using XPtrs = XPtrsHost;

@@ -84,30 +84,25 @@ hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Library spectrum layout -> natural order, undoing the 1/M scale.
-__global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict__ out, int NF, int64_t M,
+// Library spectrum layout -> natural order, undoing the 1/(2N) scale.
+__global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict__ out, int NF, int64_t N,
                                   int path, int n1, int n2, int64_t stride) {
-  const int64_t half = M / 2 + 1;
+  const int64_t half = N + 1;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)NF * half) return;
   const int64_t f = idx / half, k = idx - f * half;
-  int64_t src;
-  if (path == PATH_SINGLE) {
-    src = k;
-  } else {
-    const int64_t k1 = k % n1, k2 = k / n1;
-    src = k1 * (n2 / 2 + 1) + k2;
-  }
+  int64_t src = k;
+  if (path == PATH_FOURSTEP && k < N) src = (k % n1) * n2 + k / n1;
   const cf g = spec[f * stride + src];
-  out[2 * idx] = g.x * (float)M;
-  out[2 * idx + 1] = g.y * (float)M;
+  out[2 * idx] = g.x * (float)(2 * N);
+  out[2 * idx + 1] = g.y * (float)(2 * N);
 }
 
 hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s) {
-  const int64_t total = (int64_t)NF * (p.M / 2 + 1);
+  const int64_t total = (int64_t)NF * (p.N + 1);
   const int threads = 256;
   hipLaunchKernelGGL(k_spectrum_export, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s,
-                     (const cf*)spec, out, NF, p.M, p.path, p.n1, p.n2, p.spec_stride);
+                     (const cf*)spec, out, NF, p.N, p.path, p.n1, p.n2, p.spec_stride);
   return hipGetLastError();
 }
 

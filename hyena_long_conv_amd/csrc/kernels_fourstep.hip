@@ -1,17 +1,19 @@
 // kernels_fourstep.hip -- multi-pass Hyena forward and filter spectrum for
 // FFT lengths too long for one workgroup's LDS.
 //
-// The M-point DFT is factored as M = n1 * n2 (Bailey's four-step): with time
-// index t = n2*i1 + i2 and frequency index k = k1 + n1*k2,
-//   A[k1][i2]  = sum_{i1} z[n2*i1 + i2] W_{n1}^{i1 k1}          (column pass)
-//   X[k1+n1 k2] = sum_{i2} A[k1][i2] W_M^{i2 k1} W_{n2}^{i2 k2}  (row pass)
+// Each real row travels as an N-point complex signal c[m] = x[2m] + i x[2m+1]
+// (see fft_engine.hpp).  Its DFT is factored as N = n1 * n2 (Bailey's four-
+// step): with m = n2*i1 + i2 and k = k1 + n1*k2,
+//   A[k1][i2]    = sum_{i1} c[n2*i1 + i2] W_{n1}^{i1 k1}          (column pass)
+//   C[k1+n1 k2] = sum_{i2} A[k1][i2] W_N^{i2 k1} W_{n2}^{i2 k2}    (row pass)
 // and the inverse runs the same steps backwards with conjugate twiddles.
 // Per order the row pass does row FFT -> spectral product -> inverse row
 // FFT in one kernel, and the column pass does inverse column FFT -> gate with
 // x_n -> forward column FFT of the next order in one kernel, so each order
-// costs two passes over an M-point intermediate per row pair.  Row k1 and
-// row n1-k1 hold mirror bins (k and M-k), so each row workgroup takes such a
-// pair of rows; rows 0 and n1/2 are their own mirrors and go together.
+// costs two passes over an N-point intermediate per row.  The spectral
+// product of bin k needs bin N-k, which sits in row n1-k1; each row
+// workgroup therefore takes such a pair of rows (rows 0 and n1/2 are their
+// own mirrors and go together).
 //
 // Long convolution by FFT with zero padding (jisaku.com glossary
 // "Hyena（ハイエナ）", section "計算効率"; gist.science HyenaND summary, section
@@ -21,6 +23,13 @@
 #include "launch.hpp"
 
 namespace hyena {
+
+#ifndef HYENA_ROW_WAVES
+#define HYENA_ROW_WAVES 1
+#endif
+#ifndef HYENA_COL_WAVES
+#define HYENA_COL_WAVES 1
+#endif
 
 template <int N1> struct ColCfg {
   static constexpr int E = 16;
@@ -46,16 +55,14 @@ struct ColArgs {
   void* y;             // LAST: output
   const float* h;      // SPEC: filters [NF][L]
   cf* work;            // [group][n1][n2]
-  int B, D, NF;
   int64_t L;
   int n2;
-  int p0;              // first pair of this launch
-  int n_batch_pairs, half_b;
+  int r0;              // first row of this launch
   int n_col_blocks;
 };
 
 template <int N1, int IOT, int KIND>
-__global__ void __launch_bounds__(ColCfg<N1>::T) k_col(ColArgs a) {
+__global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1>;
   constexpr int E = C::E, W = C::W, S1 = N1 / E;
   __shared__ cf smem[C::LDS ? N1 * W : 1];
@@ -63,37 +70,24 @@ __global__ void __launch_bounds__(ColCfg<N1>::T) k_col(ColArgs a) {
   const int g = blockIdx.x / a.n_col_blocks, cb = blockIdx.x - g * a.n_col_blocks;
   const int col = cb * W + c;
   const bool valid = col < a.n2;
-  const int64_t M = (int64_t)N1 * a.n2;
-  cf* buf = a.work + (int64_t)g * M;
+  const int64_t N = (int64_t)N1 * a.n2;
+  cf* buf = a.work + (int64_t)g * N;
+  const int64_t off = (int64_t)(a.r0 + g) * a.L;
   const ColLds<W> lds{smem + c};
   BlockFFT<N1, E, typename C::R> fft;
   fft.init(j);
   cf u[E];
 
-  int64_t off_a, off_b;
-  bool has_b;
-  if constexpr (KIND == COL_SPEC) {
-    const int fa = 2 * (a.p0 + g);
-    has_b = fa + 1 < a.NF;
-    off_a = (int64_t)fa * a.L;
-    off_b = off_a + a.L;
-  } else {
-    const Pair pr = decode_pair(a.p0 + g, a.B, a.D, a.L, a.n_batch_pairs, a.half_b);
-    off_a = pr.off_a; off_b = pr.off_b; has_b = pr.has_b;
-  }
-
   if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const int64_t t = (int64_t)a.n2 * (j + i * S1) + col;
+      const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
       u[i] = make_float2(0.f, 0.f);
-      if (valid && t < a.L) {
+      if (valid) {
         if constexpr (KIND == COL_SPEC) {
-          u[i].x = a.h[off_a + t];
-          if (has_b) u[i].y = a.h[off_b + t];
+          u[i] = make_float2(t < a.L ? a.h[off + t] : 0.f, t + 1 < a.L ? a.h[off + t + 1] : 0.f);
         } else {
-          u[i].x = IO<IOT>::ld(a.v, off_a + t);
-          if (has_b) u[i].y = IO<IOT>::ld(a.v, off_b + t);
+          u[i] = make_float2(ld_masked<IOT>(a.v, off, t, a.L), ld_masked<IOT>(a.v, off, t + 1, a.L));
         }
       }
     }
@@ -104,17 +98,17 @@ __global__ void __launch_bounds__(ColCfg<N1>::T) k_col(ColArgs a) {
     fft.template run<true>(u, lds, j);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const int64_t t = (int64_t)a.n2 * (j + i * S1) + col;
-      float za = 0.f, zb = 0.f;
-      if (valid && t < a.L) {
-        za = IO<IOT>::ld(a.xg, off_a + t) * u[i].x;
-        if (has_b) zb = IO<IOT>::ld(a.xg, off_b + t) * u[i].y;
+      const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
+      cf z = make_float2(0.f, 0.f);
+      if (valid) {
+        z.x = ld_masked<IOT>(a.xg, off, t, a.L) * u[i].x;
+        z.y = ld_masked<IOT>(a.xg, off, t + 1, a.L) * u[i].y;
         if constexpr (KIND == COL_LAST) {
-          IO<IOT>::st(a.y, off_a + t, za);
-          if (has_b) IO<IOT>::st(a.y, off_b + t, zb);
+          if (t < a.L) IO<IOT>::st(a.y, off + t, z.x);
+          if (t + 1 < a.L) IO<IOT>::st(a.y, off + t + 1, z.y);
         }
       }
-      u[i] = make_float2(za, zb);
+      u[i] = z;
     }
   }
   if constexpr (KIND != COL_LAST) {
@@ -133,17 +127,17 @@ struct RowArgs {
   int n1;
   int64_t spec_stride;
   int order;           // CONV: order n (filters n*D + d)
-  int B, D, NF;
-  int64_t L;
-  int p0;
-  int n_batch_pairs, half_b;
+  int D;
+  int r0;              // first row (CONV: activation row b*D + d; SPEC: filter row)
   int n_row_pairs;     // n1 / 2
 };
 
+// Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
+// for k = k1 + n1*k2 < N, and S(N) at index N.
 template <int N2, int KIND>
-__global__ void __launch_bounds__(RowCfg<N2>::T) k_row(RowArgs a) {
+__global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs a) {
   using C = RowCfg<N2>;
-  constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E, HALF = N2 / 2 + 1;
+  constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E;
   constexpr int PADN = RowLds::padded(N2);
   __shared__ cf smem[2 * PADN];
   const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
@@ -153,74 +147,53 @@ __global__ void __launch_bounds__(RowCfg<N2>::T) k_row(RowArgs a) {
   const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
   const int mb = self_mirror ? b : 1 - b;          // row holding the mirror bins
   const int k1m = (k1 == 0) ? 0 : n1 - k1;         // its k1
-  const uint32_t M = (uint32_t)n1 * (uint32_t)N2;
-  cf* row = a.work + (int64_t)g * M + (int64_t)k1 * N2;
+  const uint32_t N = (uint32_t)n1 * (uint32_t)N2;
+  cf* row = a.work + (int64_t)g * N + (int64_t)k1 * N2;
   const RowLds lds{smem + b * PADN};
   const RowLds ldsm{smem + mb * PADN};
   BlockFFT<N2, E, typename C::R> fft;
   fft.init(j);
   cf u[E];
 
-  // four-step twiddle W_M^{k1 i2} for i2 = j + i*S2: base W_M^{k1 j} times
-  // powers of the step W_M^{k1 S2}
-  const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, M);
-  const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, M);
+  // four-step twiddle W_N^{k1 i2} for i2 = j + i*S2: base W_N^{k1 j} times
+  // powers of the step W_N^{k1 S2}
+  const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, N);
+  const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, N);
 #pragma unroll
   for (int i = 0; i < E; ++i) u[i] = cmul(row[j + i * S2], step_power<E>(tb, ts, i));
   fft.template run<false>(u, lds, j);
 
-  if constexpr (KIND == ROW_SPEC) {
-    const int fa = 2 * (a.p0 + g);
-    const bool has_b = fa + 1 < a.NF;
-    __syncthreads();
+  // bins k = k1 + n1*k2 with k2 = j + i*S2; mirror N-k at (k1m, k2m)
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
-    __syncthreads();
-    const float sc = 0.5f / (float)M;
+  for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+  __syncthreads();
+  // W_{2N}^k = W_{2N}^{k1 + n1 j} * W_{2E}^i
+  const cf wk = twiddle<false>((uint32_t)k1 + (uint32_t)n1 * (uint32_t)j, 2 * N);
+
+  if constexpr (KIND == ROW_SPEC) {
+    cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
+    const float sc = 1.0f / (float)(2 * N);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int k2 = j + i * S2;
-      if (k2 < HALF) {
-        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-        const cf zm = ldsm(k2m), z = u[i];
-        const int64_t o = (int64_t)k1 * HALF + k2;
-        a.spec_out[(int64_t)fa * a.spec_stride + o] = make_float2((z.x + zm.x) * sc, (z.y - zm.y) * sc);
-        if (has_b)
-          a.spec_out[(int64_t)(fa + 1) * a.spec_stride + o] = make_float2((z.y + zm.y) * sc, (zm.x - z.x) * sc);
-      }
+      const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+      const cf am = ldsm(k2m);
+      out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc);
+      if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
     }
   } else {
-    const Pair pr = decode_pair(a.p0 + g, a.B, a.D, a.L, a.n_batch_pairs, a.half_b);
-    const cf* ga = a.spec + (int64_t)(a.order * a.D + pr.da) * a.spec_stride;
-    const cf* gb = a.spec + (int64_t)(a.order * a.D + pr.db) * a.spec_stride;
-    if (pr.same) {
+    const int d = (a.r0 + g) % a.D;
+    const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
+    const cf wkb = opaque(wk);
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int k2 = j + i * S2;
-        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-        const cf g0 = (k2 < HALF) ? ga[(int64_t)k1 * HALF + k2] : cconj(ga[(int64_t)k1m * HALF + k2m]);
-        u[i] = cmul(g0, u[i]);
-      }
-    } else {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int k2 = j + i * S2;
-        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-        const cf zm = ldsm(k2m);
-        cf gak, gbk;
-        if (k2 < HALF) {
-          gak = ga[(int64_t)k1 * HALF + k2];
-          gbk = gb[(int64_t)k1 * HALF + k2];
-        } else {
-          gak = cconj(ga[(int64_t)k1m * HALF + k2m]);
-          gbk = cconj(gb[(int64_t)k1m * HALF + k2m]);
-        }
-        u[i] = pair_multiply(u[i], zm, gak, gbk);
-      }
+    for (int i = 0; i < E; ++i) {
+      const int k2 = j + i * S2;
+      const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+      const cf am = ldsm(k2m);
+      const cf gk = gs[(int64_t)k1 * N2 + k2];
+      const cf gm = (k1 == 0 && k2 == 0) ? gs[N] : gs[(int64_t)k1m * N2 + k2m];
+      u[i] = realconv_bin(u[i], am, gk, gm, cmul(wkb, w2e<E>(i)));
     }
     fft.template run<true>(u, lds, j);
 #pragma unroll
@@ -300,24 +273,22 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   if (W == 0) return hipErrorInvalidValue;
   ColArgs c{};
   c.v = a.v; c.y = a.y; c.h = nullptr; c.work = (cf*)a.work;
-  c.B = a.B; c.D = a.D; c.NF = a.N * a.D; c.L = a.L; c.n2 = p.n2;
-  c.n_batch_pairs = a.n_batch_pairs; c.half_b = a.half_b;
+  c.L = a.L; c.n2 = p.n2;
   c.n_col_blocks = (p.n2 + W - 1) / W;
   RowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
-  r.n1 = p.n1; r.spec_stride = a.spec_stride; r.B = a.B; r.D = a.D; r.NF = a.N * a.D; r.L = a.L;
-  r.n_batch_pairs = a.n_batch_pairs; r.half_b = a.half_b; r.n_row_pairs = p.n1 / 2;
-  for (int p0 = 0; p0 < a.n_pairs; p0 += a.pairs_per_group) {
-    const int groups = (a.n_pairs - p0 < a.pairs_per_group) ? a.n_pairs - p0 : a.pairs_per_group;
-    c.p0 = p0; r.p0 = p0;
+  r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = p.n1 / 2;
+  for (int r0 = 0; r0 < a.n_rows; r0 += a.rows_per_group) {
+    const int groups = (a.n_rows - r0 < a.rows_per_group) ? a.n_rows - r0 : a.rows_per_group;
+    c.r0 = r0; r.r0 = r0;
     hipError_t e = dispatch_col(p.n1, COL_FIRST, a.io, c, groups, s);
     if (e != hipSuccess) return e;
-    for (int n = 0; n < a.N; ++n) {
+    for (int n = 0; n < a.NORD; ++n) {
       r.order = n;
       e = dispatch_row(p.n2, ROW_CONV, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
-      e = dispatch_col(p.n1, n == a.N - 1 ? COL_LAST : COL_MID, a.io, c, groups, s);
+      e = dispatch_col(p.n1, n == a.NORD - 1 ? COL_LAST : COL_MID, a.io, c, groups, s);
       if (e != hipSuccess) return e;
     }
   }
@@ -327,16 +298,15 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
 hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s) {
   const int W = col_width(p.n1);
   if (W == 0) return hipErrorInvalidValue;
-  const int n_fpairs = (a.NF + 1) / 2;
   ColArgs c{};
-  c.h = a.h; c.work = (cf*)a.work; c.NF = a.NF; c.L = a.L; c.n2 = p.n2;
+  c.h = a.h; c.work = (cf*)a.work; c.L = a.L; c.n2 = p.n2;
   c.n_col_blocks = (p.n2 + W - 1) / W;
   RowArgs r{};
   r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = p.n1; r.spec_stride = a.spec_stride;
-  r.NF = a.NF; r.L = a.L; r.n_row_pairs = p.n1 / 2;
-  for (int p0 = 0; p0 < n_fpairs; p0 += a.pairs_per_group) {
-    const int groups = (n_fpairs - p0 < a.pairs_per_group) ? n_fpairs - p0 : a.pairs_per_group;
-    c.p0 = p0; r.p0 = p0;
+  r.n_row_pairs = p.n1 / 2;
+  for (int r0 = 0; r0 < a.NF; r0 += a.rows_per_group) {
+    const int groups = (a.NF - r0 < a.rows_per_group) ? a.NF - r0 : a.rows_per_group;
+    c.r0 = r0; r.r0 = r0;
     hipError_t e = dispatch_col(p.n1, COL_SPEC, 0, c, groups, s);
     if (e != hipSuccess) return e;
     e = dispatch_row(p.n2, ROW_SPEC, r, groups, s);

@@ -14,15 +14,13 @@ struct ForwardArgs {
   XPtrsHost x;           // N device pointers
   const void* spec;
   void* y;
-  int B, D, N;
+  int B, D, NORD;        // batch, channels, order
   int64_t L;
   int io;                // 0 fp32, 1 bf16
   int64_t spec_stride;   // complex64 elements per filter row
-  int n_pairs;           // total complex signals
-  int n_batch_pairs;     // pairs made of two batch rows of one channel
-  int half_b;            // batch pairs per channel
-  void* work;            // four-step intermediate (pairs_per_group * M complex)
-  int pairs_per_group;
+  int n_rows;            // B * D real rows
+  void* work;            // four-step intermediate (rows_per_group * N complex)
+  int rows_per_group;
 };
 
 struct SpectrumArgs {
@@ -32,7 +30,7 @@ struct SpectrumArgs {
   int64_t L;
   int64_t spec_stride;
   void* work;
-  int pairs_per_group;
+  int rows_per_group;
 };
 
 struct FilterGenArgs {
@@ -42,8 +40,8 @@ struct FilterGenArgs {
   float* h;
 };
 
-hipError_t single_forward(const ForwardArgs& a, int64_t M, hipStream_t s);
-hipError_t single_spectrum(const SpectrumArgs& a, int64_t M, hipStream_t s);
+hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
+hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);
 hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s);
 hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s);

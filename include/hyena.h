@@ -85,13 +85,14 @@ typedef struct {
 
 /* Planner result for a sequence length (host only, no GPU needed). */
 typedef struct {
-  int64_t L;            /* sequence length                                        */
-  int64_t M;            /* FFT length in complex points; M >= 2L                  */
-  int32_t path;         /* hyena_path                                             */
-  int32_t n1;           /* four-step: column FFT length (0 on the single path)    */
-  int32_t n2;           /* four-step: row FFT length (0 on the single path)       */
+  int64_t L;            /* sequence length                                          */
+  int64_t M;            /* real FFT length of a zero-padded row, M >= 2L; each row   */
+                        /* is transformed as a complex signal of N = M/2 points     */
+  int32_t path;         /* hyena_path                                               */
+  int32_t n1;           /* four-step: column FFT length, n1*n2 = N (0 single path)  */
+  int32_t n2;           /* four-step: row FFT length (0 on the single path)         */
   int32_t reserved;
-  int64_t spec_stride;  /* complex64 elements per (n, d) filter in the spectrum   */
+  int64_t spec_stride;  /* complex64 elements per (n, d) filter in the spectrum     */
 } hyena_plan_info;
 
 /* Fill *out with the plan the library uses for length L.

@@ -29,39 +29,39 @@ def test_status_strings():
     assert lib.hyena_status_str(0) == b"ok"
 
 
-@pytest.mark.parametrize("L,M,path", [(1, 64, "single"), (17, 64, "single"), (32, 64, "single"),
-                                      (33, 128, "single"), (256, 512, "single"), (1000, 2048, "single"),
-                                      (2048, 4096, "single"), (8192, 16384, "single"),
-                                      (8193, 32768, "fourstep"), (65536, 131072, "fourstep"),
-                                      (100000, 262144, "fourstep"), (131072, 262144, "fourstep"),
-                                      (1 << 20, 1 << 21, "fourstep"), (1 << 22, 1 << 23, "fourstep")])
+@pytest.mark.parametrize("L,M,path", [(1, 128, "single"), (17, 128, "single"), (32, 128, "single"),
+                                      (33, 128, "single"), (65, 256, "single"), (256, 512, "single"),
+                                      (1000, 2048, "single"), (2048, 4096, "single"), (8192, 16384, "single"),
+                                      (16384, 32768, "single"), (16385, 65536, "fourstep"),
+                                      (65536, 131072, "fourstep"), (100000, 262144, "fourstep"),
+                                      (131072, 262144, "fourstep"), (1 << 20, 1 << 21, "fourstep"),
+                                      (1 << 22, 1 << 23, "fourstep")])
 def test_plan_lengths(L, M, path):
     p = H.plan(L)
     assert p["M"] == M and p["path"] == path
     assert p["M"] >= 2 * L - 1
+    N = M // 2
     if path == "fourstep":
-        assert p["n1"] * p["n2"] == M and 16 <= p["n1"] <= 1024 and 64 <= p["n2"] <= 8192
-        assert p["spec_stride"] >= p["n1"] * (p["n2"] // 2 + 1)
-    else:
-        assert p["spec_stride"] >= M // 2 + 1
+        assert p["n1"] * p["n2"] == N and 16 <= p["n1"] <= 1024 and 64 <= p["n2"] <= 8192
+    assert p["spec_stride"] >= N + 1
     assert p["spec_stride"] % 16 == 0
 
 
 def test_plan_forced_paths(monkeypatch):
     monkeypatch.setenv("HYENA_FORCE_PATH", "fourstep")
     p = H.plan(300)
-    assert p["path"] == "fourstep" and p["M"] >= 600 and p["n1"] * p["n2"] == p["M"]
+    assert p["path"] == "fourstep" and p["M"] >= 600 and p["n1"] * p["n2"] == p["M"] // 2
     monkeypatch.setenv("HYENA_FOURSTEP_N1", "64")
     p = H.plan(300)
-    assert p["n1"] == 64 and p["n2"] >= 64
+    assert p["n1"] == 64 and p["n2"] >= 64 and p["n1"] * p["n2"] == p["M"] // 2
     monkeypatch.setenv("HYENA_FOURSTEP_N1", "48")          # not a power of two
     with pytest.raises(H.HyenaError):
         H.plan(300)
     monkeypatch.delenv("HYENA_FOURSTEP_N1")
     monkeypatch.setenv("HYENA_FORCE_PATH", "single")
-    assert H.plan(8192)["path"] == "single"
+    assert H.plan(16384)["path"] == "single"
     with pytest.raises(H.HyenaError):                       # too long for one workgroup
-        H.plan(8193)
+        H.plan(16385)
 
 
 def test_plan_bad_lengths():
@@ -77,7 +77,7 @@ def test_size_queries():
     assert H.spectrum_workspace_bytes(768, 2, 2048) == 0
     assert H.forward_workspace_bytes(4, 768, 2, 2048) == 0
     ws = H.forward_workspace_bytes(1, 768, 2, 65536, "bf16")
-    assert ws > 0 and ws % (H.plan(65536)["M"] * 8) == 0
+    assert ws > 0 and ws % (H.plan(65536)["M"] // 2 * 8) == 0
     assert H.spectrum_bytes(0, 2, 16) == -1 and H.spectrum_bytes(4, 9, 16) == -1
     assert H.forward_workspace_bytes(0, 4, 2, 16) == -1
 

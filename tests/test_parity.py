@@ -136,13 +136,13 @@ def test_forward_long_auto_path(L):
 
 
 def test_small_workspace_still_correct():
-    # A workspace for a single pair forces one pair per pass group.
+    # A workspace for a single row forces one row per pass group.
     L, cfg = 20000, _cfg(2, 2, 3, 20000)
     p = make_filter_params(cfg)
     v, xs = make_activations(cfg, DEV)
     h = H.filter_gen(params_to_device(p), L)
     spec = H.filter_spectrum(h)
-    ws = torch.empty(H.plan(L)["M"] * 8, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(H.plan(L)["M"] // 2 * 8, dtype=torch.uint8, device=DEV)
     y = H.forward(v, xs, spec, workspace=ws)
     torch.cuda.synchronize()
     check_rows(y, p, L, v, xs, [(b, d) for b in range(2) for d in range(3)], TOL_FP32)
@@ -175,6 +175,19 @@ def test_output_guard_regions_untouched(L, io):
     torch.cuda.synchronize()
     assert torch.all(big[:pad] == 12345.0) and torch.all(big[pad + n:] == 12345.0)
     check_rows(y, p, L, v, xs, [(0, 0), (0, 2)], TOL_FP32 if io == "fp32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("L", [3000, 20000])
+def test_rows_of_very_different_magnitude(L):
+    # Rounding must stay relative to each row's own scale: neighbouring rows
+    # (batch or channel) 1e4 times larger may not leak error into a small row.
+    cfg = _cfg(2, 2, 4, L)
+    p = make_filter_params(cfg)
+    v, xs = make_activations(cfg, DEV)
+    v[0] *= 1e4
+    v[1, 2] *= 1e-3
+    _, _, y = run_hip(p, L, v, xs)
+    check_rows(y, p, L, v, xs, [(b, d) for b in range(2) for d in range(4)], TOL_FP32)
 
 
 def test_spectrum_reused_across_batches():
