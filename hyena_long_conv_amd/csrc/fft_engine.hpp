@@ -33,6 +33,7 @@
 namespace hyena {
 
 typedef float2 cf;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ cf cadd(cf a, cf b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ cf csub(cf a, cf b) { return make_float2(a.x - b.x, a.y - b.y); }
@@ -453,6 +454,25 @@ __device__ __forceinline__ cf realconv_bin(cf a, cf am, cf g, cf gm, cf w) {
                      fmaf(-am.y, V.x, fmaf(am.x, V.y, fmaf(a.x, U.y, a.y * U.x))));
 }
 
+// Both bins of the pair (k, N-k) at once: a = C(k) -> C'(k), b = C(N-k) ->
+// C'(N-k), g = G(k), gm = G(N-k), w = W_M^k.  With P = G(k) + conj G(N-k) and
+// Q = conj G(N-k) - G(k):  U_k = P + sQ, V_k = -icQ, U_{N-k} = conj(P - sQ),
+// V_{N-k} = -ic conj(Q), and C'(k) = a U_k + conj(b) V_k,
+// C'(N-k) = b U_{N-k} + conj(a) V_{N-k}.
+__device__ __forceinline__ void realconv_pair(cf& a, cf& b, cf g, cf gm, cf w) {
+  const float co = w.x, si = -w.y;
+  const float px = g.x + gm.x, py = g.y - gm.y;
+  const float qx = gm.x - g.x, qy = -gm.y - g.y;
+  const cf U1 = make_float2(fmaf(si, qx, px), fmaf(si, qy, py));
+  const cf U2 = make_float2(fmaf(-si, qx, px), fmaf(si, qy, -py));
+  const float cqx = co * qx, cqy = co * qy;
+  const cf V1 = make_float2(cqy, -cqx), V2 = make_float2(-cqy, -cqx);
+  const cf na = cadd(cmul(a, U1), cmul(cconj(b), V1));
+  const cf nb = cadd(cmul(b, U2), cmul(cconj(a), V2));
+  a = na;
+  b = nb;
+}
+
 // X(k) / (2N) of the real row from C(k), C(N-k) and W = W_M^k.
 __device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
   const cf e = make_float2(a.x + am.x, a.y - am.y);          // 2 E
@@ -464,6 +484,43 @@ __device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
 template <int IOT>
 __device__ __forceinline__ float ld_masked(const void* p, int64_t row_off, int64_t t, int64_t L) {
   return t < L ? IO<IOT>::ld(p, row_off + t) : 0.f;
+}
+
+// (x[t], x[t+1]) for even t with zero padding beyond L.  EVEN: the row
+// offset and L are even, so the pair is one aligned 8-byte (fp32) or 4-byte
+// (bf16) access.
+template <int IOT, bool EVEN>
+__device__ __forceinline__ cf ld_pair(const void* p, int64_t row_off, int64_t t, int64_t L) {
+  if constexpr (EVEN) {
+    if (t >= L) return make_float2(0.f, 0.f);
+    if constexpr (IOT == 0) {
+      const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(static_cast<const float*>(p) + row_off + t));
+      return make_float2(w.x, w.y);
+    } else {
+      const uint32_t w = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + row_off + t));
+      return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    }
+  } else {
+    return make_float2(ld_masked<IOT>(p, row_off, t, L), ld_masked<IOT>(p, row_off, t + 1, L));
+  }
+}
+
+template <int IOT, bool EVEN>
+__device__ __forceinline__ void st_pair(void* p, int64_t row_off, int64_t t, int64_t L, cf v) {
+  if constexpr (EVEN) {
+    if (t >= L) return;
+    if constexpr (IOT == 0) {
+      const f32x2 w = {v.x, v.y};
+      __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(static_cast<float*>(p) + row_off + t));
+    } else {
+      const uint32_t w = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + row_off + t));
+    }
+  } else {
+    if (t < L) IO<IOT>::st(p, row_off + t, v.x);
+    if (t + 1 < L) IO<IOT>::st(p, row_off + t + 1, v.y);
+  }
 }
 
 using XPtrs = XPtrsHost;

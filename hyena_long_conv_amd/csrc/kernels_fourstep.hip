@@ -39,11 +39,16 @@ template <int N1> struct ColCfg {
   using R = typename Plan16<N1>::R;
 };
 
+#ifndef HYENA_ROW_E
+#define HYENA_ROW_E 16
+#endif
+
 template <int N2> struct RowCfg {
-  static constexpr int E = 16;
+  static constexpr int E = HYENA_ROW_E;
   static constexpr int TPR = N2 / E;  // threads per row
   static constexpr int T = 2 * TPR;
-  using R = typename Plan16<N2>::R;
+  using R = typename std::conditional<E == 16, typename Plan16<N2>::R,
+                                      typename Plan8<(N2 <= 8192 ? N2 : 8192)>::R>::type;
 };
 
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3 };
@@ -61,7 +66,7 @@ struct ColArgs {
   int n_col_blocks;
 };
 
-template <int N1, int IOT, int KIND>
+template <int N1, int IOT, int KIND, bool EVEN>
 __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1>;
   constexpr int E = C::E, W = C::W, S1 = N1 / E;
@@ -84,11 +89,8 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
       const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
       u[i] = make_float2(0.f, 0.f);
       if (valid) {
-        if constexpr (KIND == COL_SPEC) {
-          u[i] = make_float2(t < a.L ? a.h[off + t] : 0.f, t + 1 < a.L ? a.h[off + t + 1] : 0.f);
-        } else {
-          u[i] = make_float2(ld_masked<IOT>(a.v, off, t, a.L), ld_masked<IOT>(a.v, off, t + 1, a.L));
-        }
+        if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, off, t, a.L);
+        else u[i] = ld_pair<IOT, EVEN>(a.v, off, t, a.L);
       }
     }
   } else {
@@ -101,12 +103,9 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
       const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
       cf z = make_float2(0.f, 0.f);
       if (valid) {
-        z.x = ld_masked<IOT>(a.xg, off, t, a.L) * u[i].x;
-        z.y = ld_masked<IOT>(a.xg, off, t + 1, a.L) * u[i].y;
-        if constexpr (KIND == COL_LAST) {
-          if (t < a.L) IO<IOT>::st(a.y, off + t, z.x);
-          if (t + 1 < a.L) IO<IOT>::st(a.y, off + t + 1, z.y);
-        }
+        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, t, a.L);
+        z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+        if constexpr (KIND == COL_LAST) st_pair<IOT, EVEN>(a.y, off, t, a.L, z);
       }
       u[i] = z;
     }
@@ -164,14 +163,14 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   fft.template run<false>(u, lds, j);
 
   // bins k = k1 + n1*k2 with k2 = j + i*S2; mirror N-k at (k1m, k2m)
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
-  __syncthreads();
   // W_{2N}^k = W_{2N}^{k1 + n1 j} * W_{2E}^i
   const cf wk = twiddle<false>((uint32_t)k1 + (uint32_t)n1 * (uint32_t)j, 2 * N);
 
   if constexpr (KIND == ROW_SPEC) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+    __syncthreads();
     cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
     const float sc = 1.0f / (float)(2 * N);
 #pragma unroll
@@ -183,18 +182,39 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
       if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
     }
   } else {
+    // Pair-wise spectral step: the owner of the low index i < E/2 of a bin
+    // pair (k, N-k) computes both results; the partner bin is the high index
+    // E-1-i of thread S2-1-j in the mirror row (row 0 pairs inside itself:
+    // thread S2-j, or index E-i in thread 0; k = 0 and k = N/2 are their own
+    // partners).
     const int d = (a.r0 + g) % a.D;
     const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
+    const cf* gk = gs + (int64_t)k1 * N2;
+    const cf* gmr = gs + (int64_t)k1m * N2;
     const cf wkb = opaque(wk);
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
+    for (int i = E / 2; i < E; ++i) lds(j + i * S2) = u[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
       const int k2 = j + i * S2;
-      const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-      const cf am = ldsm(k2m);
-      const cf gk = gs[(int64_t)k1 * N2 + k2];
-      const cf gm = (k1 == 0 && k2 == 0) ? gs[N] : gs[(int64_t)k1m * N2 + k2m];
-      u[i] = realconv_bin(u[i], am, gk, gm, cmul(wkb, w2e<E>(i)));
+      if (k1 == 0 && i == 0 && j == 0) {
+        u[0] = realconv_bin(u[0], u[0], gs[0], gs[N], make_float2(1.f, 0.f));
+      } else {
+        const int k2m = (k1 == 0) ? (N2 - k2) : (N2 - 1 - k2);
+        cf bm = ldsm(k2m);
+        realconv_pair(u[i], bm, gk[k2], gmr[k2m], cmul(wkb, w2e<E>(i)));
+        ldsm(k2m) = bm;
+      }
     }
+    if (k1 == 0 && j == 0) {
+      const cf am = lds(N2 / 2), gh = gs[N2 / 2];
+      lds(N2 / 2) = realconv_bin(am, am, gh, gh, make_float2(0.f, -1.f));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = E / 2; i < E; ++i) u[i] = lds(j + i * S2);
     fft.template run<true>(u, lds, j);
 #pragma unroll
     for (int i = 0; i < E; ++i) row[j + i * S2] = cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i));
@@ -203,20 +223,26 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
 
 // ---------------------------------------------------------------- launchers
 
+template <int N1, bool EVEN>
+static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 block, hipStream_t s) {
+  if (kind == COL_SPEC) {
+    hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+  } else if (io == 0) {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
+  } else {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
+  }
+}
+
 template <int N1>
 static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
   const dim3 grid(groups * c.n_col_blocks), block(ColCfg<N1>::T);
-  if (kind == COL_SPEC) {
-    hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC>), grid, block, 0, s, c);
-  } else if (io == 0) {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST>), grid, block, 0, s, c);
-  } else {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST>), grid, block, 0, s, c);
-  }
+  if (c.L % 2 == 0) launch_col_t<N1, true>(kind, io, c, grid, block, s);
+  else launch_col_t<N1, false>(kind, io, c, grid, block, s);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ constexpr int64_t kMaxL = int64_t(1) << 22;
 #define HYENA_SINGLE_MAX_N 16384
 #endif
 #ifndef HYENA_ROW_MAX
-#define HYENA_ROW_MAX 8192
+#define HYENA_ROW_MAX 2048
 #endif
 #ifndef HYENA_WORK_MB
 #define HYENA_WORK_MB 256
@@ -34,6 +34,7 @@ constexpr int64_t kSingleMaxN = HYENA_SINGLE_MAX_N;
 constexpr int64_t kMinN = 64;
 constexpr int kRowMax = HYENA_ROW_MAX;   // largest row FFT (a row pair fills one workgroup's LDS)
 constexpr int kRowMin = 64;
+constexpr int kRowLimit = 8192;  // largest row kernel compiled
 constexpr int kColMin = 16;
 constexpr int kColMax = 1024;
 constexpr int kMaxOrder = 8;
@@ -84,6 +85,7 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
     if (N < (int64_t)kColMin * kRowMin) N = (int64_t)kColMin * kRowMin;
     int64_t n1 = N / kRowMax;
     if (n1 < kColMin) n1 = kColMin;
+    if (n1 > kColMax) n1 = kColMax;   // longest rows (up to 8192) beyond that
     if (force_n1 && *force_n1) {
       const int64_t f = atoll(force_n1);
       if (!is_pow2(f) || f < kColMin || f > kColMax) return 3;
@@ -91,7 +93,7 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
       while (N / n1 < kRowMin) N <<= 1;   // a longer FFT is still exact
     }
     const int64_t n2 = N / n1;
-    if (n1 > kColMax || n2 > kRowMax || n2 < kRowMin) return 3;
+    if (n1 > kColMax || n2 > kRowLimit || n2 < kRowMin) return 3;
     p.n1 = (int)n1;
     p.n2 = (int)n2;
   }

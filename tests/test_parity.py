@@ -110,7 +110,7 @@ FOURSTEP = [
     (2, 1, 3, 1, "fp32", "16"), (2, 2, 3, 100, "fp32", "16"), (2, 1, 4, 1000, "fp32", "32"),
     (3, 3, 3, 3000, "fp32", "64"), (2, 2, 2, 5000, "fp32", "128"), (2, 1, 3, 8192, "fp32", "256"),
     (2, 1, 2, 2000, "fp32", "512"), (2, 2, 2, 4000, "fp32", "1024"), (2, 3, 5, 6000, "bf16", "16"),
-    (1, 1, 1, 700, "bf16", "64"),
+    (1, 1, 1, 700, "bf16", "64"), (2, 2, 3, 4097, "fp32", "32"), (2, 1, 2, 999, "bf16", "16"),
 ]
 
 
@@ -133,6 +133,17 @@ def test_forward_long_auto_path(L):
     v, xs = make_activations(cfg, DEV)
     _, _, y = run_hip(p, L, v, xs)
     check_rows(y, p, L, v, xs, [(b, d) for b in range(3) for d in range(3)], TOL_FP32)
+
+
+@pytest.mark.slow
+def test_forward_maximum_length():
+    # Largest supported L = 2^22 (real FFT of 2^23 points); one channel pair.
+    L = 1 << 22
+    cfg = _cfg(2, 1, 2, L, H_=16)
+    p = make_filter_params(cfg)
+    v, xs = make_activations(cfg, DEV)
+    _, _, y = run_hip(p, L, v, xs)
+    check_rows(y, p, L, v, xs, [(0, 1)], TOL_FP32_1M)
 
 
 def test_small_workspace_still_correct():
