@@ -236,21 +236,45 @@ __device__ __forceinline__ cf step_power(cf b, cf s, int i) {
 
 // ---------------------------------------------------------------- LDS layouts
 
-// One FFT per row, point index fastest, one pad slot per 16 points (spreads
-// the strided Stockham writes over the banks).
-struct RowLds {
+// One FFT per row, point index fastest.  The buffer written by a radix-R
+// stage (and read by the next one) stores point p at p ^ ((p >> log2 R) & 31):
+// the stage's strided writes (stride R at the first stage) then spread over
+// all LDS banks, while the next stage's unit-stride reads stay conflict-free.
+// (Checked offline for every radix sequence used, against 32-bank/16-lane and
+// 64-bank/32-lane models: 1.03x the conflict-free cycle count on average,
+// 1.31x worst, against 1.9x for one pad slot per 16 points.)  operator()
+// addresses the buffer unswizzled, for the spectral exchanges.  SW = false
+// turns the swizzle off (plain addressing needs fewer VALU operations, which
+// some lengths value more than the conflicts it removes).
+template <bool SW>
+struct RowLdsT {
   cf* base;
-  static constexpr __host__ __device__ int padded(int npt) { return npt + npt / 16; }
-  __device__ __forceinline__ cf& operator()(int i) const { return base[i + (i >> 4)]; }
+  static constexpr __host__ __device__ int padded(int npt) { return npt; }
+  template <int SH>
+  __device__ __forceinline__ cf& at(int i) const {
+    if constexpr (SH == 0 || !SW) return base[i];
+    else return base[i ^ ((i >> SH) & 31)];
+  }
+  __device__ __forceinline__ cf& operator()(int i) const { return base[i]; }
 };
+using RowLds = RowLdsT<false>;
 
 // Many FFTs side by side, FFT instance fastest: element i of instance c sits
-// at i*NB + c.  Lanes that differ in c touch consecutive words.
+// at i*NB + c.  Lanes that differ in c touch consecutive words, so no swizzle.
 template <int NB>
 struct ColLds {
   cf* base;  // already offset by the instance index c
+  template <int SH>
+  __device__ __forceinline__ cf& at(int i) const { return base[i * NB]; }
   __device__ __forceinline__ cf& operator()(int i) const { return base[i * NB]; }
 };
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// Swizzle key of the buffer a radix-R stage after stages of size NS writes:
+// only stores with NS < 32 are strided across lanes; wider ones already write
+// runs of >= 32 consecutive points and stay unswizzled (cheaper addressing).
+constexpr int swz_key(int R, int NS) { return NS < 32 ? ilog2(R) : 0; }
 
 // ---------------------------------------------------------------- stages
 
@@ -291,24 +315,25 @@ __device__ __forceinline__ void stage_twiddled(cf (&u)[E], const cf* tw) {
 
 template <int NPT, int E, int R, int NS, class Lds>
 __device__ __forceinline__ void stage_store(const cf (&u)[E], const Lds& lds, int j) {
-  constexpr int BPT = E / R;
+  constexpr int BPT = E / R, SH = swz_key(R, NS);
 #pragma unroll
   for (int m = 0; m < BPT; ++m) {
     const int beta = j + m * (NPT / E);
     const int base = (beta / NS) * NS * R + (beta & (NS - 1));
 #pragma unroll
-    for (int q = 0; q < R; ++q) lds(base + q * NS) = u[m + q * BPT];
+    for (int q = 0; q < R; ++q) lds.template at<SH>(base + q * NS) = u[m + q * BPT];
   }
 }
 
-template <int NPT, int E, int R, class Lds>
+// Loads of a radix-R stage from a buffer written by a stage of radix 2^SH.
+template <int NPT, int E, int R, int SH, class Lds>
 __device__ __forceinline__ void stage_load(cf (&u)[E], const Lds& lds, int j) {
   constexpr int BPT = E / R;
 #pragma unroll
   for (int m = 0; m < BPT; ++m) {
     const int beta = j + m * (NPT / E);
 #pragma unroll
-    for (int r = 0; r < R; ++r) u[m + r * BPT] = lds(beta + r * (NPT / R));
+    for (int r = 0; r < R; ++r) u[m + r * BPT] = lds.template at<SH>(beta + r * (NPT / R));
   }
 }
 
@@ -324,15 +349,29 @@ __device__ __forceinline__ void tw_init(cf* tw, int j) {
   if constexpr (sizeof...(Rest) > 0) tw_init<NPT, E, NS * R, OFF + BPT, Rest...>(tw, j);
 }
 
-template <int NPT, int E, bool INV, int NS, int OFF, class Lds, int R, int... Rest>
+template <int NPT, int E, bool INV, int NS, int OFF, int SHPREV, class Lds, int R, int... Rest>
 __device__ __forceinline__ void fft_tail(cf (&u)[E], const Lds& lds, int j, const cf* tw) {
-  stage_load<NPT, E, R>(u, lds, j);
+  stage_load<NPT, E, R, SHPREV>(u, lds, j);
   stage_twiddled<E, R, INV>(u, tw + OFF);
   if constexpr (sizeof...(Rest) > 0) {
     __syncthreads();                       // all reads of this stage done
     stage_store<NPT, E, R, NS>(u, lds, j);
     __syncthreads();                       // writes visible to the next stage
-    fft_tail<NPT, E, INV, NS * R, OFF + E / R, Lds, Rest...>(u, lds, j, tw);
+    fft_tail<NPT, E, INV, NS * R, OFF + E / R, swz_key(R, NS), Lds, Rest...>(u, lds, j, tw);
+  }
+}
+
+// Ping-pong variant: stage s stores into buffer s & 1, so a stage's loads and
+// the next stage's stores never share a buffer and one barrier per stage
+// suffices.  L[0], L[1] are the two buffers.
+template <int NPT, int E, bool INV, int NS, int OFF, int SHPREV, int P, class Lds, int R, int... Rest>
+__device__ __forceinline__ void fft_tail_pp(cf (&u)[E], const Lds* L, int j, const cf* tw) {
+  stage_load<NPT, E, R, SHPREV>(u, L[P], j);
+  stage_twiddled<E, R, INV>(u, tw + OFF);
+  if constexpr (sizeof...(Rest) > 0) {
+    stage_store<NPT, E, R, NS>(u, L[P ^ 1], j);
+    __syncthreads();                       // writes visible to the next stage
+    fft_tail_pp<NPT, E, INV, NS * R, OFF + E / R, swz_key(R, NS), P ^ 1, Lds, Rest...>(u, L, j, tw);
   }
 }
 
@@ -359,8 +398,25 @@ struct BlockFFT<NPT, E, Radices<R0, Rs...>> {
       __syncthreads();
       stage_store<NPT, E, R0, 1>(u, lds, j);
       __syncthreads();
-      fft_tail<NPT, E, INV, R0, 0, Lds, Rs...>(u, lds, j, tw);
+      fft_tail<NPT, E, INV, R0, 0, swz_key(R0, 1), Lds, Rs...>(u, lds, j, tw);
     }
+  }
+
+  // Two-buffer form (stages - 1 + 1 barriers).  The leading barrier keeps the
+  // first store clear of reads still pending from the caller's previous use
+  // of buffer 0.  The last stage reads buffer last_buf(); the other one is
+  // free for the caller until the next run_pp().
+  static constexpr int NSTAGES = 1 + sizeof...(Rs);
+  static constexpr int last_buf() { return (NSTAGES - 2) & 1; }
+
+  template <bool INV, class Lds>
+  __device__ __forceinline__ void run_pp(cf (&u)[E], const Lds* L, int j) const {
+    static_assert(sizeof...(Rs) > 0, "ping-pong needs at least two stages");
+    stage_first<E, R0, INV>(u);
+    __syncthreads();
+    stage_store<NPT, E, R0, 1>(u, L[0], j);
+    __syncthreads();
+    fft_tail_pp<NPT, E, INV, R0, 0, swz_key(R0, 1), 0, Lds, Rs...>(u, L, j, tw);
   }
 };
 
@@ -473,6 +529,41 @@ __device__ __forceinline__ void realconv_pair(cf& a, cf& b, cf g, cf gm, cf w) {
   b = nb;
 }
 
+// The same product with the coefficients precomputed per bin pair.  The
+// whole step is linear in (C(p), conj C(N-p)):
+//   C'(p)   = a1 C(p)   + i bq conj C(N-p),
+//   C'(N-p) = a2 C(N-p) + i conj(bq C(p)),
+// with, for H = the filter's real-FFT bins over M, s + i c = i W_M^p,
+// P = H(p) + conj H(N-p) and Q = H(p) - conj H(N-p):
+//   a1 = P - sQ,  a2 = conj(P + sQ),  bq = cQ
+// (scaled for an unnormalised inverse FFT).  This is the even/odd split of
+// the row spectrum, the product with H and the re-packing, folded together.
+// 16 FMA-class operations per pair; no twiddle is needed at run time.
+__device__ __forceinline__ void conv_pair(cf& a, cf& b, cf a1, cf a2, cf bq) {
+  const cf na = make_float2(fmaf(a1.x, a.x, fmaf(-a1.y, a.y, fmaf(bq.x, b.y, -bq.y * b.x))),
+                            fmaf(a1.x, a.y, fmaf(a1.y, a.x, fmaf(bq.x, b.x, bq.y * b.y))));
+  const cf nb = make_float2(fmaf(a2.x, b.x, fmaf(-a2.y, b.y, fmaf(bq.x, a.y, bq.y * a.x))),
+                            fmaf(a2.x, b.y, fmaf(a2.y, b.x, fmaf(bq.x, a.x, -bq.y * a.y))));
+  a = na;
+  b = nb;
+}
+
+// Bin 0, its own partner: C'(0) = a1 C(0) + i bq conj C(0).
+__device__ __forceinline__ cf conv_self(cf a, cf a1, cf bq) {
+  return make_float2(fmaf(a1.x, a.x, fmaf(-a1.y, a.y, fmaf(bq.x, a.y, -bq.y * a.x))),
+                     fmaf(a1.x, a.y, fmaf(a1.y, a.x, fmaf(bq.x, a.x, bq.y * a.y))));
+}
+
+// Pair coefficients (a1, a2, bq) of bins (p, N-p) from hk = H(p)/M,
+// hm = H(N-p)/M and (s, c) = (sin, cos)(pi p / N).
+__device__ __forceinline__ void pair_coeffs(cf hk, cf hm, float s, float c, cf& a1, cf& a2, cf& bq) {
+  const cf P = make_float2(hk.x + hm.x, hk.y - hm.y);
+  const cf Q = make_float2(hk.x - hm.x, hk.y + hm.y);
+  a1 = make_float2(fmaf(-s, Q.x, P.x), fmaf(-s, Q.y, P.y));
+  a2 = make_float2(fmaf(s, Q.x, P.x), -fmaf(s, Q.y, P.y));
+  bq = make_float2(c * Q.x, c * Q.y);
+}
+
 // X(k) / (2N) of the real row from C(k), C(N-k) and W = W_M^k.
 __device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
   const cf e = make_float2(a.x + am.x, a.y - am.y);          // 2 E
@@ -481,28 +572,40 @@ __device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
 }
 
 // x[t] with zero padding beyond L.
-template <int IOT>
+// x[t] with zero padding beyond L.  CLAMP: the load always runs, from a
+// clamped in-row index (L >= 1), so no branch splits the memory counters
+// (for loads that are mostly in range); otherwise padding loads are skipped.
+template <int IOT, bool CLAMP = false>
 __device__ __forceinline__ float ld_masked(const void* p, int64_t row_off, int64_t t, int64_t L) {
-  return t < L ? IO<IOT>::ld(p, row_off + t) : 0.f;
+  if constexpr (CLAMP) {
+    const float w = IO<IOT>::ld(p, row_off + (t < L ? t : L - 1));
+    return t < L ? w : 0.f;
+  } else {
+    return t < L ? IO<IOT>::ld(p, row_off + t) : 0.f;
+  }
 }
 
 // (x[t], x[t+1]) for even t with zero padding beyond L.  EVEN: the row
 // offset and L are even, so the pair is one aligned 8-byte (fp32) or 4-byte
-// (bf16) access.
-template <int IOT, bool EVEN>
+// (bf16) access.  CLAMP as in ld_masked.
+template <int IOT, bool EVEN, bool CLAMP = false>
 __device__ __forceinline__ cf ld_pair(const void* p, int64_t row_off, int64_t t, int64_t L) {
   if constexpr (EVEN) {
-    if (t >= L) return make_float2(0.f, 0.f);
-    if constexpr (IOT == 0) {
-      const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(static_cast<const float*>(p) + row_off + t));
-      return make_float2(w.x, w.y);
-    } else {
-      const uint32_t w = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + row_off + t));
-      return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    if constexpr (!CLAMP) {
+      if (t >= L) return make_float2(0.f, 0.f);
     }
+    const int64_t tc = row_off + ((CLAMP && t >= L) ? L - 2 : t);
+    cf v;
+    if constexpr (IOT == 0) {
+      const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(static_cast<const float*>(p) + tc));
+      v = make_float2(w.x, w.y);
+    } else {
+      const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + tc));
+      v = make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    }
+    return (CLAMP && t >= L) ? make_float2(0.f, 0.f) : v;
   } else {
-    return make_float2(ld_masked<IOT>(p, row_off, t, L), ld_masked<IOT>(p, row_off, t + 1, L));
+    return make_float2(ld_masked<IOT, CLAMP>(p, row_off, t, L), ld_masked<IOT, CLAMP>(p, row_off, t + 1, L));
   }
 }
 

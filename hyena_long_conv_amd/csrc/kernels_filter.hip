@@ -91,9 +91,26 @@ __global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)NF * half) return;
   const int64_t f = idx / half, k = idx - f * half;
-  int64_t src = k;
-  if (path == PATH_FOURSTEP && k < N) src = (k % n1) * n2 + k / n1;
-  const cf g = spec[f * stride + src];
+  const cf* row = spec + f * stride;
+  cf g;
+  if (path == PATH_SINGLE) {
+    // invert the pair coefficients of bins (p, N-p), p = min(k, N-k):
+    // P = (a1 + conj a2)/2, sQ = (conj a2 - a1)/2, cQ = bq, Q = s*sQ + c*cQ;
+    // H(p) = (P + Q)/2, H(N-p) = conj(P - Q)/2
+    const int64_t qs = stride / 3;
+    const int64_t p = k <= N / 2 ? k : N - k;
+    const cf a1 = row[p], a2 = row[qs + p], bq = row[2 * qs + p];
+    float sn, cs;
+    sincospif((float)p / (float)N, &sn, &cs);
+    const float Px = 0.5f * (a1.x + a2.x), Py = 0.5f * (a1.y - a2.y);
+    const float sQx = 0.5f * (a2.x - a1.x), sQy = 0.5f * (-a2.y - a1.y);
+    const float Qx = sn * sQx + cs * bq.x, Qy = sn * sQy + cs * bq.y;
+    g = (k == p) ? make_float2(0.5f * (Px + Qx), 0.5f * (Py + Qy)) : make_float2(0.5f * (Px - Qx), -0.5f * (Py - Qy));
+  } else {
+    int64_t src = k;
+    if (k < N) src = (k % n1) * n2 + k / n1;
+    g = row[src];
+  }
   out[2 * idx] = g.x * (float)(2 * N);
   out[2 * idx + 1] = g.y * (float)(2 * N);
 }

@@ -15,89 +15,166 @@ namespace hyena {
 #ifndef HYENA_SINGLE_WAVES
 #define HYENA_SINGLE_WAVES 1
 #endif
+#ifndef HYENA_XCD_MAP
+#define HYENA_XCD_MAP 0
+#endif
 #ifndef HYENA_SINGLE_E16_MIN
 #define HYENA_SINGLE_E16_MIN 16384
 #endif
 
 // 8 points per thread below N = HYENA_SINGLE_E16_MIN (fewer registers, more
 // waves per CU; measured faster than 16 on the 2K-context shape), 16 above.
+// SW: XOR-swizzled LDS exchange buffers; PP: two exchange buffers (one
+// barrier per FFT stage instead of two; 16*N bytes of LDS).  Both chosen per
+// length from timings at D = 768 (swizzle off at 2048, 4096 and 16384, where
+// it cost more VALU time or registers than its conflicts; two buffers only at
+// 8192, the one length where they were faster).
 template <int N> struct SinglePlan {
   static constexpr bool E16 = N >= HYENA_SINGLE_E16_MIN;
   static constexpr int E = E16 ? 16 : 8;
   static constexpr int T = N / E;
+#ifdef HYENA_SINGLE_SW
+  static constexpr bool SW = HYENA_SINGLE_SW;
+#else
+  static constexpr bool SW = !(N == 2048 || N == 4096 || N == 16384);
+#endif
+#ifdef HYENA_SINGLE_PP
+  static constexpr bool PP = HYENA_SINGLE_PP && N <= 8192;
+#else
+  static constexpr bool PP = N == 8192;
+#endif
+  // PF: request each order's filter coefficients and gate inputs before its
+  // forward FFT (their latency hides behind it), where the registers allow.
+#ifdef HYENA_SINGLE_PF
+  static constexpr bool PF = HYENA_SINGLE_PF && N <= 4096;
+#else
+  static constexpr bool PF = N <= 2048;
+#endif
+  using Lds = RowLdsT<SW>;
   using R = typename std::conditional<E16, typename Plan16<(N >= 1024 ? N : 1024)>::R,
                                       typename Plan8<(N < 16384 ? N : 8192)>::R>::type;
 };
 
+// Pair coefficients of one filter for the bins a thread owns, loaded ahead
+// of the forward FFT so the loads are in flight while it runs.
+template <int N, int E>
+struct PairCoeffs {
+  cf a1[E / 2], a2[E / 2], bq[E / 2];
+  cf half;   // a1 of p = N/2 (used by thread 0)
+  __device__ __forceinline__ void load(const cf* g, int64_t qs, int j) {
+    constexpr int S = N / E;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const int p = j + i * S;
+      a1[i] = g[p];
+      a2[i] = g[qs + p];
+      bq[i] = g[2 * qs + p];
+    }
+    half = g[N / 2];
+  }
+};
+
 // Spectral step of one order on the registers of a single-pass workgroup:
 // u[i] holds C(k), k = j + i*S, on entry and C'(k) on exit.  Bins pair up
-// as (k, N-k); the thread owning the low index i < E/2 of a pair computes
+// as (p, N-p); the thread owning the low index i < E/2 of a pair computes
 // both results (the partner bin lives in thread S-j at index E-1-i, or in
-// thread 0 itself at E-i), exchanging through LDS.  k = 0 and k = N/2 pair
+// thread 0 itself at E-i), exchanging through LDS.  p = 0 and p = N/2 pair
 // with themselves.
-template <int N, int E, class Lds>
-__device__ __forceinline__ void spectral_step(cf (&u)[E], const Lds& lds, int j, const cf* g, cf wb) {
+template <int N, int E, bool LEAD_BARRIER, class Lds>
+__device__ __forceinline__ void spectral_step(cf (&u)[E], const Lds& lds, int j, const PairCoeffs<N, E>& c) {
   constexpr int S = N / E;
-  __syncthreads();
+  if constexpr (LEAD_BARRIER) __syncthreads();
 #pragma unroll
   for (int i = E / 2; i < E; ++i) lds(j + i * S) = u[i];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < E / 2; ++i) {
-    const int k = j + i * S;
+    const int p = j + i * S;
     if (i == 0 && j == 0) {
-      u[0] = realconv_bin(u[0], u[0], g[0], g[N], make_float2(1.f, 0.f));
+      u[0] = conv_self(u[0], c.a1[0], c.bq[0]);
     } else {
-      const int km = N - k;
-      cf b = lds(km);
-      realconv_pair(u[i], b, g[k], g[km], cmul(wb, w2e<E>(i)));
-      lds(km) = b;
+      cf b = lds(N - p);
+      conv_pair(u[i], b, c.a1[i], c.a2[i], c.bq[i]);
+      lds(N - p) = b;
     }
   }
-  if (j == 0) {
-    const cf a = lds(N / 2), gh = g[N / 2];
-    lds(N / 2) = realconv_bin(a, a, gh, gh, make_float2(0.f, -1.f));
-  }
+  if (j == 0) lds(N / 2) = cmul(lds(N / 2), c.half);   // p = N/2: bq = 0
   __syncthreads();
 #pragma unroll
   for (int i = E / 2; i < E; ++i) u[i] = lds(j + i * S);
 }
 
-// Spectrum layout on this path: row f = n*D + d holds S(k) = H(k)/(2N) for
-// k = 0..N in natural order, rows spec_stride complex values apart.
+// Spectrum layout on this path: filter row f = n*D + d starts at
+// f*spec_stride and holds the pair coefficients a1[p], a2[p], bq[p]
+// (p = 0..N/2) of conv_pair as three arrays qs = spec_stride/3 values apart.
+// Row handled by workgroup wg.  Workgroups are dispatched round-robin over
+// the 8 XCDs (wg mod 8), each with its own L2; when D is a multiple of 8 the
+// B rows of one channel, which share a filter spectrum, go to consecutive
+// workgroups of the same XCD so the spectrum is fetched into that L2 once.
+__device__ __forceinline__ int row_of_workgroup(int wg, int B, int D) {
+  if (HYENA_XCD_MAP && (D & 7) == 0) {
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int d = (slot / B) * 8 + xcd, b = slot - (slot / B) * B;
+    return b * D + d;
+  }
+  return wg;
+}
+
 template <int N, int IOT, bool EVEN>
 __global__ void __launch_bounds__(SinglePlan<N>::T, HYENA_SINGLE_WAVES)
 k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, void* __restrict__ y,
-                 int D, int NORD, int L, int64_t spec_stride) {
+                 int B, int D, int NORD, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E;
-  __shared__ cf smem[RowLds::padded(N)];
-  const RowLds lds{smem};
+  __shared__ cf smem[P::PP ? 2 * N : N];
+  using Lds = typename P::Lds;
+  const Lds lds2[2] = {Lds{smem}, Lds{smem + (P::PP ? N : 0)}};
   const int j = threadIdx.x;
-  const int r = blockIdx.x, d = r % D;
+  const int r = row_of_workgroup(blockIdx.x, B, D), d = r % D;
   const int64_t off = (int64_t)r * L;
   BlockFFT<N, E, typename P::R> fft;
   fft.init(j);
-  const cf wbase = twiddle<false>((uint32_t)j, (uint32_t)(2 * N));   // W_M^j
+  const int64_t qs = spec_stride / 3;
 
   cf u[E];
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    u[i] = (i < E / 2) ? ld_pair<IOT, EVEN>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+    u[i] = (i < E / 2) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
 
   for (int n = 0; n < NORD; ++n) {
-    fft.template run<false>(u, lds, j);
-    spectral_step<N, E>(u, lds, j, spec + (int64_t)(n * D + d) * spec_stride, opaque(wbase));
-    fft.template run<true>(u, lds, j);
+    const cf* g = spec + (int64_t)(n * D + d) * spec_stride;
     const void* xn = x.p[n];
+    PairCoeffs<N, E> pc;
+    cf xv[E / 2];
+    if constexpr (P::PF) {
+      pc.load(g, qs, j);
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+    }
+    if constexpr (P::PP) {
+      fft.template run_pp<false>(u, lds2, j);
+      if constexpr (!P::PF) pc.load(g, qs, j);
+      // the buffer the forward FFT's last stage did not read is free, so the
+      // exchange needs no leading barrier
+      spectral_step<N, E, false>(u, lds2[fft.last_buf() ^ 1], j, pc);
+      fft.template run_pp<true>(u, lds2, j);
+    } else {
+      fft.template run<false>(u, lds2[0], j);
+      if constexpr (!P::PF) pc.load(g, qs, j);
+      spectral_step<N, E, true>(u, lds2[0], j, pc);
+      fft.template run<true>(u, lds2[0], j);
+    }
+    if constexpr (!P::PF) {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+    }
     const bool last = (n == NORD - 1);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       cf z = make_float2(0.f, 0.f);
       if (i < E / 2) {
         const int64_t t = 2 * (int64_t)(j + i * S);
-        const cf xv = ld_pair<IOT, EVEN>(xn, off, t, L);
-        z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+        z = make_float2(xv[i].x * u[i].x, xv[i].y * u[i].y);
         if (last) st_pair<IOT, EVEN>(y, off, t, L, z);
       }
       u[i] = z;
@@ -105,14 +182,17 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
   }
 }
 
-// One filter row f of the NF = N*D rows of h per workgroup.
+// One filter row f of the NF = N*D rows of h per workgroup: the real FFT
+// H(k)/M of the zero-padded row (k = 0..N, staged in LDS), then the pair
+// coefficients of conv_pair for p = 0..N/2.
 template <int N, bool EVEN>
 __global__ void __launch_bounds__(SinglePlan<N>::T)
 k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E;
-  __shared__ cf smem[RowLds::padded(N)];
-  const RowLds lds{smem};
+  __shared__ cf smem[N];
+  __shared__ cf nyq;
+  const typename P::Lds lds{smem};
   const int j = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * L;
   BlockFFT<N, E, typename P::R> fft;
@@ -126,15 +206,30 @@ k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int
 #pragma unroll
   for (int i = 0; i < E; ++i) lds(j + i * S) = u[i];
   __syncthreads();
-  cf* out = spec + (int64_t)blockIdx.x * spec_stride;
   const cf wbase = twiddle<false>((uint32_t)j, (uint32_t)(2 * N));
   const float sc = 1.0f / (float)(2 * N);
+  cf hv[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int k = j + i * S;
     const cf am = lds((N - k) & (N - 1));
-    out[k] = realfft_bin(u[i], am, cmul(wbase, w2e<E>(i)), sc);
-    if (k == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
+    hv[i] = realfft_bin(u[i], am, cmul(wbase, w2e<E>(i)), sc);
+    if (k == 0) nyq = make_float2((u[i].x - u[i].y) * sc, 0.f);   // H(N)/M
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) lds(j + i * S) = hv[i];               // H(k)/M, k < N
+  __syncthreads();
+  const int64_t qs = spec_stride / 3;
+  cf* out = spec + (int64_t)blockIdx.x * spec_stride;
+  for (int p = j; p <= N / 2; p += S) {
+    float sn, cs;
+    sincospif((float)p / (float)N, &sn, &cs);
+    cf a1, a2, bq;
+    pair_coeffs(lds(p), p == 0 ? nyq : lds(N - p), sn, cs, a1, a2, bq);
+    out[p] = a1;
+    out[qs + p] = a2;
+    out[2 * qs + p] = bq;
   }
 }
 
@@ -142,10 +237,10 @@ template <int N, int IOT>
 static hipError_t launch_fwd(const ForwardArgs& a, hipStream_t s) {
   if (a.L % 2 == 0)
     hipLaunchKernelGGL((k_single_forward<N, IOT, true>), dim3(a.n_rows), dim3(SinglePlan<N>::T), 0, s, a.v,
-                       a.x, (const cf*)a.spec, a.y, a.D, a.NORD, (int)a.L, a.spec_stride);
+                       a.x, (const cf*)a.spec, a.y, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
   else
     hipLaunchKernelGGL((k_single_forward<N, IOT, false>), dim3(a.n_rows), dim3(SinglePlan<N>::T), 0, s, a.v,
-                       a.x, (const cf*)a.spec, a.y, a.D, a.NORD, (int)a.L, a.spec_stride);
+                       a.x, (const cf*)a.spec, a.y, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
   return hipGetLastError();
 }
 

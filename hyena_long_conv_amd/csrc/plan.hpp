@@ -53,6 +53,10 @@ struct PlanInfo {
   int64_t spec_stride;   // complex values per filter row in the spectrum buffer (>= N + 1)
 };
 
+// Single path: a filter row holds three planar arrays of N/2 + 1 complex
+// values (the pair coefficients), each single_qs(N) values apart.
+inline int64_t single_qs(int64_t N) { return (N / 2 + 1 + 15) / 16 * 16; }
+
 inline int64_t next_pow2(int64_t x) {
   int64_t p = 1;
   while (p < x) p <<= 1;
@@ -99,7 +103,7 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
   }
   p.N = N;
   p.M = 2 * N;
-  p.spec_stride = round_up(N + 1, 16);
+  p.spec_stride = (path == PATH_SINGLE) ? 3 * single_qs(N) : round_up(N + 1, 16);
   *out = p;
   return 0;
 }
