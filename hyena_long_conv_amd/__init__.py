@@ -179,27 +179,43 @@ def spectrum_export(spec, D: int, N: int, L: int):
     return torch.view_as_complex(out)
 
 
+class PreparedForward:
+    """hyena_forward with its arguments checked and marshalled once: each
+    call() is a single C-ABI call on the stream that was current at
+    preparation (for loops over fixed buffers, where the per-call Python
+    checks would otherwise cost as much as a short kernel)."""
+
+    def __init__(self, v, xs, spec, out=None, workspace=None):
+        import torch
+        if v.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("v must be float32 or bfloat16")
+        _need_cuda(v, "v", v.dtype)
+        B, D, L = v.shape
+        N = len(xs)
+        for i, x in enumerate(xs):
+            _need_cuda(x, f"x[{i}]", v.dtype)
+            if tuple(x.shape) != (B, D, L):
+                raise ValueError(f"x[{i}] shape {tuple(x.shape)} != {(B, D, L)}")
+        io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
+        y = out if out is not None else torch.empty_like(v)
+        _need_cuda(y, "y", v.dtype)
+        wsb = int(lib().hyena_forward_workspace_bytes(B, D, N, L, io))
+        if workspace is None and wsb > 0:
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
+        self.y = y
+        self._keep = (v, tuple(xs), spec, y, workspace)     # the buffers stay alive while prepared
+        self._fn = lib().hyena_forward
+        self._args = (_ptr(v), (ctypes.c_void_p * N)(*[x.data_ptr() for x in xs]), _ptr(spec), _ptr(y),
+                      B, D, N, L, io, _ptr(workspace),
+                      workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(v))
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise HyenaError(code, "hyena_forward")
+        return self.y
+
+
 def forward(v, xs, spec, out=None, workspace=None):
     """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16)."""
-    import torch
-    if v.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("v must be float32 or bfloat16")
-    _need_cuda(v, "v", v.dtype)
-    B, D, L = v.shape
-    N = len(xs)
-    for i, x in enumerate(xs):
-        _need_cuda(x, f"x[{i}]", v.dtype)
-        if tuple(x.shape) != (B, D, L):
-            raise ValueError(f"x[{i}] shape {tuple(x.shape)} != {(B, D, L)}")
-    io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
-    y = out if out is not None else torch.empty_like(v)
-    _need_cuda(y, "y", v.dtype)
-    wsb = int(lib().hyena_forward_workspace_bytes(B, D, N, L, io))
-    if workspace is None and wsb > 0:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
-    xp = (ctypes.c_void_p * N)(*[x.data_ptr() for x in xs])
-    _check(lib().hyena_forward(_ptr(v), xp, _ptr(spec), _ptr(y), B, D, N, L, io, _ptr(workspace),
-                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                               _stream(v)),
-           "hyena_forward")
-    return y
+    return PreparedForward(v, xs, spec, out, workspace)()
