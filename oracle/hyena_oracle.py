@@ -38,12 +38,26 @@ What the operator computes (restated):
     convolution equals the linear one.  Any FFT length >= 2L-1 gives the same
     exact result; the oracle uses the next power of two >= 2L.
 
+The block around the operator (restated):
+  * [P4] framework figure: the input u (L x D) goes through one linear
+    projection of width (N+1)D that yields v (the initial state) and the gates
+    x_1..x_N; [P1] "計算方法" counts this dense work as the D in
+    O(NDL(log L + D)).
+  * [P3] section 2 "Hyena 演算子の構造": each projected stream is featurised by
+    its own short convolution (h_T, h_H, h_K there), and the operator's output
+    is mapped back by a dense matrix M.
+
 Readings where the pages are silent (each listed in the design notes):
   positional features e(t) = [t/L, sin(2*pi*k*t/L) for k=1..K,
   cos(2*pi*k*t/L) for k=1..K]; FFN = affine -> sin -> affine -> sin -> affine
   (sin with unit frequency, "2-layer" counting hidden layers); output column
   j = n*D + d feeds filter h_n of channel d; window exp(-alpha_d * t / L) is
   the same for every order; no bias/skip term, no normalisation.
+  Block: projection weights row-major [out][in] with output column c = s*D + d
+  feeding stream s (s = 0 is v, s = n is x_n) of channel d; the short
+  convolution is causal and depthwise (one T-tap filter per projected
+  column, tap j weighting the sample j steps back, zero before t = 0); biases
+  of both projections optional; the output projection has no activation.
 """
 from __future__ import annotations
 
@@ -59,6 +73,10 @@ __all__ = [
     "causal_conv",
     "hyena_forward",
     "filter_spectrum",
+    "short_conv",
+    "in_projection",
+    "out_projection",
+    "block_forward",
     "DIRECT_MAX_L",
 ]
 
@@ -247,3 +265,54 @@ def filter_spectrum(h: np.ndarray, P: int) -> np.ndarray:
     assert P >= 2 * L
     hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
     return fft(hp)[..., : P // 2 + 1]
+
+
+# ---------------------------------------------------------------------------
+# The block around the operator ([P4] framework figure, projection node;
+# [P3] section 2, featurisation by short convolutions and output matrix M)
+# ---------------------------------------------------------------------------
+
+def short_conv(z: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Causal depthwise FIR along the last axis: out[..., c, t] =
+    sum_{j < T, j <= t} w[c, j] * z[..., c, t - j]  (z: [..., C, L], w: [C, T])."""
+    z = np.asarray(z, np.float64)
+    w = np.asarray(w, np.float64)
+    C, T = w.shape
+    L = z.shape[-1]
+    out = np.zeros_like(z)
+    for j in range(min(T, L)):
+        out[..., j:] += w[:, j, None] * z[..., : L - j]
+    return out
+
+
+def in_projection(u: np.ndarray, W_in, b_in, w_short, N: int):
+    """u [B, L, D] -> (v, [x_1..x_N]), each [B, D, L]: the (N+1)D-wide
+    projection u W_in^T (+ b_in), then the short causal FIR of every projected
+    column, split in blocks of D columns (v first)."""
+    u = np.asarray(u, np.float64)
+    W_in = np.asarray(W_in, np.float64)
+    B, L, D = u.shape
+    assert W_in.shape == ((N + 1) * D, D)
+    Z = u @ W_in.T
+    if b_in is not None:
+        Z = Z + np.asarray(b_in, np.float64)
+    S = short_conv(np.transpose(Z, (0, 2, 1)), w_short)          # [B, (N+1)D, L]
+    return S[:, :D], [S[:, n * D:(n + 1) * D] for n in range(1, N + 1)]
+
+
+def out_projection(y: np.ndarray, W_out, b_out) -> np.ndarray:
+    """y [B, D, L] -> [B, L, D]: out[b, t, e] = sum_d W_out[e, d] y[b, d, t] (+ b_out[e])."""
+    o = np.transpose(np.asarray(y, np.float64), (0, 2, 1)) @ np.asarray(W_out, np.float64).T
+    if b_out is not None:
+        o = o + np.asarray(b_out, np.float64)
+    return o
+
+
+def block_forward(u: np.ndarray, bp: dict, h: np.ndarray, conv=causal_conv) -> np.ndarray:
+    """u [B, L, D] -> [B, L, D]: in_projection, the order-N operator with
+    filters h [N, D, L], out_projection.  bp holds W_in, b_in, w_short, W_out,
+    b_out (biases may be None)."""
+    N = h.shape[0]
+    v, xs = in_projection(u, bp["W_in"], bp.get("b_in"), bp["w_short"], N)
+    y = hyena_forward(v, xs, h, conv=conv)
+    return out_projection(y, bp["W_out"], bp.get("b_out"))

@@ -17,7 +17,11 @@ for them:
   * DNA-style v: tokens i.i.d. uniform over a 4-symbol alphabet, looked up in
     a 4 x D embedding table drawn from N(0, 1);
   * filter FFN weights ~ N(0, 1/fan_in) (numpy PCG64 per layer), biases 0,
-    window rates alpha_d linearly spaced in [1, 10].
+    window rates alpha_d linearly spaced in [1, 10];
+  * block around the operator: input u [B][L][D] ~ N(0, 1), projection
+    weights W_in [(N+1)D][D] and W_out [D][D] ~ N(0, 1/D), short filters
+    [(N+1)D][T] ~ N(0, 1/T), biases zero unless asked for; projection weights
+    and u are rounded to bf16 where the I/O dtype is bf16.
 """
 from __future__ import annotations
 
@@ -26,7 +30,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_filter_params", "make_activations",
-           "config_by_name"]
+           "config_by_name", "make_block_params", "make_block_input", "bf16_round"]
 
 
 @dataclass(frozen=True)
@@ -132,3 +136,38 @@ def make_activations(cfg: Config, device="cpu", B: int | None = None):
     xs = [x.to(dt).contiguous() for x in xs]
     return v, xs
 
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to even), as float32."""
+    a = np.ascontiguousarray(a, np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def make_block_params(cfg: Config, T: int = 3, bias_scale: float = 0.0) -> dict:
+    """Weights of the block around the operator (numpy float32; W_in and W_out
+    hold bf16-representable values when the I/O dtype is bf16)."""
+    D, C = cfg.D, (cfg.N + 1) * cfg.D
+    r = [_np_rng(cfg.seed, 300 + i) for i in range(5)]
+    W_in = (r[0].standard_normal((C, D)) / np.sqrt(D)).astype(np.float32)
+    W_out = (r[1].standard_normal((D, D)) / np.sqrt(D)).astype(np.float32)
+    w_short = (r[2].standard_normal((C, T)) / np.sqrt(T)).astype(np.float32)
+    if cfg.io == "bf16":
+        W_in, W_out = bf16_round(W_in), bf16_round(W_out)
+    b_in = (bias_scale * r[3].standard_normal(C)).astype(np.float32) if bias_scale > 0 else None
+    b_out = (bias_scale * r[4].standard_normal(D)).astype(np.float32) if bias_scale > 0 else None
+    return dict(D=D, N=cfg.N, T=T, W_in=W_in, b_in=b_in, w_short=w_short, W_out=W_out, b_out=b_out)
+
+
+def make_block_input(cfg: Config, device="cpu", B: int | None = None):
+    """u [B][L][D] ~ N(0, 1) in the config's I/O dtype (torch, seeded)."""
+    import torch
+
+    B = cfg.B if B is None else B
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed * 1000 + 500)
+    u = torch.randn((B, cfg.L, cfg.D), generator=g, device=dev, dtype=torch.float32)
+    return u.to(torch.float32 if cfg.io == "fp32" else torch.bfloat16).contiguous()
