@@ -8,6 +8,11 @@ fallback: without the built library every call raises.
     h    = filter_gen(params, L)          # [N, D, L] fp32
     spec = filter_spectrum(h)             # opaque spectrum, reused across calls
     y    = forward(v, [x1, ..., xN], spec)
+
+    # the block around the operator (projections, short convolutions)
+    v, xs = in_projection(u, bp)          # u [B, L, D] -> v, x_n [B, D, L]
+    out   = out_projection(y, bp)         # [B, D, L] -> [B, L, D]
+    out   = block_forward(u, bp, spec)    # all three in one call
 """
 from __future__ import annotations
 
@@ -17,7 +22,8 @@ import re
 
 __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectrum_export",
            "forward", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
-           "LIB_PATH", "HEADER_PATH", "header_functions"]
+           "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
+           "in_projection", "out_projection", "block_forward", "block_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
@@ -44,6 +50,12 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int64), ("M", ctypes.c_int64), ("path", ctypes.c_int32),
                 ("n1", ctypes.c_int32), ("n2", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("spec_stride", ctypes.c_int64)]
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("N", ctypes.c_int32), ("T", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("W_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p), ("w_short", ctypes.c_void_p),
+                ("W_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -74,6 +86,15 @@ def lib() -> ctypes.CDLL:
     L.hyena_forward_workspace_bytes.restype = i64
     L.hyena_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, vp, i64, vp]
     L.hyena_forward.restype = i32
+    bp = ctypes.POINTER(BlockParams)
+    L.hyena_in_projection.argtypes = [vp, bp, ctypes.POINTER(vp), i64, i64, i32, vp]
+    L.hyena_in_projection.restype = i32
+    L.hyena_out_projection.argtypes = [vp, bp, vp, i64, i64, i32, vp]
+    L.hyena_out_projection.restype = i32
+    L.hyena_block_workspace_bytes.argtypes = [i64, i32, i32, i64, i32]
+    L.hyena_block_workspace_bytes.restype = i64
+    L.hyena_block_forward.argtypes = [vp, bp, vp, vp, i64, i64, i32, vp, i64, vp]
+    L.hyena_block_forward.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -219,3 +240,84 @@ class PreparedForward:
 def forward(v, xs, spec, out=None, workspace=None):
     """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16)."""
     return PreparedForward(v, xs, spec, out, workspace)()
+
+
+# ---------------------------------------------------------------- the block
+
+def _block_struct(bp: dict, io_dtype):
+    """BlockParams from a dict of torch CUDA tensors (W_in, W_out in the I/O
+    dtype; w_short and optional b_in, b_out fp32) and ints D, N, T."""
+    import torch
+    for k in ("W_in", "W_out"):
+        _need_cuda(bp[k], k, io_dtype)
+    _need_cuda(bp["w_short"], "w_short", torch.float32)
+    for k in ("b_in", "b_out"):
+        if bp.get(k) is not None:
+            _need_cuda(bp[k], k, torch.float32)
+    return BlockParams(int(bp["D"]), int(bp["N"]), int(bp["T"]), 0, _ptr(bp["W_in"]).value,
+                       _ptr(bp.get("b_in")).value, _ptr(bp["w_short"]).value, _ptr(bp["W_out"]).value,
+                       _ptr(bp.get("b_out")).value)
+
+
+def _io_of(t):
+    import torch
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("activations must be float32 or bfloat16")
+    return HYENA_FP32 if t.dtype == torch.float32 else HYENA_BF16
+
+
+def in_projection(u, bp: dict, out=None):
+    """u [B, L, D] -> (v, [x_1..x_N]), each [B, D, L] in u's dtype."""
+    import torch
+    io = _io_of(u)
+    _need_cuda(u, "u", u.dtype)
+    B, L, D = u.shape
+    N = int(bp["N"])
+    p = _block_struct(bp, u.dtype)
+    streams = out if out is not None else [torch.empty((B, D, L), dtype=u.dtype, device=u.device)
+                                           for _ in range(N + 1)]
+    for i, t in enumerate(streams):
+        _need_cuda(t, f"stream[{i}]", u.dtype)
+    sp = (ctypes.c_void_p * (N + 1))(*[t.data_ptr() for t in streams])
+    _check(lib().hyena_in_projection(_ptr(u), ctypes.byref(p), sp, B, L, io, _stream(u)), "hyena_in_projection")
+    return streams[0], list(streams[1:])
+
+
+def out_projection(y, bp: dict, out=None):
+    """y [B, D, L] -> [B, L, D] in y's dtype."""
+    import torch
+    io = _io_of(y)
+    _need_cuda(y, "y", y.dtype)
+    B, D, L = y.shape
+    p = _block_struct(bp, y.dtype)
+    o = out if out is not None else torch.empty((B, L, D), dtype=y.dtype, device=y.device)
+    _need_cuda(o, "out", y.dtype)
+    _check(lib().hyena_out_projection(_ptr(y), ctypes.byref(p), _ptr(o), B, L, io, _stream(y)),
+           "hyena_out_projection")
+    return o
+
+
+def block_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32") -> int:
+    return int(lib().hyena_block_workspace_bytes(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16))
+
+
+def block_forward(u, bp: dict, spec, out=None, workspace=None):
+    """u [B, L, D] -> [B, L, D]: in-projection, the order-N operator with the
+    filters whose spectrum is `spec`, out-projection (one C-ABI call)."""
+    import torch
+    io = _io_of(u)
+    _need_cuda(u, "u", u.dtype)
+    B, L, D = u.shape
+    N = int(bp["N"])
+    p = _block_struct(bp, u.dtype)
+    o = out if out is not None else torch.empty_like(u)
+    _need_cuda(o, "out", u.dtype)
+    wsb = block_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16")
+    if wsb < 0:
+        raise HyenaError(2, "hyena_block_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=u.device)
+    _check(lib().hyena_block_forward(_ptr(u), ctypes.byref(p), _ptr(spec), _ptr(o), B, L, io, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(u)),
+           "hyena_block_forward")
+    return o

@@ -211,4 +211,120 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ block
+
+namespace {
+
+bool block_params_ok(const hyena_block_params* p) {
+  return p->D >= 1 && p->D <= (1 << 16) && p->N >= 1 && p->T >= 1 && p->T <= HYENA_MAX_SHORT;
+}
+
+hyena_status check_in_projection(const void* u, const hyena_block_params* p, void* const* streams, int64_t B,
+                                 int64_t L, hyena_dtype io) {
+  if (!u || !p || !streams || !p->W_in || !p->w_short) return HYENA_ERR_NULL;
+  if (!block_params_ok(p) || B < 1 || B > (1 << 20) || L < 1 || L > kMaxL) return HYENA_ERR_SHAPE;
+  if (p->N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  for (int s = 0; s <= p->N; ++s)
+    if (!streams[s]) return HYENA_ERR_NULL;
+  if (!aligned16(u) || !aligned16(p->W_in) || !aligned16(p->w_short) || (p->b_in && !aligned16(p->b_in)))
+    return HYENA_ERR_ALIGN;
+  for (int s = 0; s <= p->N; ++s)
+    if (!aligned16(streams[s])) return HYENA_ERR_ALIGN;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * p->D * L * esz;
+  const int64_t C = (int64_t)(p->N + 1) * p->D;
+  for (int s = 0; s <= p->N; ++s) {
+    if (overlap(streams[s], act, u, act) || overlap(streams[s], act, p->W_in, C * p->D * esz)) return HYENA_ERR_ALIAS;
+    for (int r = 0; r < s; ++r)
+      if (overlap(streams[s], act, streams[r], act)) return HYENA_ERR_ALIAS;
+  }
+  return HYENA_OK;
+}
+
+hyena_status check_out_projection(const void* y, const hyena_block_params* p, void* out, int64_t B, int64_t L,
+                                  hyena_dtype io) {
+  if (!y || !p || !out || !p->W_out) return HYENA_ERR_NULL;
+  if (!block_params_ok(p) || B < 1 || B > (1 << 20) || L < 1 || L > kMaxL) return HYENA_ERR_SHAPE;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(p->W_out) || (p->b_out && !aligned16(p->b_out)))
+    return HYENA_ERR_ALIGN;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * p->D * L * esz;
+  if (overlap(out, act, y, act) || overlap(out, act, p->W_out, (int64_t)p->D * p->D * esz)) return HYENA_ERR_ALIAS;
+  return HYENA_OK;
+}
+
+InProjArgs in_args(const void* u, const hyena_block_params* p, void* const* streams, int64_t B, int64_t L,
+                   hyena_dtype io) {
+  InProjArgs a{};
+  a.u = u; a.W = p->W_in; a.bias = p->b_in; a.w = p->w_short;
+  for (int s = 0; s <= p->N; ++s) a.dst.p[s] = streams[s];
+  a.B = (int)B; a.D = p->D; a.C = (p->N + 1) * p->D; a.T = p->T; a.L = L;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  return a;
+}
+
+OutProjArgs out_args(const void* y, const hyena_block_params* p, void* out, int64_t B, int64_t L, hyena_dtype io) {
+  OutProjArgs a{};
+  a.y = y; a.W = p->W_out; a.bias = p->b_out; a.out = out;
+  a.B = (int)B; a.D = p->D; a.L = L;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  return a;
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+hyena_status hyena_in_projection(const void* u, const hyena_block_params* p, void* const* streams, int64_t B,
+                                 int64_t L, hyena_dtype io, void* stream) {
+  const hyena_status st = check_in_projection(u, p, streams, B, L, io);
+  if (st != HYENA_OK) return st;
+  return in_projection(in_args(u, p, streams, B, L, io), (hipStream_t)stream) == hipSuccess ? HYENA_OK
+                                                                                             : HYENA_ERR_HIP;
+}
+
+hyena_status hyena_out_projection(const void* y, const hyena_block_params* p, void* out, int64_t B, int64_t L,
+                                  hyena_dtype io, void* stream) {
+  const hyena_status st = check_out_projection(y, p, out, B, L, io);
+  if (st != HYENA_OK) return st;
+  return out_projection(out_args(y, p, out, B, L, io), (hipStream_t)stream) == hipSuccess ? HYENA_OK
+                                                                                          : HYENA_ERR_HIP;
+}
+
+int64_t hyena_block_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io) {
+  const int64_t fw = hyena_forward_workspace_bytes(B, D, N, L, io);
+  if (fw < 0) return -1;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  return (int64_t)(N + 2) * align256(B * D * L * esz) + align256(fw);
+}
+
+hyena_status hyena_block_forward(const void* u, const hyena_block_params* p, const void* spec, void* out, int64_t B,
+                                 int64_t L, hyena_dtype io, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!u || !p || !spec || !out || !workspace) return HYENA_ERR_NULL;
+  if (!block_params_ok(p) || B < 1 || B > (1 << 20) || L < 1 || L > kMaxL) return HYENA_ERR_SHAPE;
+  if (p->N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  const int64_t need = hyena_block_workspace_bytes(B, p->D, p->N, L, io);
+  if (need < 0) return HYENA_ERR_SHAPE;
+  if (!aligned16(workspace)) return HYENA_ERR_ALIGN;
+  if (workspace_bytes < need) return HYENA_ERR_WORKSPACE;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * p->D * L * esz, slot = align256(act);
+  if (overlap(out, act, u, act)) return HYENA_ERR_ALIAS;
+  if (overlap(workspace, need, u, act) || overlap(workspace, need, out, act)) return HYENA_ERR_ALIAS;
+  char* w = static_cast<char*>(workspace);
+  void* streams[9];
+  for (int s = 0; s <= p->N; ++s) streams[s] = w + s * slot;
+  void* y = w + (p->N + 1) * slot;
+  void* fws = w + (p->N + 2) * slot;
+  const int64_t fwb = need - (p->N + 2) * slot;
+  hyena_status st = hyena_in_projection(u, p, streams, B, L, io, stream);
+  if (st != HYENA_OK) return st;
+  st = hyena_forward(streams[0], streams + 1, spec, y, B, p->D, p->N, L, io, fwb > 0 ? fws : nullptr, fwb, stream);
+  if (st != HYENA_OK) return st;
+  return hyena_out_projection(y, p, out, B, L, io, stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,480 @@
+// kernels_proj.hip -- the dense projections around the operator, on the
+// matrix cores.
+//
+// In-projection (paper digest, irregular6612.github.io, section "방법 (Method)",
+// framework figure: one projection of width (N+1)D gives v and the gates;
+// homemade-llm "02. 3つの Hyena 演算子", section 2: each projected stream is
+// featurised by its own short convolution):
+//   Z[b][t][c] = sum_k u[b][t][k] W[c][k] + bias[c],
+//   S[b][c][t] = sum_{j<T} w[c][j] Z[b][t-j][c]      (Z = 0 before t = 0),
+// stored as stream c / D, channel c % D of a [B][D][L] (time-fastest) array.
+// Out-projection (same section of homemade-llm, the dense matrix M):
+//   out[b][t][e] = sum_d W[e][d] y[b][d][t] + bias[e].
+//
+// Both compute 128 x 128 output tiles per 256-thread workgroup: four waves of
+// 64 x 64, each a 2 x 2 set of 32 x 32 MFMA accumulators (fp32 operands:
+// v_mfma_f32_32x32x2f32; bf16 operands: v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation).  Operand tiles go global -> registers -> LDS, the next
+// k-stage's loads in flight while the current stage's MFMAs run.  The
+// in-projection walks a strip of consecutive time tiles and carries the last
+// rows of Z from tile to tile, so the short convolution needs no recomputed
+// halo except at a strip's first tile.
+#include <hip/hip_runtime.h>
+
+#include "fft_engine.hpp"
+#include "launch.hpp"
+
+namespace hyena {
+namespace {
+
+constexpr int TM = 128, TN = 128, TT = 256;   // tile rows, tile columns, threads
+constexpr int HALO = 16;                       // carried Z rows (T - 1 <= 15)
+constexpr int ZLD = HALO + TM + 5;             // epilogue row stride (odd: fewer bank conflicts)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int IOT> struct Op;
+template <> struct Op<0> {       // fp32: 32 k per stage, rows padded to 33
+  using E = float;
+  static constexpr int BK = 32, LDK = 33, W = 4;
+};
+template <> struct Op<1> {       // bf16: 64 k per stage, rows padded to 72 (16-byte aligned)
+  using E = uint16_t;
+  static constexpr int BK = 64, LDK = 72, W = 8;
+};
+
+__device__ __forceinline__ float ld_f(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+template <int IOT>
+__device__ __forceinline__ void st_f(void* p, int64_t i, float v) {
+  if constexpr (IOT == 0) static_cast<float*>(p)[i] = v;
+  else static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+}
+
+// Register stage of a 128-row x BK tile whose rows are contiguous in k: row r
+// at src[roff + r*ld + k].  Rows outside [0, rhi) and k >= K read as zero.
+// VEC: K is a multiple of the item width W, so an item is all in or all out.
+template <int IOT, bool VEC>
+struct RowStage {
+  using E = typename Op<IOT>::E;
+  static constexpr int W = Op<IOT>::W, LDK = Op<IOT>::LDK;
+  u32x4 v[4];
+  __device__ __forceinline__ void load(const E* src, int64_t roff, int64_t ld, int rhi, int k0, int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + TT * i;
+      const int r = idx >> 3, k = k0 + (idx & 7) * W;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (r < rhi) {
+        const E* p = src + roff + (int64_t)r * ld + k;
+        if constexpr (VEC) {
+          if (k < K) w = *reinterpret_cast<const u32x4*>(p);
+        } else if constexpr (IOT == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (k + e < K) ? __float_as_uint(p[e]) : 0u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k + e < K) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+        }
+      }
+      v[i] = w;
+    }
+  }
+  __device__ __forceinline__ void store(E* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + TT * i;
+      const int r = idx >> 3, q = (idx & 7) * W;
+      if constexpr (IOT == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds[r * LDK + q + e] = __uint_as_float(v[i][e]);
+      } else {
+        *reinterpret_cast<u32x4*>(lds + r * LDK + q) = v[i];
+      }
+    }
+  }
+};
+
+// One k-stage of MFMAs over the LDS tiles into the wave's 2 x 2 accumulators.
+// A is row-major [m][k] (stride LDK), or for fp32 with AT k-major [k][m]
+// (stride TM + 4); B is row-major [n][k].
+template <int IOT, bool AT>
+struct Mma;
+
+template <bool AT>
+struct Mma<0, AT> {
+  static __device__ __forceinline__ void run(f32x16 (&acc)[2][2], const float* As, const float* Bs, int wm, int wn,
+                                             int lane) {
+#pragma unroll
+    for (int kk = 0; kk < Op<0>::BK / 2; ++kk) {
+      const int k = 2 * kk + (lane >> 5);
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = wm * 64 + i * 32 + (lane & 31);
+        a[i] = AT ? As[k * (TM + 4) + m] : As[m * Op<0>::LDK + k];
+        b[i] = Bs[(wn * 64 + i * 32 + (lane & 31)) * Op<0>::LDK + k];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+template <>
+struct Mma<1, false> {
+  static __device__ __forceinline__ void run(f32x16 (&acc)[2][2], const uint16_t* As, const uint16_t* Bs, int wm,
+                                             int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < Op<1>::BK / 16; ++kk) {
+      const int k = 16 * kk + 8 * (lane >> 5);
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 32 + (lane & 31)) * Op<1>::LDK + k);
+        b[i] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + i * 32 + (lane & 31)) * Op<1>::LDK + k);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+// Accumulator element r of lane `lane` in a 32 x 32 block: row 8(r/4) + 4(lane/32) + r%4, column lane%32.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+template <class E, bool VEC>
+__device__ __forceinline__ float dot_row(const E* x, const E* w, int K) {
+  float acc = 0.f;
+  if constexpr (VEC && sizeof(E) == 4) {
+    for (int k = 0; k < K; k += 4) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(x + k), b = *reinterpret_cast<const u32x4*>(w + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(a[e]), __uint_as_float(b[e]), acc);
+    }
+  } else if constexpr (VEC) {
+    for (int k = 0; k < K; k += 8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(x + k), b = *reinterpret_cast<const u32x4*>(w + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+        acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
+      }
+    }
+  } else {
+    for (int k = 0; k < K; ++k) acc = fmaf(ld_f(x, k), ld_f(w, k), acc);
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------ in-projection
+//
+// Workgroup = (batch b, time strip, 128-column block).  The strip's tiles run
+// in order; carry[n][j] holds Z row (tile start - HALO + j) of column n.
+template <int IOT, bool VEC>
+__global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, int strip_len, int n_cb) {
+  using E = typename Op<IOT>::E;
+  constexpr int LDK = Op<IOT>::LDK, BK = Op<IOT>::BK;
+  constexpr int MAIN_BYTES = 2 * TM * LDK * (int)sizeof(E);
+  constexpr int EPI_BYTES = 64 * ZLD * 4;
+  constexpr int BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[BYTES];
+  __shared__ float carry[TN][HALO];
+  E* As = reinterpret_cast<E*>(smem);
+  E* Bs = As + TM * LDK;
+  float* Zs = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  int wg = blockIdx.x;
+  const int cb = wg % n_cb;
+  wg /= n_cb;
+  const int strip = wg % n_strips, b = wg / n_strips;
+  const int c0 = cb * TN, D = a.D, C = a.C, T = a.T;
+  const int64_t L = a.L;
+  const int64_t ts = (int64_t)strip * strip_len;
+  const int64_t te = (ts + strip_len < L) ? ts + strip_len : L;
+  const E* u = static_cast<const E*>(a.u);
+  const E* Wt = static_cast<const E*>(a.W);
+
+  // Z rows ts-1 .. ts-(T-1) by direct dot products (zero before t = 0).
+  for (int i = tid; i < TN * HALO; i += TT) (&carry[0][0])[i] = 0.f;
+  __syncthreads();
+  for (int i = tid; i < TN * (T - 1); i += TT) {
+    const int n = i % TN, jj = i / TN;               // row ts - 1 - jj
+    const int64_t t = ts - 1 - jj;
+    const int c = c0 + n;
+    if (t >= 0 && c < C) {
+      const float z = dot_row<E, VEC>(u + ((int64_t)b * L + t) * D, Wt + (int64_t)c * D, D);
+      carry[n][HALO - 1 - jj] = z + (a.bias ? a.bias[c] : 0.f);
+    }
+  }
+
+  const int nks = (D + BK - 1) / BK;
+  const int brhi = (C - c0 < TN) ? C - c0 : TN;
+  for (int64_t t0 = ts; t0 < te; t0 += TM) {
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int64_t aoff = ((int64_t)b * L + t0) * D;
+    const int arhi = (L - t0 < TM) ? (int)(L - t0) : TM;
+    RowStage<IOT, VEC> sa, sb;
+    sa.load(u, aoff, D, arhi, 0, D, tid);
+    sb.load(Wt, (int64_t)c0 * D, D, brhi, 0, D, tid);
+    __syncthreads();                                  // smem free (carry set / last epilogue done)
+    sa.store(As, tid);
+    sb.store(Bs, tid);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+      if (ks + 1 < nks) {
+        sa.load(u, aoff, D, arhi, (ks + 1) * BK, D, tid);
+        sb.load(Wt, (int64_t)c0 * D, D, brhi, (ks + 1) * BK, D, tid);
+      }
+      Mma<IOT, false>::run(acc, As, Bs, wm, wn, lane);
+      __syncthreads();
+      if (ks + 1 < nks) {
+        sa.store(As, tid);
+        sb.store(Bs, tid);
+        __syncthreads();
+      }
+    }
+    // Epilogue, 64 columns at a time: Z (+bias) and the carried rows into
+    // LDS, then the short FIR and the store into the column's stream.
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) __syncthreads();                    // half 0's FIR reads done
+      if (wn == h) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = j * 32 + (lane & 31);
+          const int c = c0 + 64 * h + n;
+          const float bc = (a.bias && c < C) ? a.bias[c] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Zs[n * ZLD + HALO + wm * 64 + i * 32 + acc_row(r, lane)] = acc[i][j][r] + bc;
+        }
+      }
+      for (int i = tid; i < 64 * HALO; i += TT) {
+        const int n = i / HALO, j = i % HALO;
+        Zs[n * ZLD + j] = carry[64 * h + n][j];
+      }
+      __syncthreads();
+      {
+        const int n = tid >> 2, mb = (tid & 3) * 32;
+        const int c = c0 + 64 * h + n;
+        if (c < C) {
+          float wj[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) wj[j] = (j < T) ? a.w[(int64_t)c * T + j] : 0.f;
+          const int s = c / D, d = c - (c / D) * D;
+          void* dst = a.dst.p[s];
+          const int64_t row = ((int64_t)b * D + d) * L;
+          const float* zr = Zs + n * ZLD + HALO;
+          for (int m = mb; m < mb + 32; m += 4) {
+            float o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              o[q] = 0.f;
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (j < T) o[q] = fmaf(wj[j], zr[m + q - j], o[q]);
+            }
+            const int64_t t = t0 + m;
+            if ((L & 3) == 0 && t + 3 < te) {          // 4 aligned outputs in one store
+              if constexpr (IOT == 0) {
+                const u32x4 w = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                 __float_as_uint(o[3])};
+                *reinterpret_cast<u32x4*>(static_cast<float*>(dst) + row + t) = w;
+              } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 w = {(uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16),
+                                 (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16)};
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + row + t) = w;
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (t + q < te) st_f<IOT>(dst, row + t + q, o[q]);
+            }
+          }
+        }
+      }
+      for (int i = tid; i < 64 * HALO; i += TT) {
+        const int n = i / HALO, j = i % HALO;
+        carry[64 * h + n][j] = Zs[n * ZLD + HALO + TM - HALO + j];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------- out-projection
+//
+// Workgroup = (batch b, 128 time rows, 128 output columns).  A = y^T: the
+// stage reads y rows (one channel, consecutive times); fp32 keeps them
+// k-major in LDS, bf16 transposes them to [time][channel] for the MFMA's
+// 8-consecutive-k operand.
+template <int IOT, bool VEC>
+struct YStage {
+  using E = typename Op<IOT>::E;
+  static constexpr int W = Op<IOT>::W;
+  u32x4 v[4];
+  // fp32 item: k = idx >> 5 (32 channels), 4 times; bf16 item: k = idx & 63, 8 times
+  __device__ __forceinline__ void load(const E* y, int64_t ybase, int64_t L, int D, int d0, int64_t t0, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + TT * i;
+      const int k = (IOT == 0) ? (idx >> 5) : (idx & 63);
+      const int q = (IOT == 0) ? (idx & 31) : (idx >> 6);
+      const int d = d0 + k;
+      const int64_t t = t0 + (int64_t)q * W;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (d < D && t < L) {
+        const E* p = y + ybase + (int64_t)d * L + t;
+        if constexpr (VEC) {
+          w = *reinterpret_cast<const u32x4*>(p);
+        } else if constexpr (IOT == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (t + e < L) ? __float_as_uint(p[e]) : 0u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t + e < L) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+        }
+      }
+      v[i] = w;
+    }
+  }
+  __device__ __forceinline__ void store(E* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + TT * i;
+      if constexpr (IOT == 0) {
+        const int k = idx >> 5, q = (idx & 31) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds[k * (TM + 4) + q + e] = __uint_as_float(v[i][e]);
+      } else {
+        const int k = idx & 63, q = (idx >> 6) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lds[(q + e) * Op<1>::LDK + k] = (uint16_t)(v[i][e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+};
+
+template <int IOT, bool VEC>
+__global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int n_eb) {
+  using E = typename Op<IOT>::E;
+  constexpr int LDK = Op<IOT>::LDK, BK = Op<IOT>::BK;
+  constexpr int A_ELEMS = (IOT == 0) ? BK * (TM + 4) : TM * LDK;
+  __shared__ __attribute__((aligned(16))) E As[A_ELEMS];
+  __shared__ __attribute__((aligned(16))) E Bs[TN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  int wg = blockIdx.x;
+  const int eb = wg % n_eb;
+  wg /= n_eb;
+  const int tt = wg % n_tt, b = wg / n_tt;
+  const int D = a.D, e0 = eb * TN;
+  const int64_t L = a.L, t0 = (int64_t)tt * TM;
+  const E* y = static_cast<const E*>(a.y);
+  const E* Wt = static_cast<const E*>(a.W);
+  const int64_t ybase = (int64_t)b * D * L;
+  const int brhi = (D - e0 < TN) ? D - e0 : TN;
+  const int nks = (D + BK - 1) / BK;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  YStage<IOT, VEC> sa;
+  RowStage<IOT, VEC> sb;
+  sa.load(y, ybase, L, D, 0, t0, tid);
+  sb.load(Wt, (int64_t)e0 * D, D, brhi, 0, D, tid);
+  sa.store(As, tid);
+  sb.store(Bs, tid);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    if (ks + 1 < nks) {
+      sa.load(y, ybase, L, D, (ks + 1) * BK, t0, tid);
+      sb.load(Wt, (int64_t)e0 * D, D, brhi, (ks + 1) * BK, D, tid);
+    }
+    Mma<IOT, IOT == 0>::run(acc, As, Bs, wm, wn, lane);
+    __syncthreads();
+    if (ks + 1 < nks) {
+      sa.store(As, tid);
+      sb.store(Bs, tid);
+      __syncthreads();
+    }
+  }
+  void* out = a.out;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + wn * 64 + j * 32 + (lane & 31);
+    if (e >= D) continue;
+    const float be = a.bias ? a.bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = t0 + wm * 64 + i * 32 + acc_row(r, lane);
+        if (t < L) st_f<IOT>(out, ((int64_t)b * L + t) * D + e, acc[i][j][r] + be);
+      }
+  }
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+hipError_t in_projection(const InProjArgs& a, hipStream_t s) {
+  const int n_cb = ceil_div(a.C, TN);
+  const int tiles = ceil_div(a.L, TM);
+  // enough workgroups for two per CU, strips of whole tiles
+  int n_strips = ceil_div(512, (int64_t)a.B * n_cb);
+  if (n_strips < 1) n_strips = 1;
+  if (n_strips > tiles) n_strips = tiles;
+  const int per = ceil_div(tiles, n_strips);
+  n_strips = ceil_div(tiles, per);
+  const int strip_len = per * TM;
+  const dim3 grid((unsigned)((int64_t)a.B * n_strips * n_cb)), block(TT);
+  const bool vec = a.D % (a.io == 0 ? 4 : 8) == 0;
+  if (a.io == 0) {
+    if (vec) hipLaunchKernelGGL((k_inproj<0, true>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
+    else hipLaunchKernelGGL((k_inproj<0, false>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_inproj<1, true>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
+    else hipLaunchKernelGGL((k_inproj<1, false>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t out_projection(const OutProjArgs& a, hipStream_t s) {
+  const int n_eb = ceil_div(a.D, TN), n_tt = ceil_div(a.L, TM);
+  const dim3 grid((unsigned)((int64_t)a.B * n_tt * n_eb)), block(TT);
+  const int w = (a.io == 0 ? 4 : 8);
+  const bool vec = a.D % w == 0 && a.L % w == 0;
+  if (a.io == 0) {
+    if (vec) hipLaunchKernelGGL((k_outproj<0, true>), grid, block, 0, s, a, n_tt, n_eb);
+    else hipLaunchKernelGGL((k_outproj<0, false>), grid, block, 0, s, a, n_tt, n_eb);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_outproj<1, true>), grid, block, 0, s, a, n_tt, n_eb);
+    else hipLaunchKernelGGL((k_outproj<1, false>), grid, block, 0, s, a, n_tt, n_eb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hyena

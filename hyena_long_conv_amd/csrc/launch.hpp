@@ -40,6 +40,35 @@ struct FilterGenArgs {
   float* h;
 };
 
+// Dense projections around the operator (kernels_proj.hip).
+struct StreamPtrs {
+  void* p[9];            // v, x_1..x_N (N <= 8)
+};
+
+struct InProjArgs {
+  const void* u;         // [B][L][D]
+  const void* W;         // [C][D], C = (N+1)*D
+  const float* bias;     // [C] or nullptr
+  const float* w;        // [C][T]
+  StreamPtrs dst;        // N+1 streams, each [B][D][L]
+  int B, D, C, T;
+  int64_t L;
+  int io;
+};
+
+struct OutProjArgs {
+  const void* y;         // [B][D][L]
+  const void* W;         // [D][D]
+  const float* bias;     // [D] or nullptr
+  void* out;             // [B][L][D]
+  int B, D;
+  int64_t L;
+  int io;
+};
+
+hipError_t in_projection(const InProjArgs& a, hipStream_t s);
+hipError_t out_projection(const OutProjArgs& a, hipStream_t s);
+
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);

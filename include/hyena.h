@@ -152,6 +152,63 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
                            int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
                            void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * The block around the operator (paper digest, irregular6612.github.io,
+ * section "방법 (Method)", framework figure: one projection of width (N+1)D
+ * yields v and the gates; homemade-llm "02. 3つの Hyena 演算子", section 2:
+ * every projected stream is featurised by a short convolution and the result
+ * is mapped back by a dense matrix; Hyena Hierarchy explainer section
+ * "計算方法": these projections are the D in O(NDL(log L + D))).
+ *
+ *   Z[b][t][c]  = sum_k u[b][t][k] W_in[c][k] + b_in[c]        c < (N+1)D
+ *   S[b][c][t]  = sum_{j<T, j<=t} w_short[c][j] Z[b][t-j][c]    (causal, depthwise)
+ *   v = S[:, 0:D],  x_n = S[:, nD:(n+1)D]                       ([B][D][L] each)
+ *   y = hyena_forward(v, x, spec)
+ *   out[b][t][e] = sum_d W_out[e][d] y[b][d][t] + b_out[e]      ([B][L][D])
+ *
+ * Device pointers; W_in, W_out and the activations u, out are in the I/O
+ * dtype (bf16: fp32 accumulation on the matrix cores, stored values rounded
+ * to nearest even), biases and short filters fp32.  b_in / b_out may be NULL.
+ */
+#define HYENA_MAX_SHORT 16         /* T in 1..16                                */
+
+typedef struct {
+  int32_t D;             /* width                                             */
+  int32_t N;             /* order                                             */
+  int32_t T;             /* short-filter taps                                 */
+  int32_t reserved;      /* 0                                                 */
+  const void* W_in;      /* [(N+1)*D][D], I/O dtype                           */
+  const float* b_in;     /* [(N+1)*D] or NULL                                 */
+  const float* w_short;  /* [(N+1)*D][T]                                      */
+  const void* W_out;     /* [D][D], I/O dtype                                 */
+  const float* b_out;    /* [D] or NULL                                       */
+} hyena_block_params;
+
+/* In-projection + short convolution: u [B][L][D] -> streams[0] = v,
+ * streams[n] = x_n (HOST array of N+1 device pointers, each [B][D][L], I/O
+ * dtype).  Uses W_in, b_in, w_short.  Errors: NULL -> NULL; sizes (incl. T
+ * outside 1..HYENA_MAX_SHORT) -> SHAPE; alignment -> ALIGN; a stream
+ * overlapping u or W_in -> ALIAS. */
+hyena_status hyena_in_projection(const void* u, const hyena_block_params* p, void* const* streams,
+                                 int64_t B, int64_t L, hyena_dtype io, void* stream);
+
+/* Output projection: y [B][D][L] -> out [B][L][D] (I/O dtype).  Uses W_out,
+ * b_out.  Errors as above; out overlapping y or W_out -> ALIAS. */
+hyena_status hyena_out_projection(const void* y, const hyena_block_params* p, void* out, int64_t B,
+                                  int64_t L, hyena_dtype io, void* stream);
+
+/* Scratch of hyena_block_forward: v, x_1..x_N and y ([B][D][L] each, I/O
+ * dtype, 256-byte aligned) plus the forward's own workspace.  -1 on bad sizes. */
+int64_t hyena_block_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
+
+/* The whole block: u [B][L][D] -> out [B][L][D] with the spectrum of the
+ * block's filters (hyena_filter_spectrum for (D, N, L)).  workspace: at least
+ * hyena_block_workspace_bytes() bytes.  Errors as the three calls it runs,
+ * plus WORKSPACE for a small workspace and ALIAS for out overlapping u. */
+hyena_status hyena_block_forward(const void* u, const hyena_block_params* p, const void* spec, void* out,
+                                 int64_t B, int64_t L, hyena_dtype io, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* hyena_status_str(hyena_status s);
 

@@ -144,3 +144,47 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(H, "LIB_PATH", "/nonexistent/libhyena_mi355x.so")
     with pytest.raises(RuntimeError, match="missing"):
         H.lib()
+
+
+def _bp(D=4, N=2, T=3, W_in=A, w=Bp, W_out=C, b_in=0, b_out=0):
+    return H.BlockParams(D, N, T, 0, W_in, b_in, w, W_out, b_out)
+
+
+def test_block_calls_reject_bad_arguments():
+    lib = H.lib()
+    st = (vp * 3)(Y, Y + 0x1000000, Y + 0x2000000)
+    inp = lambda u=Dp, p=None, s=st, B=1, L=64, io=0: lib.hyena_in_projection(
+        vp(u), None if p is False else ctypes.byref(p or _bp()), s, B, L, io, None)
+    assert inp(u=0) == NULL
+    assert inp(p=False) == NULL
+    assert inp(s=None) == NULL
+    assert inp(p=_bp(W_in=0)) == NULL
+    assert inp(p=_bp(w=0)) == NULL
+    assert inp(s=(vp * 3)(Y, 0, Y + 0x2000000)) == NULL
+    assert inp(B=0) == SHAPE
+    assert inp(L=0) == SHAPE
+    assert inp(p=_bp(T=0)) == SHAPE
+    assert inp(p=_bp(T=17)) == SHAPE
+    assert inp(p=_bp(N=9)) == UNSUP
+    assert inp(io=5) == UNSUP
+    assert inp(u=Dp + 8) == ALIGN
+    assert inp(s=(vp * 3)(Y, Y + 0x1000000, Y + 0x2000000 + 4)) == ALIGN
+    assert inp(s=(vp * 3)(Dp, Y + 0x1000000, Y + 0x2000000)) == ALIAS      # v over u
+    assert inp(s=(vp * 3)(Y, Y + 64, Y + 0x2000000)) == ALIAS               # two streams overlap
+    outp = lambda y=Dp, p=None, o=Y, B=1, L=64: lib.hyena_out_projection(
+        vp(y), ctypes.byref(p or _bp()), vp(o), B, L, 0, None)
+    assert outp(y=0) == NULL
+    assert outp(o=0) == NULL
+    assert outp(p=_bp(W_out=0)) == NULL
+    assert outp(L=(1 << 22) + 1) == SHAPE
+    assert outp(o=Y + 2) == ALIGN
+    assert outp(o=Dp) == ALIAS
+    assert H.block_workspace_bytes(2, 768, 2, 2048) == 4 * 2 * 768 * 2048 * 4
+    assert H.block_workspace_bytes(0, 768, 2, 2048) == -1
+    ws = H.block_workspace_bytes(1, 8, 2, 65536, "bf16")
+    assert ws > 4 * 8 * 65536 * 2
+    blk = lambda u=Dp, o=Y, w=W, wsb=1 << 30: lib.hyena_block_forward(
+        vp(u), ctypes.byref(_bp()), vp(A), vp(o), 1, 64, 0, vp(w), wsb, None)
+    assert blk(w=0) == NULL
+    assert blk(wsb=16) == WS
+    assert blk(o=Dp) == ALIAS
