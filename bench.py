@@ -141,6 +141,133 @@ def measure_copy(torch, dev, reps=4, nbytes=1 << 30):
     return 2 * nbytes / best
 
 
+MFMA_PEAK = {"fp32": 157.3e12, "bf16": 2.5e15}   # dense matrix-core peaks, FLOP/s
+
+
+def _time_steps(torch, dev, step, steps, warmup):
+    """Warm-up (given count, or >= 3 steps and 100 ms), then `steps` timed
+    steps (or >= 20 and 200 ms) bracketed by events on the current stream;
+    returns (mean ms, steps, warmup)."""
+    est = None
+    if warmup is not None:
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+    else:
+        done, t_w = 0, time.perf_counter()
+        while done < 3 or time.perf_counter() - t_w < 0.1:
+            step(done)
+            done += 1
+            if done % 8 == 0 or done < 3:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        warmup = done
+        est = (time.perf_counter() - t_w) / done
+    if steps is None:
+        if est is None:
+            t_e = time.perf_counter()
+            step(0)
+            torch.cuda.synchronize()
+            est = time.perf_counter() - t_e
+        steps = int(min(5000, max(20, math.ceil(0.2 / max(est, 1e-6)))))
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, steps, warmup
+
+
+def run_block(args, cfg, torch, H, dev):
+    """The block around the operator: u [B, L, D] -> in-projection with the
+    short convolutions -> operator -> out-projection.  One step = one
+    hyena_block_forward.  The roofline is the in-projection GEMM's (the
+    block's dominant kernel), against the dense matrix-core peak of the I/O
+    dtype; the pieces are also timed on their own."""
+    import numpy as np
+    from workloads import make_block_input, make_block_params, make_filter_params
+
+    dt = torch.float32 if cfg.io == "fp32" else torch.bfloat16
+    s = 4 if cfg.io == "fp32" else 2
+    B, D, L, N = cfg.B, cfg.D, cfg.L, cfg.N
+    bp = make_block_params(cfg)
+    bpd = {"D": D, "N": N, "T": bp["T"], "b_in": None, "b_out": None,
+           "W_in": torch.from_numpy(bp["W_in"]).to(dev).to(dt).contiguous(),
+           "W_out": torch.from_numpy(bp["W_out"]).to(dev).to(dt).contiguous(),
+           "w_short": torch.from_numpy(bp["w_short"]).to(dev)}
+    fp = make_filter_params(cfg)
+    h = H.filter_gen({k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in fp.items()}, L)
+    spec0 = H.filter_spectrum(h)
+    per_set = 2 * B * L * D * s + spec0.numel()
+    sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / per_set))
+    us, outs, specs = [], [], []
+    for k in range(sets):
+        us.append(make_block_input(cfg.with_(seed=cfg.seed * 100 + k), dev))
+        outs.append(torch.empty_like(us[-1]))
+        specs.append(spec0 if k == 0 else spec0.clone())
+    ws = torch.empty(H.block_workspace_bytes(B, D, N, L, cfg.io), dtype=torch.uint8, device=dev)
+    streams = [torch.empty((B, D, L), dtype=dt, device=dev) for _ in range(N + 1)]
+    y = torch.empty((B, D, L), dtype=dt, device=dev)
+    blk = [H.prepare_block_forward(us[k], bpd, specs[k], outs[k], ws) for k in range(sets)]
+    inp = [H.prepare_in_projection(us[k], bpd, streams) for k in range(sets)]
+    fwd = [H.PreparedForward(streams[0], streams[1:], specs[k], out=y,
+                             workspace=ws if ws.numel() > 0 else None) for k in range(sets)]
+    outp = [H.prepare_out_projection(y, bpd, outs[k]) for k in range(sets)]
+    torch.cuda.synchronize()
+    ms, steps, warmup = _time_steps(torch, dev, lambda i: blk[i % sets](), args.steps, args.warmup)
+    ms_in, _, _ = _time_steps(torch, dev, lambda i: inp[i % sets](), steps, 3)
+    ms_fwd, _, _ = _time_steps(torch, dev, lambda i: fwd[i % sets](), steps, 3)
+    ms_out, _, _ = _time_steps(torch, dev, lambda i: outp[i % sets](), steps, 3)
+    t = ms / 1e3
+    C = (N + 1) * D
+    fl_in, fl_out = 2.0 * B * L * D * C, 2.0 * B * L * D * D
+    peak = MFMA_PEAK[cfg.io]
+    roof = {"bound": "mfma", "achieved": fl_in / (ms_in / 1e3) / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+            "frac": fl_in / (ms_in / 1e3) / peak, "traffic": None,
+            "kernel": "k_inproj (in-projection GEMM + bias + short causal FIR + stream split)",
+            "algorithmic_flops_per_launch": fl_in,
+            "out_projection": {"TFLOPs": fl_out / (ms_out / 1e3) / 1e12, "frac": fl_out / (ms_out / 1e3) / peak}}
+    out = {
+        "metric": "Hyena block fwd channel-tokens/sec (B*D*L/s): projections, short convs, order-N operator",
+        "value": B * D * L / t, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32" if cfg.io == "fp32" else "bf16 operands, fp32 accumulation",
+        "data": "synthetic (seeded N(0,1) input, random-init projections, short filters and filter FFN)",
+        "config": {"workload": cfg.desc + ", full block (T=3 short filters)", "name": cfg.name, "N": N, "B": B,
+                   "D": D, "L": L, "io": cfg.io, "short_taps": bp["T"], "input_sets": sets},
+        "block": {"ms_in_projection": ms_in, "ms_operator": ms_fwd, "ms_out_projection": ms_out},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(cfg, bp, h.cpu().numpy())
+    print(json.dumps(out))
+    return 0
+
+
+def cpu_baseline_block(cfg, bp, h, budget_s: float = 12.0):
+    """The float64 oracle's block on batch row 0 over a causal prefix of the
+    sequence (the first Lp steps need only the first Lp inputs and taps),
+    Lp doubled from 64 while the run stays within the budget."""
+    import numpy as np
+    import oracle as O
+    from workloads import make_block_input
+    u = make_block_input(cfg, "cpu", B=1).float().numpy()
+    Lp, best = 64, None
+    while Lp <= cfg.L:
+        t0 = time.perf_counter()
+        O.block_forward(u[:, :Lp], bp, h[:, :, :Lp])
+        dt_ = time.perf_counter() - t0
+        best = (Lp, dt_)
+        if dt_ * 4 > budget_s or Lp == cfg.L:
+            break
+        Lp = min(cfg.L, Lp * 2)
+    Lp, dt_ = best
+    return {"value": cfg.D * Lp / dt_, "unit": "channel-tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": f"block on batch row 0, first {Lp} of {cfg.L} steps (causal prefix), float64, {dt_:.1f} s"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +278,8 @@ def main(argv=None):
     ap.add_argument("--config", default="C2")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="time the whole block (in-projection + short convolutions, operator, out-projection)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for counter scaling)")
     args = ap.parse_args(argv)
@@ -171,6 +300,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     H.lib()
+    if args.block:
+        return run_block(args, cfg, torch, H, dev)
 
     # Device-to-device copy of 1 GiB: the practical HBM ceiling on this machine,
     # reported beside the datasheet peak (also the reference dispatch for

@@ -23,7 +23,8 @@ import re
 __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectrum_export",
            "forward", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
            "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
-           "in_projection", "out_projection", "block_forward", "block_workspace_bytes"]
+           "in_projection", "out_projection", "block_forward", "block_workspace_bytes", "PreparedCall",
+           "prepare_in_projection", "prepare_out_projection", "prepare_block_forward"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
@@ -321,3 +322,52 @@ def block_forward(u, bp: dict, spec, out=None, workspace=None):
                                      workspace.numel() * workspace.element_size(), _stream(u)),
            "hyena_block_forward")
     return o
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments checked and marshalled once (for
+    loops over fixed buffers); keeps the tensors and structs it points to
+    alive.  call() returns `result`."""
+
+    def __init__(self, fn, args, keep, result, name):
+        self._fn, self._args, self._keep, self.result, self._name = fn, args, keep, result, name
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise HyenaError(code, self._name)
+        return self.result
+
+
+def prepare_in_projection(u, bp: dict, streams):
+    io = _io_of(u)
+    _need_cuda(u, "u", u.dtype)
+    B, L, D = u.shape
+    p = _block_struct(bp, u.dtype)
+    for i, t in enumerate(streams):
+        _need_cuda(t, f"stream[{i}]", u.dtype)
+    sp = (ctypes.c_void_p * len(streams))(*[t.data_ptr() for t in streams])
+    return PreparedCall(lib().hyena_in_projection, (_ptr(u), ctypes.byref(p), sp, B, L, io, _stream(u)),
+                        (u, bp, p, sp, tuple(streams)), tuple(streams), "hyena_in_projection")
+
+
+def prepare_out_projection(y, bp: dict, out):
+    io = _io_of(y)
+    _need_cuda(y, "y", y.dtype)
+    _need_cuda(out, "out", y.dtype)
+    B, D, L = y.shape
+    p = _block_struct(bp, y.dtype)
+    return PreparedCall(lib().hyena_out_projection, (_ptr(y), ctypes.byref(p), _ptr(out), B, L, io, _stream(y)),
+                        (y, bp, p, out), out, "hyena_out_projection")
+
+
+def prepare_block_forward(u, bp: dict, spec, out, workspace):
+    io = _io_of(u)
+    _need_cuda(u, "u", u.dtype)
+    _need_cuda(out, "out", u.dtype)
+    B, L, D = u.shape
+    p = _block_struct(bp, u.dtype)
+    return PreparedCall(lib().hyena_block_forward,
+                        (_ptr(u), ctypes.byref(p), _ptr(spec), _ptr(out), B, L, io, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(u)),
+                        (u, bp, p, spec, out, workspace), out, "hyena_block_forward")

@@ -449,12 +449,12 @@ template <> struct Plan8<8192> { using R = Radices<8, 2, 8, 8, 8>; };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest even; NaN stays NaN (quieted).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats to packed bf16 (low half = lo), round to nearest even, by the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int IOT> struct IO;
@@ -471,7 +471,7 @@ template <> struct IO<1> {  // bf16
     return bf16_bits_to_f32(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i));
   }
   static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
-    __builtin_nontemporal_store(f32_to_bf16_bits(v), static_cast<uint16_t*>(p) + i);
+    __builtin_nontemporal_store((uint16_t)bf16x2_bits(v, 0.f), static_cast<uint16_t*>(p) + i);
   }
 };
 
@@ -617,7 +617,7 @@ __device__ __forceinline__ void st_pair(void* p, int64_t row_off, int64_t t, int
       const f32x2 w = {v.x, v.y};
       __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(static_cast<float*>(p) + row_off + t));
     } else {
-      const uint32_t w = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+      const uint32_t w = bf16x2_bits(v.x, v.y);
       __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + row_off + t));
     }
   } else {

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int TM = 128, TN = 128, TT = 256;   // tile rows, tile columns, threads
 constexpr int HALO = 16;                       // carried Z rows (T - 1 <= 15)
-constexpr int ZLD = HALO + TM + 5;             // epilogue row stride (odd: fewer bank conflicts)
+constexpr int ZLD = HALO + TM + 4;             // epilogue row stride (16-byte rows for vector reads)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -51,7 +51,7 @@ __device__ __forceinline__ float ld_f(const uint16_t* p, int64_t i) { return bf1
 template <int IOT>
 __device__ __forceinline__ void st_f(void* p, int64_t i, float v) {
   if constexpr (IOT == 0) static_cast<float*>(p)[i] = v;
-  else static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  else static_cast<uint16_t*>(p)[i] = (uint16_t)bf16x2_bits(v, 0.f);
 }
 
 // Register stage of a 128-row x BK tile whose rows are contiguous in k: row r
@@ -280,7 +280,16 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
           const int s = c / D, d = c - (c / D) * D;
           void* dst = a.dst.p[s];
           const int64_t row = ((int64_t)b * D + d) * L;
-          const float* zr = Zs + n * ZLD + HALO;
+          // the 32 outputs' window Z[mb-16 .. mb+31] in registers, 16-byte reads
+          typedef float f32x4v __attribute__((ext_vector_type(4)));
+          float win[48];
+          const float* zr = Zs + n * ZLD + mb;        // = row start + HALO + mb - 16
+#pragma unroll
+          for (int q = 0; q < 12; ++q) {
+            const f32x4v w4 = *reinterpret_cast<const f32x4v*>(zr + 4 * q);
+            win[4 * q] = w4.x; win[4 * q + 1] = w4.y; win[4 * q + 2] = w4.z; win[4 * q + 3] = w4.w;
+          }
+#pragma unroll
           for (int m = mb; m < mb + 32; m += 4) {
             float o[4];
 #pragma unroll
@@ -288,7 +297,7 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
               o[q] = 0.f;
 #pragma unroll
               for (int j = 0; j < 16; ++j)
-                if (j < T) o[q] = fmaf(wj[j], zr[m + q - j], o[q]);
+                if (j < T) o[q] = fmaf(wj[j], win[16 + (m - mb) + q - j], o[q]);
             }
             const int64_t t = t0 + m;
             if ((L & 3) == 0 && t + 3 < te) {          // 4 aligned outputs in one store
@@ -298,8 +307,7 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
                 *reinterpret_cast<u32x4*>(static_cast<float*>(dst) + row + t) = w;
               } else {
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 w = {(uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16),
-                                 (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16)};
+                const u32x2 w = {bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3])};
                 *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + row + t) = w;
               }
             } else {
@@ -438,28 +446,35 @@ __global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int 
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-}  // namespace
-
-hipError_t in_projection(const InProjArgs& a, hipStream_t s) {
+template <int IOT, bool VEC>
+static hipError_t launch_inproj(const InProjArgs& a, hipStream_t s) {
+  const auto kern = k_inproj<IOT, VEC>;
   const int n_cb = ceil_div(a.C, TN);
   const int tiles = ceil_div(a.L, TM);
-  // enough workgroups for two per CU, strips of whole tiles
-  int n_strips = ceil_div(512, (int64_t)a.B * n_cb);
+  // Workgroups run whole strips of tiles, so they are long-lived: at most as
+  // many as fit the GPU at once, never a second partial wave.
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, TT, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  int n_strips = (int)(((int64_t)cus * per_cu) / ((int64_t)a.B * n_cb));
   if (n_strips < 1) n_strips = 1;
   if (n_strips > tiles) n_strips = tiles;
   const int per = ceil_div(tiles, n_strips);
   n_strips = ceil_div(tiles, per);
   const int strip_len = per * TM;
   const dim3 grid((unsigned)((int64_t)a.B * n_strips * n_cb)), block(TT);
-  const bool vec = a.D % (a.io == 0 ? 4 : 8) == 0;
-  if (a.io == 0) {
-    if (vec) hipLaunchKernelGGL((k_inproj<0, true>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
-    else hipLaunchKernelGGL((k_inproj<0, false>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
-  } else {
-    if (vec) hipLaunchKernelGGL((k_inproj<1, true>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
-    else hipLaunchKernelGGL((k_inproj<1, false>), grid, block, 0, s, a, n_strips, strip_len, n_cb);
-  }
+  hipLaunchKernelGGL(kern, grid, block, 0, s, a, n_strips, strip_len, n_cb);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t in_projection(const InProjArgs& a, hipStream_t s) {
+  const bool vec = a.D % (a.io == 0 ? 4 : 8) == 0;
+  if (a.io == 0) return vec ? launch_inproj<0, true>(a, s) : launch_inproj<0, false>(a, s);
+  return vec ? launch_inproj<1, true>(a, s) : launch_inproj<1, false>(a, s);
 }
 
 hipError_t out_projection(const OutProjArgs& a, hipStream_t s) {

@@ -50,6 +50,8 @@ IN_CASES = [
     (1, 5, 3, 1, 1, "fp32"), (2, 130, 16, 2, 3, "fp32"), (1, 257, 37, 2, 3, "fp32"),
     (2, 1000, 128, 3, 3, "fp32"), (1, 700, 64, 2, 16, "fp32"), (2, 300, 48, 2, 3, "bf16"),
     (1, 200, 20, 2, 5, "bf16"), (1, 3, 8, 8, 2, "fp32"), (4, 2048, 768, 2, 3, "fp32"),
+    # bf16 widths that are multiples of 64 take the direct-to-LDS staging
+    (2, 1000, 128, 2, 3, "bf16"), (1, 777, 192, 3, 4, "bf16"), (1, 4096, 768, 2, 3, "bf16"),
 ]
 
 
