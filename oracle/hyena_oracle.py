@@ -58,6 +58,10 @@ Readings where the pages are silent (each listed in the design notes):
   convolution is causal and depthwise (one T-tap filter per projected
   column, tap j weighting the sample j steps back, zero before t = 0); biases
   of both projections optional; the output projection has no activation.
+  Backward: the pages give no gradient formulas; they follow from the
+  recurrence by the chain rule (the adjoint of a causal convolution is the
+  correlation with the same filter), for a scalar loss whose gradient with
+  respect to y is gy; filter gradients are summed over the batch.
 """
 from __future__ import annotations
 
@@ -77,6 +81,9 @@ __all__ = [
     "in_projection",
     "out_projection",
     "block_forward",
+    "causal_conv_adjoint",
+    "filter_correlation",
+    "hyena_backward",
     "DIRECT_MAX_L",
 ]
 
@@ -316,3 +323,75 @@ def block_forward(u: np.ndarray, bp: dict, h: np.ndarray, conv=causal_conv) -> n
     v, xs = in_projection(u, bp["W_in"], bp.get("b_in"), bp["w_short"], N)
     y = hyena_forward(v, xs, h, conv=conv)
     return out_projection(y, bp["W_out"], bp.get("b_out"))
+
+
+# ---------------------------------------------------------------------------
+# Backward of the recurrence (chain rule through [P1] "Hyena 演算子の形";
+# [P3] section 4's causal FIR and its transpose)
+# ---------------------------------------------------------------------------
+
+def causal_conv_adjoint(h: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Transpose of c = h conv z (causal, length L) applied to g:
+    out[..., s] = sum_{t >= s} h[..., t - s] * g[..., t]."""
+    h = np.asarray(h, np.float64)
+    g = np.asarray(g, np.float64)
+    L = g.shape[-1]
+    if L <= DIRECT_MAX_L:
+        out = np.zeros(np.broadcast_shapes(h.shape[:-1], g.shape[:-1]) + (L,))
+        for k in range(L):
+            out[..., : L - k] += h[..., k:k + 1] * g[..., k:]
+        return out
+    P = 1
+    while P < 2 * L:
+        P *= 2
+    hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
+    gp = np.zeros(g.shape[:-1] + (P,)); gp[..., :L] = g
+    return np.real(fft(np.conj(fft(hp)) * fft(gp), inverse=True))[..., :L]
+
+
+def filter_correlation(g: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Gradient of c = h conv z with respect to h, contracted with g:
+    out[..., k] = sum_{t >= k} g[..., t] * z[..., t - k]."""
+    g = np.asarray(g, np.float64)
+    z = np.asarray(z, np.float64)
+    L = g.shape[-1]
+    if L <= DIRECT_MAX_L:
+        out = np.zeros(np.broadcast_shapes(g.shape, z.shape))
+        for k in range(L):
+            out[..., k] = np.sum(g[..., k:] * z[..., : L - k], axis=-1)
+        return out
+    P = 1
+    while P < 2 * L:
+        P *= 2
+    gp = np.zeros(g.shape[:-1] + (P,)); gp[..., :L] = g
+    zp = np.zeros(z.shape[:-1] + (P,)); zp[..., :L] = z
+    return np.real(fft(np.conj(fft(zp)) * fft(gp), inverse=True))[..., :L]
+
+
+def hyena_backward(v: np.ndarray, xs, h: np.ndarray, gy: np.ndarray, conv=causal_conv):
+    """Gradients of a scalar loss with dloss/dy = gy through y = z_{N+1}:
+    returns (gv, [gx_1..gx_N], gh) with gh [N, D, L] summed over the batch.
+
+    Forward intermediates: z_1 = v, c_n = h_n conv z_n, z_{n+1} = x_n * c_n.
+    Backward, n = N..1, with g = dloss/dz_{n+1}: gx_n = g * c_n;
+    gc = g * x_n; gh_n = sum_b corr(gc, z_n); g <- adjoint conv of gc by h_n.
+    """
+    v = np.asarray(v, np.float64)
+    h = np.asarray(h, np.float64)
+    N = h.shape[0]
+    zs, cs = [v], []
+    for n in range(N):
+        c = conv(h[n], zs[-1])
+        cs.append(c)
+        zs.append(np.asarray(xs[n], np.float64) * c)
+    g = np.asarray(gy, np.float64)
+    gxs = [None] * N
+    gh = np.zeros_like(h)
+    batch_axes = tuple(range(v.ndim - 2))
+    for n in reversed(range(N)):
+        x = np.asarray(xs[n], np.float64)
+        gxs[n] = g * cs[n]
+        gc = g * x
+        gh[n] = np.sum(filter_correlation(gc, zs[n]), axis=batch_axes) if batch_axes else filter_correlation(gc, zs[n])
+        g = causal_conv_adjoint(h[n], gc)
+    return g, gxs, gh
