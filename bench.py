@@ -246,6 +246,104 @@ def run_block(args, cfg, torch, H, dev):
     return 0
 
 
+def backward_bytes(cfg) -> int:
+    """Algorithmic bytes of one backward: v, x_1..x_N, gy read and gv,
+    gx_1..gx_N written in the I/O dtype, the spectrum (L+1 bins per (n, d),
+    complex64) read, gh written (fp32)."""
+    s = 4 if cfg.io == "fp32" else 2
+    return ((2 * cfg.N + 3) * cfg.B * cfg.D * cfg.L * s + cfg.N * cfg.D * (cfg.L + 1) * 8
+            + cfg.N * cfg.D * cfg.L * 4)
+
+
+def backward_flops(cfg) -> float:
+    """N * (25 log2(2L) + 20) per channel-token: five real FFTs of 2L points
+    per order (the forward's two, recomputed, plus those of z_n, of the
+    gradient and of its adjoint) and the spectral products."""
+    return cfg.N * cfg.B * cfg.D * cfg.L * (25.0 * math.log2(2 * cfg.L) + 20.0)
+
+
+def run_backward(args, cfg, torch, H, dev):
+    """The backward of the operator: one step = one hyena_backward (recomputes
+    the forward's convolutions, then gradients of v, every x_n and the
+    filters).  Single-pass lengths only."""
+    import numpy as np
+    from workloads import make_activations, make_filter_params
+
+    fp = make_filter_params(cfg)
+    h = H.filter_gen({k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in fp.items()},
+                     cfg.L)
+    spec0 = H.filter_spectrum(h)
+    del h
+    sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / backward_bytes(cfg)))
+    data = []
+    for k in range(sets):
+        c = cfg.with_(seed=cfg.seed * 100 + k)
+        v, xs = make_activations(c, dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(c.seed * 7 + 1)
+        gy = torch.randn(v.shape, generator=g, device=dev).to(v.dtype)
+        data.append((v, xs, spec0 if k == 0 else spec0.clone(), gy))
+    wsb = H.backward_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io)
+    if wsb < 0:
+        print(f"backward not available for L = {cfg.L} (single-pass lengths only)", file=sys.stderr)
+        return 2
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    gv = torch.empty_like(data[0][0])
+    gxs = [torch.empty_like(gv) for _ in range(cfg.N)]
+    gh = torch.empty((cfg.N, cfg.D, cfg.L), dtype=torch.float32, device=dev)
+    lib = H.lib()
+    import ctypes
+    io = 0 if cfg.io == "fp32" else 1
+    gp = (ctypes.c_void_p * cfg.N)(*[t.data_ptr() for t in gxs])
+    calls = []
+    for v, xs, spec, gy in data:
+        xp = (ctypes.c_void_p * cfg.N)(*[t.data_ptr() for t in xs])
+        calls.append(H.PreparedCall(lib.hyena_backward,
+                                    (H._ptr(v), xp, H._ptr(spec), H._ptr(gy), H._ptr(gv), gp, H._ptr(gh), cfg.B,
+                                     cfg.D, cfg.N, cfg.L, io, H._ptr(ws), wsb, H._stream(v)),
+                                    (v, xs, spec, gy, xp, gp), None, "hyena_backward"))
+    torch.cuda.synchronize()
+    ms, steps, warmup = _time_steps(torch, dev, lambda i: calls[i % sets](), args.steps, args.warmup)
+    t = ms / 1e3
+    mb, fl = backward_bytes(cfg), backward_flops(cfg)
+    roof = {"bound": "alu", "achieved": fl / t / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": fl / t / ALU_PEAK, "traffic": None, "kernel": "k_single_backward (one launch per step)",
+            "hbm_frac": mb / t / HBM_PEAK, "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl}
+    out = {
+        "metric": "Hyena order-N backward channel-tokens/sec (B*D*L/s)",
+        "value": cfg.B * cfg.D * cfg.L / t, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations and output gradient, random-init filter FFN)",
+        "config": {"workload": cfg.desc + ", backward", "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D,
+                   "L": cfg.L, "io": cfg.io, "input_sets": sets},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(cfg, fp)
+    print(json.dumps(out))
+    return 0
+
+
+def cpu_baseline_backward(cfg, fp, budget_s: float = 12.0):
+    """The float64 oracle's backward over all B rows of as many channels as
+    take about `budget_s` (channels are independent in the backward)."""
+    import numpy as np
+    import oracle as O
+    from workloads import make_activations
+    v, xs = make_activations(cfg, "cpu")
+    gy = np.random.default_rng(5).standard_normal(v.shape)
+    done, t0 = 0, time.perf_counter()
+    while done < cfg.D and time.perf_counter() - t0 < budget_s:
+        d = done
+        h = O.filter_gen(fp, cfg.L, channels=[d])
+        O.hyena_backward(v[:, d:d + 1].double().numpy(), [x[:, d:d + 1].double().numpy() for x in xs], h,
+                         gy[:, d:d + 1])
+        done += 1
+    wall = time.perf_counter() - t0
+    return {"value": cfg.B * done * cfg.L / wall, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {cfg.D} channels x {cfg.B} rows, float64 oracle backward, {wall:.1f} s"}
+
+
 def cpu_baseline_block(cfg, bp, h, budget_s: float = 12.0):
     """The float64 oracle's block on batch row 0 over a causal prefix of the
     sequence (the first Lp steps need only the first Lp inputs and taps),
@@ -278,6 +376,8 @@ def main(argv=None):
     ap.add_argument("--config", default="C2")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the operator (gradients of v, x_n and the filters)")
     ap.add_argument("--block", action="store_true",
                     help="time the whole block (in-projection + short convolutions, operator, out-projection)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -302,6 +402,8 @@ def main(argv=None):
     H.lib()
     if args.block:
         return run_block(args, cfg, torch, H, dev)
+    if args.backward:
+        return run_backward(args, cfg, torch, H, dev)
 
     # Device-to-device copy of 1 GiB: the practical HBM ceiling on this machine,
     # reported beside the datasheet peak (also the reference dispatch for

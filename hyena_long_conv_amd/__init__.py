@@ -24,7 +24,8 @@ __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectr
            "forward", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
            "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
            "in_projection", "out_projection", "block_forward", "block_workspace_bytes", "PreparedCall",
-           "prepare_in_projection", "prepare_out_projection", "prepare_block_forward"]
+           "prepare_in_projection", "prepare_out_projection", "prepare_block_forward", "backward",
+           "backward_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
@@ -96,6 +97,11 @@ def lib() -> ctypes.CDLL:
     L.hyena_block_workspace_bytes.restype = i64
     L.hyena_block_forward.argtypes = [vp, bp, vp, vp, i64, i64, i32, vp, i64, vp]
     L.hyena_block_forward.restype = i32
+    L.hyena_backward_workspace_bytes.argtypes = [i64, i32, i32, i64, i32]
+    L.hyena_backward_workspace_bytes.restype = i64
+    L.hyena_backward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, ctypes.POINTER(vp), vp, i64, i32, i32, i64, i32,
+                                 vp, i64, vp]
+    L.hyena_backward.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -371,3 +377,36 @@ def prepare_block_forward(u, bp: dict, spec, out, workspace):
                         (_ptr(u), ctypes.byref(p), _ptr(spec), _ptr(out), B, L, io, _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(u)),
                         (u, bp, p, spec, out, workspace), out, "hyena_block_forward")
+
+
+# ---------------------------------------------------------------- backward
+
+def backward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32") -> int:
+    return int(lib().hyena_backward_workspace_bytes(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16))
+
+
+def backward(v, xs, spec, gy, workspace=None):
+    """Gradients (gv, [gx_1..gx_N], gh) of a loss with dloss/dy = gy through
+    y = forward(v, xs, spec); gh [N, D, L] fp32 summed over the batch."""
+    import torch
+    io = _io_of(v)
+    _need_cuda(v, "v", v.dtype)
+    _need_cuda(gy, "gy", v.dtype)
+    B, D, L = v.shape
+    N = len(xs)
+    for i, t in enumerate(xs):
+        _need_cuda(t, f"x[{i}]", v.dtype)
+    gv = torch.empty_like(v)
+    gxs = [torch.empty_like(v) for _ in range(N)]
+    gh = torch.empty((N, D, L), dtype=torch.float32, device=v.device)
+    wsb = backward_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16")
+    if wsb < 0:
+        raise HyenaError(3, "hyena_backward_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
+    xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
+    gp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in gxs])
+    _check(lib().hyena_backward(_ptr(v), xp, _ptr(spec), _ptr(gy), _ptr(gv), gp, _ptr(gh), B, D, N, L, io,
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(v)),
+           "hyena_backward")
+    return gv, gxs, gh

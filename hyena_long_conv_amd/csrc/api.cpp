@@ -211,6 +211,76 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
+// --------------------------------------------------------------- backward
+
+namespace {
+constexpr int64_t kBackwardMaxN = 8192;   // complex points of the single-pass backward
+
+int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
+  const int64_t cb = (NORD * B * D * (p.N / 2) * 8 + 255) / 256 * 256;
+  return cb + NORD * D * p.N * 8;
+}
+}  // namespace
+
+int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io) {
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
+  PlanInfo p;
+  if (plan_env(L, &p)) return -1;
+  if (p.path != PATH_SINGLE || p.N > kBackwardMaxN) return -1;
+  return bwd_ws(p, B, D, N);
+}
+
+hyena_status hyena_backward(const void* v, const void* const* x, const void* spec, const void* gy, void* gv,
+                            void* const* gx, float* gh, int64_t B, int32_t D, int32_t N, int64_t L,
+                            hyena_dtype io, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!v || !x || !spec || !gy || !gv || !gx || !gh || !workspace) return HYENA_ERR_NULL;
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  for (int n = 0; n < N; ++n)
+    if (!x[n] || !gx[n]) return HYENA_ERR_NULL;
+  PlanInfo p;
+  const int c = plan_env(L, &p);
+  if (c) return from_plan_code(c);
+  if (p.path != PATH_SINGLE || p.N > kBackwardMaxN) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(v) || !aligned16(spec) || !aligned16(gy) || !aligned16(gv) || !aligned16(gh) ||
+      !aligned16(workspace))
+    return HYENA_ERR_ALIGN;
+  for (int n = 0; n < N; ++n)
+    if (!aligned16(x[n]) || !aligned16(gx[n])) return HYENA_ERR_ALIGN;
+  const int64_t need = bwd_ws(p, B, D, N);
+  if (workspace_bytes < need) return HYENA_ERR_WORKSPACE;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * D * L * esz, sb = spec_bytes(p, (int64_t)N * D), ghb = (int64_t)N * D * L * 4;
+  // outputs: gv, gx_1..gx_N, gh, workspace; inputs: v, x_1..x_N, spec, gy
+  const void* outs[11];
+  int64_t osz[11];
+  int no = 0;
+  outs[no] = gv; osz[no++] = act;
+  for (int n = 0; n < N; ++n) { outs[no] = gx[n]; osz[no++] = act; }
+  outs[no] = gh; osz[no++] = ghb;
+  outs[no] = workspace; osz[no++] = need;
+  for (int i = 0; i < no; ++i) {
+    if (overlap(outs[i], osz[i], v, act) || overlap(outs[i], osz[i], spec, sb) || overlap(outs[i], osz[i], gy, act))
+      return HYENA_ERR_ALIAS;
+    for (int n = 0; n < N; ++n)
+      if (overlap(outs[i], osz[i], x[n], act)) return HYENA_ERR_ALIAS;
+    for (int k = 0; k < i; ++k)
+      if (overlap(outs[i], osz[i], outs[k], osz[k])) return HYENA_ERR_ALIAS;
+  }
+  BackwardArgs a{};
+  a.v = v;
+  for (int n = 0; n < N; ++n) { a.x.p[n] = x[n]; a.gx.p[n] = gx[n]; }
+  a.spec = spec; a.gy = gy; a.gv = gv; a.gh = gh;
+  a.cbuf = workspace;
+  a.hacc = static_cast<char*>(workspace) + (need - (int64_t)N * D * p.N * 8);
+  a.B = (int)B; a.D = D; a.NORD = N; a.L = L;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  a.spec_stride = p.spec_stride;
+  return single_backward(a, p.N, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
 // ------------------------------------------------------------------ block
 
 namespace {

@@ -571,7 +571,6 @@ __device__ __forceinline__ cf realfft_bin(cf a, cf am, cf w, float scale) {
   return cscale(cadd(e, cmul(w, o)), 0.5f * scale);
 }
 
-// x[t] with zero padding beyond L.
 // x[t] with zero padding beyond L.  CLAMP: the load always runs, from a
 // clamped in-row index (L >= 1), so no branch splits the memory counters
 // (for loads that are mostly in range); otherwise padding loads are skipped.

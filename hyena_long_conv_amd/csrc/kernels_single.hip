@@ -233,6 +233,178 @@ k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int
   }
 }
 
+// ------------------------------------------------------------------ backward
+//
+// Gradients of the recurrence by the chain rule; the adjoint of a causal
+// convolution is the correlation with the same filter, i.e. the spectral
+// step with conjugated coefficients.  One workgroup per channel d walks the
+// B rows of that channel, so the filter gradients sum over the batch in its
+// own accumulators (deterministically).  Per row: the forward is recomputed
+// and each convolution output c_n saved (cbuf); then for n = N..1, with g the
+// gradient of z_{n+1}:  gx_n = g * c_n,  gc = g * x_n,  the spectra of z_n and
+// gc,  the filter-gradient term (spectral step whose "filter" is conj of z_n's
+// spectrum, pair coefficients built on the fly) added into hacc[n], and the
+// adjoint step plus inverse FFT give the gradient of z_n.  Finally each
+// hacc[n] is inverse transformed into gh_n.
+template <int N, int IOT, bool EVEN>
+__global__ void __launch_bounds__(SinglePlan<N>::T, 1)
+k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, const void* __restrict__ gy,
+                  void* __restrict__ gv, OutPtrs gx, float* __restrict__ gh, cf* __restrict__ cbuf,
+                  cf* __restrict__ hacc, int B, int D, int NORD, int L, int64_t spec_stride) {
+  using P = SinglePlan<N>;
+  constexpr int E = P::E, S = N / E, H2 = N / 2;
+  __shared__ cf smem[N];
+  const typename P::Lds lds{smem};
+  const int j = threadIdx.x, d = blockIdx.x;
+  BlockFFT<N, E, typename P::R> fft;
+  fft.init(j);
+  const int64_t qs = spec_stride / 3;
+  const cf wbase = twiddle<false>((uint32_t)j, (uint32_t)(2 * N));   // W_M^j
+  const float scM = 1.0f / (float)(2 * N);
+  const auto had = [](cf a, cf b) { return make_float2(a.x * b.x, a.y * b.y); };   // sample-wise product
+
+  for (int b = 0; b < B; ++b) {
+    const int64_t off = ((int64_t)b * D + d) * L;
+    cf u[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      u[i] = (i < E / 2) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+    // forward, saving c_n (packed points j + i*S, i < E/2)
+    for (int n = 0; n < NORD; ++n) {
+      PairCoeffs<N, E> pc;
+      pc.load(spec + (int64_t)(n * D + d) * spec_stride, qs, j);
+      fft.template run<false>(u, lds, j);
+      spectral_step<N, E, true>(u, lds, j, pc);
+      fft.template run<true>(u, lds, j);
+      cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * H2;
+      const void* xn = x.p[n];
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if (i < E / 2) {
+          cb[j + i * S] = u[i];
+          u[i] = had(ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L), u[i]);
+        } else {
+          u[i] = make_float2(0.f, 0.f);
+        }
+      }
+    }
+    // backward
+    cf g[E / 2];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) g[i] = ld_pair<IOT, EVEN, true>(gy, off, 2 * (int64_t)(j + i * S), L);
+    for (int n = NORD - 1; n >= 0; --n) {
+      const cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * H2;
+      const cf* cbp = cbuf + (((int64_t)(n > 0 ? n - 1 : 0) * B + b) * D + d) * H2;
+      const void* xn = x.p[n];
+      const void* xp = x.p[n > 0 ? n - 1 : 0];
+      PairCoeffs<N, E> pc;
+      pc.load(spec + (int64_t)(n * D + d) * spec_stride, qs, j);
+      cf zt[E], gt[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if (i < E / 2) {
+          const int64_t t = 2 * (int64_t)(j + i * S);
+          const cf c = cb[j + i * S];
+          st_pair<IOT, EVEN>(gx.p[n], off, t, L, had(g[i], c));                 // gx_n = g * c_n
+          gt[i] = had(g[i], ld_pair<IOT, EVEN, true>(xn, off, t, L));          // gc = g * x_n
+          zt[i] = (n == 0) ? ld_pair<IOT, EVEN, true>(v, off, t, L)
+                           : had(ld_pair<IOT, EVEN, true>(xp, off, t, L), cbp[j + i * S]);   // z_n
+        } else {
+          zt[i] = make_float2(0.f, 0.f);
+          gt[i] = make_float2(0.f, 0.f);
+        }
+      }
+      fft.template run<false>(zt, lds, j);
+      fft.template run<false>(gt, lds, j);
+      // exchange: high halves of Z at k (k >= N/2), of G at k - N/2
+      __syncthreads();
+#pragma unroll
+      for (int i = E / 2; i < E; ++i) {
+        lds(j + i * S) = zt[i];
+        lds(j + i * S - H2) = gt[i];
+      }
+      __syncthreads();
+      cf pz[E];
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        const cf w = cmul(wbase, w2e<E>(i));                 // W_M^p, p = j + i*S
+        if (i == 0 && j == 0) {                              // p = 0: its own partner
+          const cf z0 = zt[0];
+          cf f1, f2, fq;
+          pair_coeffs(make_float2((z0.x + z0.y) * scM, 0.f), make_float2((z0.x - z0.y) * scM, 0.f), 0.f, 1.f,
+                      f1, f2, fq);
+          pz[0] = conv_self(gt[0], f1, fq);
+          gt[0] = conv_self(gt[0], cconj(pc.a1[0]), cconj(pc.bq[0]));
+        } else {
+          const int m = N - (j + i * S);
+          const cf zm = lds(m), gm = lds(m - H2);
+          const cf xk = realfft_bin(zt[i], zm, w, scM);                     // X_z(p) / M
+          const cf xm = realfft_bin(zm, zt[i], make_float2(-w.x, w.y), scM);  // X_z(N-p) / M
+          cf f1, f2, fq;
+          pair_coeffs(cconj(xk), cconj(xm), -w.y, w.x, f1, f2, fq);
+          cf pa = gt[i], pb = gm;
+          conv_pair(pa, pb, f1, f2, fq);                     // filter-gradient spectrum at p, N-p
+          cf ga = gt[i], gb = gm;
+          conv_pair(ga, gb, cconj(pc.a1[i]), cconj(pc.a2[i]), cconj(pc.bq[i]));   // adjoint step
+          pz[i] = pa;
+          gt[i] = ga;
+          lds(m) = pb;
+          lds(m - H2) = gb;
+        }
+      }
+      if (j == 0) {                                          // p = N/2: its own partner
+        const cf zh = lds(H2), gq = lds(0);
+        const cf xh = realfft_bin(zh, zh, make_float2(0.f, -1.f), scM);
+        cf f1, f2, fq;
+        pair_coeffs(cconj(xh), cconj(xh), 1.f, 0.f, f1, f2, fq);
+        lds(H2) = cmul(f1, gq);
+        lds(0) = cmul(cconj(pc.half), gq);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = E / 2; i < E; ++i) {
+        pz[i] = lds(j + i * S);
+        gt[i] = lds(j + i * S - H2);
+      }
+      cf* ha = hacc + ((int64_t)n * D + d) * N;
+#pragma unroll
+      for (int i = 0; i < E; ++i) ha[j + i * S] = (b == 0) ? pz[i] : cadd(ha[j + i * S], pz[i]);
+      fft.template run<true>(gt, lds, j);
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) g[i] = gt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) st_pair<IOT, EVEN>(gv, off, 2 * (int64_t)(j + i * S), L, g[i]);
+  }
+  // filter gradients: inverse transform of each accumulated spectrum
+  for (int n = 0; n < NORD; ++n) {
+    const cf* ha = hacc + ((int64_t)n * D + d) * N;
+    cf u[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) u[i] = ha[j + i * S];
+    fft.template run<true>(u, lds, j);
+    float* out = gh + ((int64_t)n * D + d) * L;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const int64_t t = 2 * (int64_t)(j + i * S);
+      if (t < L) out[t] = u[i].x;
+      if (t + 1 < L) out[t + 1] = u[i].y;
+    }
+  }
+}
+
+template <int N, int IOT>
+static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
+  const dim3 grid(a.D), block(SinglePlan<N>::T);
+  if (a.L % 2 == 0)
+    hipLaunchKernelGGL((k_single_backward<N, IOT, true>), grid, block, 0, s, a.v, a.x, (const cf*)a.spec, a.gy, a.gv,
+                       a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
+  else
+    hipLaunchKernelGGL((k_single_backward<N, IOT, false>), grid, block, 0, s, a.v, a.x, (const cf*)a.spec, a.gy,
+                       a.gv, a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
+  return hipGetLastError();
+}
+
 template <int N, int IOT>
 static hipError_t launch_fwd(const ForwardArgs& a, hipStream_t s) {
   if (a.L % 2 == 0)
@@ -262,6 +434,18 @@ hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s) {
   switch (N) {
     HY_CASE(64) HY_CASE(128) HY_CASE(256) HY_CASE(512) HY_CASE(1024) HY_CASE(2048)
     HY_CASE(4096) HY_CASE(8192) HY_CASE(16384)
+    default: return hipErrorInvalidValue;
+  }
+#undef HY_CASE
+}
+
+hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s) {
+#define HY_CASE(NN)                                                       \
+  case NN:                                                                \
+    return a.io == 0 ? launch_bwd<NN, 0>(a, s) : launch_bwd<NN, 1>(a, s);
+  switch (N) {
+    HY_CASE(64) HY_CASE(128) HY_CASE(256) HY_CASE(512) HY_CASE(1024) HY_CASE(2048)
+    HY_CASE(4096) HY_CASE(8192)
     default: return hipErrorInvalidValue;
   }
 #undef HY_CASE

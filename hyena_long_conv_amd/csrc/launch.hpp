@@ -69,6 +69,29 @@ struct OutProjArgs {
 hipError_t in_projection(const InProjArgs& a, hipStream_t s);
 hipError_t out_projection(const OutProjArgs& a, hipStream_t s);
 
+// Backward of the recurrence (single-pass lengths).
+struct OutPtrs {
+  void* p[8];            // N device pointers
+};
+
+struct BackwardArgs {
+  const void* v;
+  XPtrsHost x;
+  const void* spec;
+  const void* gy;
+  void* gv;
+  OutPtrs gx;
+  float* gh;             // [N][D][L]
+  void* cbuf;            // workspace: N * B * D * N_c/2 complex
+  void* hacc;            // workspace: N * D * N_c complex
+  int B, D, NORD;
+  int64_t L;
+  int io;
+  int64_t spec_stride;
+};
+
+hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
+
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);

@@ -153,6 +153,26 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Backward of the recurrence (chain rule through the operator above; the
+ * pages state no gradient formulas): for a scalar loss with dloss/dy = gy,
+ *   gx_n = g_{n+1} * c_n,   gc_n = g_{n+1} * x_n,
+ *   g_n[s] = sum_{t>=s} h_n[t-s] gc_n[t]        (adjoint of the causal conv),
+ *   gh_n[k] = sum_b sum_{t>=k} gc_n[t] z_n[t-k]  (summed over the batch),
+ * with c_n = h_n conv z_n, g_{N+1} = gy and gv = g_1.  The forward
+ * intermediates are recomputed from v, x and the spectrum.
+ *   gy, gv    device [B][D][L], I/O dtype;   gx  HOST array of N device
+ *   pointers [B][D][L], I/O dtype;  gh  device fp32 [N][D][L].
+ * This build computes it for L <= 8192 (one workgroup per channel; longer
+ * rows return HYENA_ERR_UNSUPPORTED).  Errors as hyena_forward, plus ALIAS for
+ * an output overlapping an input or another output.
+ */
+int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
+
+hyena_status hyena_backward(const void* v, const void* const* x, const void* spec, const void* gy, void* gv,
+                            void* const* gx, float* gh, int64_t B, int32_t D, int32_t N, int64_t L,
+                            hyena_dtype io, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * The block around the operator (paper digest, irregular6612.github.io,
  * section "방법 (Method)", framework figure: one projection of width (N+1)D
  * yields v and the gates; homemade-llm "02. 3つの Hyena 演算子", section 2:

@@ -188,3 +188,26 @@ def test_block_calls_reject_bad_arguments():
     assert blk(w=0) == NULL
     assert blk(wsb=16) == WS
     assert blk(o=Dp) == ALIAS
+
+
+def test_backward_rejects_bad_arguments():
+    lib = H.lib()
+    x = (vp * 2)(Bp, C)
+    gx = (vp * 2)(Y + 0x100000, Y + 0x200000)
+    bw = lambda v=A, x=x, spec=Dp, gy=W, gv=Y, gx=gx, gh=Y + 0x300000, B=1, D=4, N=2, L=64, io=0, ws=0x70000000, wsb=1 << 24: \
+        lib.hyena_backward(vp(v), x, vp(spec), vp(gy), vp(gv), gx, vp(gh), B, D, N, L, io, vp(ws), wsb, None)
+    assert bw(v=0) == NULL
+    assert bw(gy=0) == NULL
+    assert bw(gh=0) == NULL
+    assert bw(ws=0) == NULL
+    assert bw(gx=(vp * 2)(Y + 0x100000, 0)) == NULL
+    assert bw(B=0) == SHAPE
+    assert bw(N=9, x=(vp * 9)(*[Bp + 0x10000 * i for i in range(9)])) == UNSUP
+    assert bw(L=9000) == UNSUP                                  # beyond the single-pass backward
+    assert bw(gv=Y + 4) == ALIGN
+    assert bw(wsb=16) == WS
+    assert bw(gv=A) == ALIAS                                    # gv over v
+    assert bw(gh=Y) == ALIAS                                    # gh over gv
+    assert bw(gx=(vp * 2)(Y + 0x100000, Bp)) == ALIAS           # gx_2 over x_1
+    assert H.backward_workspace_bytes(4, 768, 2, 2048) > 0
+    assert H.backward_workspace_bytes(1, 4, 2, 20000) == -1
