@@ -58,6 +58,12 @@ Readings where the pages are silent (each listed in the design notes):
   convolution is causal and depthwise (one T-tap filter per projected
   column, tap j weighting the sample j steps back, zero before t = 0); biases
   of both projections optional; the output projection has no activation.
+  Filter families ([P3] section 3): Hyena-LI's filter is a sum of real
+  exponentials R_s * lambda_s^t over a small state of size S (the page
+  indexes t from 1 with exponent t-1; here t = 0..L-1 with exponent t);
+  Hyena-MR's explicit filter hhat_t is damped by exp(-alpha_d * t) (the
+  page's lambda^(-alpha t) with the base folded into alpha_d); Hyena-SE's
+  short explicit filters are used as given.
   Backward: the pages give no gradient formulas; they follow from the
   recurrence by the chain rule (the adjoint of a causal convolution is the
   correlation with the same filter), for a scalar loss whose gradient with
@@ -84,6 +90,8 @@ __all__ = [
     "causal_conv_adjoint",
     "filter_correlation",
     "hyena_backward",
+    "filter_gen_li",
+    "filter_gen_mr",
     "DIRECT_MAX_L",
 ]
 
@@ -395,3 +403,25 @@ def hyena_backward(v: np.ndarray, xs, h: np.ndarray, gy: np.ndarray, conv=causal
         gh[n] = np.sum(filter_correlation(gc, zs[n]), axis=batch_axes) if batch_axes else filter_correlation(gc, zs[n])
         g = causal_conv_adjoint(h[n], gc)
     return g, gxs, gh
+
+
+# ---------------------------------------------------------------------------
+# Other filter families ([P3] section 3: Hyena-LI, Hyena-SE, Hyena-MR)
+# ---------------------------------------------------------------------------
+
+def filter_gen_li(R: np.ndarray, lam: np.ndarray, L: int) -> np.ndarray:
+    """Hyena-LI: h[f, t] = sum_s R[f, s] * lam[f, s]**t, t = 0..L-1 (0**0 = 1)."""
+    R = np.asarray(R, np.float64)
+    lam = np.asarray(lam, np.float64)
+    t = np.arange(L, dtype=np.float64)
+    return np.sum(R[..., None] * np.power(lam[..., None], t), axis=-2)
+
+
+def filter_gen_mr(hhat: np.ndarray, alpha: np.ndarray, N: int) -> np.ndarray:
+    """Hyena-MR: h[n, d, t] = hhat[n, d, t] * exp(-alpha[d] * t) (explicit
+    filter of its own length, exponentially damped per channel)."""
+    hhat = np.asarray(hhat, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    Lh = hhat.shape[-1]
+    t = np.arange(Lh, dtype=np.float64)
+    return hhat * np.exp(-alpha[None, :, None] * t)
