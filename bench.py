@@ -262,6 +262,52 @@ def backward_flops(cfg) -> float:
     return cfg.N * cfg.B * cfg.D * cfg.L * (25.0 * math.log2(2 * cfg.L) + 20.0)
 
 
+def run_fir(args, cfg, torch, H, dev):
+    """The recurrence with explicit short filters (Hyena-SE / Hyena-MR)
+    evaluated directly: one launch per step, bound by HBM (v, x_1..x_N in,
+    y out, the filters)."""
+    import ctypes
+    import numpy as np
+    from workloads import make_activations
+
+    Lh = args.fir
+    s = 4 if cfg.io == "fp32" else 2
+    mb = (cfg.N + 2) * cfg.B * cfg.D * cfg.L * s + cfg.N * cfg.D * Lh * 4
+    fl = 2.0 * cfg.N * cfg.B * cfg.D * cfg.L * (Lh + 1)
+    hs = torch.from_numpy((np.random.default_rng(cfg.seed).standard_normal((cfg.N, cfg.D, Lh)) / np.sqrt(Lh))
+                          .astype(np.float32)).to(dev)
+    sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / mb))
+    lib = H.lib()
+    io = 0 if cfg.io == "fp32" else 1
+    calls = []
+    for k in range(sets):
+        v, xs = make_activations(cfg.with_(seed=cfg.seed * 100 + k), dev)
+        y = torch.empty_like(v)
+        xp = (ctypes.c_void_p * cfg.N)(*[t.data_ptr() for t in xs])
+        calls.append(H.PreparedCall(lib.hyena_forward_fir,
+                                    (H._ptr(v), xp, H._ptr(hs), Lh, H._ptr(y), cfg.B, cfg.D, cfg.N, cfg.L, io,
+                                     H._stream(v)), (v, xs, xp, y, hs), y, "hyena_forward_fir"))
+    torch.cuda.synchronize()
+    ms, steps, warmup = _time_steps(torch, dev, lambda i: calls[i % sets](), args.steps, args.warmup)
+    t = ms / 1e3
+    copy_bps = measure_copy(torch, dev)
+    roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": mb / t / HBM_PEAK,
+            "traffic": None, "kernel": "k_fir_forward (one launch per step)", "copy_GBps": copy_bps / 1e9,
+            "hbm_frac_vs_copy": mb / t / copy_bps, "alu_frac": fl / t / ALU_PEAK,
+            "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl}
+    out = {
+        "metric": "Hyena order-N fwd with explicit short filters, channel-tokens/sec (B*D*L/s)",
+        "value": cfg.B * cfg.D * cfg.L / t, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations and filters)",
+        "config": {"workload": cfg.desc + f", explicit {Lh}-tap filters", "name": cfg.name, "N": cfg.N, "B": cfg.B,
+                   "D": cfg.D, "L": cfg.L, "io": cfg.io, "taps": Lh, "input_sets": sets},
+        "roofline": roof,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def run_backward(args, cfg, torch, H, dev):
     """The backward of the operator: one step = one hyena_backward (recomputes
     the forward's convolutions, then gradients of v, every x_n and the
@@ -378,6 +424,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the operator (gradients of v, x_n and the filters)")
+    ap.add_argument("--fir", type=int, default=0, metavar="LH",
+                    help="time the recurrence with explicit short filters of LH taps (hyena_forward_fir)")
     ap.add_argument("--block", action="store_true",
                     help="time the whole block (in-projection + short convolutions, operator, out-projection)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -404,6 +452,8 @@ def main(argv=None):
         return run_block(args, cfg, torch, H, dev)
     if args.backward:
         return run_backward(args, cfg, torch, H, dev)
+    if args.fir:
+        return run_fir(args, cfg, torch, H, dev)
 
     # Device-to-device copy of 1 GiB: the practical HBM ceiling on this machine,
     # reported beside the datasheet peak (also the reference dispatch for

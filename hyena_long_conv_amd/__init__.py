@@ -25,7 +25,7 @@ __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectr
            "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
            "in_projection", "out_projection", "block_forward", "block_workspace_bytes", "PreparedCall",
            "prepare_in_projection", "prepare_out_projection", "prepare_block_forward", "backward",
-           "backward_workspace_bytes"]
+           "backward_workspace_bytes", "filter_gen_li", "filter_gen_mr", "forward_fir"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
@@ -102,6 +102,12 @@ def lib() -> ctypes.CDLL:
     L.hyena_backward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, ctypes.POINTER(vp), vp, i64, i32, i32, i64, i32,
                                  vp, i64, vp]
     L.hyena_backward.restype = i32
+    L.hyena_filter_gen_li.argtypes = [vp, vp, i32, i32, i32, i64, vp, vp]
+    L.hyena_filter_gen_li.restype = i32
+    L.hyena_filter_gen_mr.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.hyena_filter_gen_mr.restype = i32
+    L.hyena_forward_fir.argtypes = [vp, ctypes.POINTER(vp), vp, i32, vp, i64, i32, i32, i64, i32, vp]
+    L.hyena_forward_fir.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -410,3 +416,45 @@ def backward(v, xs, spec, gy, workspace=None):
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(v)),
            "hyena_backward")
     return gv, gxs, gh
+
+
+# ---------------------------------------------------------- filter families
+
+def filter_gen_li(R, lam, D: int, N: int, L: int):
+    """Hyena-LI filters h [N, D, L] from R, lam [N*D, S] (fp32 CUDA tensors)."""
+    import torch
+    _need_cuda(R, "R", torch.float32)
+    _need_cuda(lam, "lambda", torch.float32)
+    S = R.shape[-1]
+    h = torch.empty((N, D, L), dtype=torch.float32, device=R.device)
+    _check(lib().hyena_filter_gen_li(_ptr(R), _ptr(lam), D, N, S, L, _ptr(h), _stream(R)), "hyena_filter_gen_li")
+    return h
+
+
+def filter_gen_mr(hhat, alpha):
+    """Hyena-MR filters: hhat [N, D, Lh] damped by exp(-alpha[d] t)."""
+    import torch
+    _need_cuda(hhat, "hhat", torch.float32)
+    _need_cuda(alpha, "alpha", torch.float32)
+    N, D, Lh = hhat.shape
+    h = torch.empty_like(hhat)
+    _check(lib().hyena_filter_gen_mr(_ptr(hhat), _ptr(alpha), D, N, Lh, _ptr(h), _stream(hhat)),
+           "hyena_filter_gen_mr")
+    return h
+
+
+def forward_fir(v, xs, h, out=None):
+    """The recurrence with explicit short filters h [N, D, Lh] (fp32), evaluated directly."""
+    import torch
+    io = _io_of(v)
+    _need_cuda(v, "v", v.dtype)
+    _need_cuda(h, "h", torch.float32)
+    B, D, L = v.shape
+    N = len(xs)
+    for i, t in enumerate(xs):
+        _need_cuda(t, f"x[{i}]", v.dtype)
+    y = out if out is not None else torch.empty_like(v)
+    xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
+    _check(lib().hyena_forward_fir(_ptr(v), xp, _ptr(h), h.shape[-1], _ptr(y), B, D, N, L, io, _stream(v)),
+           "hyena_forward_fir")
+    return y

@@ -211,6 +211,54 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
+// ------------------------------------------------------- filter families
+
+hyena_status hyena_filter_gen_li(const float* R, const float* lambda, int32_t D, int32_t N, int32_t S, int64_t L,
+                                 float* h, void* stream) {
+  if (!R || !lambda || !h) return HYENA_ERR_NULL;
+  if (!sizes_ok(D, N, L) || N > kMaxOrder || S < 1 || S > 64) return HYENA_ERR_SHAPE;
+  if (!aligned16(h)) return HYENA_ERR_ALIGN;
+  const int64_t NF = (int64_t)N * D;
+  if (overlap(h, NF * L * 4, R, NF * S * 4) || overlap(h, NF * L * 4, lambda, NF * S * 4)) return HYENA_ERR_ALIAS;
+  return filter_gen_li(R, lambda, (int)NF, S, L, h, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+hyena_status hyena_filter_gen_mr(const float* hhat, const float* alpha, int32_t D, int32_t N, int32_t Lh, float* h,
+                                 void* stream) {
+  if (!hhat || !alpha || !h) return HYENA_ERR_NULL;
+  if (!sizes_ok(D, N, 1) || N > kMaxOrder || Lh < 1 || Lh > kMaxL) return HYENA_ERR_SHAPE;
+  if (!aligned16(h)) return HYENA_ERR_ALIGN;
+  const int64_t NF = (int64_t)N * D;
+  if (h != hhat && overlap(h, NF * Lh * 4, hhat, NF * Lh * 4)) return HYENA_ERR_ALIAS;   // in place is fine
+  return filter_gen_mr(hhat, alpha, D, (int)NF, Lh, h, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+hyena_status hyena_forward_fir(const void* v, const void* const* x, const float* h, int32_t Lh, void* y, int64_t B,
+                               int32_t D, int32_t N, int64_t L, hyena_dtype io, void* stream) {
+  if (!v || !x || !h || !y) return HYENA_ERR_NULL;
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || Lh < 1 || Lh > HYENA_MAX_FIR) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  for (int n = 0; n < N; ++n)
+    if (!x[n]) return HYENA_ERR_NULL;
+  if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(v) || !aligned16(y) || !aligned16(h)) return HYENA_ERR_ALIGN;
+  for (int n = 0; n < N; ++n)
+    if (!aligned16(x[n])) return HYENA_ERR_ALIGN;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * D * L * esz;
+  if (overlap(y, act, v, act) || overlap(y, act, h, (int64_t)N * D * Lh * 4)) return HYENA_ERR_ALIAS;
+  for (int n = 0; n < N; ++n)
+    if (overlap(y, act, x[n], act)) return HYENA_ERR_ALIAS;
+  ForwardArgs a{};
+  a.v = v;
+  for (int n = 0; n < N; ++n) a.x.p[n] = x[n];
+  a.y = y; a.B = (int)B; a.D = D; a.NORD = N; a.L = L;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  a.n_rows = (int)(B * D);
+  return fir_forward(a, h, Lh, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
 // --------------------------------------------------------------- backward
 
 namespace {

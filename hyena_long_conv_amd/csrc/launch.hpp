@@ -92,6 +92,11 @@ struct BackwardArgs {
 
 hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 
+// Other filter families (kernels_fir.hip).
+hipError_t filter_gen_li(const float* R, const float* lam, int NF, int S, int64_t L, float* h, hipStream_t s);
+hipError_t filter_gen_mr(const float* hhat, const float* alpha, int D, int NF, int Lh, float* h, hipStream_t s);
+hipError_t fir_forward(const ForwardArgs& a, const float* h, int Lh, hipStream_t s);
+
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);

@@ -153,6 +153,33 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Other filter families (homemade-llm "02. 3つの Hyena 演算子", section 3).
+ *
+ * hyena_filter_gen_li -- Hyena-LI: each filter is a sum of S real
+ * exponentials, h[f][t] = sum_s R[f][s] * lambda[f][s]^t for t = 0..L-1
+ * (0^0 = 1), f = n*D + d.  R, lambda: device fp32 [N*D][S]; h: device fp32
+ * [N][D][L] (feed it to hyena_filter_spectrum like the FFN filters).
+ * Errors: NULL -> NULL; D, N, L or S (1..64) out of range -> SHAPE.
+ */
+hyena_status hyena_filter_gen_li(const float* R, const float* lambda, int32_t D, int32_t N, int32_t S, int64_t L,
+                                 float* h, void* stream);
+
+/* hyena_filter_gen_mr -- Hyena-MR: explicit filters of Lh taps damped per
+ * channel, h[n][d][t] = hhat[n][d][t] * exp(-alpha[d] * t), t < Lh.  hhat,
+ * h: device fp32 [N][D][Lh]; alpha: [D].  Errors as above. */
+hyena_status hyena_filter_gen_mr(const float* hhat, const float* alpha, int32_t D, int32_t N, int32_t Lh,
+                                 float* h, void* stream);
+
+/* hyena_forward_fir -- the order-N recurrence with explicit short filters
+ * (Hyena-SE, or Hyena-MR after hyena_filter_gen_mr): h device fp32
+ * [N][D][Lh], Lh in 1..HYENA_MAX_FIR, each convolution evaluated directly
+ * (c[t] = sum_{k<Lh, k<=t} h[k] z[t-k]; no FFT, no spectrum, no workspace).
+ * Other arguments and errors as hyena_forward. */
+#define HYENA_MAX_FIR 256
+hyena_status hyena_forward_fir(const void* v, const void* const* x, const float* h, int32_t Lh, void* y,
+                               int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io, void* stream);
+
+/*
  * Backward of the recurrence (chain rule through the operator above; the
  * pages state no gradient formulas): for a scalar loss with dloss/dy = gy,
  *   gx_n = g_{n+1} * c_n,   gc_n = g_{n+1} * x_n,

@@ -211,3 +211,25 @@ def test_backward_rejects_bad_arguments():
     assert bw(gx=(vp * 2)(Y + 0x100000, Bp)) == ALIAS           # gx_2 over x_1
     assert H.backward_workspace_bytes(4, 768, 2, 2048) > 0
     assert H.backward_workspace_bytes(1, 4, 2, 20000) == -1
+
+
+def test_filter_family_calls_reject_bad_arguments():
+    lib = H.lib()
+    assert lib.hyena_filter_gen_li(None, vp(Bp), 4, 2, 8, 64, vp(Y), None) == NULL
+    assert lib.hyena_filter_gen_li(vp(A), vp(Bp), 4, 2, 0, 64, vp(Y), None) == SHAPE
+    assert lib.hyena_filter_gen_li(vp(A), vp(Bp), 4, 2, 65, 64, vp(Y), None) == SHAPE
+    assert lib.hyena_filter_gen_li(vp(A), vp(Bp), 4, 2, 8, 64, vp(Y + 4), None) == ALIGN
+    assert lib.hyena_filter_gen_li(vp(A), vp(Bp), 4, 2, 8, 64, vp(A), None) == ALIAS
+    assert lib.hyena_filter_gen_mr(vp(A), None, 4, 2, 16, vp(Y), None) == NULL
+    assert lib.hyena_filter_gen_mr(vp(A), vp(Bp), 4, 2, 0, vp(Y), None) == SHAPE
+    assert lib.hyena_filter_gen_mr(vp(A), vp(Bp), 4, 2, 16, vp(A + 64), None) == ALIAS
+    x = (vp * 2)(Bp, C)
+    fir = lambda v=A, x=x, h=Dp, Lh=7, y=Y, B=1, D=4, N=2, L=64, io=0: lib.hyena_forward_fir(
+        vp(v), x, vp(h), Lh, vp(y), B, D, N, L, io, None)
+    assert fir(h=0) == NULL
+    assert fir(Lh=0) == SHAPE
+    assert fir(Lh=257) == SHAPE
+    assert fir(N=9, x=(vp * 9)(*[Bp + 0x10000 * i for i in range(9)])) == UNSUP
+    assert fir(y=Y + 2) == ALIGN
+    assert fir(y=C) == ALIAS
+    assert fir(y=Dp) == ALIAS
