@@ -34,16 +34,21 @@ ALU_PEAK_PACKED = 157.3e12        # vendor figure, needs packed-FP32 instruction
 MALL_BYTES = 256 << 20
 
 
-def min_bytes(cfg) -> int:
+def min_bytes(cfg, circular: bool = False) -> int:
     """Algorithmic HBM bytes of one forward: v, x_1..x_N, y in the I/O dtype
-    plus the spectrum read once as complex64 with L+1 bins per (n, d)."""
+    plus the spectrum read once as complex64 with L+1 bins per (n, d) (L/2+1
+    in circular mode, where the FFT length is L)."""
     s = 4 if cfg.io == "fp32" else 2
-    return (cfg.N + 2) * cfg.B * cfg.D * cfg.L * s + cfg.N * cfg.D * (cfg.L + 1) * 8
+    bins = cfg.L // 2 + 1 if circular else cfg.L + 1
+    return (cfg.N + 2) * cfg.B * cfg.D * cfg.L * s + cfg.N * cfg.D * bins * 8
 
 
-def algo_flops(cfg) -> float:
+def algo_flops(cfg, circular: bool = False) -> float:
     """N * (10 log2(2L) + 7) flops per channel-token: forward and inverse real
-    FFT of 2L points at 2.5 M log2 M each, one complex product per bin, gate."""
+    FFT of 2L points at 2.5 M log2 M each, one complex product per bin, gate
+    (circular mode, M = L: N * (5 log2 L + 4))."""
+    if circular:
+        return cfg.N * cfg.B * cfg.D * cfg.L * (5.0 * math.log2(cfg.L) + 4.0)
     return cfg.N * cfg.B * cfg.D * cfg.L * (10.0 * math.log2(2 * cfg.L) + 7.0)
 
 
@@ -422,6 +427,8 @@ def main(argv=None):
     ap.add_argument("--config", default="C2")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--circular", action="store_true",
+                    help="periodic convolution (FFT length L, no zero padding; L a power of two)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the operator (gradients of v, x_n and the filters)")
     ap.add_argument("--fir", type=int, default=0, metavar="LH",
@@ -465,7 +472,7 @@ def main(argv=None):
     p = make_filter_params(cfg)
     pd = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in p.items()}
     h = H.filter_gen(pd, cfg.L)
-    spec0 = H.filter_spectrum(h)
+    spec0 = H.filter_spectrum(h, circular=args.circular)
     del h
     data = []
     for s in range(sets):
@@ -473,13 +480,13 @@ def main(argv=None):
         v, xs = make_activations(c, dev)
         spec = spec0 if s == 0 else spec0.clone()
         data.append((v, xs, spec, torch.empty_like(v)))
-    wsb = H.forward_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io)
+    wsb = H.forward_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io, circular=args.circular)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     # One prepared C-ABI call per input set: the timed loop pays no Python
     # argument checks (the library still validates every call on the host).
-    calls = [H.PreparedForward(v, xs, spec, out=y, workspace=ws) for v, xs, spec, y in data]
+    calls = [H.PreparedForward(v, xs, spec, out=y, workspace=ws, circular=args.circular) for v, xs, spec, y in data]
 
     def step(i):
         calls[i % sets]()
@@ -527,11 +534,11 @@ def main(argv=None):
     t = ms / 1e3
     tokens = cfg.B * cfg.D * cfg.L
     value = tokens / t
-    mb, fl = min_bytes(cfg), algo_flops(cfg)
+    mb, fl = min_bytes(cfg, args.circular), algo_flops(cfg, args.circular)
     hbm_frac = mb / t / HBM_PEAK
     alu_frac = fl / t / ALU_PEAK
-    plan = H.plan(cfg.L)
-    traffic = measured_traffic(cfg.name)
+    plan = H.plan(cfg.L, circular=args.circular)
+    traffic = None if args.circular else measured_traffic(cfg.name)
     bound = "alu" if fl / mb > ALU_PEAK / HBM_PEAK else "hbm"
     if bound == "alu":
         roof = {"bound": "alu", "achieved": fl / t / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s",
@@ -553,6 +560,7 @@ def main(argv=None):
         "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations, random-init filter FFN)",
         "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D, "L": cfg.L,
                    "io": cfg.io, "ffn_hidden": cfg.H, "fft_len": plan["M"], "path": plan["path"],
+                   "conv": "circular" if args.circular else "linear (zero-padded)",
                    "input_sets": sets, "wall_s": wall},
         "timing": {"ms_median": q(0.5), "ms_p10": q(0.1), "ms_p90": q(0.9), "ms_mean": ms},
         "roofline": roof,

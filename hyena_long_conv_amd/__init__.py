@@ -108,6 +108,20 @@ def lib() -> ctypes.CDLL:
     L.hyena_filter_gen_mr.restype = i32
     L.hyena_forward_fir.argtypes = [vp, ctypes.POINTER(vp), vp, i32, vp, i64, i32, i32, i64, i32, vp]
     L.hyena_forward_fir.restype = i32
+    L.hyena_plan_ex.argtypes = [i64, i32, ctypes.POINTER(PlanInfo)]
+    L.hyena_plan_ex.restype = i32
+    L.hyena_spectrum_bytes_ex.argtypes = [i32, i32, i64, i32]
+    L.hyena_spectrum_bytes_ex.restype = i64
+    L.hyena_spectrum_workspace_bytes_ex.argtypes = [i32, i32, i64, i32]
+    L.hyena_spectrum_workspace_bytes_ex.restype = i64
+    L.hyena_filter_spectrum_ex.argtypes = [vp, i32, i32, i64, i32, vp, vp, i64, vp]
+    L.hyena_filter_spectrum_ex.restype = i32
+    L.hyena_spectrum_export_ex.argtypes = [vp, i32, i32, i64, i32, vp, vp]
+    L.hyena_spectrum_export_ex.restype = i32
+    L.hyena_forward_workspace_bytes_ex.argtypes = [i64, i32, i32, i64, i32, i32]
+    L.hyena_forward_workspace_bytes_ex.restype = i64
+    L.hyena_forward_ex.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, i32, vp, i64, vp]
+    L.hyena_forward_ex.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -145,23 +159,31 @@ def _need_cuda(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def plan(L: int) -> dict:
+HYENA_CONV_LINEAR, HYENA_CONV_CIRCULAR = 0, 1
+
+
+def _mode(circular: bool) -> int:
+    return HYENA_CONV_CIRCULAR if circular else HYENA_CONV_LINEAR
+
+
+def plan(L: int, circular: bool = False) -> dict:
     info = PlanInfo()
-    _check(lib().hyena_plan(int(L), ctypes.byref(info)), "hyena_plan")
+    _check(lib().hyena_plan_ex(int(L), _mode(circular), ctypes.byref(info)), "hyena_plan")
     return dict(L=info.L, M=info.M, path=("single" if info.path == 1 else "fourstep"),
                 n1=info.n1, n2=info.n2, spec_stride=info.spec_stride)
 
 
-def spectrum_bytes(D: int, N: int, L: int) -> int:
-    return int(lib().hyena_spectrum_bytes(D, N, L))
+def spectrum_bytes(D: int, N: int, L: int, circular: bool = False) -> int:
+    return int(lib().hyena_spectrum_bytes_ex(D, N, L, _mode(circular)))
 
 
-def spectrum_workspace_bytes(D: int, N: int, L: int) -> int:
-    return int(lib().hyena_spectrum_workspace_bytes(D, N, L))
+def spectrum_workspace_bytes(D: int, N: int, L: int, circular: bool = False) -> int:
+    return int(lib().hyena_spectrum_workspace_bytes_ex(D, N, L, _mode(circular)))
 
 
-def forward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32") -> int:
-    return int(lib().hyena_forward_workspace_bytes(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16))
+def forward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32", circular: bool = False) -> int:
+    return int(lib().hyena_forward_workspace_bytes_ex(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16,
+                                                      _mode(circular)))
 
 
 def filter_gen(params: dict, L: int, out=None):
@@ -184,32 +206,37 @@ def filter_gen(params: dict, L: int, out=None):
     return h
 
 
-def filter_spectrum(h, out=None, workspace=None):
-    """Spectrum of the filters h [N, D, L] (fp32), as an opaque uint8 buffer."""
+def filter_spectrum(h, out=None, workspace=None, circular: bool = False):
+    """Spectrum of the filters h [N, D, L] (fp32), as an opaque uint8 buffer
+    (for the linear, zero-padded convolution, or the circular one)."""
     import torch
     _need_cuda(h, "h", torch.float32)
     N, D, L = h.shape
-    nbytes = spectrum_bytes(D, N, L)
+    nbytes = spectrum_bytes(D, N, L, circular)
     if nbytes < 0:
-        raise HyenaError(2, "hyena_spectrum_bytes")
+        raise HyenaError(3 if circular else 2, "hyena_spectrum_bytes")
     spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=h.device)
-    wsb = spectrum_workspace_bytes(D, N, L)
+    wsb = spectrum_workspace_bytes(D, N, L, circular)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=h.device)
-    _check(lib().hyena_filter_spectrum(_ptr(h), D, N, L, _ptr(spec), _ptr(workspace),
-                                       workspace.numel() if workspace is not None else 0, _stream(h)),
+    _check(lib().hyena_filter_spectrum_ex(_ptr(h), D, N, L, _mode(circular), _ptr(spec), _ptr(workspace),
+                                          workspace.numel() if workspace is not None else 0, _stream(h)),
            "hyena_filter_spectrum")
     spec._hyena_shape = (D, N, L)
+    spec._hyena_circular = bool(circular)
     return spec
 
 
-def spectrum_export(spec, D: int, N: int, L: int):
+def spectrum_export(spec, D: int, N: int, L: int, circular: bool | None = None):
     """Natural-order spectrum [N, D, M/2+1] complex64 (unscaled DFT of each
-    filter zero-padded to M points)."""
+    filter zero-padded to M points; M = L in circular mode)."""
     import torch
-    M = plan(L)["M"]
+    if circular is None:
+        circular = getattr(spec, "_hyena_circular", False)
+    M = plan(L, circular)["M"]
     out = torch.empty((N, D, M // 2 + 1, 2), dtype=torch.float32, device=spec.device)
-    _check(lib().hyena_spectrum_export(_ptr(spec), D, N, L, _ptr(out), _stream(out)), "hyena_spectrum_export")
+    _check(lib().hyena_spectrum_export_ex(_ptr(spec), D, N, L, _mode(circular), _ptr(out), _stream(out)),
+           "hyena_spectrum_export")
     return torch.view_as_complex(out)
 
 
@@ -219,8 +246,10 @@ class PreparedForward:
     preparation (for loops over fixed buffers, where the per-call Python
     checks would otherwise cost as much as a short kernel)."""
 
-    def __init__(self, v, xs, spec, out=None, workspace=None):
+    def __init__(self, v, xs, spec, out=None, workspace=None, circular: bool | None = None):
         import torch
+        if circular is None:
+            circular = getattr(spec, "_hyena_circular", False)
         if v.dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("v must be float32 or bfloat16")
         _need_cuda(v, "v", v.dtype)
@@ -233,14 +262,14 @@ class PreparedForward:
         io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
         y = out if out is not None else torch.empty_like(v)
         _need_cuda(y, "y", v.dtype)
-        wsb = int(lib().hyena_forward_workspace_bytes(B, D, N, L, io))
+        wsb = int(lib().hyena_forward_workspace_bytes_ex(B, D, N, L, io, _mode(circular)))
         if workspace is None and wsb > 0:
             workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
         self.y = y
         self._keep = (v, tuple(xs), spec, y, workspace)     # the buffers stay alive while prepared
-        self._fn = lib().hyena_forward
+        self._fn = lib().hyena_forward_ex
         self._args = (_ptr(v), (ctypes.c_void_p * N)(*[x.data_ptr() for x in xs]), _ptr(spec), _ptr(y),
-                      B, D, N, L, io, _ptr(workspace),
+                      B, D, N, L, io, _mode(circular), _ptr(workspace),
                       workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(v))
 
     def __call__(self):
@@ -250,9 +279,10 @@ class PreparedForward:
         return self.y
 
 
-def forward(v, xs, spec, out=None, workspace=None):
-    """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16)."""
-    return PreparedForward(v, xs, spec, out, workspace)()
+def forward(v, xs, spec, out=None, workspace=None, circular: bool | None = None):
+    """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16).
+    The convolution mode defaults to the one the spectrum was built for."""
+    return PreparedForward(v, xs, spec, out, workspace, circular)()
 
 
 # ---------------------------------------------------------------- the block

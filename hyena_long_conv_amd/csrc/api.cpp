@@ -16,9 +16,11 @@ using namespace hyena;
 
 namespace {
 
-int plan_env(int64_t L, PlanInfo* p) {
-  return make_plan(L, std::getenv("HYENA_FORCE_PATH"), std::getenv("HYENA_FOURSTEP_N1"), p);
+int plan_env(int64_t L, PlanInfo* p, int circular = 0) {
+  return make_plan(L, std::getenv("HYENA_FORCE_PATH"), std::getenv("HYENA_FOURSTEP_N1"), p, circular);
 }
+
+bool mode_ok(hyena_conv_mode m) { return m == HYENA_CONV_LINEAR || m == HYENA_CONV_CIRCULAR; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -65,10 +67,13 @@ const char* hyena_status_str(hyena_status s) {
   return "unknown status";
 }
 
-hyena_status hyena_plan(int64_t L, hyena_plan_info* out) {
+hyena_status hyena_plan(int64_t L, hyena_plan_info* out) { return hyena_plan_ex(L, HYENA_CONV_LINEAR, out); }
+
+hyena_status hyena_plan_ex(int64_t L, hyena_conv_mode mode, hyena_plan_info* out) {
   if (!out) return HYENA_ERR_NULL;
+  if (!mode_ok(mode)) return HYENA_ERR_UNSUPPORTED;
   PlanInfo p;
-  const int c = plan_env(L, &p);
+  const int c = plan_env(L, &p, mode);
   if (c) return from_plan_code(c);
   out->L = p.L;
   out->M = p.M;
@@ -95,26 +100,39 @@ hyena_status hyena_filter_gen(const hyena_filter_params* p, int64_t L, float* h,
 }
 
 int64_t hyena_spectrum_bytes(int32_t D, int32_t N, int64_t L) {
-  if (!sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  return hyena_spectrum_bytes_ex(D, N, L, HYENA_CONV_LINEAR);
+}
+
+int64_t hyena_spectrum_bytes_ex(int32_t D, int32_t N, int64_t L, hyena_conv_mode mode) {
+  if (!sizes_ok(D, N, L) || N > kMaxOrder || !mode_ok(mode)) return -1;
   PlanInfo p;
-  if (plan_env(L, &p)) return -1;
+  if (plan_env(L, &p, mode)) return -1;
   return spec_bytes(p, (int64_t)N * D);
 }
 
 int64_t hyena_spectrum_workspace_bytes(int32_t D, int32_t N, int64_t L) {
-  if (!sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  return hyena_spectrum_workspace_bytes_ex(D, N, L, HYENA_CONV_LINEAR);
+}
+
+int64_t hyena_spectrum_workspace_bytes_ex(int32_t D, int32_t N, int64_t L, hyena_conv_mode mode) {
+  if (!sizes_ok(D, N, L) || N > kMaxOrder || !mode_ok(mode)) return -1;
   PlanInfo p;
-  if (plan_env(L, &p)) return -1;
+  if (plan_env(L, &p, mode)) return -1;
   return spectrum_ws(p, (int64_t)N * D);
 }
 
 hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t L, void* spec,
                                    void* workspace, int64_t workspace_bytes, void* stream) {
+  return hyena_filter_spectrum_ex(h, D, N, L, HYENA_CONV_LINEAR, spec, workspace, workspace_bytes, stream);
+}
+
+hyena_status hyena_filter_spectrum_ex(const float* h, int32_t D, int32_t N, int64_t L, hyena_conv_mode mode,
+                                      void* spec, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!h || !spec) return HYENA_ERR_NULL;
   if (!sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
-  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (N > kMaxOrder || !mode_ok(mode)) return HYENA_ERR_UNSUPPORTED;
   PlanInfo p;
-  const int c = plan_env(L, &p);
+  const int c = plan_env(L, &p, mode);
   if (c) return from_plan_code(c);
   const int64_t NF = (int64_t)N * D;
   if (!aligned16(h) || !aligned16(spec) || (workspace && !aligned16(workspace))) return HYENA_ERR_ALIGN;
@@ -127,6 +145,7 @@ hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t
   SpectrumArgs a{};
   a.h = h; a.spec = spec; a.NF = (int)NF; a.L = L; a.spec_stride = p.spec_stride;
   a.work = workspace;
+  a.circular = p.circular;
   hipError_t e;
   if (p.path == PATH_SINGLE) {
     e = single_spectrum(a, p.N, (hipStream_t)stream);
@@ -141,11 +160,16 @@ hyena_status hyena_filter_spectrum(const float* h, int32_t D, int32_t N, int64_t
 
 hyena_status hyena_spectrum_export(const void* spec, int32_t D, int32_t N, int64_t L, float* out,
                                    void* stream) {
+  return hyena_spectrum_export_ex(spec, D, N, L, HYENA_CONV_LINEAR, out, stream);
+}
+
+hyena_status hyena_spectrum_export_ex(const void* spec, int32_t D, int32_t N, int64_t L, hyena_conv_mode mode,
+                                      float* out, void* stream) {
   if (!spec || !out) return HYENA_ERR_NULL;
   if (!sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
-  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (N > kMaxOrder || !mode_ok(mode)) return HYENA_ERR_UNSUPPORTED;
   PlanInfo p;
-  const int c = plan_env(L, &p);
+  const int c = plan_env(L, &p, mode);
   if (c) return from_plan_code(c);
   if (!aligned16(spec) || !aligned16(out)) return HYENA_ERR_ALIGN;
   const int64_t NF = (int64_t)N * D;
@@ -155,25 +179,36 @@ hyena_status hyena_spectrum_export(const void* spec, int32_t D, int32_t N, int64
 }
 
 int64_t hyena_forward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io) {
-  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || N > kMaxOrder) return -1;
+  return hyena_forward_workspace_bytes_ex(B, D, N, L, io, HYENA_CONV_LINEAR);
+}
+
+int64_t hyena_forward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
+                                         hyena_conv_mode mode) {
+  if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || N > kMaxOrder || !mode_ok(mode)) return -1;
   if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
   PlanInfo p;
-  if (plan_env(L, &p)) return -1;
+  if (plan_env(L, &p, mode)) return -1;
   return forward_ws(p, B, D);
 }
 
 hyena_status hyena_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
                            int32_t D, int32_t N, int64_t L, hyena_dtype io, void* workspace,
                            int64_t workspace_bytes, void* stream) {
+  return hyena_forward_ex(v, x, spec, y, B, D, N, L, io, HYENA_CONV_LINEAR, workspace, workspace_bytes, stream);
+}
+
+hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                              int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
   if (!v || !x || !spec || !y) return HYENA_ERR_NULL;
   if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
-  if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
+  if (N > kMaxOrder || !mode_ok(mode)) return HYENA_ERR_UNSUPPORTED;
   if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
   for (int n = 0; n < N; ++n)
     if (!x[n]) return HYENA_ERR_NULL;
   if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
   PlanInfo p;
-  const int c = plan_env(L, &p);
+  const int c = plan_env(L, &p, mode);
   if (c) return from_plan_code(c);
   if (!aligned16(v) || !aligned16(y) || !aligned16(spec) || (workspace && !aligned16(workspace)))
     return HYENA_ERR_ALIGN;
@@ -192,6 +227,7 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   a.io = (io == HYENA_FP32) ? 0 : 1;
   a.spec_stride = p.spec_stride;
   a.n_rows = (int)(B * D);
+  a.circular = p.circular;
   hipError_t e;
   if (p.path == PATH_SINGLE) {
     e = single_forward(a, p.N, (hipStream_t)stream);

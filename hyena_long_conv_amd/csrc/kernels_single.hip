@@ -120,12 +120,14 @@ __device__ __forceinline__ int row_of_workgroup(int wg, int B, int D) {
   return wg;
 }
 
-template <int N, int IOT, bool EVEN>
+// FULL: circular mode, the row fills all M = 2N samples (no zero half);
+// otherwise the row occupies the first half of each thread's points.
+template <int N, int IOT, bool EVEN, bool FULL>
 __global__ void __launch_bounds__(SinglePlan<N>::T, HYENA_SINGLE_WAVES)
 k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, void* __restrict__ y,
                  int B, int D, int NORD, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
-  constexpr int E = P::E, S = N / E;
+  constexpr int E = P::E, S = N / E, NV = FULL ? E : E / 2;
   __shared__ cf smem[P::PP ? 2 * N : N];
   using Lds = typename P::Lds;
   const Lds lds2[2] = {Lds{smem}, Lds{smem + (P::PP ? N : 0)}};
@@ -139,17 +141,17 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
   cf u[E];
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    u[i] = (i < E / 2) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+    u[i] = (i < NV) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
 
   for (int n = 0; n < NORD; ++n) {
     const cf* g = spec + (int64_t)(n * D + d) * spec_stride;
     const void* xn = x.p[n];
     PairCoeffs<N, E> pc;
-    cf xv[E / 2];
+    cf xv[NV];
     if constexpr (P::PF) {
       pc.load(g, qs, j);
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+      for (int i = 0; i < NV; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
     }
     if constexpr (P::PP) {
       fft.template run_pp<false>(u, lds2, j);
@@ -166,13 +168,13 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
     }
     if constexpr (!P::PF) {
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+      for (int i = 0; i < NV; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
     }
     const bool last = (n == NORD - 1);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       cf z = make_float2(0.f, 0.f);
-      if (i < E / 2) {
+      if (i < NV) {
         const int64_t t = 2 * (int64_t)(j + i * S);
         z = make_float2(xv[i].x * u[i].x, xv[i].y * u[i].y);
         if (last) st_pair<IOT, EVEN>(y, off, t, L, z);
@@ -185,11 +187,11 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
 // One filter row f of the NF = N*D rows of h per workgroup: the real FFT
 // H(k)/M of the zero-padded row (k = 0..N, staged in LDS), then the pair
 // coefficients of conv_pair for p = 0..N/2.
-template <int N, bool EVEN>
+template <int N, bool EVEN, bool FULL>
 __global__ void __launch_bounds__(SinglePlan<N>::T)
 k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
-  constexpr int E = P::E, S = N / E;
+  constexpr int E = P::E, S = N / E, NV = FULL ? E : E / 2;
   __shared__ cf smem[N];
   __shared__ cf nyq;
   const typename P::Lds lds{smem};
@@ -200,7 +202,7 @@ k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int
   cf u[E];
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    u[i] = (i < E / 2) ? ld_pair<0, EVEN>(h, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+    u[i] = (i < NV) ? ld_pair<0, EVEN>(h, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
   fft.template run<false>(u, lds, j);
   __syncthreads();
 #pragma unroll
@@ -407,23 +409,32 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
 
 template <int N, int IOT>
 static hipError_t launch_fwd(const ForwardArgs& a, hipStream_t s) {
-  if (a.L % 2 == 0)
-    hipLaunchKernelGGL((k_single_forward<N, IOT, true>), dim3(a.n_rows), dim3(SinglePlan<N>::T), 0, s, a.v,
-                       a.x, (const cf*)a.spec, a.y, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
+  const dim3 grid(a.n_rows), block(SinglePlan<N>::T);
+  const cf* sp = (const cf*)a.spec;
+  if (a.circular)   // L = 2N, even
+    hipLaunchKernelGGL((k_single_forward<N, IOT, true, true>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
+                       a.NORD, (int)a.L, a.spec_stride);
+  else if (a.L % 2 == 0)
+    hipLaunchKernelGGL((k_single_forward<N, IOT, true, false>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
+                       a.NORD, (int)a.L, a.spec_stride);
   else
-    hipLaunchKernelGGL((k_single_forward<N, IOT, false>), dim3(a.n_rows), dim3(SinglePlan<N>::T), 0, s, a.v,
-                       a.x, (const cf*)a.spec, a.y, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
+    hipLaunchKernelGGL((k_single_forward<N, IOT, false, false>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
+                       a.NORD, (int)a.L, a.spec_stride);
   return hipGetLastError();
 }
 
 template <int N>
 static hipError_t launch_spec(const SpectrumArgs& a, hipStream_t s) {
-  if (a.L % 2 == 0)
-    hipLaunchKernelGGL((k_single_spectrum<N, true>), dim3(a.NF), dim3(SinglePlan<N>::T), 0, s, a.h,
-                       (cf*)a.spec, (int)a.L, a.spec_stride);
+  const dim3 grid(a.NF), block(SinglePlan<N>::T);
+  if (a.circular)
+    hipLaunchKernelGGL((k_single_spectrum<N, true, true>), grid, block, 0, s, a.h, (cf*)a.spec, (int)a.L,
+                       a.spec_stride);
+  else if (a.L % 2 == 0)
+    hipLaunchKernelGGL((k_single_spectrum<N, true, false>), grid, block, 0, s, a.h, (cf*)a.spec, (int)a.L,
+                       a.spec_stride);
   else
-    hipLaunchKernelGGL((k_single_spectrum<N, false>), dim3(a.NF), dim3(SinglePlan<N>::T), 0, s, a.h,
-                       (cf*)a.spec, (int)a.L, a.spec_stride);
+    hipLaunchKernelGGL((k_single_spectrum<N, false, false>), grid, block, 0, s, a.h, (cf*)a.spec, (int)a.L,
+                       a.spec_stride);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct ForwardArgs {
   int n_rows;            // B * D real rows
   void* work;            // four-step intermediate (rows_per_group * N complex)
   int rows_per_group;
+  int circular;          // single path: rows fill the whole FFT length (no zero half)
 };
 
 struct SpectrumArgs {
@@ -31,6 +32,7 @@ struct SpectrumArgs {
   int64_t spec_stride;
   void* work;
   int rows_per_group;
+  int circular;
 };
 
 struct FilterGenArgs {

@@ -10,6 +10,9 @@
 //   * four-step: N = n1 * n2, column FFTs of n1 points and row FFTs of n2
 //     points with a twiddle in between (Bailey's decomposition), passes
 //     linked through a workspace buffer.
+// Circular mode (periodic boundary, gist.science HyenaND summary, section
+// "手法: HyenaND", boundary handling) takes M = L with no padding; L must then
+// be a power of two >= 128.
 #pragma once
 
 #include <stdint.h>
@@ -51,6 +54,7 @@ struct PlanInfo {
   int path;
   int n1, n2;            // four-step factors of N
   int64_t spec_stride;   // complex values per filter row in the spectrum buffer (>= N + 1)
+  int circular;          // 1: M = L, periodic convolution
 };
 
 // Single path: a filter row holds three planar arrays of N/2 + 1 complex
@@ -67,10 +71,14 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Returns 0 on success, 2 (shape) for a bad L, 3 (unsupported) when a forced
 // path cannot serve L.  force_path: NULL/"" auto, "single", "fourstep".
-inline int make_plan(int64_t L, const char* force_path, const char* force_n1, PlanInfo* out) {
+inline int make_plan(int64_t L, const char* force_path, const char* force_n1, PlanInfo* out, int circular = 0) {
   if (L < 1 || L > kMaxL) return 2;
   int64_t N = next_pow2(2 * L) / 2;
   if (N < kMinN) N = kMinN;
+  if (circular) {
+    if (!is_pow2(L) || L < 2 * kMinN) return 3;
+    N = L / 2;
+  }
   int path = (N <= kSingleMaxN) ? PATH_SINGLE : PATH_FOURSTEP;
   if (force_path && *force_path) {
     if (!strcmp(force_path, "single")) {
@@ -86,7 +94,10 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
   if (path == PATH_SINGLE) {
     p.n1 = p.n2 = 0;
   } else {
-    if (N < (int64_t)kColMin * kRowMin) N = (int64_t)kColMin * kRowMin;
+    if (N < (int64_t)kColMin * kRowMin) {
+      if (circular) return 3;
+      N = (int64_t)kColMin * kRowMin;
+    }
     int64_t n1 = N / kRowMax;
     if (n1 < kColMin) n1 = kColMin;
     if (n1 > kColMax) n1 = kColMax;   // longest rows (up to 8192) beyond that
@@ -94,6 +105,7 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
       const int64_t f = atoll(force_n1);
       if (!is_pow2(f) || f < kColMin || f > kColMax) return 3;
       n1 = f;
+      if (circular && N / n1 < kRowMin) return 3;
       while (N / n1 < kRowMin) N <<= 1;   // a longer FFT is still exact
     }
     const int64_t n2 = N / n1;
@@ -103,6 +115,7 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
   }
   p.N = N;
   p.M = 2 * N;
+  p.circular = circular ? 1 : 0;
   p.spec_stride = (path == PATH_SINGLE) ? 3 * single_qs(N) : round_up(N + 1, 16);
   *out = p;
   return 0;

@@ -256,6 +256,30 @@ hyena_status hyena_block_forward(const void* u, const hyena_block_params* p, con
                                  int64_t B, int64_t L, hyena_dtype io, void* workspace,
                                  int64_t workspace_bytes, void* stream);
 
+/*
+ * Circular mode (gist.science HyenaND summary, section "手法: HyenaND",
+ * boundary handling: periodic systems use circular convolution, other data
+ * the zero-padded linear one).  c[t] = sum_{k<L} h[k] z[(t-k) mod L]: the
+ * FFT length is M = L with no padding, so L must be a power of two >= 128
+ * (HYENA_ERR_UNSUPPORTED otherwise).  The _ex calls take the mode; the calls
+ * without the suffix are HYENA_CONV_LINEAR.  A spectrum is valid only for
+ * the mode it was built with.
+ */
+typedef enum { HYENA_CONV_LINEAR = 0, HYENA_CONV_CIRCULAR = 1 } hyena_conv_mode;
+
+hyena_status hyena_plan_ex(int64_t L, hyena_conv_mode mode, hyena_plan_info* out);
+int64_t hyena_spectrum_bytes_ex(int32_t D, int32_t N, int64_t L, hyena_conv_mode mode);
+int64_t hyena_spectrum_workspace_bytes_ex(int32_t D, int32_t N, int64_t L, hyena_conv_mode mode);
+hyena_status hyena_filter_spectrum_ex(const float* h, int32_t D, int32_t N, int64_t L, hyena_conv_mode mode,
+                                      void* spec, void* workspace, int64_t workspace_bytes, void* stream);
+hyena_status hyena_spectrum_export_ex(const void* spec, int32_t D, int32_t N, int64_t L, hyena_conv_mode mode,
+                                      float* out, void* stream);
+int64_t hyena_forward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
+                                         hyena_conv_mode mode);
+hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                              int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* hyena_status_str(hyena_status s);
 

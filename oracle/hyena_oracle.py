@@ -58,6 +58,8 @@ Readings where the pages are silent (each listed in the design notes):
   convolution is causal and depthwise (one T-tap filter per projected
   column, tap j weighting the sample j steps back, zero before t = 0); biases
   of both projections optional; the output projection has no activation.
+  Circular mode ([P5] "手法: HyenaND", boundary handling: periodic systems
+  use circular convolutions): c[t] = sum_{k<L} h[k] z[(t-k) mod L].
   Filter families ([P3] section 3): Hyena-LI's filter is a sum of real
   exponentials R_s * lambda_s^t over a small state of size S (the page
   indexes t from 1 with exponent t-1; here t = 0..L-1 with exponent t);
@@ -92,6 +94,7 @@ __all__ = [
     "hyena_backward",
     "filter_gen_li",
     "filter_gen_mr",
+    "circular_conv",
     "DIRECT_MAX_L",
 ]
 
@@ -425,3 +428,19 @@ def filter_gen_mr(hhat: np.ndarray, alpha: np.ndarray, N: int) -> np.ndarray:
     Lh = hhat.shape[-1]
     t = np.arange(Lh, dtype=np.float64)
     return hhat * np.exp(-alpha[None, :, None] * t)
+
+
+def circular_conv(h: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Periodic convolution over the last axis ([P5] "手法: HyenaND", boundary
+    handling): out[..., t] = sum_{k<L} h[..., k] * z[..., (t - k) mod L].
+    Brute force for L <= DIRECT_MAX_L, else the oracle's FFT of length L
+    (L a power of two)."""
+    h = np.asarray(h, np.float64)
+    z = np.asarray(z, np.float64)
+    L = z.shape[-1]
+    if L <= DIRECT_MAX_L:
+        out = np.zeros(np.broadcast_shapes(h.shape[:-1], z.shape[:-1]) + (L,))
+        for k in range(L):
+            out += h[..., k:k + 1] * np.roll(z, k, axis=-1)
+        return out
+    return np.real(fft(fft(h) * fft(z), inverse=True))

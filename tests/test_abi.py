@@ -233,3 +233,21 @@ def test_filter_family_calls_reject_bad_arguments():
     assert fir(y=Y + 2) == ALIGN
     assert fir(y=C) == ALIAS
     assert fir(y=Dp) == ALIAS
+
+
+@pytest.mark.parametrize("L,path", [(128, "single"), (2048, "single"), (32768, "single"), (65536, "fourstep"),
+                                    (1 << 22, "fourstep")])
+def test_plan_circular(L, path):
+    p = H.plan(L, circular=True)
+    assert p["M"] == L and p["path"] == path
+    if path == "fourstep":
+        assert p["n1"] * p["n2"] == L // 2
+
+
+def test_plan_circular_rejects_other_lengths():
+    for L in (100, 64, 3000, 127):
+        with pytest.raises(H.HyenaError) as e:
+            H.plan(L, circular=True)
+        assert e.value.code == UNSUP
+    assert H.spectrum_bytes(4, 2, 1000, circular=True) == -1
+    assert H.lib().hyena_plan_ex(256, 7, ctypes.byref(H.PlanInfo())) == UNSUP

@@ -50,3 +50,30 @@ def test_short_fir_operator_equals_brute_force():
                 c[..., t] += hs[n, :, k] * z[..., t - k]
         z = xs[n] * c
     assert np.allclose(y, z, atol=1e-12)
+
+
+def test_circular_conv_matches_numpy_fft_and_roll():
+    L = 64
+    h = rng.standard_normal((2, L)); z = rng.standard_normal((2, L))
+    got = O.circular_conv(h, z)
+    ref = np.real(np.fft.ifft(np.fft.fft(h) * np.fft.fft(z)))
+    assert np.allclose(got, ref, atol=1e-12)
+    # a one-sample delay filter rotates the signal (wrap-around at t = 0)
+    d = np.zeros(L); d[3] = 1.0
+    assert np.allclose(O.circular_conv(d, z[0]), np.roll(z[0], 3))
+
+
+def test_circular_equals_linear_when_halves_are_zero():
+    # with filter and signal zero in their second halves nothing wraps
+    L = 32
+    h = np.zeros(L); z = np.zeros(L)
+    h[:8] = rng.standard_normal(8); z[:16] = rng.standard_normal(16)
+    assert np.allclose(O.circular_conv(h, z), O.causal_conv_direct(h, z), atol=1e-12)
+
+
+def test_circular_fft_path(monkeypatch):
+    L = 256
+    h = rng.standard_normal(L); z = rng.standard_normal(L)
+    a = O.circular_conv(h, z)
+    monkeypatch.setattr(O.hyena_oracle, "DIRECT_MAX_L", 16)
+    assert np.allclose(O.circular_conv(h, z), a, atol=1e-10)
