@@ -70,6 +70,18 @@ Readings where the pages are silent (each listed in the design notes):
   recurrence by the chain rule (the adjoint of a causal convolution is the
   correlation with the same filter), for a scalar loss whose gradient with
   respect to y is gy; filter gradients are summed over the batch.
+  Grids ([P5] "手法: HyenaND", native N-D convolution and boundary
+  handling): the same recurrence on a grid L_1 x .. x L_k, each long
+  convolution a k-dimensional one with a global kernel K.  Non-circular
+  mode: the kernel holds one value per offset o with |o_a| < L_a on every
+  axis (both signs, so centred kernels are expressible; a causal one is
+  zero at negative offsets) and y[t] = sum over grid points s of
+  K[t - s] z[s] -- what zero-padding every axis to twice its size and
+  keeping the first L_a samples computes.  Circular mode: K has the grid's
+  own shape and offsets wrap, y[t] = sum_s K[(t - s) mod L] z[s].  The
+  kernel may be shared by the batch or given per sample (the page's
+  input-dependent kernels); how it is generated is not part of this
+  operator.
 """
 from __future__ import annotations
 
@@ -95,6 +107,11 @@ __all__ = [
     "filter_gen_li",
     "filter_gen_mr",
     "circular_conv",
+    "ndfft",
+    "nd_conv_direct",
+    "nd_conv_fft",
+    "nd_conv",
+    "nd_forward",
     "DIRECT_MAX_L",
 ]
 
@@ -444,3 +461,112 @@ def circular_conv(h: np.ndarray, z: np.ndarray) -> np.ndarray:
             out += h[..., k:k + 1] * np.roll(z, k, axis=-1)
         return out
     return np.real(fft(fft(h) * fft(z), inverse=True))
+
+
+# ---------------------------------------------------------------------------
+# Convolution on k-dimensional grids ([P5] "手法: HyenaND": native N-D
+# convolution through the N-D FFT; boundary handling, circular for periodic
+# systems and twice-padded non-circular for images and volumes)
+# ---------------------------------------------------------------------------
+
+def _grid_shape(K: np.ndarray, ndim: int, circular: bool):
+    ext = K.shape[-ndim:]
+    if circular:
+        return tuple(ext)
+    assert all(e % 2 == 1 for e in ext), "non-circular kernels have odd extent 2L-1"
+    return tuple((e + 1) // 2 for e in ext)
+
+
+def ndfft(x: np.ndarray, ndim: int, inverse: bool = False) -> np.ndarray:
+    """DFT over the last ``ndim`` axes: the k-dimensional DFT is the 1-D DFT
+    applied along each axis in turn (the oracle's own radix-2 ``fft``)."""
+    a = np.asarray(x, dtype=np.complex128)
+    for ax in range(a.ndim - ndim, a.ndim):
+        a = np.moveaxis(fft(np.moveaxis(a, ax, -1), inverse=inverse), -1, ax)
+    return a
+
+
+def nd_conv_direct(K: np.ndarray, z: np.ndarray, ndim: int, circular: bool = False) -> np.ndarray:
+    """y[..., t] = sum_s K[..., t - s] z[..., s] over the last ``ndim`` axes,
+    brute force over the kernel offsets o = t - s.
+
+    Non-circular: K[..., o_1 + L_1 - 1, .., o_k + L_k - 1] for |o_a| < L_a,
+    and only pairs with both t and s on the grid contribute.  Circular: K has
+    the grid's shape and t - s is taken modulo L_a.  K broadcasts against z
+    on the leading axes.
+    """
+    K = np.asarray(K, np.float64)
+    z = np.asarray(z, np.float64)
+    Ls = _grid_shape(K, ndim, circular)
+    assert tuple(z.shape[-ndim:]) == Ls
+    lead = np.broadcast_shapes(K.shape[:-ndim], z.shape[:-ndim])
+    y = np.zeros(lead + Ls)
+    for idx in np.ndindex(*K.shape[-ndim:]):
+        w = K[(Ellipsis,) + idx][(Ellipsis,) + (None,) * ndim]
+        if circular:
+            y += w * np.roll(z, shift=idx, axis=tuple(range(-ndim, 0)))
+            continue
+        dst, src = [], []
+        for a, i in enumerate(idx):
+            o, L = i - (Ls[a] - 1), Ls[a]
+            dst.append(slice(max(0, o), min(L, L + o)))      # t with t - o on the grid
+            src.append(slice(max(0, -o), min(L, L - o)))     # s = t - o
+        y[(Ellipsis,) + tuple(dst)] += w * z[(Ellipsis,) + tuple(src)]
+    return y
+
+
+def nd_conv_fft(K: np.ndarray, z: np.ndarray, ndim: int, circular: bool = False) -> np.ndarray:
+    """Same result as nd_conv_direct by the k-dimensional FFT ([P5]): each
+    axis padded to P_a, the next power of two >= 2 L_a (non-circular; the
+    kernel's offset o lands at o mod P_a, z at its own index, zeros
+    elsewhere) or P_a = L_a (circular, powers of two), transform, pointwise
+    product, inverse transform, keep the grid."""
+    K = np.asarray(K, np.float64)
+    z = np.asarray(z, np.float64)
+    Ls = _grid_shape(K, ndim, circular)
+    if circular:
+        assert all(L & (L - 1) == 0 for L in Ls), "circular FFT path needs power-of-two sides"
+        Y = ndfft(ndfft(K, ndim) * ndfft(z, ndim), ndim, inverse=True)
+        return Y.real
+    Ps = []
+    for L in Ls:
+        P = 1
+        while P < 2 * L:
+            P *= 2
+        Ps.append(P)
+    Kp = np.zeros(K.shape[:-ndim] + tuple(Ps))
+    for idx in np.ndindex(*K.shape[-ndim:]):
+        dst = tuple((i - (Ls[a] - 1)) % Ps[a] for a, i in enumerate(idx))
+        Kp[(Ellipsis,) + dst] = K[(Ellipsis,) + idx]
+    zp = np.zeros(z.shape[:-ndim] + tuple(Ps))
+    zp[(Ellipsis,) + tuple(slice(0, L) for L in Ls)] = z
+    Y = ndfft(ndfft(Kp, ndim) * ndfft(zp, ndim), ndim, inverse=True)
+    return Y[(Ellipsis,) + tuple(slice(0, L) for L in Ls)].real
+
+
+def nd_conv(K: np.ndarray, z: np.ndarray, ndim: int, circular: bool = False) -> np.ndarray:
+    """Brute force while the offset count times the grid is small, else FFT."""
+    Ls = _grid_shape(np.asarray(K), ndim, circular)
+    work = int(np.prod(np.asarray(K).shape[-ndim:])) * int(np.prod(Ls))
+    pow2 = all(L & (L - 1) == 0 for L in Ls)
+    if work <= (1 << 20) or (circular and not pow2):
+        return nd_conv_direct(K, z, ndim, circular)
+    return nd_conv_fft(K, z, ndim, circular)
+
+
+def nd_forward(v: np.ndarray, xs, K: np.ndarray, ndim: int, circular: bool = False,
+               per_sample: bool = False) -> np.ndarray:
+    """The order-N recurrence of [P1]/[P4] with grid convolutions ([P5]).
+
+    v: [B, D, L_1..L_k]; xs: N arrays shaped like v.  K: [N, D, ext...]
+    shared by the batch, or [B, N, D, ext...] with per_sample (the kernel of
+    each sample).  z_1 = v, z_{n+1} = x_n * (K_n conv z_n), y = z_{N+1}.
+    """
+    z = np.asarray(v, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    N = K.shape[1] if per_sample else K.shape[0]
+    assert len(xs) == N
+    for n in range(N):
+        Kn = K[:, n] if per_sample else K[n]
+        z = np.asarray(xs[n], dtype=np.float64) * nd_conv(Kn, z, ndim, circular)
+    return z

@@ -21,7 +21,14 @@ for them:
   * block around the operator: input u [B][L][D] ~ N(0, 1), projection
     weights W_in [(N+1)D][D] and W_out [D][D] ~ N(0, 1/D), short filters
     [(N+1)D][T] ~ N(0, 1/T), biases zero unless asked for; projection weights
-    and u are rounded to bf16 where the I/O dtype is bf16.
+    and u are rounded to bf16 where the I/O dtype is bf16;
+  * grid convolutions (the HyenaND summary's images, volumes and periodic
+    physics fields, whose datasets are not available): v, x_n ~ N(0, 1) on
+    the grid (bf16-rounded for bf16 I/O); each kernel is a Gaussian window
+    exp(-|o|^2 / (2 sigma_d^2)) over the offsets o (sigma_d linearly spaced
+    from 1 to half the largest side over the channels; circular offsets
+    taken as the nearest signed representative) times N(0, 1) values,
+    scaled to unit Euclidean norm.
 """
 from __future__ import annotations
 
@@ -30,7 +37,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_filter_params", "make_activations",
-           "config_by_name", "make_block_params", "make_block_input", "bf16_round"]
+           "config_by_name", "make_block_params", "make_block_input", "bf16_round",
+           "GridConfig", "GRID_CONFIGS", "make_grid_kernel", "make_grid_activations"]
 
 
 @dataclass(frozen=True)
@@ -171,3 +179,87 @@ def make_block_input(cfg: Config, device="cpu", B: int | None = None):
     g.manual_seed(cfg.seed * 1000 + 500)
     u = torch.randn((B, cfg.L, cfg.D), generator=g, device=dev, dtype=torch.float32)
     return u.to(torch.float32 if cfg.io == "fp32" else torch.bfloat16).contiguous()
+
+
+# ------------------------------------------------------------------ grids
+
+@dataclass(frozen=True)
+class GridConfig:
+    name: str
+    N: int                  # order
+    B: int                  # batch
+    D: int                  # channels
+    dims: tuple             # grid sides L_1..L_k (last axis contiguous)
+    circular: bool
+    io: str                 # "fp32" or "bf16"
+    seed: int
+    per_sample: bool = False
+    desc: str = ""
+
+    @property
+    def ndim(self) -> int:
+        return len(self.dims)
+
+    @property
+    def kernel_shape(self) -> tuple:
+        return tuple(self.dims) if self.circular else tuple(2 * L - 1 for L in self.dims)
+
+    def with_(self, **kw) -> "GridConfig":
+        return replace(self, **kw)
+
+
+GRID_CONFIGS = {
+    "G1": GridConfig("G1", 2, 2, 4, (8, 8), False, "fp32", 21,
+                     desc="order-2, B=2, D=4, 8x8 grid, non-circular, fp32 (small parity case)"),
+    "G2": GridConfig("G2", 2, 8, 192, (56, 56), False, "bf16", 22,
+                     desc="order-2, B=8, D=192, 56x56 image grid, non-circular, bf16 I/O"),
+    "G3": GridConfig("G3", 2, 2, 128, (16, 16, 16), False, "bf16", 23,
+                     desc="order-2, B=2, D=128, 16^3 volume, non-circular, bf16 I/O"),
+    "GP": GridConfig("GP", 2, 4, 64, (128, 128), True, "fp32", 24,
+                     desc="order-2, B=4, D=64, 128x128 periodic field, circular, fp32"),
+}
+
+
+def make_grid_kernel(cfg: GridConfig) -> np.ndarray:
+    """Kernels [N][D][ext...] (or [B][N][D][ext...] per sample), float32.
+
+    Offsets: non-circular extent 2L-1 per axis, index o + L - 1; circular
+    extent L, index o mod L.
+    """
+    lead = (cfg.B, cfg.N, cfg.D) if cfg.per_sample else (cfg.N, cfg.D)
+    rng = _np_rng(cfg.seed, 600)
+    ext = cfg.kernel_shape
+    offs = []
+    for L, e in zip(cfg.dims, ext):
+        o = np.arange(e) - (L - 1) if not cfg.circular else np.arange(e)
+        if cfg.circular:
+            o = np.where(o > L // 2, o - L, o)
+        offs.append(o.astype(np.float64))
+    r2 = np.zeros(ext)
+    for a, o in enumerate(offs):
+        shape = [1] * len(ext)
+        shape[a] = len(o)
+        r2 = r2 + (o ** 2).reshape(shape)
+    smax = max(1.0, max(cfg.dims) / 2.0)
+    sig = np.linspace(1.0, smax, cfg.D) if cfg.D > 1 else np.ones(1)
+    win = np.exp(-r2[None] / (2.0 * sig.reshape((-1,) + (1,) * len(ext)) ** 2))     # [D, ext...]
+    K = rng.standard_normal(lead + ext) * win
+    norm = np.sqrt((K ** 2).sum(axis=tuple(range(-len(ext), 0)), keepdims=True))
+    return (K / np.maximum(norm, 1e-30)).astype(np.float32)
+
+
+def make_grid_activations(cfg: GridConfig, device="cpu", B: int | None = None):
+    """(v, [x_1..x_N]) as torch tensors [B][D][L_1..L_k] in the I/O dtype."""
+    import torch
+
+    B = cfg.B if B is None else B
+    dt = torch.float32 if cfg.io == "fp32" else torch.bfloat16
+    dev = torch.device(device)
+    shape = (B, cfg.D) + tuple(cfg.dims)
+
+    def draw(tid: int):
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed * 1000 + tid)
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(dt).contiguous()
+
+    return draw(0), [draw(1 + n) for n in range(cfg.N)]
