@@ -417,6 +417,120 @@ def cpu_baseline_block(cfg, bp, h, budget_s: float = 12.0):
             "kind": "oracle", "sample": f"block on batch row 0, first {Lp} of {cfg.L} steps (causal prefix), float64, {dt_:.1f} s"}
 
 
+def grid_bytes(cfg, P: int) -> int:
+    """Algorithmic bytes of one grid forward: v, x_1..x_N, y in the I/O dtype
+    plus the kernels' spectra read once, complex64 over the Hermitian half
+    of the padded grid (P^(k-1) * (P/2 + 1) bins per kernel)."""
+    s = 4 if cfg.io == "fp32" else 2
+    pts = math.prod(cfg.dims)
+    rows = cfg.N * cfg.D * (cfg.B if cfg.per_sample else 1)
+    bins = P ** (cfg.ndim - 1) * (P // 2 + 1)
+    return (cfg.N + 2) * cfg.B * cfg.D * pts * s + rows * bins * 8
+
+
+def grid_flops(cfg, P: int) -> float:
+    """Per grid and order: forward and inverse real FFT of M = P^k points at
+    2.5 M log2 M each, one complex product per Hermitian bin (3M), the gate."""
+    M = P ** cfg.ndim
+    return cfg.N * cfg.B * cfg.D * (5.0 * M * math.log2(M) + 3.0 * M + math.prod(cfg.dims))
+
+
+def _oracle_grids(cfg, pairs):
+    """Oracle grid forward for (b, d) pairs: seeded kernels of the workload,
+    activations drawn from N(0, 1) on the CPU (the cost does not depend on
+    the values)."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import make_grid_kernel
+    K = make_grid_kernel(cfg)
+    rs = np.random.default_rng([cfg.seed, len(pairs), pairs[0][0], pairs[0][1]])
+    for b, d in pairs:
+        v = rs.standard_normal((1, 1) + tuple(cfg.dims))
+        xs = [rs.standard_normal((1, 1) + tuple(cfg.dims)) for _ in range(cfg.N)]
+        Kd = K[b][:, d:d + 1] if cfg.per_sample else K[:, d:d + 1]
+        O.nd_forward(v, xs, Kd, cfg.ndim, cfg.circular)
+    return len(pairs)
+
+
+def cpu_baseline_grid(cfg, budget_s: float = 12.0):
+    import multiprocessing as mp
+
+    import numpy as np
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    _oracle_grids(cfg, [(0, 0)])
+    one = time.perf_counter() - t0
+    total = cfg.B * cfg.D
+    n = max(1, min(total, int(max(cores, budget_s * cores / max(one, 1e-3)))))
+    rng = np.random.default_rng(cfg.seed)
+    flat = sorted(rng.choice(total, size=n, replace=False).tolist())
+    pairs = [(r // cfg.D, r % cfg.D) for r in flat]
+    chunks = [pairs[i::cores] for i in range(cores) if pairs[i::cores]]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(chunks), initializer=_pin_threads) as pool:
+        pool.starmap(_oracle_grids, [(cfg, c) for c in chunks])
+    wall = time.perf_counter() - t0
+    pts = math.prod(cfg.dims)
+    return {"value": n * pts / wall, "unit": "channel-tokens/s", "cores": len(chunks), "kind": "oracle",
+            "sample": f"{n} of {total} (b,d) grids of {cfg.name} (float64 oracle, its N-D FFT path or brute force), "
+                      f"{wall:.1f} s wall",
+            "extrapolated_full_s": wall * total / n}
+
+
+def run_grid(args, torch, H, dev):
+    """Convolutions on 2-D/3-D grids: one step = one hyena_nd_forward over
+    one batch of grids (spectra precomputed), inputs rotating over sets that
+    exceed the Infinity Cache."""
+    from workloads import GRID_CONFIGS, make_grid_activations, make_grid_kernel
+
+    cfg = GRID_CONFIGS[args.grid]
+    P = H.nd_plan(cfg.dims, cfg.circular)
+    mb, fl = grid_bytes(cfg, P), grid_flops(cfg, P)
+    sets = args.sets or min(64, max(1, math.ceil(2 * MALL_BYTES / mb)))
+    K = torch.from_numpy(make_grid_kernel(cfg)).to(dev)
+    spec0 = H.nd_filter_spectrum(K, cfg.dims, cfg.circular)
+    del K
+    calls = []
+    for k in range(sets):
+        v, xs = make_grid_activations(cfg.with_(seed=cfg.seed * 100 + k), dev)
+        spec = spec0 if k == 0 else spec0.clone()
+        calls.append(H.prepare_nd_forward(v, xs, spec, cfg.circular, cfg.per_sample))
+    torch.cuda.synchronize()
+    ms, steps, warmup = _time_steps(torch, dev, lambda i: calls[i % sets](), args.steps, args.warmup)
+    t = ms / 1e3
+    copy_bps = measure_copy(torch, dev)
+    if fl / mb > ALU_PEAK / HBM_PEAK:
+        roof = {"bound": "alu", "achieved": fl / t / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": fl / t / ALU_PEAK}
+    else:
+        roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": mb / t / HBM_PEAK}
+    roof.update({"traffic": measured_traffic(cfg.name), "kernel": "k_nd_forward (one launch per step)",
+                 "launches_per_step": 1,
+                 "hbm_frac": mb / t / HBM_PEAK, "hbm_GBps": mb / t / 1e9, "copy_GBps": copy_bps / 1e9,
+                 "hbm_frac_vs_copy": mb / t / copy_bps, "alu_frac": fl / t / ALU_PEAK,
+                 "alu_TFLOPs": fl / t / 1e12, "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl})
+    pts = math.prod(cfg.dims)
+    out = {
+        "metric": "Hyena order-N fwd on grids (HyenaND), channel-tokens/sec (B*D*grid points/s)",
+        "value": cfg.B * cfg.D * pts / t, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations, Gaussian-windowed random kernels)",
+        "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D,
+                   "dims": list(cfg.dims), "circular": cfg.circular, "io": cfg.io, "per_sample": cfg.per_sample,
+                   "fft_side": P, "input_sets": sets},
+        "roofline": roof,
+    }
+    del calls
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_grid(cfg)
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +549,8 @@ def main(argv=None):
                     help="time the recurrence with explicit short filters of LH taps (hyena_forward_fir)")
     ap.add_argument("--block", action="store_true",
                     help="time the whole block (in-projection + short convolutions, operator, out-projection)")
+    ap.add_argument("--grid", default=None, metavar="NAME",
+                    help="time the grid convolutions (HyenaND) on workload G1, G2, G3 or GP")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for counter scaling)")
     args = ap.parse_args(argv)
@@ -455,6 +571,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     H.lib()
+    if args.grid:
+        return run_grid(args, torch, H, dev)
     if args.block:
         return run_block(args, cfg, torch, H, dev)
     if args.backward:

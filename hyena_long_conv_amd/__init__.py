@@ -122,6 +122,15 @@ def lib() -> ctypes.CDLL:
     L.hyena_forward_workspace_bytes_ex.restype = i64
     L.hyena_forward_ex.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, i32, vp, i64, vp]
     L.hyena_forward_ex.restype = i32
+    i64p = ctypes.POINTER(i64)
+    L.hyena_nd_plan.argtypes = [i32, i64p, i32, i64p]
+    L.hyena_nd_plan.restype = i32
+    L.hyena_nd_spectrum_bytes.argtypes = [i32, i32, i64p, i32]
+    L.hyena_nd_spectrum_bytes.restype = i64
+    L.hyena_nd_filter_spectrum.argtypes = [vp, i32, i32, i64p, i32, vp, vp]
+    L.hyena_nd_filter_spectrum.restype = i32
+    L.hyena_nd_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i32, i64p, i32, i32, i32, vp]
+    L.hyena_nd_forward.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -488,3 +497,74 @@ def forward_fir(v, xs, h, out=None):
     _check(lib().hyena_forward_fir(_ptr(v), xp, _ptr(h), h.shape[-1], _ptr(y), B, D, N, L, io, _stream(v)),
            "hyena_forward_fir")
     return y
+
+
+# ------------------------------------------------------- grid convolutions
+
+def _dims(dims):
+    dims = tuple(int(d) for d in dims)
+    return dims, (ctypes.c_int64 * len(dims))(*dims)
+
+
+def nd_plan(dims, circular: bool = False) -> int:
+    """Padded FFT side P of a 2-D or 3-D grid (a cube of side P)."""
+    dims, cd = _dims(dims)
+    side = ctypes.c_int64(0)
+    _check(lib().hyena_nd_plan(len(dims), cd, int(bool(circular)), ctypes.byref(side)), "hyena_nd_plan")
+    return int(side.value)
+
+
+def nd_spectrum_bytes(rows: int, dims, circular: bool = False) -> int:
+    dims, cd = _dims(dims)
+    return int(lib().hyena_nd_spectrum_bytes(int(rows), len(dims), cd, int(bool(circular))))
+
+
+def nd_filter_spectrum(kernel, dims, circular: bool = False, out=None):
+    """Spectrum of grid kernels [..rows.., extent...] fp32: the extent is
+    2*dims-1 per axis (non-circular, index offset + dims - 1) or dims
+    (circular).  Leading axes are flattened into kernel rows."""
+    import torch
+    _need_cuda(kernel, "kernel", torch.float32)
+    dims, cd = _dims(dims)
+    k = len(dims)
+    ext = tuple(dims) if circular else tuple(2 * d - 1 for d in dims)
+    if tuple(kernel.shape[-k:]) != ext:
+        raise ValueError(f"kernel extent {tuple(kernel.shape[-k:])} != {ext}")
+    rows = 1
+    for s_ in kernel.shape[:-k]:
+        rows *= int(s_)
+    nbytes = nd_spectrum_bytes(rows, dims, circular)
+    if nbytes < 0:
+        raise HyenaError(3, "hyena_nd_spectrum_bytes")
+    spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=kernel.device)
+    _check(lib().hyena_nd_filter_spectrum(_ptr(kernel), rows, k, cd, int(bool(circular)), _ptr(spec),
+                                          _stream(kernel)), "hyena_nd_filter_spectrum")
+    spec._hyena_nd = (dims, bool(circular), rows)
+    return spec
+
+
+def prepare_nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None):
+    """hyena_nd_forward marshalled once (v, x_n: [B, D, dims...] fp32 or bf16)."""
+    io = _io_of(v)
+    _need_cuda(v, "v", v.dtype)
+    if circular is None:
+        circular = getattr(spec, "_hyena_nd", (None, False))[1]
+    B, D = int(v.shape[0]), int(v.shape[1])
+    dims, cd = _dims(v.shape[2:])
+    N = len(xs)
+    for i, t in enumerate(xs):
+        _need_cuda(t, f"x[{i}]", v.dtype)
+        if tuple(t.shape) != tuple(v.shape):
+            raise ValueError(f"x[{i}] shape {tuple(t.shape)} != {tuple(v.shape)}")
+    import torch
+    y = out if out is not None else torch.empty_like(v)
+    _need_cuda(y, "y", v.dtype)
+    xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
+    args = (_ptr(v), xp, _ptr(spec), _ptr(y), B, D, N, len(dims), cd, int(bool(circular)), int(bool(per_sample)),
+            io, _stream(v))
+    return PreparedCall(lib().hyena_nd_forward, args, (v, tuple(xs), spec, y, xp, cd), y, "hyena_nd_forward")
+
+
+def nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None):
+    """y = z_{N+1} of the order-N recurrence with grid convolutions."""
+    return prepare_nd_forward(v, xs, spec, circular, per_sample, out)()

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhyena_mi355x.so")
 
-SOURCES = ["api.cpp", "kernels_single.hip", "kernels_fourstep.hip", "kernels_filter.hip", "kernels_proj.hip", "kernels_fir.hip"]
+SOURCES = ["api.cpp", "kernels_single.hip", "kernels_fourstep.hip", "kernels_filter.hip", "kernels_proj.hip",
+           "kernels_fir.hip", "kernels_nd.hip"]
 ARCH = os.environ.get("HYENA_OFFLOAD_ARCH", "gfx950")
 
 

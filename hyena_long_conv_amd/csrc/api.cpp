@@ -45,6 +45,61 @@ int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
   return (int64_t)rows_per_group(p.N, B * D) * p.N * 8;
 }
 
+// Grid convolutions: padded side P of the square/cube FFT grid.
+struct NdPlanH {
+  int ndim, P;
+  int Lo, Lm, Ll;
+  int64_t NC, Q, stride, points;
+};
+
+constexpr int kNdMaxSide = 4096;
+
+int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
+  if (!dims) return 1;
+  if (ndim != 2 && ndim != 3) return 3;
+  if (circular != 0 && circular != 1) return 3;
+  int64_t lmax = 0, points = 1;
+  for (int a = 0; a < ndim; ++a) {
+    if (dims[a] < 1 || dims[a] > kNdMaxSide) return 2;
+    lmax = dims[a] > lmax ? dims[a] : lmax;
+    points *= dims[a];
+  }
+  const int pmin = ndim == 2 ? 16 : 8, pmax = ndim == 2 ? 128 : 32;
+  int64_t P;
+  if (circular) {
+    P = dims[0];
+    for (int a = 1; a < ndim; ++a)
+      if (dims[a] != P) return 3;
+    if ((P & (P - 1)) != 0 || P < pmin || P > pmax) return 3;
+  } else {
+    P = pmin;
+    while (P < 2 * lmax - 1) P *= 2;
+    if (P > pmax) return 3;
+  }
+  NdPlanH p{};
+  p.ndim = ndim;
+  p.P = (int)P;
+  p.Lo = (int)dims[0];
+  p.Lm = ndim == 3 ? (int)dims[1] : 1;
+  p.Ll = (int)dims[ndim - 1];
+  p.Q = ndim == 2 ? P : P * P;
+  p.NC = p.Q * (P / 2);
+  p.stride = round_up(p.NC + p.Q, 64);
+  p.points = points;
+  *out = p;
+  return 0;
+}
+
+int64_t nd_kernel_extent(const NdPlanH& p, int32_t circular) {
+  int64_t e = 1;
+  const int sides[3] = {p.Lo, p.Lm, p.Ll};
+  for (int a = 0; a < 3; ++a) {
+    if (p.ndim == 2 && a == 1) continue;
+    e *= circular ? sides[a] : 2 * (int64_t)sides[a] - 1;
+  }
+  return e;
+}
+
 bool sizes_ok(int64_t D, int64_t N, int64_t L) {
   return D >= 1 && D <= (1 << 20) && N >= 1 && L >= 1 && L <= kMaxL;
 }
@@ -479,6 +534,85 @@ hyena_status hyena_block_forward(const void* u, const hyena_block_params* p, con
   st = hyena_forward(streams[0], streams + 1, spec, y, B, p->D, p->N, L, io, fwb > 0 ? fws : nullptr, fwb, stream);
   if (st != HYENA_OK) return st;
   return hyena_out_projection(y, p, out, B, L, io, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- grid convolutions
+
+extern "C" {
+
+hyena_status hyena_nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, int64_t* padded_side) {
+  if (!dims || !padded_side) return HYENA_ERR_NULL;
+  NdPlanH p;
+  const int c = nd_plan(ndim, dims, circular, &p);
+  if (c) return c == 2 ? HYENA_ERR_SHAPE : HYENA_ERR_UNSUPPORTED;
+  *padded_side = p.P;
+  return HYENA_OK;
+}
+
+int64_t hyena_nd_spectrum_bytes(int32_t rows, int32_t ndim, const int64_t* dims, int32_t circular) {
+  NdPlanH p;
+  if (rows < 1 || nd_plan(ndim, dims, circular, &p)) return -1;
+  return (int64_t)rows * p.stride * 8;
+}
+
+hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t ndim, const int64_t* dims,
+                                      int32_t circular, void* spec, void* stream) {
+  if (!kernel || !spec || !dims) return HYENA_ERR_NULL;
+  if (rows < 1 || rows > (1 << 24)) return HYENA_ERR_SHAPE;
+  NdPlanH p;
+  const int c = nd_plan(ndim, dims, circular, &p);
+  if (c) return c == 2 ? HYENA_ERR_SHAPE : HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(kernel) || !aligned16(spec)) return HYENA_ERR_ALIGN;
+  const int64_t kb = (int64_t)rows * nd_kernel_extent(p, circular) * 4, sb = (int64_t)rows * p.stride * 8;
+  if (overlap(spec, sb, kernel, kb)) return HYENA_ERR_ALIAS;
+  NdArgs a{};
+  a.ndim = p.ndim; a.P = p.P; a.Lo = p.Lo; a.Lm = p.Lm; a.Ll = p.Ll;
+  a.circular = circular;
+  a.spec_stride = p.stride;
+  a.spec = spec;
+  a.kernel = kernel;
+  a.rows = rows;
+  return nd_spectrum(a, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                              int32_t D, int32_t N, int32_t ndim, const int64_t* dims, int32_t circular,
+                              int32_t per_sample, hyena_dtype io, void* stream) {
+  if (!v || !x || !spec || !y || !dims) return HYENA_ERR_NULL;
+  if (B < 1 || B > (1 << 20) || D < 1 || D > (1 << 20) || N < 1) return HYENA_ERR_SHAPE;
+  if (N > kMaxOrder || (per_sample != 0 && per_sample != 1)) return HYENA_ERR_UNSUPPORTED;
+  if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  for (int n = 0; n < N; ++n)
+    if (!x[n]) return HYENA_ERR_NULL;
+  NdPlanH p;
+  const int c = nd_plan(ndim, dims, circular, &p);
+  if (c) return c == 2 ? HYENA_ERR_SHAPE : HYENA_ERR_UNSUPPORTED;
+  if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(v) || !aligned16(y) || !aligned16(spec)) return HYENA_ERR_ALIGN;
+  for (int n = 0; n < N; ++n)
+    if (!aligned16(x[n])) return HYENA_ERR_ALIGN;
+  const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
+  const int64_t act = B * D * p.points * esz;
+  const int64_t sb = (per_sample ? B : 1) * (int64_t)N * D * p.stride * 8;
+  if (overlap(y, act, v, act) || overlap(y, act, spec, sb)) return HYENA_ERR_ALIAS;
+  for (int n = 0; n < N; ++n)
+    if (overlap(y, act, x[n], act)) return HYENA_ERR_ALIAS;
+  NdArgs a{};
+  a.ndim = p.ndim; a.P = p.P; a.Lo = p.Lo; a.Lm = p.Lm; a.Ll = p.Ll;
+  a.circular = circular;
+  a.spec_stride = p.stride;
+  a.spec = const_cast<void*>(spec);
+  a.rows = (int)(B * D);
+  a.v = v;
+  for (int n = 0; n < N; ++n) a.x.p[n] = x[n];
+  a.y = y;
+  a.D = D;
+  a.NORD = N;
+  a.per_sample = per_sample;
+  a.io = (io == HYENA_FP32) ? 0 : 1;
+  return nd_forward(a, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -99,6 +99,26 @@ hipError_t filter_gen_li(const float* R, const float* lam, int NF, int S, int64_
 hipError_t filter_gen_mr(const float* hhat, const float* alpha, int D, int NF, int Lh, float* h, hipStream_t s);
 hipError_t fir_forward(const ForwardArgs& a, const float* h, int Lh, hipStream_t s);
 
+// Grid convolutions (kernels_nd.hip).
+struct NdArgs {
+  int ndim, P;            // 2 or 3 axes; padded FFT side (power of two)
+  int Lo, Lm, Ll;         // grid sides: first, middle (1 for 2-D), last (contiguous)
+  int circular;
+  int64_t spec_stride;    // complex64 elements per kernel row
+  void* spec;
+  // spectrum
+  const float* kernel;    // [rows][extent]
+  int rows;
+  // forward (rows = B * D grids)
+  const void* v;
+  XPtrsHost x;
+  void* y;
+  int D, NORD, per_sample, io;
+};
+
+hipError_t nd_spectrum(const NdArgs& a, hipStream_t s);
+hipError_t nd_forward(const NdArgs& a, hipStream_t s);
+
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);

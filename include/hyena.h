@@ -280,6 +280,50 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
                               int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
                               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Convolutions on 2-D and 3-D grids (gist.science HyenaND summary, "手法:
+ * HyenaND": native N-D long convolution evaluated through the N-D FFT, with
+ * circular boundaries for periodic systems and every axis zero-padded to
+ * twice its size for images and volumes; "実装: nSubQ": the FFT, the
+ * spectral product and the inverse FFT fused with the intermediate on chip).
+ *
+ * Grid of k = ndim in {2, 3} axes with sides dims[0..k-1] (row-major, the
+ * last axis contiguous).  The same order-N recurrence as hyena_forward,
+ * z_1 = v, z_{n+1} = x_n * (K_n conv z_n), y = z_{N+1}, with
+ *   non-circular: c[t] = sum over grid points s of K[t - s] z[s]; the kernel
+ *                 holds one value per offset o with |o_a| < dims[a], stored
+ *                 row-major with extent 2*dims[a]-1 and index o_a+dims[a]-1
+ *                 (a causal kernel is zero at negative offsets);
+ *   circular:     c[t] = sum_s K[(t - s) mod dims] z[s]; the kernel has the
+ *                 grid's shape.
+ * Supported: the FFT grid is a cube of side P, a power of two with, per
+ * dimension count, 16 <= P <= 128 (2-D) or 8 <= P <= 32 (3-D).  Non-circular
+ * grids take the smallest such P >= 2*max(dims)-1 (so sides up to 64 in 2-D
+ * and 16 in 3-D); circular grids need every side equal to one such P.  Other
+ * shapes return HYENA_ERR_UNSUPPORTED (a side outside 1..4096: SHAPE).
+ *
+ * hyena_nd_plan: writes P.
+ * hyena_nd_spectrum_bytes: bytes of the spectrum of `rows` kernels (-1 for
+ *   an invalid or unsupported shape).  The layout is private.
+ * hyena_nd_filter_spectrum: kernel [rows][extent] fp32 (device) -> spec
+ *   (device, hyena_nd_spectrum_bytes).  Row r is the kernel n*D + d for the
+ *   shared form, (b*N + n)*D + d for per-sample kernels (the summary's
+ *   input-dependent kernels, one per sample).
+ * hyena_nd_forward: v, each x[n] (host array of N device pointers) and y are
+ *   [B][D][dims...] in `io`; spec from hyena_nd_filter_spectrum with N*D
+ *   rows (per_sample = 0) or B*N*D rows (per_sample = 1).  1 <= N <= 8.
+ *   Pointers 16-byte aligned (HYENA_ERR_ALIGN); y must not overlap v, any
+ *   x[n] or spec (HYENA_ERR_ALIAS).  No workspace, no allocation; the work
+ *   is enqueued on `stream`.
+ * ---------------------------------------------------------------------- */
+hyena_status hyena_nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, int64_t* padded_side);
+int64_t hyena_nd_spectrum_bytes(int32_t rows, int32_t ndim, const int64_t* dims, int32_t circular);
+hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t ndim, const int64_t* dims,
+                                      int32_t circular, void* spec, void* stream);
+hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                              int32_t D, int32_t N, int32_t ndim, const int64_t* dims, int32_t circular,
+                              int32_t per_sample, hyena_dtype io, void* stream);
+
 /* Static description of a status code. */
 const char* hyena_status_str(hyena_status s);
 

@@ -251,3 +251,58 @@ def test_plan_circular_rejects_other_lengths():
         assert e.value.code == UNSUP
     assert H.spectrum_bytes(4, 2, 1000, circular=True) == -1
     assert H.lib().hyena_plan_ex(256, 7, ctypes.byref(H.PlanInfo())) == UNSUP
+
+
+@pytest.mark.parametrize("dims,circ,P", [((8, 8), False, 16), ((1, 1), False, 16), ((9, 9), False, 32),
+                                         ((56, 56), False, 128), ((64, 3), False, 128), ((4, 4, 4), False, 8),
+                                         ((5, 2, 3), False, 16), ((16, 16, 16), False, 32), ((16, 16), True, 16),
+                                         ((128, 128), True, 128), ((8, 8, 8), True, 8), ((32, 32, 32), True, 32)])
+def test_nd_plan(dims, circ, P):
+    assert H.nd_plan(dims, circ) == P
+    NC = P ** len(dims) // 2
+    Q = NC // (P // 2)
+    stride = -(-(NC + Q) // 64) * 64
+    assert H.nd_spectrum_bytes(6, dims, circ) == 6 * stride * 8
+
+
+def test_nd_plan_rejects_unsupported():
+    for dims, circ, code in [((65, 4), False, UNSUP), ((17, 1, 1), False, UNSUP), ((32, 16), True, UNSUP),
+                             ((8, 8), True, UNSUP), ((256, 256), True, UNSUP), ((12, 12), True, UNSUP),
+                             ((4,), False, UNSUP), ((4, 4, 4, 4), False, UNSUP), ((0, 4), False, SHAPE),
+                             ((5000, 4), False, SHAPE)]:
+        with pytest.raises(H.HyenaError) as e:
+            H.nd_plan(dims, circ)
+        assert e.value.code == code, (dims, circ)
+        assert H.nd_spectrum_bytes(2, dims, circ) == -1
+
+
+def test_nd_calls_reject_bad_arguments():
+    lib = H.lib()
+    d2 = (ctypes.c_int64 * 2)(16, 16)
+    bad = (ctypes.c_int64 * 2)(100, 16)
+    xs = (vp * 2)(Bp, C)
+    fwd = lambda **k: lib.hyena_nd_forward(
+        vp(k.get("v", A)), k.get("x", xs), vp(k.get("spec", Dp)), vp(k.get("y", Y)), k.get("B", 2),
+        k.get("D", 3), k.get("N", 2), k.get("ndim", 2), k.get("dims", d2), k.get("circ", 0), k.get("ps", 0),
+        k.get("io", 0), None)
+    assert fwd(v=0) == NULL
+    assert fwd(x=None) == NULL
+    assert fwd(x=(vp * 2)(Bp, 0)) == NULL
+    assert fwd(dims=None) == NULL
+    assert fwd(B=0) == SHAPE
+    assert fwd(N=0) == SHAPE
+    assert fwd(N=9) == UNSUP
+    assert fwd(ps=2) == UNSUP
+    assert fwd(io=5) == UNSUP
+    assert fwd(ndim=4) == UNSUP
+    assert fwd(dims=bad) == UNSUP
+    assert fwd(circ=1, dims=(ctypes.c_int64 * 2)(16, 8)) == UNSUP
+    assert fwd(v=A + 4) == ALIGN
+    assert fwd(y=A) == ALIAS
+    assert fwd(y=C + 64) == ALIAS
+    assert fwd(y=Dp + 16) == ALIAS
+    assert lib.hyena_nd_filter_spectrum(None, 4, 2, d2, 0, vp(Dp), None) == NULL
+    assert lib.hyena_nd_filter_spectrum(vp(A), 0, 2, d2, 0, vp(Dp), None) == SHAPE
+    assert lib.hyena_nd_filter_spectrum(vp(A), 4, 2, bad, 0, vp(Dp), None) == UNSUP
+    assert lib.hyena_nd_filter_spectrum(vp(A + 8), 4, 2, d2, 0, vp(Dp), None) == ALIGN
+    assert lib.hyena_nd_filter_spectrum(vp(A), 4, 2, d2, 0, vp(A + 64), None) == ALIAS

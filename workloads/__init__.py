@@ -215,8 +215,8 @@ GRID_CONFIGS = {
                      desc="order-2, B=8, D=192, 56x56 image grid, non-circular, bf16 I/O"),
     "G3": GridConfig("G3", 2, 2, 128, (16, 16, 16), False, "bf16", 23,
                      desc="order-2, B=2, D=128, 16^3 volume, non-circular, bf16 I/O"),
-    "GP": GridConfig("GP", 2, 4, 64, (128, 128), True, "fp32", 24,
-                     desc="order-2, B=4, D=64, 128x128 periodic field, circular, fp32"),
+    "GP": GridConfig("GP", 2, 16, 64, (128, 128), True, "fp32", 24,
+                     desc="order-2, B=16, D=64, 128x128 periodic field, circular, fp32"),
 }
 
 
