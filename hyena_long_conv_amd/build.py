@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhyena_mi355x.so")
 
 SOURCES = ["api.cpp", "kernels_single.hip", "kernels_fourstep.hip", "kernels_filter.hip", "kernels_proj.hip",
-           "kernels_fir.hip", "kernels_nd.hip"]
+           "kernels_fir.hip", "kernels_nd.hip", "kernels_bwd_long.hip"]
 ARCH = os.environ.get("HYENA_OFFLOAD_ARCH", "gfx950")
 
 

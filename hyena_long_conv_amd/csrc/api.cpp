@@ -355,9 +355,35 @@ hyena_status hyena_forward_fir(const void* v, const void* const* x, const float*
 namespace {
 constexpr int64_t kBackwardMaxN = 8192;   // complex points of the single-pass backward
 
-int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
+int64_t bwd_ws_single(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
   const int64_t cb = (NORD * B * D * (p.N / 2) * 8 + 255) / 256 * 256;
   return cb + NORD * D * p.N * 8;
+}
+
+bool bwd_single(const PlanInfo& p) { return p.path == PATH_SINGLE && p.N <= kBackwardMaxN; }
+
+// The four-step plan the long backward runs on (the forward's own plan, or a
+// four-step plan of the same length for single-path spectra too long for
+// the one-workgroup backward).
+int bwd_long_plan(const PlanInfo& p, PlanInfo* fs) {
+  if (p.path != PATH_SINGLE) {
+    *fs = p;
+    return 0;
+  }
+  return make_plan(p.L, "fourstep", nullptr, fs, 0);
+}
+
+int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// -1 when no backward serves the plan
+int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
+  if (p.circular) return -1;
+  if (bwd_single(p)) return bwd_ws_single(p, B, D, NORD);
+  PlanInfo fs;
+  if (bwd_long_plan(p, &fs)) return -1;
+  int64_t t = long_backward_layout(fs, B, D, NORD).total;
+  if (p.path == PATH_SINGLE) t += al256(NORD * D * fs.spec_stride * 8);   // spectrum in the four-step layout
+  return t;
 }
 }  // namespace
 
@@ -366,7 +392,7 @@ int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t 
   if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
   PlanInfo p;
   if (plan_env(L, &p)) return -1;
-  if (p.path != PATH_SINGLE || p.N > kBackwardMaxN) return -1;
+  if (B * D > ((int64_t)1 << 30)) return -1;
   return bwd_ws(p, B, D, N);
 }
 
@@ -382,13 +408,14 @@ hyena_status hyena_backward(const void* v, const void* const* x, const void* spe
   PlanInfo p;
   const int c = plan_env(L, &p);
   if (c) return from_plan_code(c);
-  if (p.path != PATH_SINGLE || p.N > kBackwardMaxN) return HYENA_ERR_UNSUPPORTED;
+  if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
+  const int64_t need = bwd_ws(p, B, D, N);
+  if (need < 0) return HYENA_ERR_UNSUPPORTED;
   if (!aligned16(v) || !aligned16(spec) || !aligned16(gy) || !aligned16(gv) || !aligned16(gh) ||
       !aligned16(workspace))
     return HYENA_ERR_ALIGN;
   for (int n = 0; n < N; ++n)
     if (!aligned16(x[n]) || !aligned16(gx[n])) return HYENA_ERR_ALIGN;
-  const int64_t need = bwd_ws(p, B, D, N);
   if (workspace_bytes < need) return HYENA_ERR_WORKSPACE;
   const int64_t esz = (io == HYENA_FP32) ? 4 : 2;
   const int64_t act = B * D * L * esz, sb = spec_bytes(p, (int64_t)N * D), ghb = (int64_t)N * D * L * 4;
@@ -412,11 +439,23 @@ hyena_status hyena_backward(const void* v, const void* const* x, const void* spe
   a.v = v;
   for (int n = 0; n < N; ++n) { a.x.p[n] = x[n]; a.gx.p[n] = gx[n]; }
   a.spec = spec; a.gy = gy; a.gv = gv; a.gh = gh;
-  a.cbuf = workspace;
-  a.hacc = static_cast<char*>(workspace) + (need - (int64_t)N * D * p.N * 8);
   a.B = (int)B; a.D = D; a.NORD = N; a.L = L;
   a.io = (io == HYENA_FP32) ? 0 : 1;
   a.spec_stride = p.spec_stride;
+  if (!bwd_single(p)) {
+    PlanInfo fs;
+    if (bwd_long_plan(p, &fs)) return HYENA_ERR_UNSUPPORTED;
+    if (p.path == PATH_SINGLE) {
+      // the caller's spectrum has the single-path layout: rewrite it after the long backward's buffers
+      void* conv = static_cast<char*>(workspace) + long_backward_layout(fs, B, D, N).total;
+      if (spectrum_to_fourstep(spec, N * D, p, fs, conv, (hipStream_t)stream) != hipSuccess) return HYENA_ERR_HIP;
+      a.spec = conv;
+    }
+    a.spec_stride = fs.spec_stride;
+    return long_backward(a, fs, workspace, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+  }
+  a.cbuf = workspace;
+  a.hacc = static_cast<char*>(workspace) + (need - (int64_t)N * D * p.N * 8);
   return single_backward(a, p.N, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 

@@ -84,6 +84,21 @@ hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// H(k)/M of filter row `row` from the single path's pair coefficients:
+// P = (a1 + conj a2)/2, sQ = (conj a2 - a1)/2, cQ = bq, Q = s*sQ + c*cQ;
+// H(p) = (P + Q)/2, H(N-p) = conj(P - Q)/2 with p = min(k, N-k).
+__device__ __forceinline__ cf single_bin(const cf* row, int64_t k, int64_t N, int64_t stride) {
+  const int64_t qs = stride / 3;
+  const int64_t p = k <= N / 2 ? k : N - k;
+  const cf a1 = row[p], a2 = row[qs + p], bq = row[2 * qs + p];
+  float sn, cs;
+  sincospif((float)p / (float)N, &sn, &cs);
+  const float Px = 0.5f * (a1.x + a2.x), Py = 0.5f * (a1.y - a2.y);
+  const float sQx = 0.5f * (a2.x - a1.x), sQy = 0.5f * (-a2.y - a1.y);
+  const float Qx = sn * sQx + cs * bq.x, Qy = sn * sQy + cs * bq.y;
+  return (k == p) ? make_float2(0.5f * (Px + Qx), 0.5f * (Py + Qy)) : make_float2(0.5f * (Px - Qx), -0.5f * (Py - Qy));
+}
+
 // Library spectrum layout -> natural order, undoing the 1/(2N) scale.
 __global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict__ out, int NF, int64_t N,
                                   int path, int n1, int n2, int64_t stride) {
@@ -94,18 +109,7 @@ __global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict
   const cf* row = spec + f * stride;
   cf g;
   if (path == PATH_SINGLE) {
-    // invert the pair coefficients of bins (p, N-p), p = min(k, N-k):
-    // P = (a1 + conj a2)/2, sQ = (conj a2 - a1)/2, cQ = bq, Q = s*sQ + c*cQ;
-    // H(p) = (P + Q)/2, H(N-p) = conj(P - Q)/2
-    const int64_t qs = stride / 3;
-    const int64_t p = k <= N / 2 ? k : N - k;
-    const cf a1 = row[p], a2 = row[qs + p], bq = row[2 * qs + p];
-    float sn, cs;
-    sincospif((float)p / (float)N, &sn, &cs);
-    const float Px = 0.5f * (a1.x + a2.x), Py = 0.5f * (a1.y - a2.y);
-    const float sQx = 0.5f * (a2.x - a1.x), sQy = 0.5f * (-a2.y - a1.y);
-    const float Qx = sn * sQx + cs * bq.x, Qy = sn * sQy + cs * bq.y;
-    g = (k == p) ? make_float2(0.5f * (Px + Qx), 0.5f * (Py + Qy)) : make_float2(0.5f * (Px - Qx), -0.5f * (Py - Qy));
+    g = single_bin(row, k, N, stride);
   } else {
     int64_t src = k;
     if (k < N) src = (k % n1) * n2 + k / n1;
@@ -113,6 +117,27 @@ __global__ void k_spectrum_export(const cf* __restrict__ spec, float* __restrict
   }
   out[2 * idx] = g.x * (float)(2 * N);
   out[2 * idx + 1] = g.y * (float)(2 * N);
+}
+
+// A single-path spectrum rewritten in the four-step layout (n1 x n2) of the
+// same FFT length: H(k)/M at (k mod n1) * n2 + k / n1, H(N)/M at N.
+__global__ void k_spectrum_to_fourstep(const cf* __restrict__ spec, cf* __restrict__ out, int NF, int64_t N,
+                                       int64_t stride_in, int n1, int n2, int64_t stride_out) {
+  const int64_t half = N + 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)NF * half) return;
+  const int64_t f = idx / half, k = idx - f * half;
+  const int64_t dst = k < N ? (k % n1) * n2 + k / n1 : N;
+  out[f * stride_out + dst] = single_bin(spec + f * stride_in, k, N, stride_in);
+}
+
+hipError_t spectrum_to_fourstep(const void* spec, int NF, const PlanInfo& single, const PlanInfo& fs, void* out,
+                                hipStream_t s) {
+  const int64_t total = (int64_t)NF * (single.N + 1);
+  const int threads = 256;
+  hipLaunchKernelGGL(k_spectrum_to_fourstep, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s,
+                     (const cf*)spec, (cf*)out, NF, single.N, single.spec_stride, fs.n1, fs.n2, fs.spec_stride);
+  return hipGetLastError();
 }
 
 hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s) {

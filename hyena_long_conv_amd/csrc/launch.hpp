@@ -94,6 +94,16 @@ struct BackwardArgs {
 
 hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 
+// Backward on the four-step path (kernels_bwd_long.hip): byte offsets of its
+// workspace buffers (saved c_n, z, g, two temporaries, an all-ones gate, the
+// per-row spectra and the four-step intermediate).
+struct LongBackwardLayout {
+  int64_t c, z, g, t1, t2, ones, sg, work, total;
+  int rows_per_group;
+};
+LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD);
+hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspace, hipStream_t s);
+
 // Other filter families (kernels_fir.hip).
 hipError_t filter_gen_li(const float* R, const float* lam, int NF, int S, int64_t L, float* h, hipStream_t s);
 hipError_t filter_gen_mr(const float* hhat, const float* alpha, int D, int NF, int Lh, float* h, hipStream_t s);
@@ -125,5 +135,7 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
 hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s);
 hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s);
 hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s);
+hipError_t spectrum_to_fourstep(const void* spec, int NF, const PlanInfo& single, const PlanInfo& fs, void* out,
+                                hipStream_t s);
 
 }  // namespace hyena

@@ -189,9 +189,13 @@ hyena_status hyena_forward_fir(const void* v, const void* const* x, const float*
  * intermediates are recomputed from v, x and the spectrum.
  *   gy, gv    device [B][D][L], I/O dtype;   gx  HOST array of N device
  *   pointers [B][D][L], I/O dtype;  gh  device fp32 [N][D][L].
- * This build computes it for L <= 8192 (one workgroup per channel; longer
- * rows return HYENA_ERR_UNSUPPORTED).  Errors as hyena_forward, plus ALIAS for
- * an output overlapping an input or another output.
+ * L <= 8192 runs in one launch, one workgroup per channel; longer rows (up
+ * to the forward's limit) express every convolution of the chain through
+ * the forward's four-step causal convolution and a row reversal, with the
+ * forward's c_n kept in the workspace (about (N + 5) * B * D * L * 4 bytes
+ * plus per-row spectra; a spectrum built on the single path is rewritten
+ * into the four-step layout there).  Linear mode only.  Errors as hyena_forward, plus ALIAS for an output
+ * overlapping an input or another output.
  */
 int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
 

@@ -203,14 +203,18 @@ def test_backward_rejects_bad_arguments():
     assert bw(gx=(vp * 2)(Y + 0x100000, 0)) == NULL
     assert bw(B=0) == SHAPE
     assert bw(N=9, x=(vp * 9)(*[Bp + 0x10000 * i for i in range(9)])) == UNSUP
-    assert bw(L=9000) == UNSUP                                  # beyond the single-pass backward
+    assert bw(L=9000, wsb=1 << 20) == WS                        # long rows need the larger workspace
     assert bw(gv=Y + 4) == ALIGN
     assert bw(wsb=16) == WS
     assert bw(gv=A) == ALIAS                                    # gv over v
     assert bw(gh=Y) == ALIAS                                    # gh over gv
     assert bw(gx=(vp * 2)(Y + 0x100000, Bp)) == ALIAS           # gx_2 over x_1
     assert H.backward_workspace_bytes(4, 768, 2, 2048) > 0
-    assert H.backward_workspace_bytes(1, 4, 2, 20000) == -1
+    # four-step lengths: saved c_n, five row buffers, per-row spectra, the pass intermediate
+    R, L = 4, 20000
+    assert H.backward_workspace_bytes(1, 4, 2, L) >= (2 + 5) * R * L * 4 + R * (32768 + 1) * 8
+    # 8192 < L <= 16384: the single-path spectrum is rewritten into the four-step layout (extra N*D rows)
+    assert H.backward_workspace_bytes(1, 4, 2, 12000) > H.backward_workspace_bytes(1, 4, 2, 8192)
 
 
 def test_filter_family_calls_reject_bad_arguments():

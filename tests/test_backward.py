@@ -1,5 +1,5 @@
-"""GPU parity of hyena_backward (single-pass lengths) against the float64
-oracle's backward on the same inputs and the same filters.
+"""GPU parity of hyena_backward (single-pass and four-step lengths) against
+the float64 oracle's backward on the same inputs and the same filters.
 
 Tolerances (per row, max |got - ref| / max |ref|): gv and gx_n 1e-4 for fp32,
 2e-2 for bf16 (stored results rounded to bf16); gh 1e-4 (fp32 output, the
@@ -31,6 +31,12 @@ CASES = [
     (2, 4, 8, 2048, "fp32"), (2, 1, 2, 8191, "fp32"), (8, 1, 2, 64, "fp32"), (1, 2, 3, 4096, "fp32"),
     (2, 2, 3, 300, "bf16"), (3, 1, 4, 4096, "bf16"), (2, 3, 2, 2047, "bf16"),
 ]
+
+
+@pytest.fixture(autouse=True)
+def _clean_env(monkeypatch):
+    monkeypatch.delenv("HYENA_FORCE_PATH", raising=False)
+    monkeypatch.delenv("HYENA_FOURSTEP_N1", raising=False)
 
 
 def _run(N, B, D, L, io, channels=None, seed=31):
@@ -80,10 +86,30 @@ def test_backward_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
 
 
-def test_backward_rejects_long_rows():
-    cfg = Config("bwd", 2, 1, 2, 9000, "fp32", 32, 3)
-    v, xs = make_activations(cfg, DEV)
-    assert H.backward_workspace_bytes(1, 2, 2, 9000) == -1
-    with pytest.raises(H.HyenaError):
-        H.backward(v, xs, torch.zeros(16, dtype=torch.uint8, device=DEV), v.clone(),
-                   workspace=torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
+LONG_CASES = [
+    # N, B, D, L, io, forced path, forced n1 (four-step at small L: the oracle's direct sums stay fast)
+    (2, 2, 3, 1000, "fp32", "fourstep", "16"), (3, 1, 2, 2048, "fp32", "fourstep", "64"),
+    (1, 3, 2, 4096, "fp32", "fourstep", "32"), (2, 2, 2, 777, "bf16", "fourstep", "16"),
+    (8, 1, 1, 512, "fp32", "fourstep", "16"),
+    (2, 2, 2, 12000, "fp32", None, None),     # single-path spectrum rewritten for the four-step backward
+    (2, 1, 2, 20000, "fp32", None, None),     # four-step plan, ragged length
+    (2, 1, 2, 65536, "bf16", None, None),     # the 64K shape's length
+]
+
+
+@pytest.mark.parametrize("N,B,D,L,io,force,n1", LONG_CASES)
+def test_backward_long_matches_oracle(N, B, D, L, io, force, n1, monkeypatch):
+    if force:
+        monkeypatch.setenv("HYENA_FORCE_PATH", force)
+    if n1:
+        monkeypatch.setenv("HYENA_FOURSTEP_N1", n1)
+    got, ref = _run(N, B, D, L, io, seed=41 + N)
+    _check(got, ref, io)
+
+
+def test_backward_long_deterministic(monkeypatch):
+    monkeypatch.setenv("HYENA_FORCE_PATH", "fourstep")
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "16")
+    a, _ = _run(2, 3, 2, 600, "fp32", channels=[1])
+    b, _ = _run(2, 3, 2, 600, "fp32", channels=[1])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
