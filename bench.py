@@ -52,9 +52,20 @@ def algo_flops(cfg, circular: bool = False) -> float:
     return cfg.N * cfg.B * cfg.D * cfg.L * (10.0 * math.log2(2 * cfg.L) + 7.0)
 
 
-def source_hash() -> str:
+# Sources that make up the code of each counted kernel (its translation unit
+# and the device headers it includes).
+KERNEL_SOURCES = {
+    "k_single_forward": ["kernels_single.hip", "fft_engine.hpp", "plan.hpp"],
+    "k_nd_forward": ["kernels_nd.hip", "fft_engine.hpp", "plan.hpp"],
+}
+
+
+def source_hash(files=None) -> str:
+    """Hash of the given csrc files (all of csrc when None)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "hyena_long_conv_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "hyena_long_conv_amd", "csrc")
+    paths = sorted(glob.glob(os.path.join(csrc, "*"))) if files is None else [os.path.join(csrc, f) for f in sorted(files)]
+    for f in paths:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
@@ -70,7 +81,7 @@ def measured_traffic(cfg_name: str):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != source_hash():
+    if d.get("source_hash") != source_hash(d.get("sources")):
         return None
     return d.get("hbm_bytes_per_step")
 

@@ -16,7 +16,7 @@ namespace hyena {
 #define HYENA_SINGLE_WAVES 1
 #endif
 #ifndef HYENA_XCD_MAP
-#define HYENA_XCD_MAP 0
+#define HYENA_XCD_MAP 1
 #endif
 #ifndef HYENA_SINGLE_E16_MIN
 #define HYENA_SINGLE_E16_MIN 16384
