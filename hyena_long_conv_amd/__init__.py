@@ -127,9 +127,12 @@ def lib() -> ctypes.CDLL:
     L.hyena_nd_plan.restype = i32
     L.hyena_nd_spectrum_bytes.argtypes = [i32, i32, i64p, i32]
     L.hyena_nd_spectrum_bytes.restype = i64
-    L.hyena_nd_filter_spectrum.argtypes = [vp, i32, i32, i64p, i32, vp, vp]
+    L.hyena_nd_workspace_bytes.argtypes = [i64, i32, i64p, i32]
+    L.hyena_nd_workspace_bytes.restype = i64
+    L.hyena_nd_filter_spectrum.argtypes = [vp, i32, i32, i64p, i32, vp, vp, i64, vp]
     L.hyena_nd_filter_spectrum.restype = i32
-    L.hyena_nd_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i32, i64p, i32, i32, i32, vp]
+    L.hyena_nd_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i32, i64p, i32, i32, i32, vp, i64,
+                                   vp]
     L.hyena_nd_forward.restype = i32
     L.hyena_status_str.argtypes = [i32]
     L.hyena_status_str.restype = ctypes.c_char_p
@@ -519,7 +522,22 @@ def nd_spectrum_bytes(rows: int, dims, circular: bool = False) -> int:
     return int(lib().hyena_nd_spectrum_bytes(int(rows), len(dims), cd, int(bool(circular))))
 
 
-def nd_filter_spectrum(kernel, dims, circular: bool = False, out=None):
+def nd_workspace_bytes(rows: int, dims, circular: bool = False) -> int:
+    dims, cd = _dims(dims)
+    return int(lib().hyena_nd_workspace_bytes(int(rows), len(dims), cd, int(bool(circular))))
+
+
+def _nd_workspace(rows, dims, circular, device, workspace):
+    import torch
+    wsb = nd_workspace_bytes(rows, dims, circular)
+    if wsb < 0:
+        raise HyenaError(3, "hyena_nd_workspace_bytes")
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=device)
+    return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
+
+
+def nd_filter_spectrum(kernel, dims, circular: bool = False, out=None, workspace=None):
     """Spectrum of grid kernels [..rows.., extent...] fp32: the extent is
     2*dims-1 per axis (non-circular, index offset + dims - 1) or dims
     (circular).  Leading axes are flattened into kernel rows."""
@@ -537,13 +555,15 @@ def nd_filter_spectrum(kernel, dims, circular: bool = False, out=None):
     if nbytes < 0:
         raise HyenaError(3, "hyena_nd_spectrum_bytes")
     spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=kernel.device)
+    workspace, wsb = _nd_workspace(rows, dims, circular, kernel.device, workspace)
     _check(lib().hyena_nd_filter_spectrum(_ptr(kernel), rows, k, cd, int(bool(circular)), _ptr(spec),
-                                          _stream(kernel)), "hyena_nd_filter_spectrum")
+                                          _ptr(workspace), wsb, _stream(kernel)), "hyena_nd_filter_spectrum")
     spec._hyena_nd = (dims, bool(circular), rows)
     return spec
 
 
-def prepare_nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None):
+def prepare_nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None,
+                       workspace=None):
     """hyena_nd_forward marshalled once (v, x_n: [B, D, dims...] fp32 or bf16)."""
     io = _io_of(v)
     _need_cuda(v, "v", v.dtype)
@@ -560,11 +580,13 @@ def prepare_nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bo
     y = out if out is not None else torch.empty_like(v)
     _need_cuda(y, "y", v.dtype)
     xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
+    workspace, wsb = _nd_workspace(B * D, dims, circular, v.device, workspace)
     args = (_ptr(v), xp, _ptr(spec), _ptr(y), B, D, N, len(dims), cd, int(bool(circular)), int(bool(per_sample)),
-            io, _stream(v))
-    return PreparedCall(lib().hyena_nd_forward, args, (v, tuple(xs), spec, y, xp, cd), y, "hyena_nd_forward")
+            io, _ptr(workspace), wsb, _stream(v))
+    return PreparedCall(lib().hyena_nd_forward, args, (v, tuple(xs), spec, y, xp, cd, workspace), y,
+                        "hyena_nd_forward")
 
 
-def nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None):
+def nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bool = False, out=None, workspace=None):
     """y = z_{N+1} of the order-N recurrence with grid convolutions."""
-    return prepare_nd_forward(v, xs, spec, circular, per_sample, out)()
+    return prepare_nd_forward(v, xs, spec, circular, per_sample, out, workspace)()

@@ -50,6 +50,7 @@ struct NdPlanH {
   int ndim, P;
   int Lo, Lm, Ll;
   int64_t NC, Q, stride, points;
+  bool multi;   // 2-D grids beyond one workgroup: column and row passes through a workspace
 };
 
 constexpr int kNdMaxSide = 4096;
@@ -64,7 +65,8 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
     lmax = dims[a] > lmax ? dims[a] : lmax;
     points *= dims[a];
   }
-  const int pmin = ndim == 2 ? 16 : 8, pmax = ndim == 2 ? 128 : 32;
+  // single pass: 2-D up to 128, 3-D up to 32; 2-D multi-pass 256..1024
+  const int pmin = ndim == 2 ? 16 : 8, pmax = ndim == 2 ? 1024 : 32;
   int64_t P;
   if (circular) {
     P = dims[0];
@@ -86,8 +88,25 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
   p.NC = p.Q * (P / 2);
   p.stride = round_up(p.NC + p.Q, 64);
   p.points = points;
+  p.multi = ndim == 2 && P > 128;
   *out = p;
   return 0;
+}
+
+int64_t nd_ws(const NdPlanH& p, int64_t rows) {
+  return p.multi ? (int64_t)rows_per_group(p.NC, rows) * p.NC * 8 : 0;
+}
+
+// 0: fine; otherwise a status.  Sets the grids per pass group.
+hyena_status nd_ws_check(const NdPlanH& p, int64_t rows, void* ws, int64_t wsb, int* group) {
+  *group = 0;
+  if (!p.multi) return HYENA_OK;
+  if (!ws || wsb < p.NC * 8) return HYENA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HYENA_ERR_ALIGN;
+  int64_t g = rows_per_group(p.NC, rows);
+  if (g * p.NC * 8 > wsb) g = wsb / (p.NC * 8);
+  *group = (int)g;
+  return HYENA_OK;
 }
 
 int64_t nd_kernel_extent(const NdPlanH& p, int32_t circular) {
@@ -596,8 +615,15 @@ int64_t hyena_nd_spectrum_bytes(int32_t rows, int32_t ndim, const int64_t* dims,
   return (int64_t)rows * p.stride * 8;
 }
 
+int64_t hyena_nd_workspace_bytes(int64_t rows, int32_t ndim, const int64_t* dims, int32_t circular) {
+  NdPlanH p;
+  if (rows < 1 || rows > ((int64_t)1 << 30) || nd_plan(ndim, dims, circular, &p)) return -1;
+  return nd_ws(p, rows);
+}
+
 hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t ndim, const int64_t* dims,
-                                      int32_t circular, void* spec, void* stream) {
+                                      int32_t circular, void* spec, void* workspace, int64_t workspace_bytes,
+                                      void* stream) {
   if (!kernel || !spec || !dims) return HYENA_ERR_NULL;
   if (rows < 1 || rows > (1 << 24)) return HYENA_ERR_SHAPE;
   NdPlanH p;
@@ -606,6 +632,11 @@ hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t
   if (!aligned16(kernel) || !aligned16(spec)) return HYENA_ERR_ALIGN;
   const int64_t kb = (int64_t)rows * nd_kernel_extent(p, circular) * 4, sb = (int64_t)rows * p.stride * 8;
   if (overlap(spec, sb, kernel, kb)) return HYENA_ERR_ALIAS;
+  int group;
+  const hyena_status ws = nd_ws_check(p, rows, workspace, workspace_bytes, &group);
+  if (ws != HYENA_OK) return ws;
+  if (p.multi && (overlap(workspace, workspace_bytes, spec, sb) || overlap(workspace, workspace_bytes, kernel, kb)))
+    return HYENA_ERR_ALIAS;
   NdArgs a{};
   a.ndim = p.ndim; a.P = p.P; a.Lo = p.Lo; a.Lm = p.Lm; a.Ll = p.Ll;
   a.circular = circular;
@@ -613,12 +644,16 @@ hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t
   a.spec = spec;
   a.kernel = kernel;
   a.rows = rows;
-  return nd_spectrum(a, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+  a.work = workspace;
+  a.rows_per_group = group;
+  const hipError_t e = p.multi ? grid2d_spectrum(a, (hipStream_t)stream) : nd_spectrum(a, (hipStream_t)stream);
+  return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
 hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
                               int32_t D, int32_t N, int32_t ndim, const int64_t* dims, int32_t circular,
-                              int32_t per_sample, hyena_dtype io, void* stream) {
+                              int32_t per_sample, hyena_dtype io, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
   if (!v || !x || !spec || !y || !dims) return HYENA_ERR_NULL;
   if (B < 1 || B > (1 << 20) || D < 1 || D > (1 << 20) || N < 1) return HYENA_ERR_SHAPE;
   if (N > kMaxOrder || (per_sample != 0 && per_sample != 1)) return HYENA_ERR_UNSUPPORTED;
@@ -638,7 +673,19 @@ hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* s
   if (overlap(y, act, v, act) || overlap(y, act, spec, sb)) return HYENA_ERR_ALIAS;
   for (int n = 0; n < N; ++n)
     if (overlap(y, act, x[n], act)) return HYENA_ERR_ALIAS;
+  int group;
+  const hyena_status ws = nd_ws_check(p, B * D, workspace, workspace_bytes, &group);
+  if (ws != HYENA_OK) return ws;
+  if (p.multi) {
+    if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
+        overlap(workspace, workspace_bytes, spec, sb))
+      return HYENA_ERR_ALIAS;
+    for (int n = 0; n < N; ++n)
+      if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
+  }
   NdArgs a{};
+  a.work = workspace;
+  a.rows_per_group = group;
   a.ndim = p.ndim; a.P = p.P; a.Lo = p.Lo; a.Lm = p.Lm; a.Ll = p.Ll;
   a.circular = circular;
   a.spec_stride = p.stride;
@@ -651,7 +698,8 @@ hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* s
   a.NORD = N;
   a.per_sample = per_sample;
   a.io = (io == HYENA_FP32) ? 0 : 1;
-  return nd_forward(a, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+  const hipError_t e = p.multi ? grid2d_forward(a, (hipStream_t)stream) : nd_forward(a, (hipStream_t)stream);
+  return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
 }  // extern "C"

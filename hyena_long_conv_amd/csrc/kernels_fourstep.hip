@@ -64,9 +64,31 @@ struct ColArgs {
   int n2;
   int r0;              // first row of this launch
   int n_col_blocks;
+  // grids (GRID kernels): a 2-D grid gL1 x gL2 per row, padded to n1 x 2*n2
+  int64_t gL1, gL2;
+  int gcirc;           // SPEC: kernel of the grid's shape (else extent 2L-1 per axis)
 };
 
-template <int N1, int IOT, int KIND, bool EVEN>
+// Kernel value at padded-grid position (i1, i2) of an n1 x P2 grid: offset
+// o at o mod P on every axis (non-circular extent 2L-1, index o + L - 1).
+__device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, int i1, int i2, int n1, int P2,
+                                                int64_t L1, int64_t L2, bool circ) {
+  int64_t a, b, e2;
+  if (circ) {
+    a = i1; b = i2; e2 = L2;
+  } else {
+    a = i1 < L1 ? i1 + L1 - 1 : (i1 > n1 - L1 ? i1 - n1 + L1 - 1 : -1);
+    b = i2 < L2 ? i2 + L2 - 1 : (i2 > P2 - L2 ? i2 - P2 + L2 - 1 : -1);
+    e2 = 2 * L2 - 1;
+  }
+  return (a >= 0 && b >= 0) ? k[koff + a * e2 + b] : 0.f;
+}
+
+// GRID: each row is a 2-D grid gL1 x gL2 (row-major) zero-padded to
+// n1 x 2*n2; the column FFT runs over the grid's first axis and no twiddle
+// follows (a 2-D DFT), the packed column index col covering grid columns
+// 2col, 2col+1.
+template <int N1, int IOT, int KIND, bool EVEN, bool GRID = false>
 __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1>;
   constexpr int E = C::E, W = C::W, S1 = N1 / E;
@@ -77,20 +99,46 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   const bool valid = col < a.n2;
   const int64_t N = (int64_t)N1 * a.n2;
   cf* buf = a.work + (int64_t)g * N;
-  const int64_t off = (int64_t)(a.r0 + g) * a.L;
+  const int64_t off = GRID ? (int64_t)(a.r0 + g) * a.gL1 * a.gL2 : (int64_t)(a.r0 + g) * a.L;
   const ColLds<W> lds{smem + c};
   BlockFFT<N1, E, typename C::R> fft;
   fft.init(j);
   cf u[E];
+  // element pair of column point i1: row offset, first real index, row length
+  const auto at = [&](int i1, int64_t& ro, int64_t& t, int64_t& len) {
+    if constexpr (GRID) {
+      ro = off + (int64_t)i1 * a.gL2;
+      t = 2 * (int64_t)col;
+      len = a.gL2;
+      return valid && i1 < a.gL1;
+    } else {
+      ro = off;
+      t = 2 * ((int64_t)a.n2 * i1 + col);
+      len = a.L;
+      return valid;
+    }
+  };
 
-  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+  if constexpr (KIND == COL_SPEC && GRID) {
+    const int64_t e = a.gcirc ? a.gL1 * a.gL2 : (2 * a.gL1 - 1) * (2 * a.gL2 - 1);
+    const int64_t koff = (int64_t)(a.r0 + g) * e;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
+      const int i1 = j + i * S1;
       u[i] = make_float2(0.f, 0.f);
-      if (valid) {
-        if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, off, t, a.L);
-        else u[i] = ld_pair<IOT, EVEN>(a.v, off, t, a.L);
+      if (valid)
+        u[i] = make_float2(grid_kernel_at(a.h, koff, i1, 2 * col, N1, 2 * a.n2, a.gL1, a.gL2, a.gcirc),
+                           grid_kernel_at(a.h, koff, i1, 2 * col + 1, N1, 2 * a.n2, a.gL1, a.gL2, a.gcirc));
+    }
+  } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      int64_t ro, t, len;
+      const bool ok = at(j + i * S1, ro, t, len);
+      u[i] = make_float2(0.f, 0.f);
+      if (ok) {
+        if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, ro, t, len);
+        else u[i] = ld_pair<IOT, EVEN>(a.v, ro, t, len);
       }
     }
   } else {
@@ -100,12 +148,13 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
     fft.template run<true>(u, lds, j);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const int64_t t = 2 * ((int64_t)a.n2 * (j + i * S1) + col);
+      int64_t ro, t, len;
+      const bool ok = at(j + i * S1, ro, t, len);
       cf z = make_float2(0.f, 0.f);
-      if (valid) {
-        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, t, a.L);
+      if (ok) {
+        const cf xv = ld_pair<IOT, EVEN>(a.xg, ro, t, len);
         z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
-        if constexpr (KIND == COL_LAST) st_pair<IOT, EVEN>(a.y, off, t, a.L, z);
+        if constexpr (KIND == COL_LAST) st_pair<IOT, EVEN>(a.y, ro, t, len, z);
       }
       u[i] = z;
     }
@@ -223,26 +272,39 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
 
 // ---------------------------------------------------------------- launchers
 
-template <int N1, bool EVEN>
+template <int N1, bool EVEN, bool GRID>
 static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 block, hipStream_t s) {
   if (kind == COL_SPEC) {
-    hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+    hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
   } else if (io == 0) {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST, EVEN, GRID>), grid, block, 0, s, c);
   } else {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST, EVEN, GRID>), grid, block, 0, s, c);
   }
 }
 
+// Grid columns exist for the first axes the grid path plans (256..1024).
+constexpr bool grid_col_ok(int n1) { return n1 >= 256; }
+
 template <int N1>
-static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s, bool grid_mode = false) {
   const dim3 grid(groups * c.n_col_blocks), block(ColCfg<N1>::T);
-  if (c.L % 2 == 0) launch_col_t<N1, true>(kind, io, c, grid, block, s);
-  else launch_col_t<N1, false>(kind, io, c, grid, block, s);
+  if (grid_mode) {
+    if constexpr (grid_col_ok(N1)) {
+      if (c.gL2 % 2 == 0) launch_col_t<N1, true, true>(kind, io, c, grid, block, s);
+      else launch_col_t<N1, false, true>(kind, io, c, grid, block, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (c.L % 2 == 0) {
+    launch_col_t<N1, true, false>(kind, io, c, grid, block, s);
+  } else {
+    launch_col_t<N1, false, false>(kind, io, c, grid, block, s);
+  }
   return hipGetLastError();
 }
 
@@ -259,15 +321,16 @@ static int col_width(int n1) {
   return 0;
 }
 
-static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int groups, hipStream_t s,
+                               bool grid_mode = false) {
   switch (n1) {
-    case 16: return launch_col<16>(kind, io, c, groups, s);
-    case 32: return launch_col<32>(kind, io, c, groups, s);
-    case 64: return launch_col<64>(kind, io, c, groups, s);
-    case 128: return launch_col<128>(kind, io, c, groups, s);
-    case 256: return launch_col<256>(kind, io, c, groups, s);
-    case 512: return launch_col<512>(kind, io, c, groups, s);
-    case 1024: return launch_col<1024>(kind, io, c, groups, s);
+    case 16: return launch_col<16>(kind, io, c, groups, s, grid_mode);
+    case 32: return launch_col<32>(kind, io, c, groups, s, grid_mode);
+    case 64: return launch_col<64>(kind, io, c, groups, s, grid_mode);
+    case 128: return launch_col<128>(kind, io, c, groups, s, grid_mode);
+    case 256: return launch_col<256>(kind, io, c, groups, s, grid_mode);
+    case 512: return launch_col<512>(kind, io, c, groups, s, grid_mode);
+    case 1024: return launch_col<1024>(kind, io, c, groups, s, grid_mode);
   }
   return hipErrorInvalidValue;
 }
@@ -336,6 +399,173 @@ hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream
     hipError_t e = dispatch_col(p.n1, COL_SPEC, 0, c, groups, s);
     if (e != hipSuccess) return e;
     e = dispatch_row(p.n2, ROW_SPEC, r, groups, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------- 2-D grids, multi-pass
+//
+// A grid row (b, d) holds a gL1 x gL2 grid, zero-padded (or, circular,
+// exactly) to P1 x P2 = n1 x 2*n2 and packed along its last axis into an
+// n1 x n2 complex array: the column pass above (GRID) transforms the first
+// axis, and the row kernel below transforms rows k1 and P1-k1 together --
+// the row holding each bin's Hermitian partner (-k1, -k2) -- with no
+// twiddle between the passes (a 2-D DFT).  Spectral step per bin, as on the
+// single-pass grid path: C'(k) = A C(k) + i B conj C(k'), A = Pg - s Qg,
+// B = c Qg from G = H(k)/M and G'' = H at the filter's partner (p = 0 pairs
+// with the packed axis' Nyquist plane), (s, c) = (sin, cos)(pi k2 / n2).
+// Spectrum layout: H/M at k1*n2 + k2, then the Nyquist plane at n1*n2 + k1.
+
+template <int N2> struct GridRowCfg {
+  static constexpr int E = 8;
+  static constexpr int TPR = N2 / E;                        // threads per row
+  static constexpr int RP = (2 * TPR >= 256) ? 1 : 256 / (2 * TPR);   // row pairs per workgroup
+  static constexpr int T = RP * 2 * TPR;
+  using R = typename Plan8<N2>::R;
+};
+
+struct GridRowArgs {
+  cf* work;
+  const cf* spec;
+  cf* spec_out;
+  int n1;
+  int64_t spec_stride;
+  int order, NORD, D, per_sample;
+  int r0;
+  int pairs_per_grid;   // n1 / 2
+};
+
+template <int N2, int KIND>
+__global__ void __launch_bounds__(GridRowCfg<N2>::T) k_grid_row(GridRowArgs a) {
+  using C = GridRowCfg<N2>;
+  constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E;
+  __shared__ cf smem[C::RP * 2 * N2];
+  const int pr = threadIdx.x / (2 * TPR), tb = threadIdx.x - pr * 2 * TPR;
+  const int b = tb / TPR, j = tb - b * TPR;
+  const int pair = blockIdx.x * C::RP + pr;
+  const int g = pair / a.pairs_per_grid, w = pair - g * a.pairs_per_grid;
+  const int n1 = a.n1;
+  const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
+  const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
+  const int mb = self_mirror ? b : 1 - b;
+  const int k1m = (n1 - k1) & (n1 - 1);
+  const int64_t NC = (int64_t)n1 * N2;
+  cf* row = a.work + (int64_t)g * NC + (int64_t)k1 * N2;
+  const RowLds lds{smem + (pr * 2 + b) * N2};
+  const RowLds ldsm{smem + (pr * 2 + mb) * N2};
+  BlockFFT<N2, E, typename C::R> fft;
+  fft.init(j);
+  cf u[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) u[i] = row[j + i * S2];
+  fft.template run<false>(u, lds, j);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+  __syncthreads();
+  const cf wb = twiddle<false>((uint32_t)j, (uint32_t)(2 * N2));     // W_{2 n2}^{k2}, k2 = j + i*S2
+  const float sc = 1.0f / (float)(2 * NC);
+  if constexpr (KIND == ROW_SPEC) {
+    cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k2 = j + i * S2;
+      const cf cm = ldsm((N2 - k2) & (N2 - 1));
+      out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], cm, cmul(wb, w2e<E>(i)), sc);
+      if (k2 == 0) out[NC + k1] = realfft_bin(u[i], cm, make_float2(-1.f, 0.f), sc);
+    }
+  } else {
+    const int rowid = a.r0 + g, bb = rowid / a.D, d = rowid - bb * a.D;
+    const int64_t f = a.per_sample ? ((int64_t)bb * a.NORD + a.order) * a.D + d : (int64_t)a.order * a.D + d;
+    const cf* gs = a.spec + f * a.spec_stride;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k2 = j + i * S2;
+      const cf cm = ldsm((N2 - k2) & (N2 - 1));
+      const cf G = gs[(int64_t)k1 * N2 + k2];
+      const cf Gm = (k2 == 0) ? gs[NC + k1m] : gs[(int64_t)k1m * N2 + (N2 - k2)];
+      const cf wk = cmul(wb, w2e<E>(i));          // (c, -s)
+      const float sn = -wk.y, cs = wk.x;
+      const cf Pg = make_float2(G.x + Gm.x, G.y - Gm.y);
+      const cf Qg = make_float2(G.x - Gm.x, G.y + Gm.y);
+      const cf A = make_float2(fmaf(-sn, Qg.x, Pg.x), fmaf(-sn, Qg.y, Pg.y));
+      const cf Bc = make_float2(cs * Qg.x, cs * Qg.y);
+      const cf z = u[i];
+      u[i] = make_float2(fmaf(A.x, z.x, fmaf(-A.y, z.y, fmaf(Bc.x, cm.y, -Bc.y * cm.x))),
+                         fmaf(A.x, z.y, fmaf(A.y, z.x, fmaf(Bc.x, cm.x, Bc.y * cm.y))));
+    }
+    fft.template run<true>(u, lds, j);
+#pragma unroll
+    for (int i = 0; i < E; ++i) row[j + i * S2] = u[i];
+  }
+}
+
+template <int N2>
+static hipError_t launch_grid_row(int kind, const GridRowArgs& r, int groups, hipStream_t s) {
+  using C = GridRowCfg<N2>;
+  const int pairs = groups * r.pairs_per_grid;
+  if (pairs % C::RP) return hipErrorInvalidValue;
+  const dim3 grid(pairs / C::RP), block(C::T);
+  if (kind == ROW_SPEC) hipLaunchKernelGGL((k_grid_row<N2, ROW_SPEC>), grid, block, 0, s, r);
+  else hipLaunchKernelGGL((k_grid_row<N2, ROW_CONV>), grid, block, 0, s, r);
+  return hipGetLastError();
+}
+
+static hipError_t dispatch_grid_row(int n2, int kind, const GridRowArgs& r, int groups, hipStream_t s) {
+  switch (n2) {
+    case 128: return launch_grid_row<128>(kind, r, groups, s);
+    case 256: return launch_grid_row<256>(kind, r, groups, s);
+    case 512: return launch_grid_row<512>(kind, r, groups, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t grid2d_forward(const NdArgs& a, hipStream_t s) {
+  const int n1 = a.P, n2 = a.P / 2;
+  const int W = col_width(n1);
+  if (W == 0 || a.ndim != 2) return hipErrorInvalidValue;
+  ColArgs c{};
+  c.v = a.v; c.y = a.y; c.work = (cf*)a.work; c.n2 = n2;
+  c.n_col_blocks = (n2 + W - 1) / W;
+  c.gL1 = a.Lo; c.gL2 = a.Ll; c.gcirc = a.circular;
+  GridRowArgs r{};
+  r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.n1 = n1; r.spec_stride = a.spec_stride;
+  r.NORD = a.NORD; r.D = a.D; r.per_sample = a.per_sample; r.pairs_per_grid = n1 / 2;
+  for (int r0 = 0; r0 < a.rows; r0 += a.rows_per_group) {
+    const int groups = (a.rows - r0 < a.rows_per_group) ? a.rows - r0 : a.rows_per_group;
+    c.r0 = r0; r.r0 = r0;
+    hipError_t e = dispatch_col(n1, COL_FIRST, a.io, c, groups, s, true);
+    if (e != hipSuccess) return e;
+    for (int n = 0; n < a.NORD; ++n) {
+      r.order = n;
+      e = dispatch_grid_row(n2, ROW_CONV, r, groups, s);
+      if (e != hipSuccess) return e;
+      c.xg = a.x.p[n];
+      e = dispatch_col(n1, n == a.NORD - 1 ? COL_LAST : COL_MID, a.io, c, groups, s, true);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s) {
+  const int n1 = a.P, n2 = a.P / 2;
+  const int W = col_width(n1);
+  if (W == 0 || a.ndim != 2) return hipErrorInvalidValue;
+  ColArgs c{};
+  c.h = a.kernel; c.work = (cf*)a.work; c.n2 = n2;
+  c.n_col_blocks = (n2 + W - 1) / W;
+  c.gL1 = a.Lo; c.gL2 = a.Ll; c.gcirc = a.circular;
+  GridRowArgs r{};
+  r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = n1; r.spec_stride = a.spec_stride;
+  r.pairs_per_grid = n1 / 2;
+  for (int r0 = 0; r0 < a.rows; r0 += a.rows_per_group) {
+    const int groups = (a.rows - r0 < a.rows_per_group) ? a.rows - r0 : a.rows_per_group;
+    c.r0 = r0; r.r0 = r0;
+    hipError_t e = dispatch_col(n1, COL_SPEC, 0, c, groups, s, true);
+    if (e != hipSuccess) return e;
+    e = dispatch_grid_row(n2, ROW_SPEC, r, groups, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

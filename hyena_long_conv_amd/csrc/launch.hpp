@@ -124,10 +124,15 @@ struct NdArgs {
   XPtrsHost x;
   void* y;
   int D, NORD, per_sample, io;
+  // multi-pass grids (2-D, P >= 256): intermediate of rows_per_group grids
+  void* work;
+  int rows_per_group;
 };
 
 hipError_t nd_spectrum(const NdArgs& a, hipStream_t s);
 hipError_t nd_forward(const NdArgs& a, hipStream_t s);
+hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s);   // kernels_fourstep.hip
+hipError_t grid2d_forward(const NdArgs& a, hipStream_t s);
 
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);

@@ -301,10 +301,15 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
  *   circular:     c[t] = sum_s K[(t - s) mod dims] z[s]; the kernel has the
  *                 grid's shape.
  * Supported: the FFT grid is a cube of side P, a power of two with, per
- * dimension count, 16 <= P <= 128 (2-D) or 8 <= P <= 32 (3-D).  Non-circular
- * grids take the smallest such P >= 2*max(dims)-1 (so sides up to 64 in 2-D
- * and 16 in 3-D); circular grids need every side equal to one such P.  Other
- * shapes return HYENA_ERR_UNSUPPORTED (a side outside 1..4096: SHAPE).
+ * dimension count, 16 <= P <= 1024 (2-D) or 8 <= P <= 32 (3-D).  Non-circular
+ * grids take the smallest such P >= 2*max(dims)-1 (so sides up to 512 in
+ * 2-D and 16 in 3-D); circular grids need every side equal to one such P.
+ * Other shapes return HYENA_ERR_UNSUPPORTED (a side outside 1..4096: SHAPE).
+ * Up to P = 128 (2-D) and for 3-D one workgroup holds a grid for all orders
+ * and no workspace is used; 2-D grids with P >= 256 run as column and row
+ * passes over a workspace of hyena_nd_workspace_bytes (at least P*P/2
+ * complex64 values; a smaller one than returned means more, smaller pass
+ * groups).
  *
  * hyena_nd_plan: writes P.
  * hyena_nd_spectrum_bytes: bytes of the spectrum of `rows` kernels (-1 for
@@ -313,20 +318,27 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
  *   (device, hyena_nd_spectrum_bytes).  Row r is the kernel n*D + d for the
  *   shared form, (b*N + n)*D + d for per-sample kernels (the summary's
  *   input-dependent kernels, one per sample).
+ * hyena_nd_workspace_bytes: workspace for `rows` grids (kernel rows for the
+ *   spectrum, B*D for the forward); 0 on the single-pass shapes, -1 for an
+ *   invalid or unsupported shape.
  * hyena_nd_forward: v, each x[n] (host array of N device pointers) and y are
  *   [B][D][dims...] in `io`; spec from hyena_nd_filter_spectrum with N*D
  *   rows (per_sample = 0) or B*N*D rows (per_sample = 1).  1 <= N <= 8.
- *   Pointers 16-byte aligned (HYENA_ERR_ALIGN); y must not overlap v, any
- *   x[n] or spec (HYENA_ERR_ALIAS).  No workspace, no allocation; the work
- *   is enqueued on `stream`.
+ *   Pointers 16-byte aligned (HYENA_ERR_ALIGN); y and the workspace must not
+ *   overlap v, any x[n], spec or each other (HYENA_ERR_ALIAS); a missing or
+ *   too small workspace where one is needed is HYENA_ERR_WORKSPACE.  No
+ *   allocation; the work is enqueued on `stream`.
  * ---------------------------------------------------------------------- */
 hyena_status hyena_nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, int64_t* padded_side);
 int64_t hyena_nd_spectrum_bytes(int32_t rows, int32_t ndim, const int64_t* dims, int32_t circular);
+int64_t hyena_nd_workspace_bytes(int64_t rows, int32_t ndim, const int64_t* dims, int32_t circular);
 hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t ndim, const int64_t* dims,
-                                      int32_t circular, void* spec, void* stream);
+                                      int32_t circular, void* spec, void* workspace, int64_t workspace_bytes,
+                                      void* stream);
 hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
                               int32_t D, int32_t N, int32_t ndim, const int64_t* dims, int32_t circular,
-                              int32_t per_sample, hyena_dtype io, void* stream);
+                              int32_t per_sample, hyena_dtype io, void* workspace, int64_t workspace_bytes,
+                              void* stream);
 
 /* Static description of a status code. */
 const char* hyena_status_str(hyena_status s);

@@ -257,7 +257,9 @@ def test_plan_circular_rejects_other_lengths():
     assert H.lib().hyena_plan_ex(256, 7, ctypes.byref(H.PlanInfo())) == UNSUP
 
 
-@pytest.mark.parametrize("dims,circ,P", [((8, 8), False, 16), ((1, 1), False, 16), ((9, 9), False, 32),
+@pytest.mark.parametrize("dims,circ,P", [((65, 4), False, 256), ((512, 3), False, 1024), ((256, 256), True, 256),
+                                         ((1024, 1024), True, 1024),
+                                         ((8, 8), False, 16), ((1, 1), False, 16), ((9, 9), False, 32),
                                          ((56, 56), False, 128), ((64, 3), False, 128), ((4, 4, 4), False, 8),
                                          ((5, 2, 3), False, 16), ((16, 16, 16), False, 32), ((16, 16), True, 16),
                                          ((128, 128), True, 128), ((8, 8, 8), True, 8), ((32, 32, 32), True, 32)])
@@ -267,11 +269,14 @@ def test_nd_plan(dims, circ, P):
     Q = NC // (P // 2)
     stride = -(-(NC + Q) // 64) * 64
     assert H.nd_spectrum_bytes(6, dims, circ) == 6 * stride * 8
+    # multi-pass 2-D grids (P >= 256) need a workspace of whole complex grids; single-pass ones none
+    ws = H.nd_workspace_bytes(6, dims, circ)
+    assert (ws >= NC * 8 and ws % (NC * 8) == 0) if (len(dims) == 2 and P >= 256) else ws == 0
 
 
 def test_nd_plan_rejects_unsupported():
-    for dims, circ, code in [((65, 4), False, UNSUP), ((17, 1, 1), False, UNSUP), ((32, 16), True, UNSUP),
-                             ((8, 8), True, UNSUP), ((256, 256), True, UNSUP), ((12, 12), True, UNSUP),
+    for dims, circ, code in [((513, 4), False, UNSUP), ((17, 1, 1), False, UNSUP), ((32, 16), True, UNSUP),
+                             ((8, 8), True, UNSUP), ((2048, 2048), True, UNSUP), ((12, 12), True, UNSUP),
                              ((4,), False, UNSUP), ((4, 4, 4, 4), False, UNSUP), ((0, 4), False, SHAPE),
                              ((5000, 4), False, SHAPE)]:
         with pytest.raises(H.HyenaError) as e:
@@ -283,12 +288,12 @@ def test_nd_plan_rejects_unsupported():
 def test_nd_calls_reject_bad_arguments():
     lib = H.lib()
     d2 = (ctypes.c_int64 * 2)(16, 16)
-    bad = (ctypes.c_int64 * 2)(100, 16)
+    bad = (ctypes.c_int64 * 2)(600, 16)
     xs = (vp * 2)(Bp, C)
     fwd = lambda **k: lib.hyena_nd_forward(
         vp(k.get("v", A)), k.get("x", xs), vp(k.get("spec", Dp)), vp(k.get("y", Y)), k.get("B", 2),
         k.get("D", 3), k.get("N", 2), k.get("ndim", 2), k.get("dims", d2), k.get("circ", 0), k.get("ps", 0),
-        k.get("io", 0), None)
+        k.get("io", 0), vp(k.get("ws", 0)), k.get("wsb", 0), None)
     assert fwd(v=0) == NULL
     assert fwd(x=None) == NULL
     assert fwd(x=(vp * 2)(Bp, 0)) == NULL
@@ -305,8 +310,19 @@ def test_nd_calls_reject_bad_arguments():
     assert fwd(y=A) == ALIAS
     assert fwd(y=C + 64) == ALIAS
     assert fwd(y=Dp + 16) == ALIAS
-    assert lib.hyena_nd_filter_spectrum(None, 4, 2, d2, 0, vp(Dp), None) == NULL
-    assert lib.hyena_nd_filter_spectrum(vp(A), 0, 2, d2, 0, vp(Dp), None) == SHAPE
-    assert lib.hyena_nd_filter_spectrum(vp(A), 4, 2, bad, 0, vp(Dp), None) == UNSUP
-    assert lib.hyena_nd_filter_spectrum(vp(A + 8), 4, 2, d2, 0, vp(Dp), None) == ALIGN
-    assert lib.hyena_nd_filter_spectrum(vp(A), 4, 2, d2, 0, vp(A + 64), None) == ALIAS
+    big = (ctypes.c_int64 * 2)(200, 200)                        # P = 512: multi-pass, needs a workspace
+    assert fwd(dims=big) == WS
+    assert fwd(dims=big, ws=W, wsb=1024) == WS
+    assert fwd(dims=big, ws=W + 8, wsb=1 << 24) == ALIGN
+    assert fwd(dims=big, ws=A, wsb=1 << 24) == ALIAS
+    sp = lambda k=A, rows=4, dims=d2, spec=Dp, ws=0, wsb=0: lib.hyena_nd_filter_spectrum(
+        vp(k), rows, 2, dims, 0, vp(spec), vp(ws), wsb, None)
+    assert sp(k=0) == NULL
+    assert sp(rows=0) == SHAPE
+    assert sp(dims=bad) == UNSUP
+    assert sp(k=A + 8) == ALIGN
+    assert sp(spec=A + 64) == ALIAS
+    assert sp(dims=big) == WS
+    assert sp(dims=big, ws=Dp + 64, wsb=1 << 24) == ALIAS
+    assert H.nd_workspace_bytes(4, (200, 200)) >= 512 * 256 * 8
+    assert H.nd_workspace_bytes(4, (8, 8)) == 0

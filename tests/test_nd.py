@@ -78,6 +78,14 @@ CASES = [
     (2, 3, 2, (12, 10), False, "fp32", True),         # per-sample kernels
     (2, 2, 2, (16, 16), True, "bf16", True),
     (2, 2, 1, (6, 5, 4), False, "fp32", True),
+    # multi-pass 2-D grids (P >= 256): column and row passes over a workspace
+    (2, 2, 2, (100, 130), False, "fp32", False),      # P = 256
+    (3, 1, 2, (200, 255), False, "fp32", False),      # P = 512, odd last side
+    (1, 1, 1, (300, 17), False, "fp32", False),       # P = 1024
+    (2, 1, 2, (224, 224), False, "bf16", False),      # image grid
+    (2, 1, 2, (256, 256), True, "fp32", False),
+    (2, 1, 1, (512, 512), True, "fp32", False),
+    (2, 2, 2, (120, 90), False, "fp32", True),        # per-sample kernels
 ]
 
 
@@ -89,7 +97,7 @@ def test_nd_forward_matches_oracle(N, B, D, dims, circ, io, ps):
     assert err <= _tol(cfg), f"max normalised error {err:.3e}"
 
 
-@pytest.mark.parametrize("name", ["G2", "G3", "GP"])
+@pytest.mark.parametrize("name", ["G2", "G3", "GP", "G4", "GP2"])
 def test_nd_configs_sampled(name):
     """The measured grid workloads at full size, checked on sampled grids."""
     cfg = GRID_CONFIGS[name]
@@ -133,12 +141,24 @@ def test_nd_repeat_calls_identical():
     assert torch.equal(a, b)
 
 
+def test_nd_multipass_small_workspace_matches():
+    """A workspace smaller than the one asked for only splits the passes into more groups."""
+    cfg = GridConfig("w", 2, 3, 2, (150, 150), False, "fp32", 9)
+    v, xs = make_grid_activations(cfg, DEV)
+    K = torch.from_numpy(make_grid_kernel(cfg)).to(DEV)
+    spec = H.nd_filter_spectrum(K, cfg.dims)
+    y_full = H.nd_forward(v, xs, spec).clone()
+    one = torch.empty(512 * 256 * 8, dtype=torch.uint8, device=DEV)        # one grid per pass group
+    y_one = H.nd_forward(v, xs, spec, workspace=one)
+    torch.cuda.synchronize()
+    assert torch.equal(y_full, y_one)
+
+
 def test_nd_errors():
     dev = DEV
-    v = torch.zeros((1, 1, 65, 8), device=dev)
-    K = torch.zeros((1, 1, 129, 15), device=dev)
-    with pytest.raises(H.HyenaError):           # needs P = 256 > 128
-        H.nd_filter_spectrum(K, (65, 8))
+    K = torch.zeros((1, 1, 1025, 15), device=dev)
+    with pytest.raises(H.HyenaError):           # needs P = 2048 > 1024
+        H.nd_filter_spectrum(K, (513, 8))
     v = torch.zeros((1, 1, 32, 16), device=dev)
     with pytest.raises(H.HyenaError):           # circular needs equal power-of-two sides
         H.nd_filter_spectrum(torch.zeros((1, 1, 32, 16), device=dev), (32, 16), circular=True)

@@ -217,6 +217,10 @@ GRID_CONFIGS = {
                      desc="order-2, B=2, D=128, 16^3 volume, non-circular, bf16 I/O"),
     "GP": GridConfig("GP", 2, 16, 64, (128, 128), True, "fp32", 24,
                      desc="order-2, B=16, D=64, 128x128 periodic field, circular, fp32"),
+    "G4": GridConfig("G4", 2, 4, 96, (224, 224), False, "bf16", 25,
+                     desc="order-2, B=4, D=96, 224x224 pixel grid, non-circular, bf16 I/O (multi-pass)"),
+    "GP2": GridConfig("GP2", 2, 2, 32, (512, 512), True, "fp32", 26,
+                      desc="order-2, B=2, D=32, 512x512 periodic field, circular, fp32 (multi-pass)"),
 }
 
 
