@@ -524,9 +524,10 @@ def run_grid(args, torch, H, dev):
     else:
         roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": mb / t / HBM_PEAK}
-    multi = cfg.ndim == 2 and P > 128
+    multi = P > (128 if cfg.ndim == 2 else 32)
+    passes = "k_grid_row" if cfg.ndim == 2 else "k_grid_plane"
     roof.update({"traffic": measured_traffic(cfg.name),
-                 "kernel": ("2-D grid passes (k_col grid mode + k_grid_row, 2N+1 passes per pass group)" if multi
+                 "kernel": (f"grid passes (k_col grid mode + {passes}, 2N+1 passes per pass group)" if multi
                             else "k_nd_forward (one launch per step)"),
                  "launches_per_step": None if multi else 1,
                  "hbm_frac": mb / t / HBM_PEAK, "hbm_GBps": mb / t / 1e9, "copy_GBps": copy_bps / 1e9,
@@ -569,7 +570,7 @@ def main(argv=None):
     ap.add_argument("--block", action="store_true",
                     help="time the whole block (in-projection + short convolutions, operator, out-projection)")
     ap.add_argument("--grid", default=None, metavar="NAME",
-                    help="time the grid convolutions (HyenaND) on workload G1, G2, G3, GP, G4 or GP2")
+                    help="time the grid convolutions (HyenaND) on workload G1, G2, G3, GP, G4, GP2 or G5")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for counter scaling)")
     args = ap.parse_args(argv)

@@ -65,8 +65,8 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
     lmax = dims[a] > lmax ? dims[a] : lmax;
     points *= dims[a];
   }
-  // single pass: 2-D up to 128, 3-D up to 32; 2-D multi-pass 256..1024
-  const int pmin = ndim == 2 ? 16 : 8, pmax = ndim == 2 ? 1024 : 32;
+  // single pass: 2-D up to 128, 3-D up to 32; multi-pass: 2-D 256..1024, 3-D 64 and 128
+  const int pmin = ndim == 2 ? 16 : 8, pmax = ndim == 2 ? 1024 : 128;
   int64_t P;
   if (circular) {
     P = dims[0];
@@ -88,7 +88,7 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
   p.NC = p.Q * (P / 2);
   p.stride = round_up(p.NC + p.Q, 64);
   p.points = points;
-  p.multi = ndim == 2 && P > 128;
+  p.multi = (ndim == 2 && P > 128) || (ndim == 3 && P > 32);
   *out = p;
   return 0;
 }
@@ -646,7 +646,9 @@ hyena_status hyena_nd_filter_spectrum(const float* kernel, int32_t rows, int32_t
   a.rows = rows;
   a.work = workspace;
   a.rows_per_group = group;
-  const hipError_t e = p.multi ? grid2d_spectrum(a, (hipStream_t)stream) : nd_spectrum(a, (hipStream_t)stream);
+  const hipError_t e = !p.multi ? nd_spectrum(a, (hipStream_t)stream)
+                                : (p.ndim == 2 ? grid2d_spectrum(a, (hipStream_t)stream)
+                                               : grid3d_spectrum(a, (hipStream_t)stream));
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 
@@ -698,7 +700,9 @@ hyena_status hyena_nd_forward(const void* v, const void* const* x, const void* s
   a.NORD = N;
   a.per_sample = per_sample;
   a.io = (io == HYENA_FP32) ? 0 : 1;
-  const hipError_t e = p.multi ? grid2d_forward(a, (hipStream_t)stream) : nd_forward(a, (hipStream_t)stream);
+  const hipError_t e = !p.multi ? nd_forward(a, (hipStream_t)stream)
+                                : (p.ndim == 2 ? grid2d_forward(a, (hipStream_t)stream)
+                                               : grid3d_forward(a, (hipStream_t)stream));
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
 }
 

@@ -64,24 +64,29 @@ struct ColArgs {
   int n2;
   int r0;              // first row of this launch
   int n_col_blocks;
-  // grids (GRID kernels): a 2-D grid gL1 x gL2 per row, padded to n1 x 2*n2
-  int64_t gL1, gL2;
+  // grids (GRID kernels): a grid gL1 x gLm x gL2 per row (gLm = 1 for 2-D),
+  // padded to n1 x (n1 x) 2*NL, columns col = i2*NL + m (m on the packed axis)
+  int64_t gL1, gLm, gL2;
+  int gNLs;            // log2 NL
   int gcirc;           // SPEC: kernel of the grid's shape (else extent 2L-1 per axis)
 };
 
-// Kernel value at padded-grid position (i1, i2) of an n1 x P2 grid: offset
-// o at o mod P on every axis (non-circular extent 2L-1, index o + L - 1).
-__device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, int i1, int i2, int n1, int P2,
-                                                int64_t L1, int64_t L2, bool circ) {
-  int64_t a, b, e2;
-  if (circ) {
-    a = i1; b = i2; e2 = L2;
-  } else {
-    a = i1 < L1 ? i1 + L1 - 1 : (i1 > n1 - L1 ? i1 - n1 + L1 - 1 : -1);
-    b = i2 < L2 ? i2 + L2 - 1 : (i2 > P2 - L2 ? i2 - P2 + L2 - 1 : -1);
-    e2 = 2 * L2 - 1;
-  }
-  return (a >= 0 && b >= 0) ? k[koff + a * e2 + b] : 0.f;
+// Kernel index of padded position n on an axis of padded size P and grid
+// side L (offset o at o mod P; non-circular index o + L - 1; -1: gap).
+__device__ __forceinline__ int64_t grid_kidx(int64_t n, int64_t P, int64_t L, bool circ) {
+  if (circ) return n;
+  return n < L ? n + L - 1 : (n > P - L ? n - P + L - 1 : -1);
+}
+
+// Kernel value at padded-grid position (i1, i2, i3) of an n1 x Pm x P3 grid
+// (2-D: Pm = Lm = 1, i2 = 0).
+__device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, int i1, int i2, int i3, int n1,
+                                                int Pm, int P3, int64_t L1, int64_t Lm, int64_t L3, bool circ) {
+  const int64_t a = grid_kidx(i1, n1, L1, circ);
+  const int64_t b = Lm == 1 && Pm == 1 ? 0 : grid_kidx(i2, Pm, Lm, circ);
+  const int64_t c = grid_kidx(i3, P3, L3, circ);
+  const int64_t em = circ ? Lm : 2 * Lm - 1, e3 = circ ? L3 : 2 * L3 - 1;
+  return (a >= 0 && b >= 0 && c >= 0) ? k[koff + (a * em + b) * e3 + c] : 0.f;
 }
 
 // GRID: each row is a 2-D grid gL1 x gL2 (row-major) zero-padded to
@@ -99,7 +104,8 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   const bool valid = col < a.n2;
   const int64_t N = (int64_t)N1 * a.n2;
   cf* buf = a.work + (int64_t)g * N;
-  const int64_t off = GRID ? (int64_t)(a.r0 + g) * a.gL1 * a.gL2 : (int64_t)(a.r0 + g) * a.L;
+  const int64_t off = GRID ? (int64_t)(a.r0 + g) * a.gL1 * a.gLm * a.gL2 : (int64_t)(a.r0 + g) * a.L;
+  const int gi2 = col >> a.gNLs, gm = col & ((1 << a.gNLs) - 1);     // GRID: column -> (i2, packed m)
   const ColLds<W> lds{smem + c};
   BlockFFT<N1, E, typename C::R> fft;
   fft.init(j);
@@ -107,10 +113,10 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   // element pair of column point i1: row offset, first real index, row length
   const auto at = [&](int i1, int64_t& ro, int64_t& t, int64_t& len) {
     if constexpr (GRID) {
-      ro = off + (int64_t)i1 * a.gL2;
-      t = 2 * (int64_t)col;
+      ro = off + ((int64_t)i1 * a.gLm + gi2) * a.gL2;
+      t = 2 * (int64_t)gm;
       len = a.gL2;
-      return valid && i1 < a.gL1;
+      return valid && i1 < a.gL1 && gi2 < a.gLm;
     } else {
       ro = off;
       t = 2 * ((int64_t)a.n2 * i1 + col);
@@ -120,15 +126,17 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   };
 
   if constexpr (KIND == COL_SPEC && GRID) {
-    const int64_t e = a.gcirc ? a.gL1 * a.gL2 : (2 * a.gL1 - 1) * (2 * a.gL2 - 1);
+    const int64_t e = a.gcirc ? a.gL1 * a.gLm * a.gL2 : (2 * a.gL1 - 1) * (2 * a.gLm - 1) * (2 * a.gL2 - 1);
     const int64_t koff = (int64_t)(a.r0 + g) * e;
+    const int P3 = 2 << a.gNLs, Pm = a.gLm == 1 && (a.n2 >> a.gNLs) == 1 ? 1 : N1;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int i1 = j + i * S1;
       u[i] = make_float2(0.f, 0.f);
       if (valid)
-        u[i] = make_float2(grid_kernel_at(a.h, koff, i1, 2 * col, N1, 2 * a.n2, a.gL1, a.gL2, a.gcirc),
-                           grid_kernel_at(a.h, koff, i1, 2 * col + 1, N1, 2 * a.n2, a.gL1, a.gL2, a.gcirc));
+        u[i] = make_float2(
+            grid_kernel_at(a.h, koff, i1, gi2, 2 * gm, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc),
+            grid_kernel_at(a.h, koff, i1, gi2, 2 * gm + 1, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc));
     }
   } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
 #pragma unroll
@@ -287,8 +295,9 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
   }
 }
 
-// Grid columns exist for the first axes the grid path plans (256..1024).
-constexpr bool grid_col_ok(int n1) { return n1 >= 256; }
+// Grid columns exist for the first axes the grid paths plan (2-D 256..1024,
+// 3-D 64 and 128).
+constexpr bool grid_col_ok(int n1) { return n1 >= 64; }
 
 template <int N1>
 static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s, bool grid_mode = false) {
@@ -528,7 +537,7 @@ hipError_t grid2d_forward(const NdArgs& a, hipStream_t s) {
   ColArgs c{};
   c.v = a.v; c.y = a.y; c.work = (cf*)a.work; c.n2 = n2;
   c.n_col_blocks = (n2 + W - 1) / W;
-  c.gL1 = a.Lo; c.gL2 = a.Ll; c.gcirc = a.circular;
+  c.gL1 = a.Lo; c.gLm = 1; c.gL2 = a.Ll; c.gNLs = ilog2(n2); c.gcirc = a.circular;
   GridRowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.n1 = n1; r.spec_stride = a.spec_stride;
   r.NORD = a.NORD; r.D = a.D; r.per_sample = a.per_sample; r.pairs_per_grid = n1 / 2;
@@ -556,7 +565,7 @@ hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s) {
   ColArgs c{};
   c.h = a.kernel; c.work = (cf*)a.work; c.n2 = n2;
   c.n_col_blocks = (n2 + W - 1) / W;
-  c.gL1 = a.Lo; c.gL2 = a.Ll; c.gcirc = a.circular;
+  c.gL1 = a.Lo; c.gLm = 1; c.gL2 = a.Ll; c.gNLs = ilog2(n2); c.gcirc = a.circular;
   GridRowArgs r{};
   r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = n1; r.spec_stride = a.spec_stride;
   r.pairs_per_grid = n1 / 2;
@@ -566,6 +575,52 @@ hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s) {
     hipError_t e = dispatch_col(n1, COL_SPEC, 0, c, groups, s, true);
     if (e != hipSuccess) return e;
     e = dispatch_grid_row(n2, ROW_SPEC, r, groups, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// 3-D grids, multi-pass: the column pass transforms the first axis (columns
+// = (i2, m) of a P x P/2 plane), and the plane pass (kernels_nd.hip) takes
+// planes k1 and P-k1 together through a 2-D FFT, the spectral step and back.
+hipError_t grid3d_forward(const NdArgs& a, hipStream_t s) {
+  const int P = a.P, NL = P / 2, n2 = P * NL;
+  const int W = col_width(P);
+  if (W == 0 || a.ndim != 3) return hipErrorInvalidValue;
+  ColArgs c{};
+  c.v = a.v; c.y = a.y; c.work = (cf*)a.work; c.n2 = n2;
+  c.n_col_blocks = (n2 + W - 1) / W;
+  c.gL1 = a.Lo; c.gLm = a.Lm; c.gL2 = a.Ll; c.gNLs = ilog2(NL); c.gcirc = a.circular;
+  for (int r0 = 0; r0 < a.rows; r0 += a.rows_per_group) {
+    const int groups = (a.rows - r0 < a.rows_per_group) ? a.rows - r0 : a.rows_per_group;
+    c.r0 = r0;
+    hipError_t e = dispatch_col(P, COL_FIRST, a.io, c, groups, s, true);
+    if (e != hipSuccess) return e;
+    for (int n = 0; n < a.NORD; ++n) {
+      e = grid_plane_pass(a, r0, groups, n, false, s);
+      if (e != hipSuccess) return e;
+      c.xg = a.x.p[n];
+      e = dispatch_col(P, n == a.NORD - 1 ? COL_LAST : COL_MID, a.io, c, groups, s, true);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t grid3d_spectrum(const NdArgs& a, hipStream_t s) {
+  const int P = a.P, NL = P / 2, n2 = P * NL;
+  const int W = col_width(P);
+  if (W == 0 || a.ndim != 3) return hipErrorInvalidValue;
+  ColArgs c{};
+  c.h = a.kernel; c.work = (cf*)a.work; c.n2 = n2;
+  c.n_col_blocks = (n2 + W - 1) / W;
+  c.gL1 = a.Lo; c.gLm = a.Lm; c.gL2 = a.Ll; c.gNLs = ilog2(NL); c.gcirc = a.circular;
+  for (int r0 = 0; r0 < a.rows; r0 += a.rows_per_group) {
+    const int groups = (a.rows - r0 < a.rows_per_group) ? a.rows - r0 : a.rows_per_group;
+    c.r0 = r0;
+    hipError_t e = dispatch_col(P, COL_SPEC, 0, c, groups, s, true);
+    if (e != hipSuccess) return e;
+    e = grid_plane_pass(a, r0, groups, 0, true, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

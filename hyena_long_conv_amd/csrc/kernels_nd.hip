@@ -345,6 +345,120 @@ k_nd_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, v
   }
 }
 
+// Plane pass of the 3-D multi-pass grids: after the column pass over the
+// first axis, plane k1 of a grid is a P x P/2 complex array (rows i2, packed
+// columns m).  A workgroup takes planes k1 and P-k1 (each bin's Hermitian
+// partner (-k1, -k2, -k3) lies in the mirror plane; planes 0 and P/2 are
+// their own mirrors and go together), runs the 2-D FFT of each (the grid
+// FFT above, two axes), the per-bin spectral step, and the inverse 2-D FFT.
+// Spectrum layout: H/M of plane k1 at k1*NCp + k (k in the plane FFT's
+// reversed layout), then the packed axis' Nyquist plane at NC + k1*P + a.
+struct PlaneArgs {
+  cf* work;
+  const cf* spec;
+  cf* spec_out;
+  int64_t spec_stride;
+  int order, NORD, D, per_sample, r0;
+};
+
+template <int P, bool SPEC>
+__global__ void __launch_bounds__((2 * NdPlan<2, P, false>::T)) k_grid_plane(PlaneArgs a) {
+  using PL = NdPlan<2, P, false>;
+  constexpr int E = PL::E, S = PL::S, NCP = PL::NC, NL = PL::NL, T = PL::T;
+  constexpr int64_t NC = (int64_t)P * NCP;
+  __shared__ cf smem[2 * NCP];
+  __shared__ float2 tws[NL];
+  const int b = threadIdx.x / T, j = threadIdx.x - b * T;
+  const int w = blockIdx.x % (P / 2), g = blockIdx.x / (P / 2);
+  const int k1 = (b == 0) ? w : (w == 0 ? P / 2 : P - w);
+  const bool self_mirror = (k1 == 0) || (2 * k1 == P);
+  const int mb = self_mirror ? b : 1 - b;
+  const int k1m = (P - k1) & (P - 1);
+  const typename PL::Lds lds{smem + b * NCP}, ldsm{smem + mb * NCP};
+  cf* plane = a.work + (int64_t)g * NC + (int64_t)k1 * NCP;
+  for (int p = threadIdx.x; p < NL; p += 2 * T) {
+    float sn, cs;
+    sincospif((float)p / (float)NL, &sn, &cs);
+    tws[p] = make_float2(sn, cs);
+  }
+  NdFFT<NCP, E, typename PL::RF, typename PL::BF> ff;
+  ff.init(j);
+  cf u[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) u[i] = plane[j + i * S];
+  ff.template run<false>(u, lds, j);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) lds(j + i * S) = u[i];
+  __syncthreads();
+  const float sc = 1.0f / (float)(2 * NC);
+  if constexpr (SPEC) {
+    cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k = j + i * S;
+      const int ka = k & (P - 1), p = k >> PL::LQ;
+      const int na = nd_neg_other<2, P>(ka);
+      const cf cm = ldsm(na + P * ((NL - p) & (NL - 1)));
+      const float2 t = tws[p];
+      out[(int64_t)k1 * NCP + k] = realfft_bin(u[i], cm, make_float2(t.y, -t.x), sc);
+      if (p == 0) out[NC + (int64_t)k1 * P + ka] = realfft_bin(u[i], cm, make_float2(-1.f, 0.f), sc);
+    }
+  } else {
+    const int rowid = a.r0 + g, bb = rowid / a.D, d = rowid - bb * a.D;
+    const int64_t f = a.per_sample ? ((int64_t)bb * a.NORD + a.order) * a.D + d : (int64_t)a.order * a.D + d;
+    const cf* gs = a.spec + f * a.spec_stride;
+    constexpr int CH = E > 8 ? 4 : E;       // bins whose filter values are in flight together
+#pragma unroll
+    for (int i0 = 0; i0 < E; i0 += CH) {
+      const int jc = (CH < E) ? fresh(j) : j;
+      cf G[CH], Gm[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int k = jc + (i0 + c) * S;
+        const int ka = k & (P - 1), p = k >> PL::LQ;
+        const int na = nd_neg_other<2, P>(ka);
+        G[c] = gs[(int64_t)k1 * NCP + k];
+        Gm[c] = (p == 0) ? gs[NC + (int64_t)k1m * P + na] : gs[(int64_t)k1m * NCP + na + P * (NL - p)];
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int i = i0 + c, k = jc + i * S;
+        const int ka = k & (P - 1), p = k >> PL::LQ;
+        const cf cm = ldsm(nd_neg_other<2, P>(ka) + P * ((NL - p) & (NL - 1)));
+        const float2 t = tws[p];
+        const cf Pg = make_float2(G[c].x + Gm[c].x, G[c].y - Gm[c].y);
+        const cf Qg = make_float2(G[c].x - Gm[c].x, G[c].y + Gm[c].y);
+        const cf A = make_float2(fmaf(-t.x, Qg.x, Pg.x), fmaf(-t.x, Qg.y, Pg.y));
+        const cf Bc = make_float2(t.y * Qg.x, t.y * Qg.y);
+        const cf z = u[i];
+        u[i] = make_float2(fmaf(A.x, z.x, fmaf(-A.y, z.y, fmaf(Bc.x, cm.y, -Bc.y * cm.x))),
+                           fmaf(A.x, z.y, fmaf(A.y, z.x, fmaf(Bc.x, cm.x, Bc.y * cm.y))));
+      }
+    }
+    // the inverse's twiddles are made here, so they are not live during the step above
+    NdFFT<NCP, E, typename PL::RI, typename PL::BI> fi;
+    fi.init(fresh(j));
+    fi.template run<true>(u, lds, j);
+#pragma unroll
+    for (int i = 0; i < E; ++i) plane[j + i * S] = u[i];
+  }
+}
+
+template <int P>
+hipError_t launch_grid_plane(const NdArgs& a, int r0, int groups, int n, bool spec, hipStream_t s) {
+  PlaneArgs pa{};
+  pa.work = (cf*)a.work;
+  pa.spec = (const cf*)a.spec;
+  pa.spec_out = (cf*)a.spec;
+  pa.spec_stride = a.spec_stride;
+  pa.order = n; pa.NORD = a.NORD; pa.D = a.D; pa.per_sample = a.per_sample; pa.r0 = r0;
+  const dim3 grid((unsigned)(groups * (P / 2))), block(2 * NdPlan<2, P, false>::T);
+  if (spec) hipLaunchKernelGGL((k_grid_plane<P, true>), grid, block, 0, s, pa);
+  else hipLaunchKernelGGL((k_grid_plane<P, false>), grid, block, 0, s, pa);
+  return hipGetLastError();
+}
+
 template <int NDIM, int P>
 hipError_t launch_nd_spectrum(const NdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.rows);
@@ -414,6 +528,14 @@ hipError_t nd_forward(const NdArgs& a, hipStream_t s) {
       case 16: return launch_nd_forward<3, 16>(a, s);
       case 32: return launch_nd_forward<3, 32>(a, s);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t grid_plane_pass(const NdArgs& a, int r0, int groups, int n, bool spec, hipStream_t s) {
+  switch (a.P) {
+    case 64: return launch_grid_plane<64>(a, r0, groups, n, spec, s);
+    case 128: return launch_grid_plane<128>(a, r0, groups, n, spec, s);
   }
   return hipErrorInvalidValue;
 }

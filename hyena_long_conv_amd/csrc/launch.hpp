@@ -133,6 +133,11 @@ hipError_t nd_spectrum(const NdArgs& a, hipStream_t s);
 hipError_t nd_forward(const NdArgs& a, hipStream_t s);
 hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s);   // kernels_fourstep.hip
 hipError_t grid2d_forward(const NdArgs& a, hipStream_t s);
+hipError_t grid3d_spectrum(const NdArgs& a, hipStream_t s);
+hipError_t grid3d_forward(const NdArgs& a, hipStream_t s);
+// plane pass of the 3-D multi-pass grids over `groups` grids from row r0
+// (order n; spec: build the spectrum instead), kernels_nd.hip
+hipError_t grid_plane_pass(const NdArgs& a, int r0, int groups, int n, bool spec, hipStream_t s);
 
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);

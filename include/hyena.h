@@ -301,15 +301,15 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
  *   circular:     c[t] = sum_s K[(t - s) mod dims] z[s]; the kernel has the
  *                 grid's shape.
  * Supported: the FFT grid is a cube of side P, a power of two with, per
- * dimension count, 16 <= P <= 1024 (2-D) or 8 <= P <= 32 (3-D).  Non-circular
+ * dimension count, 16 <= P <= 1024 (2-D) or 8 <= P <= 128 (3-D).  Non-circular
  * grids take the smallest such P >= 2*max(dims)-1 (so sides up to 512 in
- * 2-D and 16 in 3-D); circular grids need every side equal to one such P.
+ * 2-D and 64 in 3-D); circular grids need every side equal to one such P.
  * Other shapes return HYENA_ERR_UNSUPPORTED (a side outside 1..4096: SHAPE).
- * Up to P = 128 (2-D) and for 3-D one workgroup holds a grid for all orders
- * and no workspace is used; 2-D grids with P >= 256 run as column and row
- * passes over a workspace of hyena_nd_workspace_bytes (at least P*P/2
- * complex64 values; a smaller one than returned means more, smaller pass
- * groups).
+ * Up to P = 128 (2-D) or 32 (3-D) one workgroup holds a grid for all orders
+ * and no workspace is used; larger grids run as passes over the first axis
+ * and over rows (2-D) or planes (3-D) through a workspace of
+ * hyena_nd_workspace_bytes (at least one grid, P^k/2 complex64 values; a
+ * smaller one than returned means more, smaller pass groups).
  *
  * hyena_nd_plan: writes P.
  * hyena_nd_spectrum_bytes: bytes of the spectrum of `rows` kernels (-1 for

@@ -86,6 +86,13 @@ CASES = [
     (2, 1, 2, (256, 256), True, "fp32", False),
     (2, 1, 1, (512, 512), True, "fp32", False),
     (2, 2, 2, (120, 90), False, "fp32", True),        # per-sample kernels
+    # multi-pass 3-D grids (P >= 64): column pass over the first axis, plane pass over the other two
+    (2, 2, 2, (20, 24, 18), False, "fp32", False),    # P = 64
+    (3, 1, 1, (32, 31, 17), False, "bf16", False),
+    (1, 1, 2, (40, 9, 33), False, "fp32", False),     # P = 128
+    (2, 1, 2, (64, 64, 64), True, "fp32", False),
+    (1, 1, 1, (128, 128, 128), True, "fp32", False),
+    (2, 2, 1, (17, 20, 19), False, "fp32", True),     # per-sample kernels
 ]
 
 
@@ -97,7 +104,7 @@ def test_nd_forward_matches_oracle(N, B, D, dims, circ, io, ps):
     assert err <= _tol(cfg), f"max normalised error {err:.3e}"
 
 
-@pytest.mark.parametrize("name", ["G2", "G3", "GP", "G4", "GP2"])
+@pytest.mark.parametrize("name", ["G2", "G3", "GP", "G4", "GP2", "G5"])
 def test_nd_configs_sampled(name):
     """The measured grid workloads at full size, checked on sampled grids."""
     cfg = GRID_CONFIGS[name]

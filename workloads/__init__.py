@@ -221,6 +221,8 @@ GRID_CONFIGS = {
                      desc="order-2, B=4, D=96, 224x224 pixel grid, non-circular, bf16 I/O (multi-pass)"),
     "GP2": GridConfig("GP2", 2, 2, 32, (512, 512), True, "fp32", 26,
                       desc="order-2, B=2, D=32, 512x512 periodic field, circular, fp32 (multi-pass)"),
+    "G5": GridConfig("G5", 2, 2, 64, (32, 32, 32), False, "bf16", 27,
+                     desc="order-2, B=2, D=64, 32^3 volume, non-circular, bf16 I/O (multi-pass)"),
 }
 
 
