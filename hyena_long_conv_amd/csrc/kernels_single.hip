@@ -26,9 +26,10 @@ namespace hyena {
 // waves per CU; measured faster than 16 on the 2K-context shape), 16 above.
 // SW: XOR-swizzled LDS exchange buffers; PP: two exchange buffers (one
 // barrier per FFT stage instead of two; 16*N bytes of LDS).  Both chosen per
-// length from timings at D = 768 (swizzle off at 2048, 4096 and 16384, where
-// it cost more VALU time or registers than its conflicts; two buffers only at
-// 8192, the one length where they were faster).
+// length from timings at D = 768 with the batch rows of a channel on one XCD
+// (swizzle off only at 16384, where it costs registers and spills; two
+// buffers from 2048 to 8192, where together with the swizzle they were
+// faster by 1.5-3%).
 template <int N> struct SinglePlan {
   static constexpr bool E16 = N >= HYENA_SINGLE_E16_MIN;
   static constexpr int E = E16 ? 16 : 8;
@@ -36,12 +37,12 @@ template <int N> struct SinglePlan {
 #ifdef HYENA_SINGLE_SW
   static constexpr bool SW = HYENA_SINGLE_SW;
 #else
-  static constexpr bool SW = !(N == 2048 || N == 4096 || N == 16384);
+  static constexpr bool SW = N != 16384;
 #endif
 #ifdef HYENA_SINGLE_PP
   static constexpr bool PP = HYENA_SINGLE_PP && N <= 8192;
 #else
-  static constexpr bool PP = N == 8192;
+  static constexpr bool PP = N >= 2048 && N <= 8192;
 #endif
   // PF: request each order's filter coefficients and gate inputs before its
   // forward FFT (their latency hides behind it), where the registers allow.
