@@ -62,11 +62,6 @@ __global__ void k_bw_load(const void* __restrict__ src, float* __restrict__ dst,
   }
 }
 
-__global__ void k_bw_fill(float* __restrict__ dst, float v, int64_t n) {
-  EW_LOOP4(n) *reinterpret_cast<float4*>(dst + 4 * q) = make_float4(v, v, v, v);
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) dst[(n & ~int64_t(3)) + threadIdx.x] = v;
-}
-
 // z = x * c  (x in the I/O dtype)
 template <int IOT>
 __global__ void k_bw_gate(const void* __restrict__ x, const float* __restrict__ c, float* __restrict__ z, int64_t n) {
@@ -153,13 +148,13 @@ hipError_t bw_ew(int io, int op, const void* a, const void* b, void* out, int64_
 }
 
 // Causal convolution of every row of z with a filter spectrum: an order-1
-// four-step forward whose gate is the all-ones buffer.  filters_per_row:
-// the spectrum holds one filter per row (else one per channel).
-hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* out, const float* ones, int B, int D,
+// four-step forward without the gate.  filters_per_row: the spectrum holds
+// one filter per row (else one per channel).
+hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s) {
   ForwardArgs f{};
   f.v = z;
-  f.x.p[0] = ones;
+  f.no_gate = 1;
   f.spec = spec;
   f.y = out;
   f.B = filters_per_row ? 1 : B;
@@ -187,7 +182,6 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   w.g = o;     o += act;
   w.t1 = o;    o += act;
   w.t2 = o;    o += act;
-  w.ones = o;  o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);
   w.rows_per_group = rows_per_group(p.N, R);
   w.work = o;  o += al((int64_t)w.rows_per_group * p.N * 8);
@@ -204,7 +198,6 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   float* G = reinterpret_cast<float*>(ws + w.g);
   float* T1 = reinterpret_cast<float*>(ws + w.t1);
   float* T2 = reinterpret_cast<float*>(ws + w.t2);
-  float* ones = reinterpret_cast<float*>(ws + w.ones);
   void* sg = ws + w.sg;
   void* work = ws + w.work;
   const int64_t cstride = (w.z - w.c) / a.NORD / 4;   // floats between saved c_n
@@ -212,13 +205,11 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   const auto spec_n = [&](int nn) { return static_cast<const void*>(spec + (int64_t)nn * D * p.spec_stride); };
   hipError_t e;
 #define BW_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-  hipLaunchKernelGGL(k_bw_fill, ew_grid(n), dim3(EW_THREADS), 0, s, ones, 1.0f, n);
-  BW_TRY(hipGetLastError());
   // forward: c_n = h_n conv z_n (kept), z_{n+1} = x_n * c_n
   BW_TRY(bw_ew(a.io, BW_LOAD, a.v, nullptr, Z, n, s));
   for (int nn = 0; nn < a.NORD; ++nn) {
     float* Cn = C + nn * cstride;
-    BW_TRY(bw_conv(p, spec_n(nn), Z, Cn, ones, (int)B, (int)D, false, work, w.rows_per_group, s));
+    BW_TRY(bw_conv(p, spec_n(nn), Z, Cn, (int)B, (int)D, false, work, w.rows_per_group, s));
     if (nn < a.NORD - 1) BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn], Cn, Z, n, s));
   }
   // backward, g = dloss/dz_{n+1}; after each adjoint convolution g is left
@@ -238,12 +229,12 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     sa.h = T2; sa.spec = sg; sa.NF = (int)R; sa.L = L; sa.spec_stride = p.spec_stride;
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
     BW_TRY(fourstep_spectrum(sa, p, s));
-    BW_TRY(bw_conv(p, sg, Z, T1, ones, (int)B, (int)D, true, work, w.rows_per_group, s));
+    BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
     hipLaunchKernelGGL(k_bw_batch_sum_rev, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
                        a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
     BW_TRY(hipGetLastError());
     // adjoint: g_n = R(h_n conv T2); kept reversed in T1
-    BW_TRY(bw_conv(p, spec_n(nn), T2, T1, ones, (int)B, (int)D, false, work, w.rows_per_group, s));
+    BW_TRY(bw_conv(p, spec_n(nn), T2, T1, (int)B, (int)D, false, work, w.rows_per_group, s));
     gcur = T1;
     grev = true;
   }

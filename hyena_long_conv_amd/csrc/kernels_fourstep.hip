@@ -51,7 +51,8 @@ template <int N2> struct RowCfg {
                                       typename Plan8<(N2 <= 8192 ? N2 : 8192)>::R>::type;
 };
 
-enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3 };
+// COL_OUT: as COL_LAST without the gate (the plain causal convolution).
+enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4 };
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
 
 struct ColArgs {
@@ -160,14 +161,18 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
       const bool ok = at(j + i * S1, ro, t, len);
       cf z = make_float2(0.f, 0.f);
       if (ok) {
-        const cf xv = ld_pair<IOT, EVEN>(a.xg, ro, t, len);
-        z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
-        if constexpr (KIND == COL_LAST) st_pair<IOT, EVEN>(a.y, ro, t, len, z);
+        if constexpr (KIND == COL_OUT) {
+          z = u[i];
+        } else {
+          const cf xv = ld_pair<IOT, EVEN>(a.xg, ro, t, len);
+          z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+        }
+        if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, ro, t, len, z);
       }
       u[i] = z;
     }
   }
-  if constexpr (KIND != COL_LAST) {
+  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
     fft.template run<false>(u, lds, j);
     if (valid) {
 #pragma unroll
@@ -284,6 +289,8 @@ template <int N1, bool EVEN, bool GRID>
 static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 block, hipStream_t s) {
   if (kind == COL_SPEC) {
     hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
+  } else if (kind == COL_OUT) {
+    if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
   } else if (io == 0) {
     if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
     else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
@@ -386,7 +393,7 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
       e = dispatch_row(p.n2, ROW_CONV, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
-      e = dispatch_col(p.n1, n == a.NORD - 1 ? COL_LAST : COL_MID, a.io, c, groups, s);
+      e = dispatch_col(p.n1, n < a.NORD - 1 ? COL_MID : (a.no_gate ? COL_OUT : COL_LAST), a.io, c, groups, s);
       if (e != hipSuccess) return e;
     }
   }

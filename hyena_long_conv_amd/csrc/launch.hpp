@@ -22,6 +22,7 @@ struct ForwardArgs {
   void* work;            // four-step intermediate (rows_per_group * N complex)
   int rows_per_group;
   int circular;          // single path: rows fill the whole FFT length (no zero half)
+  int no_gate;           // four-step, fp32 rows: the last order stores the convolution without a gate
 };
 
 struct SpectrumArgs {
@@ -95,10 +96,10 @@ struct BackwardArgs {
 hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 
 // Backward on the four-step path (kernels_bwd_long.hip): byte offsets of its
-// workspace buffers (saved c_n, z, g, two temporaries, an all-ones gate, the
-// per-row spectra and the four-step intermediate).
+// workspace buffers (saved c_n, z, g, two temporaries, the per-row spectra
+// and the four-step intermediate).
 struct LongBackwardLayout {
-  int64_t c, z, g, t1, t2, ones, sg, work, total;
+  int64_t c, z, g, t1, t2, sg, work, total;
   int rows_per_group;
 };
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD);
