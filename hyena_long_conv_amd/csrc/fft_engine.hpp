@@ -608,6 +608,29 @@ __device__ __forceinline__ cf ld_pair(const void* p, int64_t row_off, int64_t t,
   }
 }
 
+// (x[t], x[t+1]) of a row whose every requested pair is in range (t + 1 < L,
+// row offset and t even): one aligned access, no mask.
+template <int IOT>
+__device__ __forceinline__ cf ld_pair_in(const void* p, int64_t row_off, int t) {
+  if constexpr (IOT == 0) {
+    const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(static_cast<const float*>(p) + row_off) + (t >> 1));
+    return make_float2(w.x, w.y);
+  } else {
+    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + row_off) + (t >> 1));
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  }
+}
+
+template <int IOT>
+__device__ __forceinline__ void st_pair_in(void* p, int64_t row_off, int t, cf v) {
+  if constexpr (IOT == 0) {
+    const f32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(static_cast<float*>(p) + row_off) + (t >> 1));
+  } else {
+    __builtin_nontemporal_store(bf16x2_bits(v.x, v.y), reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + row_off) + (t >> 1));
+  }
+}
+
 template <int IOT, bool EVEN>
 __device__ __forceinline__ void st_pair(void* p, int64_t row_off, int64_t t, int64_t L, cf v) {
   if constexpr (EVEN) {

@@ -123,12 +123,19 @@ __device__ __forceinline__ int row_of_workgroup(int wg, int B, int D) {
 
 // FULL: circular mode, the row fills all M = 2N samples (no zero half);
 // otherwise the row occupies the first half of each thread's points.
-template <int N, int IOT, bool EVEN, bool FULL>
+// EXACT: L = N, so (like FULL) every sample a thread reads or writes is in
+// the row and the accesses need no mask.
+template <int N, int IOT, bool EVEN, bool FULL, bool EXACT = false>
 __global__ void __launch_bounds__(SinglePlan<N>::T, HYENA_SINGLE_WAVES)
 k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, void* __restrict__ y,
                  int B, int D, int NORD, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E, NV = FULL ? E : E / 2;
+  constexpr bool IN = FULL || EXACT;
+  const auto ldp = [&](const void* p, int64_t o, int t) {
+    if constexpr (IN) return ld_pair_in<IOT>(p, o, t);
+    else return ld_pair<IOT, EVEN, true>(p, o, (int64_t)t, L);
+  };
   __shared__ cf smem[P::PP ? 2 * N : N];
   using Lds = typename P::Lds;
   const Lds lds2[2] = {Lds{smem}, Lds{smem + (P::PP ? N : 0)}};
@@ -141,8 +148,7 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
 
   cf u[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i)
-    u[i] = (i < NV) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+  for (int i = 0; i < E; ++i) u[i] = (i < NV) ? ldp(v, off, 2 * (j + i * S)) : make_float2(0.f, 0.f);
 
   for (int n = 0; n < NORD; ++n) {
     const cf* g = spec + (int64_t)(n * D + d) * spec_stride;
@@ -152,7 +158,7 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
     if constexpr (P::PF) {
       pc.load(g, qs, j);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+      for (int i = 0; i < NV; ++i) xv[i] = ldp(xn, off, 2 * (j + i * S));
     }
     if constexpr (P::PP) {
       fft.template run_pp<false>(u, lds2, j);
@@ -169,16 +175,19 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
     }
     if constexpr (!P::PF) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) xv[i] = ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L);
+      for (int i = 0; i < NV; ++i) xv[i] = ldp(xn, off, 2 * (j + i * S));
     }
     const bool last = (n == NORD - 1);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       cf z = make_float2(0.f, 0.f);
       if (i < NV) {
-        const int64_t t = 2 * (int64_t)(j + i * S);
+        const int t = 2 * (j + i * S);
         z = make_float2(xv[i].x * u[i].x, xv[i].y * u[i].y);
-        if (last) st_pair<IOT, EVEN>(y, off, t, L, z);
+        if (last) {
+          if constexpr (IN) st_pair_in<IOT>(y, off, t, z);
+          else st_pair<IOT, EVEN>(y, off, (int64_t)t, L, z);
+        }
       }
       u[i] = z;
     }
@@ -415,6 +424,9 @@ static hipError_t launch_fwd(const ForwardArgs& a, hipStream_t s) {
   if (a.circular)   // L = 2N, even
     hipLaunchKernelGGL((k_single_forward<N, IOT, true, true>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
                        a.NORD, (int)a.L, a.spec_stride);
+  else if (a.L == N)
+    hipLaunchKernelGGL((k_single_forward<N, IOT, true, false, true>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B,
+                       a.D, a.NORD, (int)a.L, a.spec_stride);
   else if (a.L % 2 == 0)
     hipLaunchKernelGGL((k_single_forward<N, IOT, true, false>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
                        a.NORD, (int)a.L, a.spec_stride);
