@@ -29,7 +29,7 @@ namespace {
 
 constexpr int TM = 128, TN = 128, TT = 256;   // tile rows, tile columns, threads
 constexpr int HALO = 16;                       // carried Z rows (T - 1 <= 15)
-constexpr int ZLD = HALO + TM + 4;             // epilogue row stride (16-byte rows for vector reads)
+constexpr int ZLD = HALO + TM + 1;             // epilogue row stride (odd: conflict-free column writes)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -175,12 +175,101 @@ __device__ __forceinline__ float dot_row(const E* x, const E* w, int K) {
   return acc;
 }
 
+// Workgroup -> (row job, column block) map.  Workgroup w runs on XCD w mod 8,
+// and each XCD has its own L2.  The 8 XCDs form a grid of (8 / cg) row-job
+// groups x cg column-block groups; XCD x takes row jobs [(x / cg) * spx, +spx)
+// and column blocks [(x % cg) * cbx, +cbx), its workgroups w = x + 8k walking
+// them column block fastest.  An operand tile is then read into few L2s
+// (A-rows by cg of them, weight blocks by 8 / cg), instead of into most of
+// the eight.  Slots past the end of either range are idle.  The map is a
+// permutation of the jobs whatever the hardware does with it.
+struct XcdTiles {
+  int cg, spx, cbx;
+  __device__ __forceinline__ bool tile_of(int w, int jobs, int cbs, int& job, int& cb) const {
+    const int x = w & 7, k = w >> 3;
+    const int jl = k / cbx;
+    job = (x / cg) * spx + jl;
+    cb = (x % cg) * cbx + (k - jl * cbx);
+    return jl < spx && job < jobs && cb < cbs;
+  }
+};
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// The map for `jobs` row jobs and `cbs` column blocks whose operand tiles
+// are the same size: the split of the 8 XCDs that keeps the fewest tiles
+// live per L2 (spx + cbx), then the fewest workgroups.
+static XcdTiles plan_xcd(int jobs, int cbs, int64_t& grid) {
+  XcdTiles best{1, jobs, cbs};
+  int64_t best_cost = -1;
+  for (int cg = 1; cg <= 8; cg *= 2) {
+    const int spx = ceil_div(jobs, 8 / cg), cbx = ceil_div(cbs, cg);
+    const int64_t g = 8LL * spx * cbx, cost = (int64_t)(spx + cbx) << 32 | g;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = XcdTiles{cg, spx, cbx};
+      grid = g;
+    }
+  }
+  return best;
+}
+
+// In-projection epilogue for one half (64 columns) of a tile: Z of column n
+// sits at Zs[n*ZLD + HALO + m] (m = 0..127, tile rows) after HALO carried
+// rows, and taps[c][j] = w[c][j] (zero for j >= T).  K >= T taps are applied.
+template <int IOT, int K>
+__device__ __forceinline__ void fir_store(const InProjArgs& a, const float* Zs, const float (*taps)[HALO], int h,
+                                          int c0, int b, int64_t t0, int64_t te, int wave, int lane) {
+  constexpr int G = K <= 4 ? 4 : 1;                   // columns per step
+  const int D = a.D, C = a.C;
+  const int64_t L = a.L;
+  for (int n0 = wave; n0 < 64; n0 += G * (TT / 64)) {
+    float o0[G], o1[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int n = n0 + g * (TT / 64);
+      const float* zr = Zs + n * ZLD + HALO + 2 * lane;
+      const float* wc = taps[64 * h + n];
+      float z[K + 1];                                 // z[k] = Z(t + 1 - k), t = 2 lane
+#pragma unroll
+      for (int k = 0; k <= K; ++k) z[k] = zr[1 - k];
+      o0[g] = 0.f;
+      o1[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const float wj = wc[j];
+        o0[g] = fmaf(wj, z[j + 1], o0[g]);
+        o1[g] = fmaf(wj, z[j], o1[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int c = c0 + 64 * h + n0 + g * (TT / 64);
+      if (c >= C) break;
+      const int s = c / D, d = c - (c / D) * D;
+      void* dst = a.dst.p[s];
+      const int64_t row = ((int64_t)b * D + d) * L, t = t0 + 2 * lane;
+      if ((L & 1) == 0 && t + 1 < te) {
+        if constexpr (IOT == 0) {
+          typedef float f32x2v __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<f32x2v*>(static_cast<float*>(dst) + row + t) = f32x2v{o0[g], o1[g]};
+        } else {
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(dst) + row + t) = bf16x2_bits(o0[g], o1[g]);
+        }
+      } else {
+        if (t < te) st_f<IOT>(dst, row + t, o0[g]);
+        if (t + 1 < te) st_f<IOT>(dst, row + t + 1, o1[g]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ in-projection
 //
 // Workgroup = (batch b, time strip, 128-column block).  The strip's tiles run
 // in order; carry[n][j] holds Z row (tile start - HALO + j) of column n.
 template <int IOT, bool VEC>
-__global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, int strip_len, int n_cb) {
+__global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, int strip_len, int n_cb, XcdTiles m) {
   using E = typename Op<IOT>::E;
   constexpr int LDK = Op<IOT>::LDK, BK = Op<IOT>::BK;
   constexpr int MAIN_BYTES = 2 * TM * LDK * (int)sizeof(E);
@@ -188,15 +277,16 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
   constexpr int BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[BYTES];
   __shared__ float carry[TN][HALO];
+  __shared__ float taps[TN][HALO];
+  __shared__ float bias[TN];
   E* As = reinterpret_cast<E*>(smem);
   E* Bs = As + TM * LDK;
   float* Zs = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  int wg = blockIdx.x;
-  const int cb = wg % n_cb;
-  wg /= n_cb;
-  const int strip = wg % n_strips, b = wg / n_strips;
+  int job, cb;
+  if (!m.tile_of(blockIdx.x, a.B * n_strips, n_cb, job, cb)) return;   // idle slot (whole workgroup)
+  const int strip = job % n_strips, b = job / n_strips;
   const int c0 = cb * TN, D = a.D, C = a.C, T = a.T;
   const int64_t L = a.L;
   const int64_t ts = (int64_t)strip * strip_len;
@@ -205,7 +295,12 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
   const E* Wt = static_cast<const E*>(a.W);
 
   // Z rows ts-1 .. ts-(T-1) by direct dot products (zero before t = 0).
-  for (int i = tid; i < TN * HALO; i += TT) (&carry[0][0])[i] = 0.f;
+  for (int i = tid; i < TN * HALO; i += TT) {
+    const int n = i / HALO, j = i % HALO, c = c0 + n;
+    (&carry[0][0])[i] = 0.f;
+    taps[n][j] = (j < T && c < C) ? a.w[(int64_t)c * T + j] : 0.f;
+    if (j == 0) bias[n] = (a.bias && c < C) ? a.bias[c] : 0.f;
+  }
   __syncthreads();
   for (int i = tid; i < TN * (T - 1); i += TT) {
     const int n = i % TN, jj = i / TN;               // row ts - 1 - jj
@@ -219,6 +314,11 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
 
   const int nks = (D + BK - 1) / BK;
   const int brhi = (C - c0 < TN) ? C - c0 : TN;
+  // The first k-stage of every tile is requested before the previous tile's
+  // epilogue, so its loads are not queued behind that epilogue's stores.
+  RowStage<IOT, VEC> sa, sb;
+  sa.load(u, ((int64_t)b * L + ts) * D, D, (L - ts < TM) ? (int)(L - ts) : TM, 0, D, tid);
+  sb.load(Wt, (int64_t)c0 * D, D, brhi, 0, D, tid);
   for (int64_t t0 = ts; t0 < te; t0 += TM) {
     f32x16 acc[2][2];
 #pragma unroll
@@ -229,9 +329,6 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int64_t aoff = ((int64_t)b * L + t0) * D;
     const int arhi = (L - t0 < TM) ? (int)(L - t0) : TM;
-    RowStage<IOT, VEC> sa, sb;
-    sa.load(u, aoff, D, arhi, 0, D, tid);
-    sb.load(Wt, (int64_t)c0 * D, D, brhi, 0, D, tid);
     __syncthreads();                                  // smem free (carry set / last epilogue done)
     sa.store(As, tid);
     sb.store(Bs, tid);
@@ -249,6 +346,11 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
         __syncthreads();
       }
     }
+    if (t0 + TM < te) {
+      const int64_t t1 = t0 + TM;
+      sa.load(u, aoff + (int64_t)TM * D, D, (L - t1 < TM) ? (int)(L - t1) : TM, 0, D, tid);
+      sb.load(Wt, (int64_t)c0 * D, D, brhi, 0, D, tid);
+    }
     // Epilogue, 64 columns at a time: Z (+bias) and the carried rows into
     // LDS, then the short FIR and the store into the column's stream.
     for (int h = 0; h < 2; ++h) {
@@ -257,8 +359,7 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = j * 32 + (lane & 31);
-          const int c = c0 + 64 * h + n;
-          const float bc = (a.bias && c < C) ? a.bias[c] : 0.f;
+          const float bc = bias[64 * h + n];   // from LDS: no global load (and wait) in the epilogue
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -270,54 +371,13 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
         Zs[n * ZLD + j] = carry[64 * h + n][j];
       }
       __syncthreads();
-      {
-        const int n = tid >> 2, mb = (tid & 3) * 32;
-        const int c = c0 + 64 * h + n;
-        if (c < C) {
-          float wj[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) wj[j] = (j < T) ? a.w[(int64_t)c * T + j] : 0.f;
-          const int s = c / D, d = c - (c / D) * D;
-          void* dst = a.dst.p[s];
-          const int64_t row = ((int64_t)b * D + d) * L;
-          // the 32 outputs' window Z[mb-16 .. mb+31] in registers, 16-byte reads
-          typedef float f32x4v __attribute__((ext_vector_type(4)));
-          float win[48];
-          const float* zr = Zs + n * ZLD + mb;        // = row start + HALO + mb - 16
-#pragma unroll
-          for (int q = 0; q < 12; ++q) {
-            const f32x4v w4 = *reinterpret_cast<const f32x4v*>(zr + 4 * q);
-            win[4 * q] = w4.x; win[4 * q + 1] = w4.y; win[4 * q + 2] = w4.z; win[4 * q + 3] = w4.w;
-          }
-#pragma unroll
-          for (int m = mb; m < mb + 32; m += 4) {
-            float o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              o[q] = 0.f;
-#pragma unroll
-              for (int j = 0; j < 16; ++j)
-                if (j < T) o[q] = fmaf(wj[j], win[16 + (m - mb) + q - j], o[q]);
-            }
-            const int64_t t = t0 + m;
-            if ((L & 3) == 0 && t + 3 < te) {          // 4 aligned outputs in one store
-              if constexpr (IOT == 0) {
-                const u32x4 w = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                                 __float_as_uint(o[3])};
-                *reinterpret_cast<u32x4*>(static_cast<float*>(dst) + row + t) = w;
-              } else {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 w = {bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3])};
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + row + t) = w;
-              }
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (t + q < te) st_f<IOT>(dst, row + t + q, o[q]);
-            }
-          }
-        }
-      }
+      // FIR and store: a wave takes columns wave, wave + 4, ... four at a
+      // time; lane l makes outputs t0 + 2l and t0 + 2l + 1 of each, so the
+      // wave writes every column's 128 outputs as one contiguous run.  The
+      // taps beyond T are zero, so K = 4 covers T <= 4 with all loads issued
+      // at once.
+      if (T <= 4) fir_store<IOT, 4>(a, Zs, taps, h, c0, b, t0, te, wave, lane);
+      else fir_store<IOT, HALO>(a, Zs, taps, h, c0, b, t0, te, wave, lane);
       for (int i = tid; i < 64 * HALO; i += TT) {
         const int n = i / HALO, j = i % HALO;
         carry[64 * h + n][j] = Zs[n * ZLD + HALO + TM - HALO + j];
@@ -381,7 +441,7 @@ struct YStage {
 };
 
 template <int IOT, bool VEC>
-__global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int n_eb) {
+__global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int n_eb, XcdTiles m) {
   using E = typename Op<IOT>::E;
   constexpr int LDK = Op<IOT>::LDK, BK = Op<IOT>::BK;
   constexpr int A_ELEMS = (IOT == 0) ? BK * (TM + 4) : TM * LDK;
@@ -389,10 +449,9 @@ __global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int 
   __shared__ __attribute__((aligned(16))) E Bs[TN * LDK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  int wg = blockIdx.x;
-  const int eb = wg % n_eb;
-  wg /= n_eb;
-  const int tt = wg % n_tt, b = wg / n_tt;
+  int job, eb;
+  if (!m.tile_of(blockIdx.x, a.B * n_tt, n_eb, job, eb)) return;       // idle slot (whole workgroup)
+  const int tt = job % n_tt, b = job / n_tt;
   const int D = a.D, e0 = eb * TN;
   const int64_t L = a.L, t0 = (int64_t)tt * TM;
   const E* y = static_cast<const E*>(a.y);
@@ -444,8 +503,6 @@ __global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int 
   }
 }
 
-int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
 template <int IOT, bool VEC>
 static hipError_t launch_inproj(const InProjArgs& a, hipStream_t s) {
   const auto kern = k_inproj<IOT, VEC>;
@@ -458,14 +515,21 @@ static hipError_t launch_inproj(const InProjArgs& a, hipStream_t s) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, TT, 0) != hipSuccess || per_cu < 1) per_cu = 1;
-  int n_strips = (int)(((int64_t)cus * per_cu) / ((int64_t)a.B * n_cb));
-  if (n_strips < 1) n_strips = 1;
-  if (n_strips > tiles) n_strips = tiles;
-  const int per = ceil_div(tiles, n_strips);
-  n_strips = ceil_div(tiles, per);
+  const int64_t cap = (int64_t)cus * per_cu;
+  int want = (int)(cap / ((int64_t)a.B * n_cb));
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  int n_strips, per;
+  int64_t grid = 0;
+  XcdTiles m;
+  for (;; --want) {                 // fewer strips until the mapped grid fits at once
+    per = ceil_div(tiles, want);
+    n_strips = ceil_div(tiles, per);
+    m = plan_xcd(a.B * n_strips, n_cb, grid);
+    if (grid <= cap || want == 1) break;
+  }
   const int strip_len = per * TM;
-  const dim3 grid((unsigned)((int64_t)a.B * n_strips * n_cb)), block(TT);
-  hipLaunchKernelGGL(kern, grid, block, 0, s, a, n_strips, strip_len, n_cb);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TT), 0, s, a, n_strips, strip_len, n_cb, m);
   return hipGetLastError();
 }
 
@@ -479,15 +543,17 @@ hipError_t in_projection(const InProjArgs& a, hipStream_t s) {
 
 hipError_t out_projection(const OutProjArgs& a, hipStream_t s) {
   const int n_eb = ceil_div(a.D, TN), n_tt = ceil_div(a.L, TM);
-  const dim3 grid((unsigned)((int64_t)a.B * n_tt * n_eb)), block(TT);
+  int64_t g = 0;
+  const XcdTiles m = plan_xcd(a.B * n_tt, n_eb, g);
+  const dim3 grid((unsigned)g), block(TT);
   const int w = (a.io == 0 ? 4 : 8);
   const bool vec = a.D % w == 0 && a.L % w == 0;
   if (a.io == 0) {
-    if (vec) hipLaunchKernelGGL((k_outproj<0, true>), grid, block, 0, s, a, n_tt, n_eb);
-    else hipLaunchKernelGGL((k_outproj<0, false>), grid, block, 0, s, a, n_tt, n_eb);
+    if (vec) hipLaunchKernelGGL((k_outproj<0, true>), grid, block, 0, s, a, n_tt, n_eb, m);
+    else hipLaunchKernelGGL((k_outproj<0, false>), grid, block, 0, s, a, n_tt, n_eb, m);
   } else {
-    if (vec) hipLaunchKernelGGL((k_outproj<1, true>), grid, block, 0, s, a, n_tt, n_eb);
-    else hipLaunchKernelGGL((k_outproj<1, false>), grid, block, 0, s, a, n_tt, n_eb);
+    if (vec) hipLaunchKernelGGL((k_outproj<1, true>), grid, block, 0, s, a, n_tt, n_eb, m);
+    else hipLaunchKernelGGL((k_outproj<1, false>), grid, block, 0, s, a, n_tt, n_eb, m);
   }
   return hipGetLastError();
 }
