@@ -70,7 +70,18 @@ struct ColArgs {
   int64_t gL1, gLm, gL2;
   int gNLs;            // log2 NL
   int gcirc;           // SPEC: kernel of the grid's shape (else extent 2L-1 per axis)
+  int cmB, cmD;        // > 1: channel-major launch, see launch_row_of
 };
+
+// Activation row (b*D + d) of the launch's local row g.  Natural launches
+// (cmB <= 1) cover rows r0, r0 + 1, ...; channel-major ones cover channels
+// r0, r0 + 1, ... with their cmB batch rows next to each other (g = c*cmB + b),
+// so the batch rows that share a channel's spectrum run in the same launch.
+__device__ __forceinline__ int launch_row_of(int r0, int g, int cmB, int D) {
+  if (cmB <= 1) return r0 + g;
+  const int c = g / cmB;
+  return (g - c * cmB) * D + r0 + c;
+}
 
 // Kernel index of padded position n on an axis of padded size P and grid
 // side L (offset o at o mod P; non-circular index o + L - 1; -1: gap).
@@ -105,7 +116,7 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   const bool valid = col < a.n2;
   const int64_t N = (int64_t)N1 * a.n2;
   cf* buf = a.work + (int64_t)g * N;
-  const int64_t off = GRID ? (int64_t)(a.r0 + g) * a.gL1 * a.gLm * a.gL2 : (int64_t)(a.r0 + g) * a.L;
+  const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * (GRID ? a.gL1 * a.gLm * a.gL2 : a.L);
   const int gi2 = col >> a.gNLs, gm = col & ((1 << a.gNLs) - 1);     // GRID: column -> (i2, packed m)
   const ColLds<W> lds{smem + c};
   BlockFFT<N1, E, typename C::R> fft;
@@ -191,6 +202,7 @@ struct RowArgs {
   int D;
   int r0;              // first row (CONV: activation row b*D + d; SPEC: filter row)
   int n_row_pairs;     // n1 / 2
+  int cmB;             // CONV, > 1: channel-major launch (r0 = first channel, cmB batch rows each)
 };
 
 // Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
@@ -202,7 +214,20 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   constexpr int PADN = RowLds::padded(N2);
   __shared__ cf smem[2 * PADN];
   const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
-  const int g = blockIdx.x / a.n_row_pairs, w = blockIdx.x - g * a.n_row_pairs;
+  int g, w;
+  if (KIND == ROW_CONV && a.cmB > 1) {
+    // Channel-major launch: the cmB workgroups of one (channel, row pair)
+    // read the same spectrum slice, so they are placed on one XCD (workgroup
+    // i runs on XCD i mod 8) one after another, and the slice is fetched
+    // into that XCD's L2 once.  n_row_pairs is a multiple of 8.
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int unit = (slot / a.cmB) * 8 + x, c = unit / a.n_row_pairs;
+    w = unit - c * a.n_row_pairs;
+    g = c * a.cmB + (slot - (slot / a.cmB) * a.cmB);
+  } else {
+    g = blockIdx.x / a.n_row_pairs;
+    w = blockIdx.x - g * a.n_row_pairs;
+  }
   const int n1 = a.n1;
   const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
   const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
@@ -249,7 +274,7 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     // E-1-i of thread S2-1-j in the mirror row (row 0 pairs inside itself:
     // thread S2-j, or index E-i in thread 0; k = 0 and k = N/2 are their own
     // partners).
-    const int d = (a.r0 + g) % a.D;
+    const int d = (a.cmB > 1) ? a.r0 + g / a.cmB : (a.r0 + g) % a.D;
     const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
     const cf* gk = gs + (int64_t)k1 * N2;
     const cf* gmr = gs + (int64_t)k1m * N2;
@@ -383,8 +408,14 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   RowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
   r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = p.n1 / 2;
-  for (int r0 = 0; r0 < a.n_rows; r0 += a.rows_per_group) {
-    const int groups = (a.n_rows - r0 < a.rows_per_group) ? a.n_rows - r0 : a.rows_per_group;
+  // With B > 1 a launch covers whole channels (all their batch rows), so the
+  // row pass reads each channel's spectrum once instead of once per batch row.
+  const bool cm = a.B > 1 && a.n_rows == a.B * a.D && a.rows_per_group >= a.B && r.n_row_pairs % 8 == 0;
+  const int units = cm ? a.D : a.n_rows, per = cm ? a.rows_per_group / a.B : a.rows_per_group;
+  c.cmB = r.cmB = cm ? a.B : 1;
+  c.cmD = a.D;
+  for (int r0 = 0; r0 < units; r0 += per) {
+    const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? a.B : 1);
     c.r0 = r0; r.r0 = r0;
     hipError_t e = dispatch_col(p.n1, COL_FIRST, a.io, c, groups, s);
     if (e != hipSuccess) return e;
@@ -450,6 +481,7 @@ struct GridRowArgs {
   int order, NORD, D, per_sample;
   int r0;
   int pairs_per_grid;   // n1 / 2
+  int cmB;              // CONV, > 1: channel-major launch (r0 = first channel, cmB batch rows each)
 };
 
 template <int N2, int KIND>
@@ -459,8 +491,20 @@ __global__ void __launch_bounds__(GridRowCfg<N2>::T) k_grid_row(GridRowArgs a) {
   __shared__ cf smem[C::RP * 2 * N2];
   const int pr = threadIdx.x / (2 * TPR), tb = threadIdx.x - pr * 2 * TPR;
   const int b = tb / TPR, j = tb - b * TPR;
-  const int pair = blockIdx.x * C::RP + pr;
-  const int g = pair / a.pairs_per_grid, w = pair - g * a.pairs_per_grid;
+  int g, w;
+  if (KIND == ROW_CONV && a.cmB > 1) {
+    // channel-major launch: the cmB workgroups of one (channel, row pairs)
+    // share the spectrum slice and run one after another on one XCD
+    const int wpg = a.pairs_per_grid / C::RP;     // workgroups per grid, a multiple of 8
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int unit = (slot / a.cmB) * 8 + x, c = unit / wpg;
+    g = c * a.cmB + (slot - (slot / a.cmB) * a.cmB);
+    w = (unit - c * wpg) * C::RP + pr;
+  } else {
+    const int pair = blockIdx.x * C::RP + pr;
+    g = pair / a.pairs_per_grid;
+    w = pair - g * a.pairs_per_grid;
+  }
   const int n1 = a.n1;
   const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
   const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
@@ -492,7 +536,7 @@ __global__ void __launch_bounds__(GridRowCfg<N2>::T) k_grid_row(GridRowArgs a) {
       if (k2 == 0) out[NC + k1] = realfft_bin(u[i], cm, make_float2(-1.f, 0.f), sc);
     }
   } else {
-    const int rowid = a.r0 + g, bb = rowid / a.D, d = rowid - bb * a.D;
+    const int rowid = launch_row_of(a.r0, g, a.cmB, a.D), bb = rowid / a.D, d = rowid - bb * a.D;
     const int64_t f = a.per_sample ? ((int64_t)bb * a.NORD + a.order) * a.D + d : (int64_t)a.order * a.D + d;
     const cf* gs = a.spec + f * a.spec_stride;
 #pragma unroll
@@ -548,8 +592,15 @@ hipError_t grid2d_forward(const NdArgs& a, hipStream_t s) {
   GridRowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.n1 = n1; r.spec_stride = a.spec_stride;
   r.NORD = a.NORD; r.D = a.D; r.per_sample = a.per_sample; r.pairs_per_grid = n1 / 2;
-  for (int r0 = 0; r0 < a.rows; r0 += a.rows_per_group) {
-    const int groups = (a.rows - r0 < a.rows_per_group) ? a.rows - r0 : a.rows_per_group;
+  // Shared kernels and B > 1: launches of whole channels, as in fourstep_forward.
+  const int B = a.rows / a.D, tpr = n2 / 8, rp = (2 * tpr >= 256) ? 1 : 256 / (2 * tpr);
+  const bool cm = !a.per_sample && B > 1 && a.rows == B * a.D && a.rows_per_group >= B &&
+                  (n1 / 2) % (8 * rp) == 0;
+  const int units = cm ? a.D : a.rows, per = cm ? a.rows_per_group / B : a.rows_per_group;
+  c.cmB = r.cmB = cm ? B : 1;
+  c.cmD = a.D;
+  for (int r0 = 0; r0 < units; r0 += per) {
+    const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? B : 1);
     c.r0 = r0; r.r0 = r0;
     hipError_t e = dispatch_col(n1, COL_FIRST, a.io, c, groups, s, true);
     if (e != hipSuccess) return e;

@@ -149,16 +149,18 @@ def test_nd_repeat_calls_identical():
 
 
 def test_nd_multipass_small_workspace_matches():
-    """A workspace smaller than the one asked for only splits the passes into more groups."""
+    """A workspace smaller than the one asked for only splits the passes into
+    more groups (single grids below B, whole channels of B grids above)."""
     cfg = GridConfig("w", 2, 3, 2, (150, 150), False, "fp32", 9)
     v, xs = make_grid_activations(cfg, DEV)
     K = torch.from_numpy(make_grid_kernel(cfg)).to(DEV)
     spec = H.nd_filter_spectrum(K, cfg.dims)
     y_full = H.nd_forward(v, xs, spec).clone()
-    one = torch.empty(512 * 256 * 8, dtype=torch.uint8, device=DEV)        # one grid per pass group
-    y_one = H.nd_forward(v, xs, spec, workspace=one)
-    torch.cuda.synchronize()
-    assert torch.equal(y_full, y_one)
+    for grids in (1, 2, 3, 4):
+        ws = torch.empty(grids * 512 * 256 * 8, dtype=torch.uint8, device=DEV)
+        y_ws = H.nd_forward(v, xs, spec, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_full, y_ws), f"workspace of {grids} grids"
 
 
 def test_nd_errors():

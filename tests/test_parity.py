@@ -159,6 +159,24 @@ def test_small_workspace_still_correct():
     check_rows(y, p, L, v, xs, [(b, d) for b in range(2) for d in range(3)], TOL_FP32)
 
 
+def test_fourstep_pass_groups_bitwise_equal(monkeypatch):
+    """Pass groups of whole channels (all batch rows of each) or of single
+    rows, whatever the workspace allows, compute every row the same way."""
+    monkeypatch.setenv("HYENA_FORCE_PATH", "fourstep")
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "16")
+    cfg = _cfg(2, 3, 5, 3000)
+    p = make_filter_params(cfg)
+    v, xs = make_activations(cfg, DEV)
+    _, spec, y = run_hip(p, cfg.L, v, xs)
+    check_rows(y, p, cfg.L, v, xs, [(0, 0), (1, 2), (2, 4)], TOL_FP32)
+    row_bytes = H.plan(cfg.L)["M"] // 2 * 8
+    for rows in (1, 2, 3, 4, 7):      # below B, one channel, one channel + spare, several channels
+        ws = torch.empty(rows * row_bytes, dtype=torch.uint8, device=DEV)
+        y2 = H.forward(v, xs, spec, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), f"workspace of {rows} rows"
+
+
 # ------------------------------------------------------------- robustness
 
 def test_deterministic_bitwise():
