@@ -148,16 +148,17 @@ def test_nd_repeat_calls_identical():
     assert torch.equal(a, b)
 
 
-def test_nd_multipass_small_workspace_matches():
+@pytest.mark.parametrize("dims,grid_bytes", [((150, 150), 512 * 256 * 8), ((20, 20, 20), 64 * 64 * 32 * 8)])
+def test_nd_multipass_small_workspace_matches(dims, grid_bytes):
     """A workspace smaller than the one asked for only splits the passes into
     more groups (single grids below B, whole channels of B grids above)."""
-    cfg = GridConfig("w", 2, 3, 2, (150, 150), False, "fp32", 9)
+    cfg = GridConfig("w", 2, 3, 2, dims, False, "fp32", 9)
     v, xs = make_grid_activations(cfg, DEV)
     K = torch.from_numpy(make_grid_kernel(cfg)).to(DEV)
     spec = H.nd_filter_spectrum(K, cfg.dims)
     y_full = H.nd_forward(v, xs, spec).clone()
     for grids in (1, 2, 3, 4):
-        ws = torch.empty(grids * 512 * 256 * 8, dtype=torch.uint8, device=DEV)
+        ws = torch.empty(grids * grid_bytes, dtype=torch.uint8, device=DEV)
         y_ws = H.nd_forward(v, xs, spec, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y_full, y_ws), f"workspace of {grids} grids"
