@@ -25,7 +25,8 @@ __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectr
            "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
            "in_projection", "out_projection", "block_forward", "block_workspace_bytes", "PreparedCall",
            "prepare_in_projection", "prepare_out_projection", "prepare_block_forward", "backward",
-           "backward_workspace_bytes", "filter_gen_li", "filter_gen_mr", "forward_fir"]
+           "backward_workspace_bytes", "filter_gen_li", "filter_gen_mr", "forward_fir", "nd_plan",
+           "nd_spectrum_bytes", "nd_workspace_bytes", "nd_filter_spectrum", "prepare_nd_forward", "nd_forward"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
