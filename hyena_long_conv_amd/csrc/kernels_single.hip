@@ -18,6 +18,9 @@ namespace hyena {
 #ifndef HYENA_XCD_MAP
 #define HYENA_XCD_MAP 1
 #endif
+#ifndef HYENA_SINGLE_PERSIST
+#define HYENA_SINGLE_PERSIST 1
+#endif
 #ifndef HYENA_SINGLE_E16_MIN
 #define HYENA_SINGLE_E16_MIN 16384
 #endif
@@ -128,7 +131,7 @@ __device__ __forceinline__ int row_of_workgroup(int wg, int B, int D) {
 template <int N, int IOT, bool EVEN, bool FULL, bool EXACT = false>
 __global__ void __launch_bounds__(SinglePlan<N>::T, HYENA_SINGLE_WAVES)
 k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, void* __restrict__ y,
-                 int B, int D, int NORD, int L, int64_t spec_stride) {
+                 int B, int D, int NORD, int L, int64_t spec_stride, int n_rows) {
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E, NV = FULL ? E : E / 2;
   constexpr bool IN = FULL || EXACT;
@@ -140,11 +143,15 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
   using Lds = typename P::Lds;
   const Lds lds2[2] = {Lds{smem}, Lds{smem + (P::PP ? N : 0)}};
   const int j = threadIdx.x;
-  const int r = row_of_workgroup(blockIdx.x, B, D), d = r % D;
-  const int64_t off = (int64_t)r * L;
   BlockFFT<N, E, typename P::R> fft;
   fft.init(j);
   const int64_t qs = spec_stride / 3;
+  // A workgroup takes rows wg, wg + gridDim.x, ... (one row when the grid
+  // covers them all).  Each row's first LDS store follows a barrier inside
+  // the forward FFT, so consecutive rows need no extra synchronisation.
+  for (int wg = blockIdx.x; wg < n_rows; wg += gridDim.x) {
+  const int r = row_of_workgroup(wg, B, D), d = r % D;
+  const int64_t off = (int64_t)r * L;
 
   cf u[E];
 #pragma unroll
@@ -191,6 +198,7 @@ k_single_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spe
       }
       u[i] = z;
     }
+  }
   }
 }
 
@@ -417,22 +425,36 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroups of kernel k that fit the GPU at once (0 if the query fails).
+template <class K>
+static int resident_workgroups(K k, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+template <int N, int IOT, bool EVEN, bool FULL, bool EXACT>
+static void launch_fwd_k(const ForwardArgs& a, hipStream_t s) {
+  const auto k = k_single_forward<N, IOT, EVEN, FULL, EXACT>;
+  int grid = a.n_rows;
+#if HYENA_SINGLE_PERSIST
+  // One resident set of workgroups walks all rows (a multiple of 8, so the
+  // XCD of virtual workgroup wg is still wg mod 8).
+  static const int cap = resident_workgroups(k, SinglePlan<N>::T) & ~7;
+  if (cap > 0 && grid > cap) grid = cap;
+#endif
+  hipLaunchKernelGGL(k, dim3(grid), dim3(SinglePlan<N>::T), 0, s, a.v, a.x, (const cf*)a.spec, a.y, a.B, a.D,
+                     a.NORD, (int)a.L, a.spec_stride, a.n_rows);
+}
+
 template <int N, int IOT>
 static hipError_t launch_fwd(const ForwardArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_rows), block(SinglePlan<N>::T);
-  const cf* sp = (const cf*)a.spec;
-  if (a.circular)   // L = 2N, even
-    hipLaunchKernelGGL((k_single_forward<N, IOT, true, true>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
-                       a.NORD, (int)a.L, a.spec_stride);
-  else if (a.L == N)
-    hipLaunchKernelGGL((k_single_forward<N, IOT, true, false, true>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B,
-                       a.D, a.NORD, (int)a.L, a.spec_stride);
-  else if (a.L % 2 == 0)
-    hipLaunchKernelGGL((k_single_forward<N, IOT, true, false>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
-                       a.NORD, (int)a.L, a.spec_stride);
-  else
-    hipLaunchKernelGGL((k_single_forward<N, IOT, false, false>), grid, block, 0, s, a.v, a.x, sp, a.y, a.B, a.D,
-                       a.NORD, (int)a.L, a.spec_stride);
+  if (a.circular) launch_fwd_k<N, IOT, true, true, false>(a, s);   // L = 2N, even
+  else if (a.L == N) launch_fwd_k<N, IOT, true, false, true>(a, s);
+  else if (a.L % 2 == 0) launch_fwd_k<N, IOT, true, false, false>(a, s);
+  else launch_fwd_k<N, IOT, false, false, false>(a, s);
   return hipGetLastError();
 }
 
