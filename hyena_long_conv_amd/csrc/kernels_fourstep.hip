@@ -51,6 +51,29 @@ template <int N2> struct RowCfg {
                                       typename Plan8<(N2 <= 8192 ? N2 : 8192)>::R>::type;
 };
 
+// Intermediate accesses (each element is written by one pass and read back
+// by the next, long after it left the caches).
+#ifndef HYENA_WORK_NT
+#define HYENA_WORK_NT 0
+#endif
+__device__ __forceinline__ cf ld_work(const cf* p) {
+  if constexpr (HYENA_WORK_NT) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+    return make_float2(w.x, w.y);
+  } else {
+    return *p;
+  }
+}
+__device__ __forceinline__ void st_work(cf* p, cf v) {
+  if constexpr (HYENA_WORK_NT) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(f32x2{v.x, v.y}, reinterpret_cast<f32x2*>(p));
+  } else {
+    *p = v;
+  }
+}
+
 // COL_OUT: as COL_LAST without the gate (the plain causal convolution).
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4 };
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
@@ -164,7 +187,7 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
   } else {
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      u[i] = valid ? buf[(int64_t)(j + i * S1) * a.n2 + col] : make_float2(0.f, 0.f);
+      u[i] = valid ? ld_work(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
     fft.template run<true>(u, lds, j);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
@@ -187,7 +210,7 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
     fft.template run<false>(u, lds, j);
     if (valid) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) buf[(int64_t)(j + i * S1) * a.n2 + col] = u[i];
+      for (int i = 0; i < E; ++i) st_work(buf + (int64_t)(j + i * S1) * a.n2 + col, u[i]);
     }
   }
 }
@@ -246,7 +269,7 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, N);
   const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, N);
 #pragma unroll
-  for (int i = 0; i < E; ++i) u[i] = cmul(row[j + i * S2], step_power<E>(tb, ts, i));
+  for (int i = 0; i < E; ++i) u[i] = cmul(ld_work(row + j + i * S2), step_power<E>(tb, ts, i));
   fft.template run<false>(u, lds, j);
 
   // bins k = k1 + n1*k2 with k2 = j + i*S2; mirror N-k at (k1m, k2m)
@@ -304,7 +327,7 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     for (int i = E / 2; i < E; ++i) u[i] = lds(j + i * S2);
     fft.template run<true>(u, lds, j);
 #pragma unroll
-    for (int i = 0; i < E; ++i) row[j + i * S2] = cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i));
+    for (int i = 0; i < E; ++i) st_work(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
   }
 }
 
