@@ -19,9 +19,12 @@
  * Conventions shared by every call:
  *   - Device pointers point to memory of the current HIP device; the caller
  *     allocates and frees all of it.  The library never allocates device
- *     memory, keeps no global state, and is reentrant.
+ *     memory and is reentrant; the only state it keeps across calls is the
+ *     resident-workgroup count of a kernel, looked up once.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     default stream) and returns; results are ready after the stream syncs.
+ *     No call allocates, clears memory or synchronises, so the calls can be
+ *     captured into a HIP graph and replayed.
  *   - Argument errors are detected on the host before anything is enqueued
  *     and returned as a status; nothing is written in that case.  A failed
  *     kernel launch returns HYENA_ERR_HIP.  Device faults surface at the
