@@ -266,7 +266,10 @@ k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int
 // spectrum, pair coefficients built on the fly) added into hacc[n], and the
 // adjoint step plus inverse FFT give the gradient of z_n.  Finally each
 // hacc[n] is inverse transformed into gh_n.
-template <int N, int IOT, bool EVEN>
+// HL: the filter-gradient accumulators live in LDS (NORD x N values of
+// dynamic shared memory; each thread only touches its own points, so no
+// barrier guards them) instead of the hacc workspace.
+template <int N, int IOT, bool EVEN, bool HL>
 __global__ void __launch_bounds__(SinglePlan<N>::T, 1)
 k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, const void* __restrict__ gy,
                   void* __restrict__ gv, OutPtrs gx, float* __restrict__ gh, cf* __restrict__ cbuf,
@@ -274,6 +277,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E, H2 = N / 2;
   __shared__ cf smem[N];
+  extern __shared__ cf hl[];
   const typename P::Lds lds{smem};
   const int j = threadIdx.x, d = blockIdx.x;
   BlockFFT<N, E, typename P::R> fft;
@@ -386,7 +390,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
         pz[i] = lds(j + i * S);
         gt[i] = lds(j + i * S - H2);
       }
-      cf* ha = hacc + ((int64_t)n * D + d) * N;
+      cf* ha = HL ? hl + n * N : hacc + ((int64_t)n * D + d) * N;
 #pragma unroll
       for (int i = 0; i < E; ++i) ha[j + i * S] = (b == 0) ? pz[i] : cadd(ha[j + i * S], pz[i]);
       fft.template run<true>(gt, lds, j);
@@ -398,7 +402,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
   }
   // filter gradients: inverse transform of each accumulated spectrum
   for (int n = 0; n < NORD; ++n) {
-    const cf* ha = hacc + ((int64_t)n * D + d) * N;
+    const cf* ha = HL ? hl + n * N : hacc + ((int64_t)n * D + d) * N;
     cf u[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) u[i] = ha[j + i * S];
@@ -413,15 +417,30 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
   }
 }
 
+#ifndef HYENA_BWD_LDS_ACC
+#define HYENA_BWD_LDS_ACC (52 * 1024)   // LDS budget per workgroup for accumulators in LDS (0: never)
+#endif
+
+template <int N, int IOT, bool EVEN, bool HL>
+static void launch_bwd_k(const BackwardArgs& a, size_t shared, hipStream_t s) {
+  hipLaunchKernelGGL((k_single_backward<N, IOT, EVEN, HL>), dim3(a.D), dim3(SinglePlan<N>::T), shared, s, a.v, a.x,
+                     (const cf*)a.spec, a.gy, a.gv, a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD,
+                     (int)a.L, a.spec_stride);
+}
+
 template <int N, int IOT>
 static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
-  const dim3 grid(a.D), block(SinglePlan<N>::T);
-  if (a.L % 2 == 0)
-    hipLaunchKernelGGL((k_single_backward<N, IOT, true>), grid, block, 0, s, a.v, a.x, (const cf*)a.spec, a.gy, a.gv,
-                       a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
-  else
-    hipLaunchKernelGGL((k_single_backward<N, IOT, false>), grid, block, 0, s, a.v, a.x, (const cf*)a.spec, a.gy,
-                       a.gv, a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD, (int)a.L, a.spec_stride);
+  // Accumulators in LDS when they and the FFT buffer fit the budget that
+  // keeps three workgroups per CU (the launch has only D workgroups).
+  const size_t acc = (size_t)a.NORD * N * sizeof(cf);
+  const bool hl = acc + N * sizeof(cf) <= (size_t)HYENA_BWD_LDS_ACC;
+  if (a.L % 2 == 0) {
+    if (hl) launch_bwd_k<N, IOT, true, true>(a, acc, s);
+    else launch_bwd_k<N, IOT, true, false>(a, 0, s);
+  } else {
+    if (hl) launch_bwd_k<N, IOT, false, true>(a, acc, s);
+    else launch_bwd_k<N, IOT, false, false>(a, 0, s);
+  }
   return hipGetLastError();
 }
 
