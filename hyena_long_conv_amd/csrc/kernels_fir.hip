@@ -51,9 +51,13 @@ __global__ void k_filter_gen_mr(const float* __restrict__ hhat, const float* __r
 // N*(Lh-1) earlier samples (zero before t = 0); each order consumes Lh-1 of
 // the halo, so after N orders exactly the tile remains, with nothing read
 // from other tiles.  Two LDS buffers alternate between orders.  A thread
-// computes FR consecutive outputs from a sliding register window: per tap
-// one LDS read of the window, one broadcast read of the tap, FR FMAs.
-constexpr int FIR_THREADS = 256, FR = 4;
+// computes FR = 4 consecutive outputs, taking the taps four at a time: one
+// 16-byte LDS read of the next four window samples, one broadcast 16-byte
+// read of four taps, 16 FMAs.  Taps are stored per order in rows of Lh4 =
+// Lh rounded up to 4 (zero beyond Lh), and each buffer has PAD zeroed
+// floats before it for the window reads left of the first output.
+constexpr int FIR_THREADS = 256, FR = 4, PAD = 8;
+typedef float fir_f4 __attribute__((ext_vector_type(4)));
 
 template <int IOT>
 __device__ __forceinline__ void ld4(const void* p, int64_t i, float (&o)[4]) {   // i a multiple of 4, in range
@@ -79,14 +83,18 @@ __global__ void __launch_bounds__(FIR_THREADS) k_fir_forward(const void* __restr
   const int64_t t0 = (int64_t)blockIdx.y * TT;
   const int Hh = (NORD * (Lh - 1) + 3) / 4 * 4;  // halo, a multiple of 4 (extra samples are harmless)
   const int W = TT + Hh;                         // buffer index i <-> time t0 - Hh + i
-  float* b0 = sm;
-  float* b1 = sm + W;
-  float* taps = sm + 2 * W;
+  const int Lh4 = (Lh + 3) / 4 * 4;
+  float* b0 = sm + PAD;
+  float* b1 = sm + 2 * PAD + W;
+  float* taps = sm + 2 * (PAD + W);
   const int64_t off = (int64_t)row * L;
   const int tid = threadIdx.x;
   const bool vec = (L & 3) == 0;                 // rows start on 16-byte (fp32) / 8-byte (bf16) boundaries
-  for (int i = tid; i < NORD * Lh; i += FIR_THREADS)
-    taps[i] = h[((int64_t)(i / Lh) * D + d) * Lh + (i % Lh)];
+  if (tid < 2 * PAD) sm[tid < PAD ? tid : W + tid] = 0.f;   // the two pads
+  for (int i = tid; i < NORD * Lh4; i += FIR_THREADS) {
+    const int n = i / Lh4, k = i - n * Lh4;
+    taps[i] = k < Lh ? h[((int64_t)n * D + d) * Lh + k] : 0.f;
+  }
   for (int i4 = 4 * tid; i4 < W; i4 += 4 * FIR_THREADS) {
     const int64_t t = t0 - Hh + i4;
     float o[4];
@@ -97,27 +105,31 @@ __global__ void __launch_bounds__(FIR_THREADS) k_fir_forward(const void* __restr
       for (int q = 0; q < 4; ++q) o[q] = (t + q >= 0 && t + q < L) ? IO<IOT>::ld(v, off + t + q) : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b0[i4 + q] = o[q];
+    for (int q = 0; q < 4; ++q) {
+      b0[i4 + q] = o[q];
+      b1[i4 + q] = 0.f;   // an order writes b1 from its first full-history output on; the
+    }                     // rest must hold finite values, since zero taps beyond Lh still read it
   }
   __syncthreads();
   for (int n = 0; n < NORD; ++n) {
     const int lo = (n + 1) * (Lh - 1);           // first index with a full history
     const int lo4 = lo / 4 * 4;
-    const float* tp = taps + n * Lh;
+    const float* tp = taps + n * Lh4;
     const void* xn = x.p[n];
     for (int i0 = lo4 + FR * tid; i0 < W; i0 += FR * FIR_THREADS) {
-      // outputs i0 .. i0+3; window w[r] = b0[i0 + r - k] for the current tap k
+      // outputs i0 .. i0+3: acc[r] = sum_k h[k] b0[i0 + r - k].  For the taps
+      // k0 .. k0+3, cur = b0[i0-k0 .. i0-k0+3] and prv = the four before it
+      // (the lowest read is i0 - Lh4 >= -7, inside the pad).
       float acc[FR] = {0.f, 0.f, 0.f, 0.f};
-      float w[FR];
+      fir_f4 cur = *reinterpret_cast<const fir_f4*>(b0 + i0);
+      for (int k0 = 0; k0 < Lh4; k0 += 4) {
+        const fir_f4 prv = *reinterpret_cast<const fir_f4*>(b0 + i0 - k0 - 4);
+        const fir_f4 hv = *reinterpret_cast<const fir_f4*>(tp + k0);
 #pragma unroll
-      for (int r = 0; r < FR; ++r) w[r] = b0[i0 + r];
-      for (int k = 0; k < Lh; ++k) {
-        const float hk = tp[k];
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int r = 0; r < FR; ++r) acc[r] = fmaf(hk, w[r], acc[r]);
-#pragma unroll
-        for (int r = FR - 1; r > 0; --r) w[r] = w[r - 1];
-        w[0] = (i0 - k - 1 >= 0) ? b0[i0 - k - 1] : 0.f;
+          for (int r = 0; r < FR; ++r) acc[r] = fmaf(hv[m], r >= m ? cur[r - m] : prv[4 + r - m], acc[r]);
+        cur = prv;
       }
       const int64_t t = t0 - Hh + i0;
       float xv[4];
@@ -177,7 +189,7 @@ hipError_t fir_forward(const ForwardArgs& a, const float* h, int Lh, hipStream_t
   const int TT = 2048;
   const int64_t tiles = (a.L + TT - 1) / TT;
   const int halo = (a.NORD * (Lh - 1) + 3) / 4 * 4;
-  const size_t lds = (size_t)(2 * (TT + halo) + a.NORD * Lh) * sizeof(float);
+  const size_t lds = (size_t)(2 * (PAD + TT + halo) + a.NORD * ((Lh + 3) / 4 * 4)) * sizeof(float);
   const dim3 grid((unsigned)a.n_rows, (unsigned)tiles), block(FIR_THREADS);
   if (a.io == 0)
     hipLaunchKernelGGL(k_fir_forward<0>, grid, block, lds, s, a.v, a.x, h, Lh, a.y, a.D, a.NORD, a.L, TT);

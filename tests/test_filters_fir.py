@@ -60,6 +60,8 @@ FIR_CASES = [
     (1, 1, 1, 1, 1, "fp32"), (2, 2, 3, 100, 3, "fp32"), (2, 1, 4, 5000, 7, "fp32"), (3, 2, 2, 4097, 14, "fp32"),
     (8, 1, 2, 3000, 5, "fp32"), (2, 1, 3, 2500, 256, "fp32"), (2, 2, 3, 1000, 4, "bf16"), (2, 1, 2, 9000, 128, "bf16"),
     (2, 1, 2, 7, 40, "fp32"),
+    # tap counts that are not multiples of 4 over several orders and tiles
+    (3, 2, 3, 6000, 6, "fp32"), (4, 1, 2, 5000, 9, "bf16"),
 ]
 
 
