@@ -91,32 +91,90 @@ inline dim3 row_grid(int64_t rows, int64_t L) {
   return dim3((unsigned)bx, (unsigned)(by < 1 ? 1 : by));
 }
 
+// V4 (L a multiple of 4): a thread takes positions t .. t+3 of a row, whose
+// mirror images L-4-t .. L-1-t are one aligned group of four as well, so
+// every access is a 16-byte (fp32) or 8-byte (bf16) vector.
+#define ROW_LOOP4(rows, L)                                                                        \
+  for (int64_t r = blockIdx.y; r < (rows); r += gridDim.y)                                       \
+    for (int64_t t = 4 * (blockIdx.x * (int64_t)blockDim.x + threadIdx.x); t < (L);                 \
+         t += 4 * (int64_t)gridDim.x * blockDim.x)
+
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st_f4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <int IOT>
+__device__ __forceinline__ void st4_io(void* p, int64_t i, float a, float b, float c, float d) {
+  if constexpr (IOT == 0) {
+    st_f4(static_cast<float*>(p) + i, a, b, c, d);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
+  }
+}
+
 // One order's elementwise work on the incoming gradient g (held reversed,
 // g = R(gsrc), when REV: the previous adjoint convolution leaves it so):
 //   gx = g * c  (I/O dtype)   and   t2 = R(g * x)  (fp32).
-template <int IOT, bool REV>
+template <int IOT, bool REV, bool V4>
 __global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restrict__ c, const void* __restrict__ x,
                           void* __restrict__ gx, float* __restrict__ t2, int64_t rows, int64_t L) {
-  ROW_LOOP(rows, L) {
-    const int64_t i = r * L + t, ri = r * L + (L - 1 - t);
-    const float g = gsrc[REV ? ri : i];
-    IO<IOT>::st(gx, i, g * c[i]);
-    t2[ri] = g * IO<IOT>::ld(x, i);
+  if constexpr (V4) {
+    ROW_LOOP4(rows, L) {
+      const int64_t i = r * L + t, ri = r * L + (L - 4 - t);     // ri: mirror of t + 3
+      float g[4], xv[4];
+      if constexpr (REV) {
+        const float4 w = ld_f4(gsrc + ri);
+        g[0] = w.w; g[1] = w.z; g[2] = w.y; g[3] = w.x;
+      } else {
+        const float4 w = ld_f4(gsrc + i);
+        g[0] = w.x; g[1] = w.y; g[2] = w.z; g[3] = w.w;
+      }
+      const float4 cv = ld_f4(c + i);
+      ld4_io<IOT>(x, i, xv);
+      st4_io<IOT>(gx, i, g[0] * cv.x, g[1] * cv.y, g[2] * cv.z, g[3] * cv.w);
+      st_f4(t2 + ri, g[3] * xv[3], g[2] * xv[2], g[1] * xv[1], g[0] * xv[0]);
+    }
+  } else {
+    ROW_LOOP(rows, L) {
+      const int64_t i = r * L + t, ri = r * L + (L - 1 - t);
+      const float g = gsrc[REV ? ri : i];
+      IO<IOT>::st(gx, i, g * c[i]);
+      t2[ri] = g * IO<IOT>::ld(x, i);
+    }
   }
 }
 
 // out = R(a) in the I/O dtype (the final gradient of v)
-template <int IOT>
+template <int IOT, bool V4>
 __global__ void k_bw_store_rev(const float* __restrict__ a, void* __restrict__ out, int64_t rows, int64_t L) {
-  ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + (L - 1 - t)]);
+  if constexpr (V4) {
+    ROW_LOOP4(rows, L) {
+      const float4 w = ld_f4(a + r * L + (L - 4 - t));
+      st4_io<IOT>(out, r * L + t, w.w, w.z, w.y, w.x);
+    }
+  } else {
+    ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + (L - 1 - t)]);
+  }
 }
 
 // gh[d][k] = sum_b t[b*D + d][L-1-k]  (fixed batch order: deterministic)
+template <bool V4>
 __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restrict__ gh, int B, int D, int64_t L) {
-  ROW_LOOP(D, L) {
-    float acc = 0.f;
-    for (int b = 0; b < B; ++b) acc += tt[((int64_t)b * D + r) * L + (L - 1 - t)];
-    gh[r * L + t] = acc;
+  if constexpr (V4) {
+    ROW_LOOP4(D, L) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int b = 0; b < B; ++b) {
+        const float4 w = ld_f4(tt + ((int64_t)b * D + r) * L + (L - 4 - t));
+        acc.x += w.w; acc.y += w.z; acc.z += w.y; acc.w += w.x;
+      }
+      st_f4(gh + r * L + t, acc.x, acc.y, acc.z, acc.w);
+    }
+  } else {
+    ROW_LOOP(D, L) {
+      float acc = 0.f;
+      for (int b = 0; b < B; ++b) acc += tt[((int64_t)b * D + r) * L + (L - 1 - t)];
+      gh[r * L + t] = acc;
+    }
   }
 }
 
@@ -137,9 +195,16 @@ template <int IOT>
 hipError_t bw_step_io(bool rev, const float* g, const float* c, const void* x, void* gx, float* t2, int64_t L,
                       int64_t n, hipStream_t s) {
   const int64_t rows = n / L;
-  const dim3 grid = row_grid(rows, L), blk(EW_THREADS);
-  if (rev) hipLaunchKernelGGL((k_bw_step<IOT, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
-  else hipLaunchKernelGGL((k_bw_step<IOT, false>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+  const dim3 blk(EW_THREADS);
+  if (L % 4 == 0) {
+    const dim3 grid = row_grid(rows, L / 4);
+    if (rev) hipLaunchKernelGGL((k_bw_step<IOT, true, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+    else hipLaunchKernelGGL((k_bw_step<IOT, false, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+  } else {
+    const dim3 grid = row_grid(rows, L);
+    if (rev) hipLaunchKernelGGL((k_bw_step<IOT, true, false>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+    else hipLaunchKernelGGL((k_bw_step<IOT, false, false>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+  }
   return hipGetLastError();
 }
 
@@ -230,16 +295,26 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
     BW_TRY(fourstep_spectrum(sa, p, s));
     BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
-    hipLaunchKernelGGL(k_bw_batch_sum_rev, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
-                       a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
+    if (L % 4 == 0)
+      hipLaunchKernelGGL(k_bw_batch_sum_rev<true>, row_grid(D, L / 4), dim3(EW_THREADS), 0, s, T1,
+                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
+    else
+      hipLaunchKernelGGL(k_bw_batch_sum_rev<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
+                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
     BW_TRY(hipGetLastError());
     // adjoint: g_n = R(h_n conv T2); kept reversed in T1
     BW_TRY(bw_conv(p, spec_n(nn), T2, T1, (int)B, (int)D, false, work, w.rows_per_group, s));
     gcur = T1;
     grev = true;
   }
-  if (a.io == 0) hipLaunchKernelGGL(k_bw_store_rev<0>, row_grid(R, L), dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
-  else hipLaunchKernelGGL(k_bw_store_rev<1>, row_grid(R, L), dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+  const dim3 rg = row_grid(R, L % 4 == 0 ? L / 4 : L);
+  if (L % 4 == 0) {
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+  } else {
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, false>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+  }
   BW_TRY(hipGetLastError());
 #undef BW_TRY
   return hipSuccess;
