@@ -123,6 +123,11 @@ def lib() -> ctypes.CDLL:
     L.hyena_forward_workspace_bytes_ex.restype = i64
     L.hyena_forward_ex.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, i32, vp, i64, vp]
     L.hyena_forward_ex.restype = i32
+    L.hyena_backward_workspace_bytes_ex.argtypes = [i64, i32, i32, i64, i32, i32]
+    L.hyena_backward_workspace_bytes_ex.restype = i64
+    L.hyena_backward_ex.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, ctypes.POINTER(vp), vp, i64, i32, i32, i64,
+                                    i32, i32, vp, i64, vp]
+    L.hyena_backward_ex.restype = i32
     i64p = ctypes.POINTER(i64)
     L.hyena_nd_plan.argtypes = [i32, i64p, i32, i64p]
     L.hyena_nd_plan.restype = i32
@@ -430,14 +435,18 @@ def prepare_block_forward(u, bp: dict, spec, out, workspace):
 
 # ---------------------------------------------------------------- backward
 
-def backward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32") -> int:
-    return int(lib().hyena_backward_workspace_bytes(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16))
+def backward_workspace_bytes(B: int, D: int, N: int, L: int, io: str = "fp32", circular: bool = False) -> int:
+    return int(lib().hyena_backward_workspace_bytes_ex(B, D, N, L, HYENA_FP32 if io == "fp32" else HYENA_BF16,
+                                                       _mode(circular)))
 
 
-def backward(v, xs, spec, gy, workspace=None):
+def backward(v, xs, spec, gy, workspace=None, circular: bool | None = None):
     """Gradients (gv, [gx_1..gx_N], gh) of a loss with dloss/dy = gy through
-    y = forward(v, xs, spec); gh [N, D, L] fp32 summed over the batch."""
+    y = forward(v, xs, spec); gh [N, D, L] fp32 summed over the batch.  The
+    convolution mode defaults to the one the spectrum was built for."""
     import torch
+    if circular is None:
+        circular = getattr(spec, "_hyena_circular", False)
     io = _io_of(v)
     _need_cuda(v, "v", v.dtype)
     _need_cuda(gy, "gy", v.dtype)
@@ -448,16 +457,16 @@ def backward(v, xs, spec, gy, workspace=None):
     gv = torch.empty_like(v)
     gxs = [torch.empty_like(v) for _ in range(N)]
     gh = torch.empty((N, D, L), dtype=torch.float32, device=v.device)
-    wsb = backward_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16")
+    wsb = backward_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16", circular)
     if wsb < 0:
         raise HyenaError(3, "hyena_backward_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
     xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
     gp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in gxs])
-    _check(lib().hyena_backward(_ptr(v), xp, _ptr(spec), _ptr(gy), _ptr(gv), gp, _ptr(gh), B, D, N, L, io,
-                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(v)),
-           "hyena_backward")
+    _check(lib().hyena_backward_ex(_ptr(v), xp, _ptr(spec), _ptr(gy), _ptr(gv), gp, _ptr(gh), B, D, N, L, io,
+                                   _mode(circular), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(v)), "hyena_backward")
     return gv, gxs, gh
 
 

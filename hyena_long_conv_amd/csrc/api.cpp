@@ -375,7 +375,7 @@ namespace {
 constexpr int64_t kBackwardMaxN = 8192;   // complex points of the single-pass backward
 
 int64_t bwd_ws_single(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
-  const int64_t cb = (NORD * B * D * (p.N / 2) * 8 + 255) / 256 * 256;
+  const int64_t cb = (NORD * B * D * (p.circular ? p.N : p.N / 2) * 8 + 255) / 256 * 256;
   return cb + NORD * D * p.N * 8;
 }
 
@@ -396,8 +396,8 @@ int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // -1 when no backward serves the plan
 int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
-  if (p.circular) return -1;
   if (bwd_single(p)) return bwd_ws_single(p, B, D, NORD);
+  if (p.circular) return -1;     // circular rows beyond the single-pass backward: not served
   PlanInfo fs;
   if (bwd_long_plan(p, &fs)) return -1;
   int64_t t = long_backward_layout(fs, B, D, NORD).total;
@@ -407,10 +407,16 @@ int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
 }  // namespace
 
 int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io) {
+  return hyena_backward_workspace_bytes_ex(B, D, N, L, io, HYENA_CONV_LINEAR);
+}
+
+int64_t hyena_backward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
+                                          hyena_conv_mode mode) {
   if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L) || N > kMaxOrder) return -1;
   if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
+  if (mode != HYENA_CONV_LINEAR && mode != HYENA_CONV_CIRCULAR) return -1;
   PlanInfo p;
-  if (plan_env(L, &p)) return -1;
+  if (plan_env(L, &p, mode)) return -1;
   if (B * D > ((int64_t)1 << 30)) return -1;
   return bwd_ws(p, B, D, N);
 }
@@ -418,14 +424,23 @@ int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t 
 hyena_status hyena_backward(const void* v, const void* const* x, const void* spec, const void* gy, void* gv,
                             void* const* gx, float* gh, int64_t B, int32_t D, int32_t N, int64_t L,
                             hyena_dtype io, void* workspace, int64_t workspace_bytes, void* stream) {
+  return hyena_backward_ex(v, x, spec, gy, gv, gx, gh, B, D, N, L, io, HYENA_CONV_LINEAR, workspace,
+                           workspace_bytes, stream);
+}
+
+hyena_status hyena_backward_ex(const void* v, const void* const* x, const void* spec, const void* gy, void* gv,
+                               void* const* gx, float* gh, int64_t B, int32_t D, int32_t N, int64_t L,
+                               hyena_dtype io, hyena_conv_mode mode, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
   if (!v || !x || !spec || !gy || !gv || !gx || !gh || !workspace) return HYENA_ERR_NULL;
   if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
   if (N > kMaxOrder) return HYENA_ERR_UNSUPPORTED;
   if (io != HYENA_FP32 && io != HYENA_BF16) return HYENA_ERR_UNSUPPORTED;
+  if (mode != HYENA_CONV_LINEAR && mode != HYENA_CONV_CIRCULAR) return HYENA_ERR_UNSUPPORTED;
   for (int n = 0; n < N; ++n)
     if (!x[n] || !gx[n]) return HYENA_ERR_NULL;
   PlanInfo p;
-  const int c = plan_env(L, &p);
+  const int c = plan_env(L, &p, mode);
   if (c) return from_plan_code(c);
   if (B * D > ((int64_t)1 << 30)) return HYENA_ERR_UNSUPPORTED;
   const int64_t need = bwd_ws(p, B, D, N);
@@ -461,6 +476,7 @@ hyena_status hyena_backward(const void* v, const void* const* x, const void* spe
   a.B = (int)B; a.D = D; a.NORD = N; a.L = L;
   a.io = (io == HYENA_FP32) ? 0 : 1;
   a.spec_stride = p.spec_stride;
+  a.circular = p.circular;
   if (!bwd_single(p)) {
     PlanInfo fs;
     if (bwd_long_plan(p, &fs)) return HYENA_ERR_UNSUPPORTED;

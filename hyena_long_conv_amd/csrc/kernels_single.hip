@@ -269,13 +269,16 @@ k_single_spectrum(const float* __restrict__ h, cf* __restrict__ spec, int L, int
 // HL: the filter-gradient accumulators live in LDS (NORD x N values of
 // dynamic shared memory; each thread only touches its own points, so no
 // barrier guards them) instead of the hacc workspace.
-template <int N, int IOT, bool EVEN, bool HL>
+// FULL: circular mode (L = 2N, every point of the row is a sample).
+template <int N, int IOT, bool EVEN, bool HL, bool FULL>
 __global__ void __launch_bounds__(SinglePlan<N>::T, 1)
 k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, const void* __restrict__ gy,
                   void* __restrict__ gv, OutPtrs gx, float* __restrict__ gh, cf* __restrict__ cbuf,
                   cf* __restrict__ hacc, int B, int D, int NORD, int L, int64_t spec_stride) {
   using P = SinglePlan<N>;
   constexpr int E = P::E, S = N / E, H2 = N / 2;
+  constexpr int NV = FULL ? E : E / 2;           // points of a thread that hold samples
+  constexpr int CBS = FULL ? N : H2;             // saved c_n per row (packed points)
   __shared__ cf smem[N];
   extern __shared__ cf hl[];
   const typename P::Lds lds{smem};
@@ -292,7 +295,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
     cf u[E];
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      u[i] = (i < E / 2) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
+      u[i] = (i < NV) ? ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L) : make_float2(0.f, 0.f);
     // forward, saving c_n (packed points j + i*S, i < E/2)
     for (int n = 0; n < NORD; ++n) {
       PairCoeffs<N, E> pc;
@@ -300,11 +303,11 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
       fft.template run<false>(u, lds, j);
       spectral_step<N, E, true>(u, lds, j, pc);
       fft.template run<true>(u, lds, j);
-      cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * H2;
+      cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * CBS;
       const void* xn = x.p[n];
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        if (i < E / 2) {
+        if (i < NV) {
           cb[j + i * S] = u[i];
           u[i] = had(ld_pair<IOT, EVEN, true>(xn, off, 2 * (int64_t)(j + i * S), L), u[i]);
         } else {
@@ -313,12 +316,12 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
       }
     }
     // backward
-    cf g[E / 2];
+    cf g[NV];
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) g[i] = ld_pair<IOT, EVEN, true>(gy, off, 2 * (int64_t)(j + i * S), L);
+    for (int i = 0; i < NV; ++i) g[i] = ld_pair<IOT, EVEN, true>(gy, off, 2 * (int64_t)(j + i * S), L);
     for (int n = NORD - 1; n >= 0; --n) {
-      const cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * H2;
-      const cf* cbp = cbuf + (((int64_t)(n > 0 ? n - 1 : 0) * B + b) * D + d) * H2;
+      const cf* cb = cbuf + (((int64_t)n * B + b) * D + d) * CBS;
+      const cf* cbp = cbuf + (((int64_t)(n > 0 ? n - 1 : 0) * B + b) * D + d) * CBS;
       const void* xn = x.p[n];
       const void* xp = x.p[n > 0 ? n - 1 : 0];
       PairCoeffs<N, E> pc;
@@ -326,7 +329,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
       cf zt[E], gt[E];
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        if (i < E / 2) {
+        if (i < NV) {
           const int64_t t = 2 * (int64_t)(j + i * S);
           const cf c = cb[j + i * S];
           st_pair<IOT, EVEN>(gx.p[n], off, t, L, had(g[i], c));                 // gx_n = g * c_n
@@ -395,10 +398,10 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
       for (int i = 0; i < E; ++i) ha[j + i * S] = (b == 0) ? pz[i] : cadd(ha[j + i * S], pz[i]);
       fft.template run<true>(gt, lds, j);
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) g[i] = gt[i];
+      for (int i = 0; i < NV; ++i) g[i] = gt[i];
     }
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) st_pair<IOT, EVEN>(gv, off, 2 * (int64_t)(j + i * S), L, g[i]);
+    for (int i = 0; i < NV; ++i) st_pair<IOT, EVEN>(gv, off, 2 * (int64_t)(j + i * S), L, g[i]);
   }
   // filter gradients: inverse transform of each accumulated spectrum
   for (int n = 0; n < NORD; ++n) {
@@ -409,7 +412,7 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
     fft.template run<true>(u, lds, j);
     float* out = gh + ((int64_t)n * D + d) * L;
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int64_t t = 2 * (int64_t)(j + i * S);
       if (t < L) out[t] = u[i].x;
       if (t + 1 < L) out[t + 1] = u[i].y;
@@ -421,9 +424,9 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
 #define HYENA_BWD_LDS_ACC (52 * 1024)   // LDS budget per workgroup for accumulators in LDS (0: never)
 #endif
 
-template <int N, int IOT, bool EVEN, bool HL>
+template <int N, int IOT, bool EVEN, bool HL, bool FULL = false>
 static void launch_bwd_k(const BackwardArgs& a, size_t shared, hipStream_t s) {
-  hipLaunchKernelGGL((k_single_backward<N, IOT, EVEN, HL>), dim3(a.D), dim3(SinglePlan<N>::T), shared, s, a.v, a.x,
+  hipLaunchKernelGGL((k_single_backward<N, IOT, EVEN, HL, FULL>), dim3(a.D), dim3(SinglePlan<N>::T), shared, s, a.v, a.x,
                      (const cf*)a.spec, a.gy, a.gv, a.gx, a.gh, (cf*)a.cbuf, (cf*)a.hacc, a.B, a.D, a.NORD,
                      (int)a.L, a.spec_stride);
 }
@@ -434,7 +437,10 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
   // keeps three workgroups per CU (the launch has only D workgroups).
   const size_t acc = (size_t)a.NORD * N * sizeof(cf);
   const bool hl = acc + N * sizeof(cf) <= (size_t)HYENA_BWD_LDS_ACC;
-  if (a.L % 2 == 0) {
+  if (a.circular) {   // L = 2N, even
+    if (hl) launch_bwd_k<N, IOT, true, true, true>(a, acc, s);
+    else launch_bwd_k<N, IOT, true, false, true>(a, 0, s);
+  } else if (a.L % 2 == 0) {
     if (hl) launch_bwd_k<N, IOT, true, true>(a, acc, s);
     else launch_bwd_k<N, IOT, true, false>(a, 0, s);
   } else {

@@ -85,12 +85,13 @@ struct BackwardArgs {
   void* gv;
   OutPtrs gx;
   float* gh;             // [N][D][L]
-  void* cbuf;            // workspace: N * B * D * N_c/2 complex
+  void* cbuf;            // workspace: N * B * D * N_c/2 complex (N_c when circular)
   void* hacc;            // workspace: N * D * N_c complex
   int B, D, NORD;
   int64_t L;
   int io;
   int64_t spec_stride;
+  int circular;          // single path, L = 2 N_c: periodic convolution
 };
 
 hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);

@@ -197,8 +197,11 @@ hyena_status hyena_forward_fir(const void* v, const void* const* x, const float*
  * the forward's four-step causal convolution and a row reversal, with the
  * forward's c_n kept in the workspace (about (N + 4) * B * D * L * 4 bytes
  * plus per-row spectra; a spectrum built on the single path is rewritten
- * into the four-step layout there).  Linear mode only.  Errors as hyena_forward, plus ALIAS for an output
- * overlapping an input or another output.
+ * into the four-step layout there).  Errors as hyena_forward, plus ALIAS for an output overlapping an
+ * input or another output.  hyena_backward_ex takes the convolution mode (see the circular mode below):
+ * circular rows (periodic convolution, c[t] = sum_k h[k] z[(t - k) mod L], whose adjoint and filter
+ * gradient are the circular correlations) are served up to L = 16384 by the one-launch kernel;
+ * longer circular rows return HYENA_ERR_UNSUPPORTED and the workspace query -1.
  */
 int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
 
@@ -286,6 +289,12 @@ int64_t hyena_forward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_
 hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
                               int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
                               void* workspace, int64_t workspace_bytes, void* stream);
+int64_t hyena_backward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io,
+                                          hyena_conv_mode mode);
+hyena_status hyena_backward_ex(const void* v, const void* const* x, const void* spec, const void* gy, void* gv,
+                               void* const* gx, float* gh, int64_t B, int32_t D, int32_t N, int64_t L,
+                               hyena_dtype io, hyena_conv_mode mode, void* workspace, int64_t workspace_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * Convolutions on 2-D and 3-D grids (gist.science HyenaND summary, "手法:

@@ -107,6 +107,8 @@ __all__ = [
     "filter_gen_li",
     "filter_gen_mr",
     "circular_conv",
+    "circular_conv_adjoint",
+    "circular_filter_correlation",
     "ndfft",
     "nd_conv_direct",
     "nd_conv_fft",
@@ -396,14 +398,22 @@ def filter_correlation(g: np.ndarray, z: np.ndarray) -> np.ndarray:
     return np.real(fft(np.conj(fft(zp)) * fft(gp), inverse=True))[..., :L]
 
 
-def hyena_backward(v: np.ndarray, xs, h: np.ndarray, gy: np.ndarray, conv=causal_conv):
+def hyena_backward(v: np.ndarray, xs, h: np.ndarray, gy: np.ndarray, conv=causal_conv, circular: bool = False):
     """Gradients of a scalar loss with dloss/dy = gy through y = z_{N+1}:
     returns (gv, [gx_1..gx_N], gh) with gh [N, D, L] summed over the batch.
 
     Forward intermediates: z_1 = v, c_n = h_n conv z_n, z_{n+1} = x_n * c_n.
     Backward, n = N..1, with g = dloss/dz_{n+1}: gx_n = g * c_n;
     gc = g * x_n; gh_n = sum_b corr(gc, z_n); g <- adjoint conv of gc by h_n.
+    circular: the convolution is periodic (conv defaults to circular_conv),
+    and the adjoint and the correlation are the periodic ones.
     """
+    if circular:
+        if conv is causal_conv:
+            conv = circular_conv
+        adjoint, correlation = circular_conv_adjoint, circular_filter_correlation
+    else:
+        adjoint, correlation = causal_conv_adjoint, filter_correlation
     v = np.asarray(v, np.float64)
     h = np.asarray(h, np.float64)
     N = h.shape[0]
@@ -420,8 +430,8 @@ def hyena_backward(v: np.ndarray, xs, h: np.ndarray, gy: np.ndarray, conv=causal
         x = np.asarray(xs[n], np.float64)
         gxs[n] = g * cs[n]
         gc = g * x
-        gh[n] = np.sum(filter_correlation(gc, zs[n]), axis=batch_axes) if batch_axes else filter_correlation(gc, zs[n])
-        g = causal_conv_adjoint(h[n], gc)
+        gh[n] = np.sum(correlation(gc, zs[n]), axis=batch_axes) if batch_axes else correlation(gc, zs[n])
+        g = adjoint(h[n], gc)
     return g, gxs, gh
 
 
@@ -461,6 +471,34 @@ def circular_conv(h: np.ndarray, z: np.ndarray) -> np.ndarray:
             out += h[..., k:k + 1] * np.roll(z, k, axis=-1)
         return out
     return np.real(fft(fft(h) * fft(z), inverse=True))
+
+
+def circular_conv_adjoint(h: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Transpose of the periodic convolution c = h conv z applied to g:
+    out[..., s] = sum_t h[..., (t - s) mod L] * g[..., t]."""
+    h = np.asarray(h, np.float64)
+    g = np.asarray(g, np.float64)
+    L = g.shape[-1]
+    if L <= DIRECT_MAX_L:
+        out = np.zeros(np.broadcast_shapes(h.shape[:-1], g.shape[:-1]) + (L,))
+        for k in range(L):
+            out += h[..., k:k + 1] * np.roll(g, -k, axis=-1)
+        return out
+    return np.real(fft(np.conj(fft(h)) * fft(g), inverse=True))
+
+
+def circular_filter_correlation(g: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Gradient of the periodic c = h conv z with respect to h, contracted
+    with g: out[..., k] = sum_t g[..., t] * z[..., (t - k) mod L]."""
+    g = np.asarray(g, np.float64)
+    z = np.asarray(z, np.float64)
+    L = g.shape[-1]
+    if L <= DIRECT_MAX_L:
+        out = np.zeros(np.broadcast_shapes(g.shape, z.shape))
+        for k in range(L):
+            out[..., k] = np.sum(g * np.roll(z, k, axis=-1), axis=-1)
+        return out
+    return np.real(fft(np.conj(fft(z)) * fft(g), inverse=True))
 
 
 # ---------------------------------------------------------------------------

@@ -39,19 +39,20 @@ def _clean_env(monkeypatch):
     monkeypatch.delenv("HYENA_FOURSTEP_N1", raising=False)
 
 
-def _run(N, B, D, L, io, channels=None, seed=31):
+def _run(N, B, D, L, io, channels=None, seed=31, circular=False):
     cfg = Config("bwd", N, B, D, L, io, 32, seed)
     p = make_filter_params(cfg, bias_scale=0.2)
     v, xs = make_activations(cfg, DEV)
     g = torch.Generator(device=DEV); g.manual_seed(seed + 7)
     gy = torch.randn((B, D, L), generator=g, device=DEV).to(v.dtype)
     h = H.filter_gen(params_to_device(p), L)
-    spec = H.filter_spectrum(h)
+    spec = H.filter_spectrum(h, circular=circular)
     gv, gxs, gh = H.backward(v, xs, spec, gy)
     torch.cuda.synchronize()
     ds = list(range(D)) if channels is None else channels
     hn = _np(h)[:, ds]
-    rv, rxs, rgh = O.hyena_backward(_np(v)[:, ds], [_np(x)[:, ds] for x in xs], hn, _np(gy)[:, ds])
+    rv, rxs, rgh = O.hyena_backward(_np(v)[:, ds], [_np(x)[:, ds] for x in xs], hn, _np(gy)[:, ds],
+                                    circular=circular)
     return (_np(gv)[:, ds], [_np(t)[:, ds] for t in gxs], _np(gh)[:, ds]), (rv, rxs, rgh)
 
 
@@ -72,6 +73,20 @@ def _check(got, ref, io):
 def test_backward_matches_oracle(N, B, D, L, io):
     got, ref = _run(N, B, D, L, io)
     _check(got, ref, io)
+
+
+@pytest.mark.parametrize("N,B,D,L,io", [(1, 1, 2, 128, "fp32"), (2, 3, 4, 256, "fp32"), (3, 2, 3, 2048, "fp32"),
+                                        (2, 1, 2, 16384, "fp32"), (2, 2, 3, 1024, "bf16")])
+def test_backward_circular_matches_oracle(N, B, D, L, io):
+    """Periodic convolution (L = FFT length): the adjoint and the filter
+    gradient are circular correlations."""
+    got, ref = _run(N, B, D, L, io, circular=True)
+    _check(got, ref, io)
+
+
+def test_backward_circular_beyond_one_launch_is_unsupported():
+    assert H.backward_workspace_bytes(1, 2, 2, 32768, circular=True) == -1
+    assert H.backward_workspace_bytes(1, 2, 2, 16384, circular=True) > 0
 
 
 def test_backward_full_width_sampled_channels():

@@ -82,3 +82,66 @@ def test_backward_order2_by_dense_matrices():
     assert np.allclose(gv[0], T1.T @ X1 @ T2.T @ X2 @ gy, atol=1e-12)
     assert np.allclose(gxs[1][0], gy * (T2 @ X1 @ T1 @ v), atol=1e-12)
     assert np.allclose(gxs[0][0], (T2.T @ X2 @ gy) * (T1 @ v), atol=1e-12)
+
+
+# ------------------------------------------------------------ circular mode
+
+def _circulant(h, L):
+    C = np.zeros((L, L))
+    for t in range(L):
+        for k in range(L):
+            C[t, (t - k) % L] += h[k]
+    return C
+
+
+def test_circular_adjoint_is_the_circulant_transpose():
+    L = 8
+    h = rng.standard_normal(L); g = rng.standard_normal(L); z = rng.standard_normal(L)
+    C = _circulant(h, L)
+    assert np.allclose(O.circular_conv(h, z), C @ z, atol=1e-12)
+    assert np.allclose(O.circular_conv_adjoint(h, g), C.T @ g, atol=1e-12)
+
+
+def test_circular_correlation_against_numpy_fft():
+    # out[k] = sum_t g[t] z[t - k mod L]: by the correlation theorem ifft(fft(g) * conj(fft(z)))
+    L = 16
+    g = rng.standard_normal(L); z = rng.standard_normal(L)
+    ref = np.real(np.fft.ifft(np.fft.fft(g) * np.conj(np.fft.fft(z))))
+    assert np.allclose(O.circular_filter_correlation(g, z), ref, atol=1e-12)
+    h = rng.standard_normal(L)
+    assert np.isclose(np.dot(O.circular_conv(h, z), g), np.dot(h, O.circular_filter_correlation(g, z)))
+
+
+def test_circular_fft_and_direct_paths_agree(monkeypatch):
+    L = 256
+    h = rng.standard_normal((2, L)); g = rng.standard_normal((2, L)); z = rng.standard_normal((2, L))
+    a1, c1 = O.circular_conv_adjoint(h, g), O.circular_filter_correlation(g, z)
+    monkeypatch.setattr(O.hyena_oracle, "DIRECT_MAX_L", 16)
+    a2, c2 = O.circular_conv_adjoint(h, g), O.circular_filter_correlation(g, z)
+    assert np.allclose(a1, a2, atol=1e-10) and np.allclose(c1, c2, atol=1e-10)
+
+
+@pytest.mark.parametrize("N", [1, 2])
+def test_circular_backward_matches_finite_differences(N):
+    B, D, L = 2, 2, 8
+    v = rng.standard_normal((B, D, L))
+    xs = [rng.standard_normal((B, D, L)) for _ in range(N)]
+    h = rng.standard_normal((N, D, L)) * 0.5
+    gy = rng.standard_normal((B, D, L))
+    loss = lambda: float(np.sum(gy * O.hyena_forward(v, xs, h, conv=O.circular_conv)))
+    gv, gxs, gh = O.hyena_backward(v, xs, h, gy, circular=True)
+    eps = 1e-6
+
+    def fd(arr, idx):
+        a0 = arr[idx]
+        arr[idx] = a0 + eps; lp = loss()
+        arr[idx] = a0 - eps; lm = loss()
+        arr[idx] = a0
+        return (lp - lm) / (2 * eps)
+
+    for idx in [(0, 0, 0), (1, 1, 3), (0, 1, 7)]:
+        assert np.isclose(gv[idx], fd(v, idx), rtol=1e-6, atol=1e-8)
+        for n in range(N):
+            assert np.isclose(gxs[n][idx], fd(xs[n], idx), rtol=1e-6, atol=1e-8)
+    for idx in [(0, 0, 0), (N - 1, 1, 5), (0, 1, 7)]:
+        assert np.isclose(gh[idx], fd(h, idx), rtol=1e-6, atol=1e-8)
