@@ -389,7 +389,7 @@ int bwd_long_plan(const PlanInfo& p, PlanInfo* fs) {
     *fs = p;
     return 0;
   }
-  return make_plan(p.L, "fourstep", nullptr, fs, 0);
+  return make_plan(p.L, "fourstep", nullptr, fs, p.circular);
 }
 
 int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -397,7 +397,6 @@ int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
 // -1 when no backward serves the plan
 int64_t bwd_ws(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
   if (bwd_single(p)) return bwd_ws_single(p, B, D, NORD);
-  if (p.circular) return -1;     // circular rows beyond the single-pass backward: not served
   PlanInfo fs;
   if (bwd_long_plan(p, &fs)) return -1;
   int64_t t = long_backward_layout(fs, B, D, NORD).total;

@@ -115,7 +115,14 @@ __device__ __forceinline__ void st4_io(void* p, int64_t i, float a, float b, flo
 // One order's elementwise work on the incoming gradient g (held reversed,
 // g = R(gsrc), when REV: the previous adjoint convolution leaves it so):
 //   gx = g * c  (I/O dtype)   and   t2 = R(g * x)  (fp32).
-template <int IOT, bool REV, bool V4>
+// CIRC: periodic rows, whose reversal is R'(t) = (L - t) mod L instead of
+// R(t) = L - 1 - t (one position per thread: the mirrored groups of four
+// are not aligned).
+__device__ __forceinline__ int64_t mirror(int64_t t, int64_t L, bool circ) {
+  return circ ? (t == 0 ? 0 : L - t) : L - 1 - t;
+}
+
+template <int IOT, bool REV, bool V4, bool CIRC = false>
 __global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restrict__ c, const void* __restrict__ x,
                           void* __restrict__ gx, float* __restrict__ t2, int64_t rows, int64_t L) {
   if constexpr (V4) {
@@ -136,7 +143,7 @@ __global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restric
     }
   } else {
     ROW_LOOP(rows, L) {
-      const int64_t i = r * L + t, ri = r * L + (L - 1 - t);
+      const int64_t i = r * L + t, ri = r * L + mirror(t, L, CIRC);
       const float g = gsrc[REV ? ri : i];
       IO<IOT>::st(gx, i, g * c[i]);
       t2[ri] = g * IO<IOT>::ld(x, i);
@@ -145,7 +152,7 @@ __global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restric
 }
 
 // out = R(a) in the I/O dtype (the final gradient of v)
-template <int IOT, bool V4>
+template <int IOT, bool V4, bool CIRC = false>
 __global__ void k_bw_store_rev(const float* __restrict__ a, void* __restrict__ out, int64_t rows, int64_t L) {
   if constexpr (V4) {
     ROW_LOOP4(rows, L) {
@@ -153,12 +160,12 @@ __global__ void k_bw_store_rev(const float* __restrict__ a, void* __restrict__ o
       st4_io<IOT>(out, r * L + t, w.w, w.z, w.y, w.x);
     }
   } else {
-    ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + (L - 1 - t)]);
+    ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + mirror(t, L, CIRC)]);
   }
 }
 
 // gh[d][k] = sum_b t[b*D + d][L-1-k]  (fixed batch order: deterministic)
-template <bool V4>
+template <bool V4, bool CIRC = false>
 __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restrict__ gh, int B, int D, int64_t L) {
   if constexpr (V4) {
     ROW_LOOP4(D, L) {
@@ -172,7 +179,7 @@ __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restri
   } else {
     ROW_LOOP(D, L) {
       float acc = 0.f;
-      for (int b = 0; b < B; ++b) acc += tt[((int64_t)b * D + r) * L + (L - 1 - t)];
+      for (int b = 0; b < B; ++b) acc += tt[((int64_t)b * D + r) * L + mirror(t, L, CIRC)];
       gh[r * L + t] = acc;
     }
   }
@@ -193,10 +200,14 @@ enum { BW_LOAD = 0, BW_GATE = 2 };
 
 template <int IOT>
 hipError_t bw_step_io(bool rev, const float* g, const float* c, const void* x, void* gx, float* t2, int64_t L,
-                      int64_t n, hipStream_t s) {
+                      int64_t n, bool circ, hipStream_t s) {
   const int64_t rows = n / L;
   const dim3 blk(EW_THREADS);
-  if (L % 4 == 0) {
+  if (circ) {
+    const dim3 grid = row_grid(rows, L);
+    if (rev) hipLaunchKernelGGL((k_bw_step<IOT, true, false, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+    else hipLaunchKernelGGL((k_bw_step<IOT, false, false, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
+  } else if (L % 4 == 0) {
     const dim3 grid = row_grid(rows, L / 4);
     if (rev) hipLaunchKernelGGL((k_bw_step<IOT, true, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
     else hipLaunchKernelGGL((k_bw_step<IOT, false, true>), grid, blk, 0, s, g, c, x, gx, t2, rows, L);
@@ -256,6 +267,10 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
 
 hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspace, hipStream_t s) {
   const int64_t B = a.B, D = a.D, L = a.L, R = B * D, n = R * L;
+  // periodic rows: the same chain with R' (t -> -t mod L) in place of R and
+  // periodic convolutions (the four-step passes need no flag: with L equal to
+  // the FFT length no sample is padding)
+  const bool circ = a.circular != 0;
   const LongBackwardLayout w = long_backward_layout(p, B, D, a.NORD);
   char* ws = static_cast<char*>(workspace);
   float* C = reinterpret_cast<float*>(ws + w.c);
@@ -285,8 +300,8 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   for (int nn = a.NORD - 1; nn >= 0; --nn) {
     const float* Cn = C + nn * cstride;
     // gx_n = g * c_n, T2 = R(g * x_n)
-    BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, s)
-                     : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, s));
+    BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s)
+                     : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
     if (nn == 0) BW_TRY(bw_ew(a.io, BW_LOAD, a.v, nullptr, Z, n, s));          // z_1 = v
     else BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn - 1], C + (nn - 1) * cstride, Z, n, s));
     // filter gradient: spectra of the rows of T2, then (T2 conv z) reversed and summed over the batch
@@ -295,7 +310,10 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
     BW_TRY(fourstep_spectrum(sa, p, s));
     BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
-    if (L % 4 == 0)
+    if (circ)
+      hipLaunchKernelGGL((k_bw_batch_sum_rev<false, true>), row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
+                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
+    else if (L % 4 == 0)
       hipLaunchKernelGGL(k_bw_batch_sum_rev<true>, row_grid(D, L / 4), dim3(EW_THREADS), 0, s, T1,
                          a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
     else
@@ -307,8 +325,11 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     gcur = T1;
     grev = true;
   }
-  const dim3 rg = row_grid(R, L % 4 == 0 ? L / 4 : L);
-  if (L % 4 == 0) {
+  const dim3 rg = row_grid(R, L % 4 == 0 && !circ ? L / 4 : L);
+  if (circ) {
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, false, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+  } else if (L % 4 == 0) {
     if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
     else hipLaunchKernelGGL((k_bw_store_rev<1, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
   } else {

@@ -199,9 +199,9 @@ hyena_status hyena_forward_fir(const void* v, const void* const* x, const float*
  * plus per-row spectra; a spectrum built on the single path is rewritten
  * into the four-step layout there).  Errors as hyena_forward, plus ALIAS for an output overlapping an
  * input or another output.  hyena_backward_ex takes the convolution mode (see the circular mode below):
- * circular rows (periodic convolution, c[t] = sum_k h[k] z[(t - k) mod L], whose adjoint and filter
- * gradient are the circular correlations) are served up to L = 16384 by the one-launch kernel;
- * longer circular rows return HYENA_ERR_UNSUPPORTED and the workspace query -1.
+ * for circular rows (periodic convolution, c[t] = sum_k h[k] z[(t - k) mod L]) the adjoint and the
+ * filter gradient are circular correlations; the one-launch kernel serves L <= 16384, longer rows the
+ * four-step pipeline with the periodic reversal t -> -t mod L.
  */
 int64_t hyena_backward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io);
 

@@ -84,9 +84,13 @@ def test_backward_circular_matches_oracle(N, B, D, L, io):
     _check(got, ref, io)
 
 
-def test_backward_circular_beyond_one_launch_is_unsupported():
-    assert H.backward_workspace_bytes(1, 2, 2, 32768, circular=True) == -1
-    assert H.backward_workspace_bytes(1, 2, 2, 16384, circular=True) > 0
+@pytest.mark.parametrize("N,B,D,L,io", [(2, 2, 2, 32768, "fp32"), (2, 1, 2, 65536, "bf16"), (3, 1, 1, 131072, "fp32")])
+def test_backward_circular_long_matches_oracle(N, B, D, L, io):
+    """Periodic rows beyond the one-launch kernel: the four-step pipeline with
+    the periodic reversal (32768 is planned on the single path forward, its
+    spectrum rewritten into the four-step layout)."""
+    got, ref = _run(N, B, D, L, io, circular=True)
+    _check(got, ref, io)
 
 
 def test_backward_full_width_sampled_channels():
