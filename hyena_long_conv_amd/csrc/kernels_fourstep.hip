@@ -31,9 +31,12 @@ namespace hyena {
 #define HYENA_COL_WAVES 1
 #endif
 
+// Columns per workgroup: at most 64 KB of LDS from N1 = 256 on, so two
+// workgroups share a CU and one's loads overlap the other's FFT; never fewer
+// than 16 (each row segment a whole 128-byte line).
 template <int N1> struct ColCfg {
   static constexpr int E = 16;
-  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 512 ? 32 : 16;
+  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 256 ? 32 : 16;
   static constexpr int T = W * N1 / E;
   static constexpr bool LDS = N1 > E;
   using R = typename Plan16<N1>::R;
