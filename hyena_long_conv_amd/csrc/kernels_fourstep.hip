@@ -31,14 +31,22 @@ namespace hyena {
 #define HYENA_COL_WAVES 1
 #endif
 
-// Columns per workgroup: at most 64 KB of LDS from N1 = 256 on, so two
-// workgroups share a CU and one's loads overlap the other's FFT; never fewer
-// than 16 (each row segment a whole 128-byte line).
-template <int N1> struct ColCfg {
+
+// Columns per workgroup.  Row convolutions: at most 64 KB of LDS from
+// N1 = 256 on, so two workgroups share a CU and one's loads overlap the
+// other's FFT, and never fewer than 16 (each row segment a whole 128-byte
+// line).  Gate inputs requested before the inverse FFT where two workgroups
+// share a CU (N1 = 256, 512: 5% faster); shorter columns run more workgroups
+// per CU and lose more by the registers, and at 1024 it spills.  The grid
+// passes (GRID) keep 32 columns up to N1 = 512 and no early gate loads: the
+// row settings were 14% slower on a padded 224 x 224 grid.
+template <int N1, bool GRID = false> struct ColCfg {
   static constexpr int E = 16;
-  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 256 ? 32 : 16;
+  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64
+                         : (N1 <= (GRID ? 512 : 256)) ? 32 : 16;
   static constexpr int T = W * N1 / E;
   static constexpr bool LDS = N1 > E;
+  static constexpr int PFX = (!GRID && (N1 == 256 || N1 == 512)) ? E : 0;
   using R = typename Plan16<N1>::R;
 };
 
@@ -132,8 +140,8 @@ __device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, in
 // follows (a 2-D DFT), the packed column index col covering grid columns
 // 2col, 2col+1.
 template <int N1, int IOT, int KIND, bool EVEN, bool GRID = false>
-__global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs a) {
-  using C = ColCfg<N1>;
+__global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(ColArgs a) {
+  using C = ColCfg<N1, GRID>;
   constexpr int E = C::E, W = C::W, S1 = N1 / E;
   __shared__ cf smem[C::LDS ? N1 * W : 1];
   const int c = threadIdx.x % W, j = threadIdx.x / W;
@@ -191,6 +199,13 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
 #pragma unroll
     for (int i = 0; i < E; ++i)
       u[i] = valid ? ld_work(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
+    constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
+    cf xp[PFX > 0 ? PFX : 1];
+#pragma unroll
+    for (int i = 0; i < PFX; ++i) {
+      int64_t ro, t, len;
+      xp[i] = at(j + i * S1, ro, t, len) ? ld_pair<IOT, EVEN>(a.xg, ro, t, len) : make_float2(0.f, 0.f);
+    }
     fft.template run<true>(u, lds, j);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
@@ -201,7 +216,7 @@ __global__ void __launch_bounds__(ColCfg<N1>::T, HYENA_COL_WAVES) k_col(ColArgs 
         if constexpr (KIND == COL_OUT) {
           z = u[i];
         } else {
-          const cf xv = ld_pair<IOT, EVEN>(a.xg, ro, t, len);
+          const cf xv = i < PFX ? xp[i < PFX ? i : 0] : ld_pair<IOT, EVEN>(a.xg, ro, t, len);
           z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
         }
         if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, ro, t, len, z);
@@ -361,6 +376,7 @@ template <int N1>
 static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hipStream_t s, bool grid_mode = false) {
   const dim3 grid(groups * c.n_col_blocks), block(ColCfg<N1>::T);
   if (grid_mode) {
+    const dim3 block(ColCfg<N1, true>::T);
     if constexpr (grid_col_ok(N1)) {
       if (c.gL2 % 2 == 0) launch_col_t<N1, true, true>(kind, io, c, grid, block, s);
       else launch_col_t<N1, false, true>(kind, io, c, grid, block, s);
@@ -375,15 +391,15 @@ static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hip
   return hipGetLastError();
 }
 
-static int col_width(int n1) {
+static int col_width(int n1, bool grid = false) {
   switch (n1) {
     case 16: return ColCfg<16>::W;
     case 32: return ColCfg<32>::W;
-    case 64: return ColCfg<64>::W;
-    case 128: return ColCfg<128>::W;
-    case 256: return ColCfg<256>::W;
-    case 512: return ColCfg<512>::W;
-    case 1024: return ColCfg<1024>::W;
+    case 64: return grid ? ColCfg<64, true>::W : ColCfg<64>::W;
+    case 128: return grid ? ColCfg<128, true>::W : ColCfg<128>::W;
+    case 256: return grid ? ColCfg<256, true>::W : ColCfg<256>::W;
+    case 512: return grid ? ColCfg<512, true>::W : ColCfg<512>::W;
+    case 1024: return grid ? ColCfg<1024, true>::W : ColCfg<1024>::W;
   }
   return 0;
 }
@@ -609,7 +625,7 @@ static hipError_t dispatch_grid_row(int n2, int kind, const GridRowArgs& r, int 
 
 hipError_t grid2d_forward(const NdArgs& a, hipStream_t s) {
   const int n1 = a.P, n2 = a.P / 2;
-  const int W = col_width(n1);
+  const int W = col_width(n1, true);
   if (W == 0 || a.ndim != 2) return hipErrorInvalidValue;
   ColArgs c{};
   c.v = a.v; c.y = a.y; c.work = (cf*)a.work; c.n2 = n2;
@@ -644,7 +660,7 @@ hipError_t grid2d_forward(const NdArgs& a, hipStream_t s) {
 
 hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s) {
   const int n1 = a.P, n2 = a.P / 2;
-  const int W = col_width(n1);
+  const int W = col_width(n1, true);
   if (W == 0 || a.ndim != 2) return hipErrorInvalidValue;
   ColArgs c{};
   c.h = a.kernel; c.work = (cf*)a.work; c.n2 = n2;
@@ -669,7 +685,7 @@ hipError_t grid2d_spectrum(const NdArgs& a, hipStream_t s) {
 // planes k1 and P-k1 together through a 2-D FFT, the spectral step and back.
 hipError_t grid3d_forward(const NdArgs& a, hipStream_t s) {
   const int P = a.P, NL = P / 2, n2 = P * NL;
-  const int W = col_width(P);
+  const int W = col_width(P, true);
   if (W == 0 || a.ndim != 3) return hipErrorInvalidValue;
   ColArgs c{};
   c.v = a.v; c.y = a.y; c.work = (cf*)a.work; c.n2 = n2;
@@ -693,7 +709,7 @@ hipError_t grid3d_forward(const NdArgs& a, hipStream_t s) {
 
 hipError_t grid3d_spectrum(const NdArgs& a, hipStream_t s) {
   const int P = a.P, NL = P / 2, n2 = P * NL;
-  const int W = col_width(P);
+  const int W = col_width(P, true);
   if (W == 0 || a.ndim != 3) return hipErrorInvalidValue;
   ColArgs c{};
   c.h = a.kernel; c.work = (cf*)a.work; c.n2 = n2;
