@@ -32,18 +32,19 @@ namespace hyena {
 #endif
 
 
-// Columns per workgroup.  Row convolutions: at most 64 KB of LDS from
-// N1 = 256 on, so two workgroups share a CU and one's loads overlap the
-// other's FFT, and never fewer than 16 (each row segment a whole 128-byte
-// line).  Gate inputs requested before the inverse FFT where two workgroups
+// Columns per workgroup.  Row convolutions: 2048 points per workgroup up to
+// N1 = 64 (1-2% faster than 4096 on the 64K and 128K shapes), at most 64 KB
+// of LDS from N1 = 256 on, so two workgroups share a CU and one's loads
+// overlap the other's FFT, and never fewer than 16 (each row segment a
+// whole 128-byte line).  Gate inputs requested before the inverse FFT where two workgroups
 // share a CU (N1 = 256, 512: 5% faster); shorter columns run more workgroups
 // per CU and lose more by the registers, and at 1024 it spills.  The grid
 // passes (GRID) keep 32 columns up to N1 = 512 and no early gate loads: the
 // row settings were 14% slower on a padded 224 x 224 grid.
 template <int N1, bool GRID = false> struct ColCfg {
   static constexpr int E = 16;
-  static constexpr int W = N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64
-                         : (N1 <= (GRID ? 512 : 256)) ? 32 : 16;
+  static constexpr int W = GRID ? (N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 512 ? 32 : 16)
+                                : (N1 <= 64 ? 2048 / N1 : N1 <= 256 ? 32 : 16);
   static constexpr int T = W * N1 / E;
   static constexpr bool LDS = N1 > E;
   static constexpr int PFX = (!GRID && (N1 == 256 || N1 == 512)) ? E : 0;
