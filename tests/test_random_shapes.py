@@ -54,3 +54,28 @@ def test_backward_random_shape(N, B, D, L, io, circular):
     got, ref = _run(N, B, D, L, io, channels=[0, D - 1] if D > 2 else None, seed=500 + L % 89 + N,
                     circular=circular)
     _check(got, ref, io)
+
+
+def _circ_cases(n, seed):
+    r = random.Random(seed)
+    return [(r.choice([1, 2, 3, 4]), r.choice([1, 2, 3]), r.choice([1, 2, 3]),
+             r.choice([64, 128, 512, 1024, 4096, 8192, 16384, 32768, 65536]), r.choice(["fp32", "bf16"]))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("N,B,D,L,io", _circ_cases(10, 4242))
+def test_circular_forward_random_shape(N, B, D, L, io):
+    import numpy as np
+
+    import oracle as O
+    from tests.gpu_helpers import channel_errors
+
+    cfg = Config("randc", N, B, D, L, io, 32, 300 + L % 101 + N)
+    p = make_filter_params(cfg, bias_scale=0.2)
+    h = H.filter_gen(params_to_device(p), L)
+    v, xs = make_activations(cfg, "cuda:0")
+    y = H.forward(v, xs, H.filter_spectrum(h, circular=True))
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    ref = O.hyena_forward(f64(v), [f64(x) for x in xs], f64(h), conv=O.circular_conv)
+    assert channel_errors(f64(y), ref).max() <= (1e-4 if io == "fp32" else 2e-2)
