@@ -40,9 +40,17 @@ int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
   return (int64_t)rows_per_group(p.N, NF) * p.N * 8;
 }
 
+// Rows per pass group of the four-step forward: as many groups as the work
+// budget needs, of equal size (768 rows as 384 + 384 rather than 512 + 256:
+// 2% faster on the 64K shape, the equal halves using the GPU alike).
+int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows) {
+  const int64_t g = rows_per_group(p.N, n_rows), groups = (n_rows + g - 1) / g;
+  return (n_rows + groups - 1) / groups;
+}
+
 int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
   if (p.path == PATH_SINGLE) return 0;
-  return (int64_t)rows_per_group(p.N, B * D) * p.N * 8;
+  return forward_group_rows(p, B * D) * p.N * 8;
 }
 
 // Grid convolutions: padded side P of the square/cube FFT grid.
@@ -312,7 +320,7 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
       return HYENA_ERR_ALIAS;
     for (int n = 0; n < N; ++n)
       if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
-    int64_t g = rows_per_group(p.N, B * D);
+    int64_t g = forward_group_rows(p, B * D);
     if (g * p.N * 8 > workspace_bytes) g = workspace_bytes / (p.N * 8);
     a.work = workspace;
     a.rows_per_group = (int)g;
