@@ -259,7 +259,10 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   w.t1 = o;    o += act;
   w.t2 = o;    o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);
-  w.rows_per_group = rows_per_group(p.N, R);
+  {  // as many pass groups as the work budget needs, of equal size
+    const int64_t g = rows_per_group(p.N, R), groups = (R + g - 1) / g;
+    w.rows_per_group = (int)((R + groups - 1) / groups);
+  }
   w.work = o;  o += al((int64_t)w.rows_per_group * p.N * 8);
   w.total = o;
   return w;
