@@ -259,8 +259,11 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   w.t1 = o;    o += act;
   w.t2 = o;    o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);
-  {  // as many pass groups as the work budget needs, of equal size
-    const int64_t g = rows_per_group(p.N, R), groups = (R + g - 1) / g;
+  {  // as many pass groups as the work budget needs, of equal size; rows of
+     // 8 MiB and more take 224 MB groups, as the forward's
+    int64_t g = rows_per_group(p.N, R);
+    if ((int64_t)p.N * 8 >= (int64_t(8) << 20)) g = std::min<int64_t>(R, (int64_t(224) << 20) / ((int64_t)p.N * 8));
+    const int64_t groups = (R + g - 1) / g;
     w.rows_per_group = (int)((R + groups - 1) / groups);
   }
   w.work = o;  o += al((int64_t)w.rows_per_group * p.N * 8);
