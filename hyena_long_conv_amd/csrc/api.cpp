@@ -109,8 +109,14 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
   return 0;
 }
 
+// Grids per pass group: as many groups as the work budget needs, of equal size.
+int64_t nd_group_rows(const NdPlanH& p, int64_t rows) {
+  const int64_t g = rows_per_group(p.NC, rows), groups = (rows + g - 1) / g;
+  return (rows + groups - 1) / groups;
+}
+
 int64_t nd_ws(const NdPlanH& p, int64_t rows) {
-  return p.multi ? (int64_t)rows_per_group(p.NC, rows) * p.NC * 8 : 0;
+  return p.multi ? nd_group_rows(p, rows) * p.NC * 8 : 0;
 }
 
 // 0: fine; otherwise a status.  Sets the grids per pass group.
@@ -119,7 +125,7 @@ hyena_status nd_ws_check(const NdPlanH& p, int64_t rows, void* ws, int64_t wsb, 
   if (!p.multi) return HYENA_OK;
   if (!ws || wsb < p.NC * 8) return HYENA_ERR_WORKSPACE;
   if (!aligned16(ws)) return HYENA_ERR_ALIGN;
-  int64_t g = rows_per_group(p.NC, rows);
+  int64_t g = nd_group_rows(p, rows);
   if (g * p.NC * 8 > wsb) g = wsb / (p.NC * 8);
   *group = (int)g;
   return HYENA_OK;
