@@ -1,16 +1,19 @@
 """Benchmark of the Hyena order-N forward (hyena_forward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4] [--also C3]
 
 A step is one hyena_forward over one batch of synthetic inputs already
 resident in HBM (v, x_1..x_N and the precomputed filter spectrum).  Inputs
 rotate over several independent sets so the working set exceeds the 256 MB
 Infinity Cache and every step reads from HBM.  Prints one JSON line with
-channel-tokens/s (B*D*L per second), the roofline of the forward kernel and
-the float64 CPU oracle timed on a bounded sample on the host cores.
+channel-tokens/s (B*D*L per second), the HBM roofline fraction of the forward
+(algorithmic bytes over the event-timed forward), and the float64 CPU oracle
+run on a bounded sample of the same rows on the host cores -- its time is the
+CPU baseline and its output checks the GPU's on those rows (parity).
 
-The default workload is the 2K-context shape (order 2, B=4, D=768, L=2048,
-fp32); --config selects the other shapes (C1, C3, C4, C5a, C5b).
+The default workload is the 1M-token shape (order 2, B=1, D=256, L=2^20,
+fp32), with the 64K shape (order 2, B=1, D=768, L=65536, bf16 I/O) reported
+under "also"; --config selects the main shape (C1, C2, C3, C4, C5a, C5b).
 """
 from __future__ import annotations
 
@@ -57,6 +60,8 @@ def algo_flops(cfg, circular: bool = False) -> float:
 KERNEL_SOURCES = {
     "k_single_forward": ["kernels_single.hip", "fft_engine.hpp", "plan.hpp"],
     "k_nd_forward": ["kernels_nd.hip", "fft_engine.hpp", "plan.hpp"],
+    # the four-step forward: its kernels, and the host code that sizes its pass groups
+    "fourstep_forward": ["api.cpp", "kernels_fourstep.hip", "fft_engine.hpp", "plan.hpp", "launch.hpp"],
 }
 
 
@@ -86,33 +91,26 @@ def measured_traffic(cfg_name: str):
     return d.get("hbm_bytes_per_step")
 
 
-def cpu_baseline(cfg, budget_s: float = 12.0):
-    """Time the float64 oracle on a bounded sample of (b, d) rows of the same
-    workload on the host cores (one single-threaded worker per core)."""
-    import multiprocessing as mp
+TOL = {"fp32": 1e-4, "fp32_1M": 5e-4, "bf16": 2e-2}
 
+
+def tolerance(cfg) -> float:
+    """Per-row normalised max error bound: 1e-4 (fp32, L <= 64K), 5e-4 (fp32
+    beyond), 2e-2 (bf16 I/O against the oracle fed the same bf16 inputs)."""
+    if cfg.io == "bf16":
+        return TOL["bf16"]
+    return TOL["fp32"] if cfg.L <= 65536 else TOL["fp32_1M"]
+
+
+def sample_rows(cfg, n: int):
+    """n flat rows b*D + d: (0, 0), (0, D-1), (B-1, D-1) first, then a seeded
+    uniform sample."""
     import numpy as np
-
-    cores = min(16, len(os.sched_getaffinity(0)))
-    # calibrate on one row, then size the sample to about budget_s of wall time
-    t0 = time.perf_counter()
-    _oracle_rows(cfg, [0])
-    one = time.perf_counter() - t0
-    rows_total = cfg.B * cfg.D
-    n = int(max(cores, min(rows_total, budget_s * cores / max(one, 1e-3))))
-    n = max(1, min(n, rows_total))
-    rng = np.random.default_rng(cfg.seed)
-    sample = sorted(rng.choice(rows_total, size=n, replace=False).tolist())
-    chunks = [sample[i::cores] for i in range(cores) if sample[i::cores]]
-    ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(len(chunks), initializer=_pin_threads) as pool:
-        pool.starmap(_oracle_rows, [(cfg, c) for c in chunks])
-    wall = time.perf_counter() - t0
-    return {"value": n * cfg.L / wall, "unit": "channel-tokens/s", "cores": len(chunks), "kind": "oracle",
-            "sample": f"{n} of {rows_total} (b,d) rows of {cfg.name} (float64 oracle, direct conv for "
-                      f"L<=8192 else its radix-2 FFT), {wall:.1f} s wall",
-            "extrapolated_full_s": wall * rows_total / n}
+    total = cfg.B * cfg.D
+    first = [0, cfg.D - 1, total - 1]
+    rows = list(dict.fromkeys(r for r in first if r < total))
+    rest = [r for r in np.random.default_rng(cfg.seed).permutation(total).tolist() if r not in rows]
+    return (rows + rest)[:max(1, min(n, total))]
 
 
 def _pin_threads():
@@ -120,10 +118,10 @@ def _pin_threads():
     os.environ["OPENBLAS_NUM_THREADS"] = "1"
 
 
-def _oracle_rows(cfg, rows):
-    """Oracle forward for flat row indices b*D + d: filters from the same
-    seeded FFN weights, activation rows drawn from N(0, 1) on the CPU (the
-    oracle's cost does not depend on the values)."""
+def _oracle_rows(cfg, rows, v_rows, x_rows):
+    """Float64 oracle forward for flat rows b*D + d on the given inputs
+    (v_rows [n, L], x_rows [N][n, L], float64): filters from the same seeded
+    FFN weights, then the recurrence.  Returns y [n, L]."""
     import numpy as np
 
     import oracle as O
@@ -132,11 +130,81 @@ def _oracle_rows(cfg, rows):
     ds = sorted({r % cfg.D for r in rows})
     h = O.filter_gen(p, cfg.L, channels=ds)
     col = {d: i for i, d in enumerate(ds)}
-    rs = np.random.default_rng([cfg.seed, len(rows), rows[0]])
-    v = rs.standard_normal((len(rows), cfg.L))
-    xs = [rs.standard_normal((len(rows), cfg.L)) for _ in range(cfg.N)]
     hh = np.stack([h[:, col[r % cfg.D]] for r in rows], axis=1)  # [N, rows, L]
-    return O.hyena_forward(v, xs, hh).shape
+    return O.hyena_forward(np.asarray(v_rows), [np.asarray(x) for x in x_rows], hh)
+
+
+def cpu_baseline_parity(cfg, v, xs, y, budget_s: float = 12.0):
+    """The float64 oracle on a bounded sample of the measured workload's own
+    rows, on the host cores (one single-threaded worker per core, at most 16),
+    and the GPU output's error on those rows.
+
+    One row ((0, 0): alpha = 1, the longest filter memory) runs first on its
+    own and sizes the sample to about ``budget_s`` of wall time on the
+    workers; rows (0, D-1) and (B-1, D-1) are always part of it.  Returns
+    (cpu_baseline, parity) dicts."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    host_cores = len(os.sched_getaffinity(0))
+    total = cfg.B * cfg.D
+
+    def rows_of(rows):
+        b = [r // cfg.D for r in rows]
+        d = [r % cfg.D for r in rows]
+        vr = v[b, d].double().cpu().numpy()
+        xr = [x[b, d].double().cpu().numpy() for x in xs]
+        yr = y[b, d].double().cpu().numpy()
+        return vr, xr, yr
+
+    t0 = time.perf_counter()
+    v0, x0, y0 = rows_of([0])
+    ref0 = _oracle_rows(cfg, [0], v0, x0)
+    one = time.perf_counter() - t0
+    workers = max(1, min(16, host_cores))
+    n = int(min(total, max(workers + 1, 1 + budget_s * workers / max(one, 1e-3))))
+    rows = sample_rows(cfg, n)
+    pool_rows = [r for r in rows if r != 0]
+    refs, gots, checked = [ref0], [y0], [0]
+    wall, used = 0.0, 0
+    if pool_rows:
+        used = min(workers, len(pool_rows))
+        chunks = [pool_rows[i::used] for i in range(used)]
+        args = []
+        for c in chunks:
+            vr, xr, yr = rows_of(c)
+            args.append((cfg, c, vr, xr))
+            gots.append(yr)
+            checked += c
+        ctx = mp.get_context("spawn")
+        t1 = time.perf_counter()
+        with ctx.Pool(used, initializer=_pin_threads) as pool:
+            refs += pool.starmap(_oracle_rows, args)
+        wall = time.perf_counter() - t1
+    ref = np.concatenate(refs, axis=0)
+    got = np.concatenate(gots, axis=0)
+    num = np.max(np.abs(got - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    err = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num <= 1e-30, 0.0, np.inf))
+    worst = int(np.argmax(err))
+    tol = tolerance(cfg)
+    parity = {"max_norm_err": float(err[worst]),
+              "worst_channel": {"b": checked[worst] // cfg.D, "d": checked[worst] % cfg.D},
+              "channels_checked": len(checked), "tolerance": tol, "pass": bool(err[worst] <= tol),
+              "metric": "max over checked (b,d) rows of max_t|y - y_ref| / max_t|y_ref|, y_ref the float64 oracle"}
+    if pool_rows:
+        base = {"value": len(pool_rows) * cfg.L / wall, "unit": "channel-tokens/s", "cores": used,
+                "host_cores": host_cores, "kind": "oracle",
+                "sample": f"{len(pool_rows)} of {total} (b,d) rows of {cfg.name} on {used} single-threaded workers "
+                          f"(float64 oracle: filter FFN for the rows' channels, then direct conv for L<=8192 else "
+                          f"its radix-2 FFT), {wall:.1f} s wall",
+                "extrapolated_full_s": wall * total / len(pool_rows), "extrapolated": True}
+    else:
+        base = {"value": cfg.L / one, "unit": "channel-tokens/s", "cores": 1, "host_cores": host_cores,
+                "kind": "oracle", "sample": f"1 of {total} rows of {cfg.name}, {one:.1f} s",
+                "extrapolated_full_s": one * total, "extrapolated": True}
+    return base, parity
 
 
 def measure_copy(torch, dev, reps=4, nbytes=1 << 30):
@@ -558,7 +626,11 @@ def main(argv=None):
                     help="timed steps (default: >= 20 and >= 200 ms of work)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: >= 3 and >= 100 ms of work)")
-    ap.add_argument("--config", default="C2")
+    ap.add_argument("--config", default="C4",
+                    help="forward workload of the main line (default C4: order 2, L = 1M, fp32)")
+    ap.add_argument("--also", default="C3",
+                    help="comma-separated forward workloads reported under 'also' after the main line "
+                         "(default C3, the 64K shape; '' for none)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--circular", action="store_true",
@@ -604,6 +676,33 @@ def main(argv=None):
     # reported beside the datasheet peak (also the reference dispatch for
     # rocprofv3 counter scaling).
     copy_bps = measure_copy(torch, dev, reps=1 if args.copy_calib else 4)
+    out, keep = run_forward(args, cfg, torch, H, dev, copy_bps, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["parity"] = cpu_baseline_parity(cfg, *keep)
+    del keep
+    torch.cuda.empty_cache()
+    also = [c for c in (args.also or "").split(",") if c and c != cfg.name]
+    if also:
+        out["also"] = {}
+        for name in also:
+            c = CONFIGS[name]
+            o, keep = run_forward(args, c, torch, H, dev, copy_bps, None, None)
+            line = {"workload": c.desc, "value": o["value"], "unit": o["unit"], "ms_per_step": o["ms_per_step"],
+                    "steps": o["steps"], "dtype": o["dtype"], "roofline": o["roofline"], "timing": o["timing"]}
+            if not args.no_cpu_baseline:
+                line["cpu_baseline"], line["parity"] = cpu_baseline_parity(c, *keep)
+            out["also"][name] = line
+            del keep
+            torch.cuda.empty_cache()
+    print(json.dumps(out))
+    return 0
+
+
+def run_forward(args, cfg, torch, H, dev, copy_bps, steps, warmup):
+    """Time hyena_forward on one configuration.  Returns the JSON dict and
+    (v, xs, y) of input set 0 for the parity check."""
+    import numpy as np
+    from workloads import make_activations, make_filter_params
 
     per_set = min_bytes(cfg)
     sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / per_set))
@@ -647,8 +746,8 @@ def main(argv=None):
     # clocks settle); the timed count likewise defaults to >= 20 steps and
     # >= 200 ms.
     est = None   # seconds per step, from the warm-up
-    if args.warmup is not None:
-        for i in range(args.warmup):
+    if warmup is not None:
+        for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
     else:
@@ -659,15 +758,15 @@ def main(argv=None):
             if done % 8 == 0 or done < 3:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        args.warmup = done
+        warmup = done
         est = (time.perf_counter() - t_w) / done
-    if args.steps is None:
+    if steps is None:
         if est is None:
             t_e = time.perf_counter()
             step(0)
             torch.cuda.synchronize()
             est = time.perf_counter() - t_e
-        args.steps = int(min(5000, max(20, math.ceil(0.2 / max(est, 1e-6)))))
+        steps = int(min(5000, max(20, math.ceil(0.2 / max(est, 1e-6)))))
     # Timed region: K back-to-back steps between two events on the stream the
     # library launches on (torch's current stream), synchronised on both sides.
     stream = torch.cuda.current_stream(dev)
@@ -675,16 +774,16 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
     # Step-to-step spread, from a second, untimed pass with an event before
     # every step (each event adds a few microseconds between launches, so
     # these per-step figures sit slightly above ms_per_step).
-    n_spread = min(args.steps, 1000)
+    n_spread = min(steps, 1000)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
     for i in range(n_spread):
         ev[i].record(stream)
@@ -701,27 +800,35 @@ def main(argv=None):
     alu_frac = fl / t / ALU_PEAK
     plan = H.plan(cfg.L, circular=args.circular)
     traffic = None if args.circular else measured_traffic(cfg.name)
-    bound = "alu" if fl / mb > ALU_PEAK / HBM_PEAK else "hbm"
-    if bound == "alu":
-        roof = {"bound": "alu", "achieved": fl / t / 1e12, "peak": ALU_PEAK / 1e12, "unit": "TFLOP/s",
-                "frac": alu_frac}
-    else:
-        roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": hbm_frac}
-    roof.update({"traffic": traffic, "kernel": ("k_single_forward" if plan["path"] == "single"
-                                                 else f"four-step forward ({2 * cfg.N + 1} passes per pair group)"),
-                 "launches_per_step": 1 if plan["path"] == "single" else None,
-                 "hbm_frac": hbm_frac, "hbm_GBps": mb / t / 1e9, "copy_GBps": copy_bps / 1e9,
-                 "hbm_frac_vs_copy": mb / t / copy_bps, "alu_frac": alu_frac,
-                 "alu_TFLOPs": fl / t / 1e12, "alu_frac_vs_packed_peak": fl / t / ALU_PEAK_PACKED,
-                 "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl})
+    single = plan["path"] == "single"
+    nc = plan["M"] // 2
+    rows = cfg.B * cfg.D
+    group = max(1, wsb // (nc * 8)) if not single else rows
+    groups = -(-rows // group)
+    # The metric's roofline is HBM bandwidth: algorithmic bytes (v, x_1..x_N,
+    # y in the I/O dtype, the spectrum once) over the event-timed forward.
+    # The unit is one forward: one launch on the single path, (2N + 1)
+    # launches per pass group on the four-step path.
+    roof = {"bound": "hbm", "achieved": mb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": hbm_frac,
+            "traffic": traffic,
+            "kernel": ("k_single_forward" if single else
+                       f"four-step forward: {groups} pass group(s) x {2 * cfg.N + 1} launches "
+                       f"(k_col FIRST, then per order k_row + k_col)"),
+            "unit_of_work": "one hyena_forward (all launches of one step)",
+            "launches_per_step": 1 if single else groups * (2 * cfg.N + 1),
+            "hbm_GBps": mb / t / 1e9, "copy_GBps": copy_bps / 1e9, "hbm_frac_vs_copy": mb / t / copy_bps,
+            "alu_frac": alu_frac, "alu_TFLOPs": fl / t / 1e12, "alu_peak_unpacked_TFLOPs": ALU_PEAK / 1e12,
+            "alu_frac_vs_packed_peak": fl / t / ALU_PEAK_PACKED,
+            "algorithmic_bytes_per_step": mb, "algorithmic_flops_per_step": fl}
     out = {
         "metric": "Hyena order-N fwd channel-tokens/sec (B*D*L/s) + % of HBM roofline",
-        "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations, random-init filter FFN)",
+        "dtype": "fp32" if cfg.io == "fp32" else "bf16 I/O, fp32 compute",
+        "data": "synthetic (seeded N(0,1) activations, DNA-token v for the 1M shape, random-init filter FFN)",
         "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D, "L": cfg.L,
                    "io": cfg.io, "ffn_hidden": cfg.H, "fft_len": plan["M"], "path": plan["path"],
+                   "n1": plan["n1"], "n2": plan["n2"], "rows_per_group": group if not single else None,
                    "conv": "circular" if args.circular else "linear (zero-padded)",
                    "input_sets": sets, "wall_s": wall},
         "timing": {"ms_mean": ms, "ms_median": q(0.5), "ms_p10": q(0.1), "ms_p90": q(0.9),
@@ -729,11 +836,9 @@ def main(argv=None):
         "setup": setup,
         "roofline": roof,
     }
-    del data
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
-    print(json.dumps(out))
-    return 0
+    v0, xs0, _, y0 = data[0]
+    del data, calls, ws
+    return out, (v0, xs0, y0)
 
 
 if __name__ == "__main__":

@@ -28,7 +28,10 @@ __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectr
            "backward_workspace_bytes", "filter_gen_li", "filter_gen_mr", "forward_fir", "nd_plan",
            "nd_spectrum_bytes", "nd_workspace_bytes", "nd_filter_spectrum", "prepare_nd_forward", "nd_forward"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhyena_mi355x.so")
+# HYENA_LIB names another build of the same library (tuning variants, the
+# host-sanitized build of the argument checks); the in-tree build otherwise.
+LIB_PATH = os.environ.get("HYENA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       "libhyena_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hyena.h")
 
 HYENA_FP32, HYENA_BF16 = 0, 1
@@ -60,6 +63,27 @@ class BlockParams(ctypes.Structure):
                 ("W_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p), ("w_short", ctypes.c_void_p),
                 ("W_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p)]
 
+
+
+def _poison(t):
+    """Buffers the binding allocates for the library to fill (outputs,
+    spectra, workspaces) start as NaN -- every byte 0xFF -- when HYENA_POISON=1
+    is set, so a kernel that reads memory it never wrote shows up as NaN
+    instead of passing on stale values.  A test instrument, off by default."""
+    if os.environ.get("HYENA_POISON") == "1":
+        import torch
+        t.fill_(255 if t.dtype == torch.uint8 else float("nan"))
+    return t
+
+
+def _empty(*args, **kw):
+    import torch
+    return _poison(torch.empty(*args, **kw))
+
+
+def _empty_like(t):
+    import torch
+    return _poison(torch.empty_like(t))
 
 _lib = None
 
@@ -218,7 +242,7 @@ def filter_gen(params: dict, L: int, out=None):
             _need_cuda(t, k, torch.float32)
         keep[k] = t
     p = FilterParams(D, N, K, H, *[_ptr(keep[k]).value for k in ("W1", "b1", "W2", "b2", "W3", "b3", "alpha")])
-    h = out if out is not None else torch.empty((N, D, L), dtype=torch.float32, device=W1.device)
+    h = out if out is not None else _empty((N, D, L), dtype=torch.float32, device=W1.device)
     _need_cuda(h, "h", torch.float32)
     _check(lib().hyena_filter_gen(ctypes.byref(p), int(L), _ptr(h), _stream(h)), "hyena_filter_gen")
     return h
@@ -233,10 +257,10 @@ def filter_spectrum(h, out=None, workspace=None, circular: bool = False):
     nbytes = spectrum_bytes(D, N, L, circular)
     if nbytes < 0:
         raise HyenaError(3 if circular else 2, "hyena_spectrum_bytes")
-    spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=h.device)
+    spec = out if out is not None else _empty(nbytes, dtype=torch.uint8, device=h.device)
     wsb = spectrum_workspace_bytes(D, N, L, circular)
     if workspace is None and wsb > 0:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=h.device)
+        workspace = _empty(wsb, dtype=torch.uint8, device=h.device)
     _check(lib().hyena_filter_spectrum_ex(_ptr(h), D, N, L, _mode(circular), _ptr(spec), _ptr(workspace),
                                           workspace.numel() if workspace is not None else 0, _stream(h)),
            "hyena_filter_spectrum")
@@ -252,7 +276,7 @@ def spectrum_export(spec, D: int, N: int, L: int, circular: bool | None = None):
     if circular is None:
         circular = getattr(spec, "_hyena_circular", False)
     M = plan(L, circular)["M"]
-    out = torch.empty((N, D, M // 2 + 1, 2), dtype=torch.float32, device=spec.device)
+    out = _empty((N, D, M // 2 + 1, 2), dtype=torch.float32, device=spec.device)
     _check(lib().hyena_spectrum_export_ex(_ptr(spec), D, N, L, _mode(circular), _ptr(out), _stream(out)),
            "hyena_spectrum_export")
     return torch.view_as_complex(out)
@@ -278,11 +302,11 @@ class PreparedForward:
             if tuple(x.shape) != (B, D, L):
                 raise ValueError(f"x[{i}] shape {tuple(x.shape)} != {(B, D, L)}")
         io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
-        y = out if out is not None else torch.empty_like(v)
+        y = out if out is not None else _empty_like(v)
         _need_cuda(y, "y", v.dtype)
         wsb = int(lib().hyena_forward_workspace_bytes_ex(B, D, N, L, io, _mode(circular)))
         if workspace is None and wsb > 0:
-            workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
+            workspace = _empty(wsb, dtype=torch.uint8, device=v.device)
         self.y = y
         self._keep = (v, tuple(xs), spec, y, workspace)     # the buffers stay alive while prepared
         self._fn = lib().hyena_forward_ex
@@ -335,7 +359,7 @@ def in_projection(u, bp: dict, out=None):
     B, L, D = u.shape
     N = int(bp["N"])
     p = _block_struct(bp, u.dtype)
-    streams = out if out is not None else [torch.empty((B, D, L), dtype=u.dtype, device=u.device)
+    streams = out if out is not None else [_empty((B, D, L), dtype=u.dtype, device=u.device)
                                            for _ in range(N + 1)]
     for i, t in enumerate(streams):
         _need_cuda(t, f"stream[{i}]", u.dtype)
@@ -351,7 +375,7 @@ def out_projection(y, bp: dict, out=None):
     _need_cuda(y, "y", y.dtype)
     B, D, L = y.shape
     p = _block_struct(bp, y.dtype)
-    o = out if out is not None else torch.empty((B, L, D), dtype=y.dtype, device=y.device)
+    o = out if out is not None else _empty((B, L, D), dtype=y.dtype, device=y.device)
     _need_cuda(o, "out", y.dtype)
     _check(lib().hyena_out_projection(_ptr(y), ctypes.byref(p), _ptr(o), B, L, io, _stream(y)),
            "hyena_out_projection")
@@ -371,13 +395,13 @@ def block_forward(u, bp: dict, spec, out=None, workspace=None):
     B, L, D = u.shape
     N = int(bp["N"])
     p = _block_struct(bp, u.dtype)
-    o = out if out is not None else torch.empty_like(u)
+    o = out if out is not None else _empty_like(u)
     _need_cuda(o, "out", u.dtype)
     wsb = block_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16")
     if wsb < 0:
         raise HyenaError(2, "hyena_block_workspace_bytes")
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=u.device)
+        workspace = _empty(wsb, dtype=torch.uint8, device=u.device)
     _check(lib().hyena_block_forward(_ptr(u), ctypes.byref(p), _ptr(spec), _ptr(o), B, L, io, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(u)),
            "hyena_block_forward")
@@ -454,14 +478,14 @@ def backward(v, xs, spec, gy, workspace=None, circular: bool | None = None):
     N = len(xs)
     for i, t in enumerate(xs):
         _need_cuda(t, f"x[{i}]", v.dtype)
-    gv = torch.empty_like(v)
-    gxs = [torch.empty_like(v) for _ in range(N)]
-    gh = torch.empty((N, D, L), dtype=torch.float32, device=v.device)
+    gv = _empty_like(v)
+    gxs = [_empty_like(v) for _ in range(N)]
+    gh = _empty((N, D, L), dtype=torch.float32, device=v.device)
     wsb = backward_workspace_bytes(B, D, N, L, "fp32" if io == HYENA_FP32 else "bf16", circular)
     if wsb < 0:
         raise HyenaError(3, "hyena_backward_workspace_bytes")
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=v.device)
+        workspace = _empty(wsb, dtype=torch.uint8, device=v.device)
     xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
     gp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in gxs])
     _check(lib().hyena_backward_ex(_ptr(v), xp, _ptr(spec), _ptr(gy), _ptr(gv), gp, _ptr(gh), B, D, N, L, io,
@@ -478,7 +502,7 @@ def filter_gen_li(R, lam, D: int, N: int, L: int):
     _need_cuda(R, "R", torch.float32)
     _need_cuda(lam, "lambda", torch.float32)
     S = R.shape[-1]
-    h = torch.empty((N, D, L), dtype=torch.float32, device=R.device)
+    h = _empty((N, D, L), dtype=torch.float32, device=R.device)
     _check(lib().hyena_filter_gen_li(_ptr(R), _ptr(lam), D, N, S, L, _ptr(h), _stream(R)), "hyena_filter_gen_li")
     return h
 
@@ -489,7 +513,7 @@ def filter_gen_mr(hhat, alpha):
     _need_cuda(hhat, "hhat", torch.float32)
     _need_cuda(alpha, "alpha", torch.float32)
     N, D, Lh = hhat.shape
-    h = torch.empty_like(hhat)
+    h = _empty_like(hhat)
     _check(lib().hyena_filter_gen_mr(_ptr(hhat), _ptr(alpha), D, N, Lh, _ptr(h), _stream(hhat)),
            "hyena_filter_gen_mr")
     return h
@@ -505,7 +529,7 @@ def forward_fir(v, xs, h, out=None):
     N = len(xs)
     for i, t in enumerate(xs):
         _need_cuda(t, f"x[{i}]", v.dtype)
-    y = out if out is not None else torch.empty_like(v)
+    y = out if out is not None else _empty_like(v)
     xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
     _check(lib().hyena_forward_fir(_ptr(v), xp, _ptr(h), h.shape[-1], _ptr(y), B, D, N, L, io, _stream(v)),
            "hyena_forward_fir")
@@ -543,7 +567,7 @@ def _nd_workspace(rows, dims, circular, device, workspace):
     if wsb < 0:
         raise HyenaError(3, "hyena_nd_workspace_bytes")
     if workspace is None and wsb > 0:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=device)
+        workspace = _empty(wsb, dtype=torch.uint8, device=device)
     return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
 
 
@@ -564,7 +588,7 @@ def nd_filter_spectrum(kernel, dims, circular: bool = False, out=None, workspace
     nbytes = nd_spectrum_bytes(rows, dims, circular)
     if nbytes < 0:
         raise HyenaError(3, "hyena_nd_spectrum_bytes")
-    spec = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=kernel.device)
+    spec = out if out is not None else _empty(nbytes, dtype=torch.uint8, device=kernel.device)
     workspace, wsb = _nd_workspace(rows, dims, circular, kernel.device, workspace)
     _check(lib().hyena_nd_filter_spectrum(_ptr(kernel), rows, k, cd, int(bool(circular)), _ptr(spec),
                                           _ptr(workspace), wsb, _stream(kernel)), "hyena_nd_filter_spectrum")
@@ -587,7 +611,7 @@ def prepare_nd_forward(v, xs, spec, circular: bool | None = None, per_sample: bo
         if tuple(t.shape) != tuple(v.shape):
             raise ValueError(f"x[{i}] shape {tuple(t.shape)} != {tuple(v.shape)}")
     import torch
-    y = out if out is not None else torch.empty_like(v)
+    y = out if out is not None else _empty_like(v)
     _need_cuda(y, "y", v.dtype)
     xp = (ctypes.c_void_p * N)(*[t.data_ptr() for t in xs])
     workspace, wsb = _nd_workspace(B * D, dims, circular, v.device, workspace)

@@ -72,6 +72,26 @@ def build(verbose: bool = True, defines=(), out: str | None = None) -> str:
     return out
 
 
+HOSTCHECK_LIB = os.path.join(BUILD, "libhyena_hostcheck.so")
+
+
+def build_hostcheck(out: str = HOSTCHECK_LIB) -> str:
+    """Host-only build of the C ABI for the sanitizers: api.cpp (argument
+    checks, planning, size queries) and stand-ins for the kernel launchers
+    (csrc/hostcheck_stubs.cpp), compiled by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer.  No device code is involved.  Load it with
+    the sanitizer runtimes preloaded (tests/test_hostcheck.py)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "hostcheck_stubs.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host-check build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)

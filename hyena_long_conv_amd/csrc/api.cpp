@@ -40,21 +40,9 @@ int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
   return (int64_t)rows_per_group(p.N, NF) * p.N * 8;
 }
 
-// Rows per pass group of the four-step forward: as many groups as the work
-// budget needs, of equal size (768 rows as 384 + 384 rather than 512 + 256:
-// 2% faster on the 64K shape).  Rows of 8 MiB and more (L >= 2^20) take a
-// 224 MB budget instead of 256 (3.5% faster at 1M and 2.3% at 2M; with 1 MiB
-// rows it was 1.3% slower).
-int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows) {
-  int64_t g = rows_per_group(p.N, n_rows);
-  const int64_t row_bytes = (int64_t)p.N * 8;
-  if (row_bytes >= (int64_t(8) << 20)) {
-    g = (int64_t(224) << 20) / row_bytes;
-    if (g > n_rows) g = n_rows;
-  }
-  const int64_t groups = (n_rows + g - 1) / g;
-  return (n_rows + groups - 1) / groups;
-}
+// Rows per pass group of the four-step forward (equal-size groups under the
+// work budget, plan.hpp).
+int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows) { return rows_per_group(p.N, n_rows); }
 
 int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
   if (p.path == PATH_SINGLE) return 0;
@@ -110,10 +98,7 @@ int nd_plan(int32_t ndim, const int64_t* dims, int32_t circular, NdPlanH* out) {
 }
 
 // Grids per pass group: as many groups as the work budget needs, of equal size.
-int64_t nd_group_rows(const NdPlanH& p, int64_t rows) {
-  const int64_t g = rows_per_group(p.NC, rows), groups = (rows + g - 1) / g;
-  return (rows + groups - 1) / groups;
-}
+int64_t nd_group_rows(const NdPlanH& p, int64_t rows) { return rows_per_group(p.NC, rows); }
 
 int64_t nd_ws(const NdPlanH& p, int64_t rows) {
   return p.multi ? nd_group_rows(p, rows) * p.NC * 8 : 0;
@@ -146,6 +131,31 @@ bool sizes_ok(int64_t D, int64_t N, int64_t L) {
 }
 
 }  // namespace
+
+namespace hyena {
+
+// Byte offsets of the long backward's workspace buffers: N saved c_n, z, g,
+// two temporaries (fp32 rows), the per-row spectra and the four-step
+// intermediate of one pass group.
+LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
+  const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t R = B * D, act = al(R * p.L * 4);
+  LongBackwardLayout w{};
+  int64_t o = 0;
+  w.c = o;     o += NORD * act;
+  w.z = o;     o += act;
+  w.g = o;     o += act;
+  w.t1 = o;    o += act;
+  w.t2 = o;    o += act;
+  w.sg = o;    o += al(R * p.spec_stride * 8);
+  // as many pass groups as the work budget needs, of equal size (plan.hpp)
+  w.rows_per_group = rows_per_group(p.N, R);
+  w.work = o;  o += al((int64_t)w.rows_per_group * p.N * 8);
+  w.total = o;
+  return w;
+}
+
+}  // namespace hyena
 
 extern "C" {
 

@@ -248,29 +248,6 @@ hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* o
 
 }  // namespace
 
-LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
-  const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-  const int64_t R = B * D, act = al(R * p.L * 4);
-  LongBackwardLayout w{};
-  int64_t o = 0;
-  w.c = o;     o += NORD * act;
-  w.z = o;     o += act;
-  w.g = o;     o += act;
-  w.t1 = o;    o += act;
-  w.t2 = o;    o += act;
-  w.sg = o;    o += al(R * p.spec_stride * 8);
-  {  // as many pass groups as the work budget needs, of equal size; rows of
-     // 8 MiB and more take 224 MB groups, as the forward's
-    int64_t g = rows_per_group(p.N, R);
-    if ((int64_t)p.N * 8 >= (int64_t(8) << 20)) g = std::min<int64_t>(R, (int64_t(224) << 20) / ((int64_t)p.N * 8));
-    const int64_t groups = (R + g - 1) / g;
-    w.rows_per_group = (int)((R + groups - 1) / groups);
-  }
-  w.work = o;  o += al((int64_t)w.rows_per_group * p.N * 8);
-  w.total = o;
-  return w;
-}
-
 hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspace, hipStream_t s) {
   const int64_t B = a.B, D = a.D, L = a.L, R = B * D, n = R * L;
   // periodic rows: the same chain with R' (t -> -t mod L) in place of R and

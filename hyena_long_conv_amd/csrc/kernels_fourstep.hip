@@ -86,6 +86,22 @@ __device__ __forceinline__ void st_work(cf* p, cf v) {
   }
 }
 
+// Spectrum reads of the row pass.  Each slice is read once per forward (by
+// one workgroup, or by the B consecutive workgroups of one XCD when batch
+// rows share a channel), so the loads are nontemporal, like those of the
+// activations: 7% faster than plain loads on the 1M shape, 1.5% on 64K.
+#ifndef HYENA_SPEC_NT
+#define HYENA_SPEC_NT 1
+#endif
+__device__ __forceinline__ cf ld_spec(const cf* p) {
+  if constexpr (HYENA_SPEC_NT) {
+    const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+    return make_float2(w.x, w.y);
+  } else {
+    return *p;
+  }
+}
+
 // COL_OUT: as COL_LAST without the gate (the plain causal convolution).
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4 };
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
@@ -257,18 +273,19 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   __shared__ cf smem[2 * PADN];
   const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
   int g, w;
+  const int bid = blockIdx.x;
   if (KIND == ROW_CONV && a.cmB > 1) {
     // Channel-major launch: the cmB workgroups of one (channel, row pair)
     // read the same spectrum slice, so they are placed on one XCD (workgroup
     // i runs on XCD i mod 8) one after another, and the slice is fetched
     // into that XCD's L2 once.  n_row_pairs is a multiple of 8.
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int x = bid & 7, slot = bid >> 3;
     const int unit = (slot / a.cmB) * 8 + x, c = unit / a.n_row_pairs;
     w = unit - c * a.n_row_pairs;
     g = c * a.cmB + (slot - (slot / a.cmB) * a.cmB);
   } else {
-    g = blockIdx.x / a.n_row_pairs;
-    w = blockIdx.x - g * a.n_row_pairs;
+    g = bid / a.n_row_pairs;
+    w = bid - g * a.n_row_pairs;
   }
   const int n1 = a.n1;
   const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
@@ -329,16 +346,16 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     for (int i = 0; i < E / 2; ++i) {
       const int k2 = j + i * S2;
       if (k1 == 0 && i == 0 && j == 0) {
-        u[0] = realconv_bin(u[0], u[0], gs[0], gs[N], make_float2(1.f, 0.f));
+        u[0] = realconv_bin(u[0], u[0], ld_spec(gs), ld_spec(gs + N), make_float2(1.f, 0.f));
       } else {
         const int k2m = (k1 == 0) ? (N2 - k2) : (N2 - 1 - k2);
         cf bm = ldsm(k2m);
-        realconv_pair(u[i], bm, gk[k2], gmr[k2m], cmul(wkb, w2e<E>(i)));
+        realconv_pair(u[i], bm, ld_spec(gk + k2), ld_spec(gmr + k2m), cmul(wkb, w2e<E>(i)));
         ldsm(k2m) = bm;
       }
     }
     if (k1 == 0 && j == 0) {
-      const cf am = lds(N2 / 2), gh = gs[N2 / 2];
+      const cf am = lds(N2 / 2), gh = ld_spec(gs + N2 / 2);
       lds(N2 / 2) = realconv_bin(am, am, gh, gh, make_float2(0.f, -1.f));
     }
     __syncthreads();

@@ -124,11 +124,32 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
 // Four-step intermediate: one N-point complex signal per row in flight.
 constexpr int64_t kWorkBudget = int64_t(HYENA_WORK_MB) << 20;
 
-inline int rows_per_group(int64_t N, int64_t n_rows) {
-  int64_t g = kWorkBudget / (N * 8);
+// Bytes of intermediate a pass group may hold.  The environment variable
+// HYENA_WORK_MB (a positive number of MiB), when set, overrides the built-in
+// budget at run time: tests force several pass groups with it and tuning
+// sweeps size the groups.  Host code only.
+inline int64_t work_budget_bytes() {
+  const char* e = getenv("HYENA_WORK_MB");
+  if (e && *e) {
+    const long long mb = atoll(e);
+    if (mb > 0 && mb < (1LL << 24)) return (int64_t)mb << 20;
+  }
+  return kWorkBudget;
+}
+
+// Rows per pass group for rows of row_bytes each: as many groups as the
+// budget needs (at least one row per group), all of equal size (768 rows as
+// 384 + 384 rather than 512 + 256), never more than n_rows.
+inline int64_t group_rows(int64_t row_bytes, int64_t n_rows) {
+  if (n_rows < 1) return 1;
+  int64_t g = row_bytes > 0 ? work_budget_bytes() / row_bytes : n_rows;
   if (g < 1) g = 1;
   if (g > n_rows) g = n_rows;
-  return (int)g;
+  const int64_t groups = (n_rows + g - 1) / g;
+  return (n_rows + groups - 1) / groups;
 }
+
+// The same for rows of an N-point complex intermediate.
+inline int rows_per_group(int64_t N, int64_t n_rows) { return (int)group_rows(N * 8, n_rows); }
 
 }  // namespace hyena

@@ -2,6 +2,11 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Outputs, spectra and workspaces that the binding allocates for the library
+# start as NaN in every test, so a kernel that reads memory it did not write
+# fails parity instead of passing on stale values.
+os.environ["HYENA_POISON"] = "1"
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 

@@ -48,8 +48,8 @@ def test_forward_graph_replays(N, B, D, L, io):
     h = H.filter_gen(params_to_device(make_filter_params(cfg)), L)
     spec = H.filter_spectrum(h)
     v, xs = make_activations(cfg, DEV)
-    y = torch.empty_like(v)
-    ws = torch.empty(max(1, H.forward_workspace_bytes(B, D, N, L, io)), dtype=torch.uint8, device=DEV)
+    y = H._empty_like(v)
+    ws = H._empty(max(1, H.forward_workspace_bytes(B, D, N, L, io)), dtype=torch.uint8, device=DEV)
     H.forward(v, xs, spec, out=y, workspace=ws)
     torch.cuda.synchronize()
     ref = y.clone()
@@ -61,8 +61,8 @@ def test_nd_forward_graph_replays():
     v, xs = make_grid_activations(cfg, DEV)
     K = torch.from_numpy(make_grid_kernel(cfg)).to(DEV)
     spec = H.nd_filter_spectrum(K, cfg.dims)
-    y = torch.empty_like(v)
-    ws = torch.empty(H.nd_workspace_bytes(cfg.B * cfg.D, cfg.dims), dtype=torch.uint8, device=DEV)
+    y = H._empty_like(v)
+    ws = H._empty(H.nd_workspace_bytes(cfg.B * cfg.D, cfg.dims), dtype=torch.uint8, device=DEV)
     H.nd_forward(v, xs, spec, out=y, workspace=ws)
     torch.cuda.synchronize()
     ref = y.clone()
@@ -74,8 +74,8 @@ def test_block_forward_graph_replays():
     bpd = _bp_device(make_block_params(cfg), cfg.io)
     u = make_block_input(cfg, DEV)
     spec = H.filter_spectrum(H.filter_gen(params_to_device(make_filter_params(cfg)), cfg.L))
-    out = torch.empty_like(u)
-    ws = torch.empty(H.block_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io), dtype=torch.uint8, device=DEV)
+    out = H._empty_like(u)
+    ws = H._empty(H.block_workspace_bytes(cfg.B, cfg.D, cfg.N, cfg.L, cfg.io), dtype=torch.uint8, device=DEV)
     H.block_forward(u, bpd, spec, out=out, workspace=ws)
     torch.cuda.synchronize()
     ref = out.clone()

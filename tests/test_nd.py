@@ -158,7 +158,7 @@ def test_nd_multipass_small_workspace_matches(dims, grid_bytes):
     spec = H.nd_filter_spectrum(K, cfg.dims)
     y_full = H.nd_forward(v, xs, spec).clone()
     for grids in (1, 2, 3, 4):
-        ws = torch.empty(grids * grid_bytes, dtype=torch.uint8, device=DEV)
+        ws = H._empty(grids * grid_bytes, dtype=torch.uint8, device=DEV)
         y_ws = H.nd_forward(v, xs, spec, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y_full, y_ws), f"workspace of {grids} grids"

@@ -153,7 +153,7 @@ def test_small_workspace_still_correct():
     v, xs = make_activations(cfg, DEV)
     h = H.filter_gen(params_to_device(p), L)
     spec = H.filter_spectrum(h)
-    ws = torch.empty(H.plan(L)["M"] // 2 * 8, dtype=torch.uint8, device=DEV)
+    ws = H._empty(H.plan(L)["M"] // 2 * 8, dtype=torch.uint8, device=DEV)
     y = H.forward(v, xs, spec, workspace=ws)
     torch.cuda.synchronize()
     check_rows(y, p, L, v, xs, [(b, d) for b in range(2) for d in range(3)], TOL_FP32)
@@ -171,7 +171,7 @@ def test_fourstep_pass_groups_bitwise_equal(monkeypatch):
     check_rows(y, p, cfg.L, v, xs, [(0, 0), (1, 2), (2, 4)], TOL_FP32)
     row_bytes = H.plan(cfg.L)["M"] // 2 * 8
     for rows in (1, 2, 3, 4, 7):      # below B, one channel, one channel + spare, several channels
-        ws = torch.empty(rows * row_bytes, dtype=torch.uint8, device=DEV)
+        ws = H._empty(rows * row_bytes, dtype=torch.uint8, device=DEV)
         y2 = H.forward(v, xs, spec, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y, y2), f"workspace of {rows} rows"
