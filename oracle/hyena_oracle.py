@@ -295,13 +295,25 @@ def hyena_forward(v: np.ndarray, xs, h: np.ndarray, conv=causal_conv) -> np.ndar
 def filter_spectrum(h: np.ndarray, P: int) -> np.ndarray:
     """Half spectrum H[..., k] = sum_{t<L} h[..., t] exp(-2*pi*i*k*t/P),
     k = 0..P/2, of the filter zero-padded to P points ([P2] "計算効率", first
-    step applied to the filter).  P must be a power of two >= 2L.
+    step applied to the filter; any even P >= 2L serves the zero-padded
+    convolution, [P5] "手法: HyenaND", boundary handling).  A power-of-two P
+    goes through the oracle's radix-2 FFT; any other P is the sum above
+    evaluated as written, with the phase k*t reduced mod P in integers
+    (O(L P) work: small cases only).
     """
     h = np.asarray(h, np.float64)
     L = h.shape[-1]
-    assert P >= 2 * L
-    hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
-    return fft(hp)[..., : P // 2 + 1]
+    assert P >= 2 * L and P % 2 == 0
+    if P & (P - 1) == 0:
+        hp = np.zeros(h.shape[:-1] + (P,)); hp[..., :L] = h
+        return fft(hp)[..., : P // 2 + 1]
+    t = np.arange(L, dtype=np.int64)
+    out = np.empty(h.shape[:-1] + (P // 2 + 1,), np.complex128)
+    for k0 in range(0, P // 2 + 1, 256):
+        k = np.arange(k0, min(P // 2 + 1, k0 + 256), dtype=np.int64)
+        ph = (np.outer(t, k) % P).astype(np.float64) * (2.0 * np.pi / P)
+        out[..., k0:k0 + len(k)] = h @ np.exp(-1j * ph)
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -319,6 +319,35 @@ def test_spectrum_window_only_closed_form():
         np.testing.assert_allclose(S[d, 0], np.sum(h[d]), rtol=1e-13)
 
 
+@pytest.mark.parametrize("L,P", [(256, 600), (100, 384), (300, 2 * 5 * 64), (37, 90)])
+def test_spectrum_any_even_length_closed_form(L, P):
+    # The same closed form at FFT lengths that are not powers of two (the
+    # direct DFT branch), and numpy's real FFT of the zero-padded filter as a
+    # library special case.
+    D = 2
+    p = _params(D=D, N=1, bias=False)
+    p["W3"] = np.zeros_like(p["W3"]); p["b3"] = np.ones(D)
+    h = O.filter_gen(p, L)[0]
+    S = O.filter_spectrum(h, P)
+    k = np.arange(P // 2 + 1)
+    w = np.exp(-2j * np.pi * k / P)
+    for d in range(D):
+        a = math.exp(-p["alpha"][d] / L)
+        ref = (1 - (a * w) ** L) / (1 - a * w)
+        np.testing.assert_allclose(S[d], ref, rtol=1e-11, atol=1e-11)
+    hr = O.filter_gen(_params(D=3, N=2), L)
+    np.testing.assert_allclose(O.filter_spectrum(hr, P), np.fft.rfft(hr, n=P), rtol=1e-10, atol=1e-10)
+
+
+def test_spectrum_direct_branch_matches_fft_branch():
+    # A power of two through the radix-2 FFT equals the written-out sum.
+    L, P = 50, 128
+    h = O.filter_gen(_params(D=3, N=2), L)
+    t = np.arange(L); k = np.arange(P // 2 + 1)
+    direct = h @ np.exp(-2j * np.pi * np.outer(t, k) / P)
+    np.testing.assert_allclose(O.filter_spectrum(h, P), direct, rtol=1e-11, atol=1e-11)
+
+
 # ----------------------------------------------------------- bf16 rounding
 
 def test_bf16_rounding_is_rne():
