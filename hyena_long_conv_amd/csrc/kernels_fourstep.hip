@@ -20,6 +20,7 @@
 // "手法: HyenaND", boundary handling); gating recurrence of the Hyena
 // Hierarchy explainer, section "Hyena 演算子の形".
 #include "fft_engine.hpp"
+#include "fft_odd.hpp"
 #include "launch.hpp"
 
 namespace hyena {
@@ -250,6 +251,159 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   }
 }
 
+// Column pass for odd column lengths (n1 in 3, 5, 9, 15, 25, 27: FFT
+// lengths 2^a 3^b 5^c, fft_odd.hpp): one thread per column holds the whole
+// n1-point column in registers, so the pass needs no LDS and no barrier.
+// A wave covers 64 consecutive columns, i.e. 512-byte runs of every row of
+// the intermediate.  Same kinds and arguments as k_col (no grids).
+constexpr int kColOddThreads = 128;
+
+// The same pointer, hidden from common-subexpression elimination: the stores
+// at the end of a column pass then recompute their addresses instead of
+// keeping the loads' (one 64-bit address per point) live through the DFTs.
+__device__ __forceinline__ cf* fresh_ptr(cf* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+v"(v));
+  return reinterpret_cast<cf*>(v);
+}
+
+template <int N1, int IOT, int KIND, bool EVEN>
+__global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
+  const int g = blockIdx.x / a.n_col_blocks, cb = blockIdx.x - g * a.n_col_blocks;
+  const int col = cb * kColOddThreads + (int)threadIdx.x;
+  if (col >= a.n2) return;
+  const int64_t N = (int64_t)N1 * a.n2;
+  cf* buf = a.work + (int64_t)g * N + col;
+  const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
+  cf u[N1];
+  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+      const int64_t t = 2 * ((int64_t)a.n2 * i + col);
+      if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, off, t, a.L);
+      else u[i] = ld_pair<IOT, EVEN>(a.v, off, t, a.L);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N1; ++i) u[i] = ld_work(buf + (int64_t)i * a.n2);
+    RegDft<N1, true>::run(u);
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+      const int64_t t = 2 * ((int64_t)a.n2 * i + col);
+      cf z = u[i];
+      if constexpr (KIND != COL_OUT) {
+        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, t, a.L);
+        z = make_float2(xv.x * z.x, xv.y * z.y);
+      }
+      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, off, t, a.L, z);
+      u[i] = z;
+    }
+  }
+  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
+    RegDft<N1, false>::run(u);
+    cf* dst = fresh_ptr(buf);
+#pragma unroll
+    for (int i = 0; i < N1; ++i) st_work(dst + (int64_t)i * a.n2, u[i]);
+  }
+}
+
+// Column pass for column lengths n1 = 2q (q odd, as above): the two lanes
+// of a lane pair (lane bit 0 = a) share a column, q points each, so rows stay
+// at most 2048 points (the 4096-point row pass ran 11% slower per point).
+// Forward DFT of a column whose lane a holds the interleaved samples
+// x[a + 2m] (m < q):  Y_a = DFT_q(x[a + 2m]),  Y_a[k] *= W_2q^(a k),  then the
+// 2-point DFT across the pair, X[k + q a] = Y_0[k] + (-1)^a Y_1[k], leaves
+// the contiguous half X[q a + k] in lane a.  The inverse runs the same steps
+// backwards (2-point DFT across the pair, conjugate twiddle, inverse DFT_q),
+// returning the interleaved samples, so every pass reads what the previous
+// one wrote.  The exchange is one DPP quad permutation per float (lanes
+// 2i <-> 2i+1); no LDS, no barrier.
+__device__ __forceinline__ float swap_lane_pair(float v) {
+  // quad_perm [1, 0, 3, 2]: each lane reads its pair partner
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+// X = partner + s * own for both components (s = +1 in lane 0 of the pair, -1 in lane 1)
+__device__ __forceinline__ cf cross_pair(cf v, float s) {
+  const float px = swap_lane_pair(v.x), py = swap_lane_pair(v.y);
+  return make_float2(fmaf(s, v.x, px), fmaf(s, v.y, py));
+}
+
+template <int Q, bool INV, int K>
+__device__ __forceinline__ void pair_twiddle_one(cf* u, bool odd_lane) {
+  if constexpr (K != 0) {
+    const cf w = wconst<K, 2 * Q, INV>();
+    const cf t = cmul(u[K], w);
+    u[K] = odd_lane ? t : u[K];
+  }
+}
+template <int Q, bool INV, int... K>
+__device__ __forceinline__ void pair_twiddle(cf* u, bool odd_lane, std::integer_sequence<int, K...>) {
+  (pair_twiddle_one<Q, INV, K>(u, odd_lane), ...);
+}
+
+// forward: interleaved samples in, contiguous half of the spectrum out
+template <int Q>
+__device__ __forceinline__ void pair_dft_fwd(cf (&u)[Q], int a) {
+  RegDft<Q, false>::run(u);
+  pair_twiddle<Q, false>(u, a != 0, std::make_integer_sequence<int, Q>{});
+  const float s = a ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < Q; ++k) u[k] = cross_pair(u[k], s);
+}
+
+// inverse (unnormalised): contiguous half in, interleaved samples out
+template <int Q>
+__device__ __forceinline__ void pair_dft_inv(cf (&u)[Q], int a) {
+  const float s = a ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < Q; ++k) u[k] = cross_pair(u[k], s);
+  pair_twiddle<Q, true>(u, a != 0, std::make_integer_sequence<int, Q>{});
+  RegDft<Q, true>::run(u);
+}
+
+template <int Q, int IOT, int KIND, bool EVEN>
+__global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
+  constexpr int CPB = kColOddThreads / 2;   // columns per workgroup
+  const int g = blockIdx.x / a.n_col_blocks, cb = blockIdx.x - g * a.n_col_blocks;
+  const int lane_a = (int)threadIdx.x & 1;
+  const int col = cb * CPB + ((int)threadIdx.x >> 1);
+  if (col >= a.n2) return;                  // both lanes of a pair leave together
+  const int64_t N = (int64_t)(2 * Q) * a.n2;
+  cf* buf = a.work + (int64_t)g * N + col;
+  const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
+  // time row of point m: lane_a + 2m;  spectrum row of point k: Q*lane_a + k
+  const auto trow = [&](int m) { return 2 * ((int64_t)a.n2 * (lane_a + 2 * m) + col); };
+  cf u[Q];
+  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+      if constexpr (KIND == COL_SPEC) u[m] = ld_pair<0, EVEN>(a.h, off, trow(m), a.L);
+      else u[m] = ld_pair<IOT, EVEN>(a.v, off, trow(m), a.L);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < Q; ++k) u[k] = ld_work(buf + (int64_t)(Q * lane_a + k) * a.n2);
+    pair_dft_inv<Q>(u, lane_a);
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+      cf z = u[m];
+      if constexpr (KIND != COL_OUT) {
+        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, trow(m), a.L);
+        z = make_float2(xv.x * z.x, xv.y * z.y);
+      }
+      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, off, trow(m), a.L, z);
+      u[m] = z;
+    }
+  }
+  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
+    pair_dft_fwd<Q>(u, lane_a);
+    cf* dst = fresh_ptr(buf + (int64_t)Q * lane_a * a.n2);
+#pragma unroll
+    for (int k = 0; k < Q; ++k) st_work(dst + (int64_t)k * a.n2, u[k]);
+  }
+}
+
 struct RowArgs {
   cf* work;
   const cf* spec;      // CONV: spectrum (read)
@@ -259,8 +413,9 @@ struct RowArgs {
   int order;           // CONV: order n (filters n*D + d)
   int D;
   int r0;              // first row (CONV: activation row b*D + d; SPEC: filter row)
-  int n_row_pairs;     // n1 / 2
+  int n_row_pairs;     // workgroups per row: n1 / 2 (even n1) or (n1 + 1) / 2 (odd n1)
   int cmB;             // CONV, > 1: channel-major launch (r0 = first channel, cmB batch rows each)
+  int n_units;         // channel-major launch: (channel, row pair) units; the grid is padded to a multiple of 8
 };
 
 // Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
@@ -278,9 +433,12 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     // Channel-major launch: the cmB workgroups of one (channel, row pair)
     // read the same spectrum slice, so they are placed on one XCD (workgroup
     // i runs on XCD i mod 8) one after another, and the slice is fetched
-    // into that XCD's L2 once.  n_row_pairs is a multiple of 8.
+    // into that XCD's L2 once.  The grid holds 8 * ceil(n_units / 8) * cmB
+    // workgroups; those of the padding units leave before any barrier.
     const int x = bid & 7, slot = bid >> 3;
-    const int unit = (slot / a.cmB) * 8 + x, c = unit / a.n_row_pairs;
+    const int unit = (slot / a.cmB) * 8 + x;
+    if (unit >= a.n_units) return;
+    const int c = unit / a.n_row_pairs;
     w = unit - c * a.n_row_pairs;
     g = c * a.cmB + (slot - (slot / a.cmB) * a.cmB);
   } else {
@@ -288,7 +446,14 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     w = bid - g * a.n_row_pairs;
   }
   const int n1 = a.n1;
-  const int k1 = (b == 0) ? w : (w == 0 ? n1 / 2 : n1 - w);
+  // Row k1 pairs with row n1 - k1 (its bins' Hermitian partners).  Even n1:
+  // rows 0 and n1/2 are their own mirrors and share workgroup 0.  Odd n1:
+  // row 0 is the only self-mirror row, and the second half of workgroup 0
+  // repeats it as a shadow that stores nothing (its loads stay unconditional:
+  // predicating them kept the compiler from issuing them early).
+  const bool odd = (n1 & 1) != 0;
+  const int k1 = (b == 0) ? w : (w == 0 ? (odd ? 0 : n1 / 2) : n1 - w);
+  const bool live = !(odd && w == 0 && b == 1);
   const bool self_mirror = (k1 == 0) || (2 * k1 == n1);
   const int mb = self_mirror ? b : 1 - b;          // row holding the mirror bins
   const int k1m = (k1 == 0) ? 0 : n1 - k1;         // its k1
@@ -319,13 +484,15 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     __syncthreads();
     cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
     const float sc = 1.0f / (float)(2 * N);
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const int k2 = j + i * S2;
-      const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-      const cf am = ldsm(k2m);
-      out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc);
-      if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
+      for (int i = 0; i < E; ++i) {
+        const int k2 = j + i * S2;
+        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+        const cf am = ldsm(k2m);
+        out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc);
+        if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
+      }
     }
   } else {
     // Pair-wise spectral step: the owner of the low index i < E/2 of a bin
@@ -362,8 +529,10 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
 #pragma unroll
     for (int i = E / 2; i < E; ++i) u[i] = lds(j + i * S2);
     fft.template run<true>(u, lds, j);
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) st_work(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
+      for (int i = 0; i < E; ++i) st_work(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
+    }
   }
 }
 
@@ -384,6 +553,54 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
     else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
     else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST, EVEN, GRID>), grid, block, 0, s, c);
   }
+}
+
+template <int N1, bool EVEN>
+static void launch_col_odd_t(int kind, int io, const ColArgs& c, dim3 grid, hipStream_t s) {
+  const dim3 block(kColOddThreads);
+  if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
+  else if (io == 0) {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col_odd<N1, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
+  } else {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_odd<N1, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_odd<N1, 1, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col_odd<N1, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
+  }
+}
+
+template <int Q, bool EVEN>
+static void launch_col_pair_t(int kind, int io, const ColArgs& c, dim3 grid, hipStream_t s) {
+  const dim3 block(kColOddThreads);
+  if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
+  else if (io == 0) {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col_pair<Q, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
+  } else {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_pair<Q, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_pair<Q, 1, COL_MID, EVEN>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col_pair<Q, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
+  }
+}
+
+template <int Q>
+static hipError_t launch_col_pair(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+  const dim3 grid(groups * c.n_col_blocks);
+  if (c.L % 2 == 0) launch_col_pair_t<Q, true>(kind, io, c, grid, s);
+  else launch_col_pair_t<Q, false>(kind, io, c, grid, s);
+  return hipGetLastError();
+}
+
+template <int N1>
+static hipError_t launch_col_odd(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
+  const dim3 grid(groups * c.n_col_blocks);
+  if (c.L % 2 == 0) launch_col_odd_t<N1, true>(kind, io, c, grid, s);
+  else launch_col_odd_t<N1, false>(kind, io, c, grid, s);
+  return hipGetLastError();
 }
 
 // Grid columns exist for the first axes the grid paths plan (2-D 256..1024,
@@ -410,6 +627,8 @@ static hipError_t launch_col(int kind, int io, const ColArgs& c, int groups, hip
 }
 
 static int col_width(int n1, bool grid = false) {
+  if (!grid && odd_col_ok(n1)) return kColOddThreads;
+  if (!grid && n1 % 2 == 0 && odd_col_ok(n1 / 2)) return kColOddThreads / 2;
   switch (n1) {
     case 16: return ColCfg<16>::W;
     case 32: return ColCfg<32>::W;
@@ -424,6 +643,22 @@ static int col_width(int n1, bool grid = false) {
 
 static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int groups, hipStream_t s,
                                bool grid_mode = false) {
+  if (!grid_mode) {
+    switch (n1) {
+      case 3: return launch_col_odd<3>(kind, io, c, groups, s);
+      case 5: return launch_col_odd<5>(kind, io, c, groups, s);
+      case 9: return launch_col_odd<9>(kind, io, c, groups, s);
+      case 15: return launch_col_odd<15>(kind, io, c, groups, s);
+      case 25: return launch_col_odd<25>(kind, io, c, groups, s);
+      case 27: return launch_col_odd<27>(kind, io, c, groups, s);
+      case 6: return launch_col_pair<3>(kind, io, c, groups, s);
+      case 10: return launch_col_pair<5>(kind, io, c, groups, s);
+      case 18: return launch_col_pair<9>(kind, io, c, groups, s);
+      case 30: return launch_col_pair<15>(kind, io, c, groups, s);
+      case 50: return launch_col_pair<25>(kind, io, c, groups, s);
+      case 54: return launch_col_pair<27>(kind, io, c, groups, s);
+    }
+  }
   switch (n1) {
     case 16: return launch_col<16>(kind, io, c, groups, s, grid_mode);
     case 32: return launch_col<32>(kind, io, c, groups, s, grid_mode);
@@ -438,7 +673,9 @@ static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int g
 
 template <int N2>
 static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t s) {
-  const dim3 grid(groups * r.n_row_pairs), block(RowCfg<N2>::T);
+  // channel-major: n_units (channel, row pair) units padded to a multiple of 8, cmB workgroups each
+  const int blocks = (kind == ROW_CONV && r.cmB > 1) ? (r.n_units + 7) / 8 * 8 * r.cmB : groups * r.n_row_pairs;
+  const dim3 grid(blocks), block(RowCfg<N2>::T);
   if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, block, 0, s, r);
   else hipLaunchKernelGGL((k_row<N2, ROW_CONV>), grid, block, 0, s, r);
   return hipGetLastError();
@@ -467,16 +704,17 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   c.n_col_blocks = (p.n2 + W - 1) / W;
   RowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
-  r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = p.n1 / 2;
+  r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = (p.n1 + 1) / 2;
   // With B > 1 a launch covers whole channels (all their batch rows), so the
   // row pass reads each channel's spectrum once instead of once per batch row.
-  const bool cm = a.B > 1 && a.n_rows == a.B * a.D && a.rows_per_group >= a.B && r.n_row_pairs % 8 == 0;
+  const bool cm = a.B > 1 && a.n_rows == a.B * a.D && a.rows_per_group >= a.B;
   const int units = cm ? a.D : a.n_rows, per = cm ? a.rows_per_group / a.B : a.rows_per_group;
   c.cmB = r.cmB = cm ? a.B : 1;
   c.cmD = a.D;
   for (int r0 = 0; r0 < units; r0 += per) {
     const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? a.B : 1);
     c.r0 = r0; r.r0 = r0;
+    r.n_units = cm ? groups / a.B * r.n_row_pairs : 0;
     hipError_t e = dispatch_col(p.n1, COL_FIRST, a.io, c, groups, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < a.NORD; ++n) {
@@ -499,7 +737,7 @@ hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream
   c.n_col_blocks = (p.n2 + W - 1) / W;
   RowArgs r{};
   r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = p.n1; r.spec_stride = a.spec_stride;
-  r.n_row_pairs = p.n1 / 2;
+  r.n_row_pairs = (p.n1 + 1) / 2;
   for (int r0 = 0; r0 < a.NF; r0 += a.rows_per_group) {
     const int groups = (a.NF - r0 < a.rows_per_group) ? a.NF - r0 : a.rows_per_group;
     c.r0 = r0; r.r0 = r0;

@@ -69,8 +69,61 @@ inline int64_t next_pow2(int64_t x) {
 inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Column lengths of the four-step path beyond the powers of two: q odd (one
+// thread per column, the whole column DFT in registers) and 2q (a lane pair
+// per column).  With power-of-two rows they give complex lengths
+// N = n1 * n2 = 2^a 3^b 5^c, so a zero-padded row of a length L that is not
+// a power of two needs at most ~20% more points than 2L instead of up to
+// 100% more.
+constexpr int kOddCols[] = {3, 5, 9, 15, 25, 27};
+constexpr int kRowMaxOdd = 4096;    // longest row with an odd column length
+constexpr int kRowMaxPair = 2048;   // longest row with a 2q column length
+inline bool is_odd_col(int64_t n) {
+  for (int q : kOddCols)
+    if (n == q) return true;
+  return false;
+}
+inline bool is_pair_col(int64_t n) { return n % 2 == 0 && is_odd_col(n / 2); }
+
+// Relative cost of one complex point per pass on each kind of plan, from
+// timings of the order-3, B = 2, D = 1024, bf16 shapes on MI355X (points per
+// ms per order): power-of-two plans 14.0, odd or 2q columns with rows of at
+// most 2048 points 12.6, odd columns with 4096-point rows 11.3.
+inline double plan_cost(int64_t n1, int64_t n2) {
+  const double rate = is_pow2(n1) ? 14.0 : (n2 <= 2048 ? 12.6 : 11.3);
+  return (double)(n1 * n2) / rate;
+}
+
+// Cheapest odd or 2q factorisation with n1 * n2 >= Nmin (n2 a power of two
+// in [kRowMin, kRowMaxOdd or kRowMaxPair]); 0 if none.
+inline int64_t best_smooth_plan(int64_t Nmin, int64_t* n1_out, int64_t* n2_out) {
+  int64_t best = 0;
+  double best_cost = 0;
+  for (int q : kOddCols) {
+    for (int n1 = q; n1 <= 2 * q; n1 += q) {
+      int64_t n2 = next_pow2((Nmin + n1 - 1) / n1);
+      if (n2 < kRowMin) n2 = kRowMin;
+      if (n2 > (n1 % 2 ? kRowMaxOdd : kRowMaxPair)) continue;
+      const double c = plan_cost(n1, n2);
+      if (best == 0 || c < best_cost) {
+        best = n1 * n2;
+        best_cost = c;
+        *n1_out = n1;
+        *n2_out = n2;
+      }
+    }
+  }
+  return best;
+}
+
 // Returns 0 on success, 2 (shape) for a bad L, 3 (unsupported) when a forced
 // path cannot serve L.  force_path: NULL/"" auto, "single", "fourstep".
+// A forced column length (force_n1) is a power of two in [kColMin, kColMax],
+// an odd q of kOddCols or 2q.  Lengths long enough for the four-step path by
+// themselves (and not circular) take the cheaper (plan_cost) of the
+// power-of-two and the best 2^a 3^b 5^c factorisation; forced four-step runs
+// of shorter lengths keep the power of two, so their spectra match the
+// single path's.
 inline int make_plan(int64_t L, const char* force_path, const char* force_n1, PlanInfo* out, int circular = 0) {
   if (L < 1 || L > kMaxL) return 2;
   int64_t N = next_pow2(2 * L) / 2;
@@ -101,15 +154,34 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
     int64_t n1 = N / kRowMax;
     if (n1 < kColMin) n1 = kColMin;
     if (n1 > kColMax) n1 = kColMax;   // longest rows (up to 8192) beyond that
+    int64_t n2 = N / n1;
+    const bool natural = (next_pow2(2 * L) / 2) > kSingleMaxN;
     if (force_n1 && *force_n1) {
       const int64_t f = atoll(force_n1);
-      if (!is_pow2(f) || f < kColMin || f > kColMax) return 3;
-      n1 = f;
-      if (circular && N / n1 < kRowMin) return 3;
-      while (N / n1 < kRowMin) N <<= 1;   // a longer FFT is still exact
+      if (is_odd_col(f) || is_pair_col(f)) {
+        if (circular) return 3;
+        n1 = f;
+        n2 = next_pow2((L + f - 1) / f);
+        if (n2 < kRowMin) n2 = kRowMin;
+        if (n2 > (f % 2 ? kRowMaxOdd : kRowMaxPair)) return 3;
+      } else {
+        if (!is_pow2(f) || f < kColMin || f > kColMax) return 3;
+        n1 = f;
+        if (circular && N / n1 < kRowMin) return 3;
+        while (N / n1 < kRowMin) N <<= 1;   // a longer FFT is still exact
+        n2 = N / n1;
+      }
+      N = n1 * n2;
+    } else if (natural && !circular) {
+      int64_t q = 0, r = 0;
+      const int64_t smooth = best_smooth_plan(L, &q, &r);
+      if (smooth > 0 && plan_cost(q, r) < plan_cost(n1, n2)) {
+        n1 = q;
+        n2 = r;
+        N = smooth;
+      }
     }
-    const int64_t n2 = N / n1;
-    if (n1 > kColMax || n2 > kRowLimit || n2 < kRowMin) return 3;
+    if (n1 > kColMax || n2 > kRowLimit || n2 < kRowMin || n1 * n2 != N) return 3;
     p.n1 = (int)n1;
     p.n2 = (int)n2;
   }

@@ -32,8 +32,10 @@ def test_status_strings():
 @pytest.mark.parametrize("L,M,path", [(1, 128, "single"), (17, 128, "single"), (32, 128, "single"),
                                       (33, 128, "single"), (65, 256, "single"), (256, 512, "single"),
                                       (1000, 2048, "single"), (2048, 4096, "single"), (8192, 16384, "single"),
-                                      (16384, 32768, "single"), (16385, 65536, "fourstep"),
-                                      (65536, 131072, "fourstep"), (100000, 262144, "fourstep"),
+                                      (16384, 32768, "single"), (16385, 36864, "fourstep"),
+                                      (20000, 40960, "fourstep"), (50000, 102400, "fourstep"),
+                                      (70000, 204800, "fourstep"),
+                                      (65536, 131072, "fourstep"), (100000, 204800, "fourstep"),
                                       (131072, 262144, "fourstep"), (1 << 20, 1 << 21, "fourstep"),
                                       (1 << 22, 1 << 23, "fourstep")])
 def test_plan_lengths(L, M, path):
@@ -42,7 +44,12 @@ def test_plan_lengths(L, M, path):
     assert p["M"] >= 2 * L - 1
     N = M // 2
     if path == "fourstep":
-        assert p["n1"] * p["n2"] == N and 16 <= p["n1"] <= 1024 and 64 <= p["n2"] <= 8192
+        assert p["n1"] * p["n2"] == N and 64 <= p["n2"] <= 8192 and p["n2"] & (p["n2"] - 1) == 0
+        # power-of-two columns, or an odd column length (FFT length 2^a 3^b 5^c)
+        assert (16 <= p["n1"] <= 1024 and p["n1"] & (p["n1"] - 1) == 0
+                or p["n1"] in (3, 5, 9, 15, 25, 27) or p["n1"] in (6, 10, 18, 30, 50, 54) and p["n2"] <= 2048)
+        # never longer than the power of two >= 2L
+        assert M <= 1 << (2 * L - 1).bit_length()
     assert p["spec_stride"] >= N + 1
     assert p["spec_stride"] % 16 == 0
 
@@ -54,7 +61,13 @@ def test_plan_forced_paths(monkeypatch):
     monkeypatch.setenv("HYENA_FOURSTEP_N1", "64")
     p = H.plan(300)
     assert p["n1"] == 64 and p["n2"] >= 64 and p["n1"] * p["n2"] == p["M"] // 2
-    monkeypatch.setenv("HYENA_FOURSTEP_N1", "48")          # not a power of two
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "25")          # odd column length: FFT length 2 * 25 * 16
+    p = H.plan(300)
+    assert (p["n1"], p["n2"], p["M"]) == (25, 64, 3200)
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "50")          # lane-pair column length 2 x 25
+    p = H.plan(300)
+    assert (p["n1"], p["n2"], p["M"]) == (50, 64, 6400)
+    monkeypatch.setenv("HYENA_FOURSTEP_N1", "48")          # neither a power of two nor an odd column length
     with pytest.raises(H.HyenaError):
         H.plan(300)
     monkeypatch.delenv("HYENA_FOURSTEP_N1")

@@ -110,6 +110,8 @@ LONG_CASES = [
     (2, 2, 3, 1000, "fp32", "fourstep", "16"), (3, 1, 2, 2048, "fp32", "fourstep", "64"),
     (1, 3, 2, 4096, "fp32", "fourstep", "32"), (2, 2, 2, 777, "bf16", "fourstep", "16"),
     (8, 1, 1, 512, "fp32", "fourstep", "16"),
+    (2, 2, 2, 1000, "fp32", "fourstep", "25"), (2, 1, 3, 777, "bf16", "fourstep", "3"),   # odd column lengths
+    (3, 2, 1, 2000, "fp32", "fourstep", "9"), (2, 2, 2, 1500, "fp32", "fourstep", "50"),
     (2, 2, 2, 12000, "fp32", None, None),     # single-path spectrum rewritten for the four-step backward
     (2, 1, 2, 20000, "fp32", None, None),     # four-step plan, ragged length
     (2, 1, 2, 65536, "bf16", None, None),     # the 64K shape's length
@@ -124,6 +126,23 @@ def test_backward_long_matches_oracle(N, B, D, L, io, force, n1, monkeypatch):
         monkeypatch.setenv("HYENA_FOURSTEP_N1", n1)
     got, ref = _run(N, B, D, L, io, seed=41 + N)
     _check(got, ref, io)
+
+
+@pytest.mark.parametrize("B,D,L,circular,n1", [(3, 31, 2048, False, "16"), (2, 5, 32768, True, None),
+                                               (2, 15, 6000, False, "25")])
+def test_backward_long_several_pass_groups(B, D, L, circular, n1, monkeypatch):
+    """A 1 MiB work budget splits the rows into several channel-major pass
+    groups, the last one ragged: 93 rows of 16 KiB as 15 + 15 + 1 channels;
+    10 periodic rows of 128 KiB as 2 + 2 + 1 channels; 30 rows of 50 KiB at
+    an odd column length (25 x 256) as 7 + 7 + 1 channels.  Channels on both
+    sides of every group boundary are checked."""
+    monkeypatch.setenv("HYENA_WORK_MB", "1")
+    if n1:
+        monkeypatch.setenv("HYENA_FORCE_PATH", "fourstep")
+        monkeypatch.setenv("HYENA_FOURSTEP_N1", n1)
+    chans = sorted({0, 1, D // 2 - 1, D // 2, D - 2, D - 1} | ({14, 15, 29, 30} if D == 31 else set()))
+    got, ref = _run(2, B, D, L, "fp32", channels=chans, seed=57, circular=circular)
+    _check(got, ref, "fp32")
 
 
 def test_backward_long_deterministic(monkeypatch):
