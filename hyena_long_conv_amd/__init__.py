@@ -21,7 +21,7 @@ import os
 import re
 
 __all__ = ["HyenaError", "lib", "plan", "filter_gen", "filter_spectrum", "spectrum_export",
-           "forward", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
+           "forward", "forward_static", "forward_workspace_bytes", "spectrum_bytes", "spectrum_workspace_bytes",
            "LIB_PATH", "HEADER_PATH", "header_functions", "PreparedForward", "BlockParams",
            "in_projection", "out_projection", "block_forward", "block_workspace_bytes", "PreparedCall",
            "prepare_in_projection", "prepare_out_projection", "prepare_block_forward", "backward",
@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.hyena_forward_workspace_bytes.restype = i64
     L.hyena_forward.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, vp, i64, vp]
     L.hyena_forward.restype = i32
+    L.hyena_forward_static.argtypes = [vp, ctypes.POINTER(vp), vp, vp, i64, i32, i32, i64, i32, vp]
+    L.hyena_forward_static.restype = i32
     bp = ctypes.POINTER(BlockParams)
     L.hyena_in_projection.argtypes = [vp, bp, ctypes.POINTER(vp), i64, i64, i32, vp]
     L.hyena_in_projection.restype = i32
@@ -325,6 +327,29 @@ def forward(v, xs, spec, out=None, workspace=None, circular: bool | None = None)
     """y = z_{N+1} of the order-N Hyena recurrence (v, x_n: [B, D, L] fp32 or bf16).
     The convolution mode defaults to the one the spectrum was built for."""
     return PreparedForward(v, xs, spec, out, workspace, circular)()
+
+
+def forward_static(v, xs, spec, out):
+    """hyena_forward_static: the forward with its four-step intermediate in the
+    library's static device scratch (no workspace, no device allocation by the
+    library or here: the caller passes the output).  Calls on one GPU share
+    that scratch; serialise them (one stream)."""
+    import torch
+    if v.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("v must be float32 or bfloat16")
+    _need_cuda(v, "v", v.dtype)
+    _need_cuda(out, "out", v.dtype)
+    B, D, L = v.shape
+    N = len(xs)
+    for i, x in enumerate(xs):
+        _need_cuda(x, f"x[{i}]", v.dtype)
+        if tuple(x.shape) != (B, D, L):
+            raise ValueError(f"x[{i}] shape {tuple(x.shape)} != {(B, D, L)}")
+    io = HYENA_FP32 if v.dtype == torch.float32 else HYENA_BF16
+    xp = (ctypes.c_void_p * N)(*[x.data_ptr() for x in xs])
+    _check(lib().hyena_forward_static(_ptr(v), xp, _ptr(spec), _ptr(out), B, D, N, L, io, _stream(v)),
+           "hyena_forward_static")
+    return out
 
 
 # ---------------------------------------------------------------- the block

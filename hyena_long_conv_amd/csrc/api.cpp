@@ -303,9 +303,16 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
   return hyena_forward_ex(v, x, spec, y, B, D, N, L, io, HYENA_CONV_LINEAR, workspace, workspace_bytes, stream);
 }
 
-hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
-                              int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
-                              void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward's argument checks and launch.  static_ws: the four-step
+// intermediate goes to the library's static device scratch (looked up on
+// the current device) instead of the caller's workspace.
+hyena_status forward_impl(const void* v, const void* const* x, const void* spec, void* y, int64_t B, int32_t D,
+                          int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode, void* workspace,
+                          int64_t workspace_bytes, bool static_ws, void* stream) {
   if (!v || !x || !spec || !y) return HYENA_ERR_NULL;
   if (B < 1 || B > (1 << 20) || !sizes_ok(D, N, L)) return HYENA_ERR_SHAPE;
   if (N > kMaxOrder || !mode_ok(mode)) return HYENA_ERR_UNSUPPORTED;
@@ -326,6 +333,13 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
   if (overlap(y, act, v, act) || overlap(y, act, spec, sb)) return HYENA_ERR_ALIAS;
   for (int n = 0; n < N; ++n)
     if (overlap(y, act, x[n], act)) return HYENA_ERR_ALIAS;
+  if (static_ws) {
+    void* sp = nullptr;
+    int64_t sbytes = 0;
+    if (static_scratch(&sp, &sbytes) != hipSuccess) return HYENA_ERR_HIP;
+    workspace = sp;
+    workspace_bytes = sbytes;
+  }
   ForwardArgs a{};
   a.v = v;
   for (int n = 0; n < N; ++n) a.x.p[n] = x[n];
@@ -338,12 +352,16 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
   if (p.path == PATH_SINGLE) {
     e = single_forward(a, p.N, (hipStream_t)stream);
   } else {
-    if (!workspace || workspace_bytes < p.N * 8) return HYENA_ERR_WORKSPACE;
-    if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
-        overlap(workspace, workspace_bytes, spec, sb))
-      return HYENA_ERR_ALIAS;
-    for (int n = 0; n < N; ++n)
-      if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
+    if (static_ws) {
+      if (p.N * 8 > workspace_bytes) return HYENA_ERR_WORKSPACE;   // one row's intermediate must fit
+    } else {
+      if (!workspace || workspace_bytes < p.N * 8) return HYENA_ERR_WORKSPACE;
+      if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
+          overlap(workspace, workspace_bytes, spec, sb))
+        return HYENA_ERR_ALIAS;
+      for (int n = 0; n < N; ++n)
+        if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
+    }
     int64_t g = forward_group_rows(p, B * D);
     if (g * p.N * 8 > workspace_bytes) g = workspace_bytes / (p.N * 8);
     a.work = workspace;
@@ -351,6 +369,23 @@ hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* s
     e = fourstep_forward(a, p, (hipStream_t)stream);
   }
   return e == hipSuccess ? HYENA_OK : HYENA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status hyena_forward_ex(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                              int32_t D, int32_t N, int64_t L, hyena_dtype io, hyena_conv_mode mode,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  return forward_impl(v, x, spec, y, B, D, N, L, io, mode, workspace, workspace_bytes, false, stream);
+}
+
+static_assert(HYENA_STATIC_SCRATCH_BYTES == kStaticScratchBytes, "header and library disagree on the scratch size");
+
+hyena_status hyena_forward_static(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
+                                  int32_t D, int32_t N, int64_t L, hyena_dtype io, void* stream) {
+  return forward_impl(v, x, spec, y, B, D, N, L, io, HYENA_CONV_LINEAR, nullptr, 0, true, stream);
 }
 
 // ------------------------------------------------------- filter families

@@ -33,6 +33,7 @@ hipError_t fourstep_forward(const ForwardArgs&, const PlanInfo&, hipStream_t) { 
 hipError_t fourstep_spectrum(const SpectrumArgs&, const PlanInfo&, hipStream_t) { return kNoKernels; }
 hipError_t filter_gen(const FilterGenArgs&, hipStream_t) { return kNoKernels; }
 hipError_t spectrum_export(const void*, int, const PlanInfo&, float*, hipStream_t) { return kNoKernels; }
+hipError_t static_scratch(void**, int64_t*) { return kNoKernels; }
 hipError_t spectrum_to_fourstep(const void*, int, const PlanInfo&, const PlanInfo&, void*, hipStream_t) {
   return kNoKernels;
 }

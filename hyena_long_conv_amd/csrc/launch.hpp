@@ -141,6 +141,11 @@ hipError_t grid3d_forward(const NdArgs& a, hipStream_t s);
 // (order n; spec: build the spectrum instead), kernels_nd.hip
 hipError_t grid_plane_pass(const NdArgs& a, int r0, int groups, int n, bool spec, hipStream_t s);
 
+// The static device scratch of hyena_forward_static (scratch.hip): its
+// address on the current device (looked up once per device) and its size.
+constexpr int64_t kStaticScratchBytes = int64_t(128) << 20;
+hipError_t static_scratch(void** ptr, int64_t* bytes);
+
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);

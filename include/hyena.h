@@ -156,6 +156,29 @@ hyena_status hyena_forward(const void* v, const void* const* x, const void* spec
                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * hyena_forward_static: hyena_forward for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, checks, kernels and results as
+ * hyena_forward (linear mode), without the workspace: the four-step
+ * intermediate lives in one static device buffer of the library,
+ * HYENA_STATIC_SCRATCH_BYTES (128 MiB) per GPU, held from the library's load
+ * until the process ends; pass groups are sized to it (at most 256 rows of
+ * 512 KiB for L = 64K, 16 rows of 8 MiB for L = 1M).  The buffer needs no
+ * clearing: each pass group writes its intermediate before reading it.  The
+ * call allocates nothing (no hipMalloc, no hipFree); its first call on a
+ * device looks the buffer's address up there, once.  All calls on one GPU
+ * share that buffer: calls that may overlap in time on one GPU (different
+ * streams, threads) race and must be serialised by the caller, e.g. by
+ * issuing them on one stream.
+ * Errors as hyena_forward; WORKSPACE if one row's intermediate (8 * M / 2
+ * bytes) exceeded the buffer, which no supported L reaches (L = 2^22 needs
+ * 32 MiB); HIP if the buffer's address cannot be obtained.
+ */
+#define HYENA_STATIC_SCRATCH_BYTES (128LL << 20)
+hyena_status hyena_forward_static(const void* v, const void* const* x, const void* spec, void* y,
+                                  int64_t B, int32_t D, int32_t N, int64_t L, hyena_dtype io, void* stream);
+
+/*
  * Other filter families (homemade-llm "02. 3つの Hyena 演算子", section 3).
  *
  * hyena_filter_gen_li -- Hyena-LI: each filter is a sum of S real

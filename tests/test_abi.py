@@ -131,6 +131,24 @@ def test_forward_rejects_bad_arguments():
     assert _fwd(L=65536, ws=A, wsb=1 << 24, y=Y) == ALIAS
 
 
+def _fwd_static(v=A, x=(Bp, C), spec=Dp, y=Y, B=1, D=4, N=2, L=64, io=0):
+    xs = None if x is None else (vp * max(1, len(x)))(*x)
+    return H.lib().hyena_forward_static(vp(v), xs, vp(spec), vp(y), B, D, N, L, io, None)
+
+
+def test_forward_static_rejects_bad_arguments():
+    # the same host checks as hyena_forward, before the scratch is looked up
+    assert _fwd_static(v=0) == NULL
+    assert _fwd_static(x=(Bp, 0)) == NULL
+    assert _fwd_static(B=0) == SHAPE
+    assert _fwd_static(L=(1 << 22) + 1) == SHAPE
+    assert _fwd_static(N=9, x=tuple(Bp + 0x1000000 * i for i in range(9))) == UNSUP
+    assert _fwd_static(io=7) == UNSUP
+    assert _fwd_static(y=Y + 2) == ALIGN
+    assert _fwd_static(y=A) == ALIAS
+    assert _fwd_static(L=65536, y=C + 64) == ALIAS
+
+
 def test_spectrum_and_filter_gen_reject_bad_arguments():
     lib = H.lib()
     assert lib.hyena_filter_spectrum(None, 4, 2, 64, vp(Dp), None, 0, None) == NULL
