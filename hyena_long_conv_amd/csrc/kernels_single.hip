@@ -460,6 +460,247 @@ static int resident_workgroups(K k, int threads) {
   return cus * per_cu;
 }
 
+// ------------------------------------------- cross-lane variant (N = 2048)
+//
+// HYENA_SINGLE_XLANE=1 builds a variant of the forward for N = 2048 complex
+// points (rows of L <= 2048) whose FFT exchanges data inside a wave with
+// lane permutations instead of LDS: of the three exchanges per FFT of the
+// LDS version, only the one across the four waves stays in LDS.  Index
+// n = j + 256 i (thread j = 64 w + l, lane l = l0 + 8 l1, register i):
+//   1. DFT_8 over i in registers, twiddle W_2048^(j k_i);
+//   2. DFT_4 over w (LDS exchange: wave w' takes the series k_i = 2w', 2w'+1),
+//      twiddle W_256^(l k_w);
+//   3. DFT_64 over l: swap register bits with lane bits 3..5 (8x8
+//      register/lane transpose: DPP row_ror:8, v_permlane16_swap,
+//      v_permlane32_swap), DFT_8 over l1, twiddle W_64^(l0 k0), swap register
+//      bits with lane bits 0..2 (DPP quad permutations and row shifts), DFT_8
+//      over l0.
+// Thread (w, L) then holds bin k = 2w + (L >> 5) + 8 ((L >> 3) & 3) +
+// 32 (L & 7) + 256 r in register r.  The spectral step pairs bins through
+// LDS, each thread computing its own bins' outputs, and the inverse FFT is
+// the forward's adjoint (same steps in reverse, conjugate twiddles), which
+// returns the natural layout for the gate.  Built to measure the cross-lane
+// exchanges against LDS exchanges on the VALU-bound single-pass kernel.
+#ifndef HYENA_SINGLE_XLANE
+#define HYENA_SINGLE_XLANE 0
+#endif
+#if HYENA_SINGLE_XLANE
+
+namespace xlane {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// value of lane l ^ 4 (within rows of 16): row_shr:4 into lanes 4-7, 12-15,
+// row_shl:4 into lanes 0-3, 8-11
+__device__ __forceinline__ float xor4(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const int t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xA, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, x, 0x104, 0xF, 0x5, false));
+}
+template <int LB>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (LB == 0) return dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (LB == 1) return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (LB == 2) return xor4(v);
+  else return dpp<0x128>(v);                         // row_ror:8
+}
+
+// One 2x2 block step of a register/lane transpose: lane bit LB <-> register
+// bit RB.  For lanes L0 (bit clear) and L1 (bit set) and registers r0 (bit
+// clear) and r1 (bit set): L0.r1 <- L1.r0 and L1.r0 <- L0.r1.
+template <int LB, int RB>
+__device__ __forceinline__ void tstep(cf (&u)[8], int lane) {
+#pragma unroll
+  for (int r0 = 0; r0 < 8; ++r0) {
+    if (r0 & (1 << RB)) continue;
+    const int r1 = r0 | (1 << RB);
+    if constexpr (LB == 4 || LB == 5) {
+      uint32_t ax = __float_as_uint(u[r0].x), bx = __float_as_uint(u[r1].x);
+      uint32_t ay = __float_as_uint(u[r0].y), by = __float_as_uint(u[r1].y);
+      if constexpr (LB == 4) {
+        const auto px = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+        const auto py = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+        ax = px[0]; bx = px[1]; ay = py[0]; by = py[1];
+      } else {
+        const auto px = __builtin_amdgcn_permlane32_swap(ax, bx, false, false);
+        const auto py = __builtin_amdgcn_permlane32_swap(ay, by, false, false);
+        ax = px[0]; bx = px[1]; ay = py[0]; by = py[1];
+      }
+      u[r0] = make_float2(__uint_as_float(ax), __uint_as_float(ay));
+      u[r1] = make_float2(__uint_as_float(bx), __uint_as_float(by));
+    } else {
+      // value selects only: selecting between array elements became a
+      // run-time index, i.e. a trip through scratch memory
+      const bool hi = (lane >> LB) & 1;
+      const cf a0 = u[r0], a1 = u[r1];
+      const float sx = hi ? a0.x : a1.x, sy = hi ? a0.y : a1.y;
+      const float rx = lane_xor<LB>(sx), ry = lane_xor<LB>(sy);
+      u[r0] = make_float2(hi ? rx : a0.x, hi ? ry : a0.y);
+      u[r1] = make_float2(hi ? a1.x : rx, hi ? a1.y : ry);
+    }
+  }
+}
+
+// register bits 0..2 <-> lane bits 0..2, and <-> lane bits 3..5
+__device__ __forceinline__ void transpose_low(cf (&u)[8], int lane) {
+  tstep<0, 0>(u, lane);
+  tstep<1, 1>(u, lane);
+  tstep<2, 2>(u, lane);
+}
+__device__ __forceinline__ void transpose_high(cf (&u)[8], int lane) {
+  tstep<3, 0>(u, lane);
+  tstep<4, 1>(u, lane);
+  tstep<5, 2>(u, lane);
+}
+
+template <bool INV>
+__device__ __forceinline__ void twiddle_powers(cf (&u)[8], cf w, int mask) {
+  // u[r] *= w^(r & mask), w conjugated for the inverse; the powers are
+  // recomputed at every use rather than kept live across the row loop
+  const cf b = opaque(INV ? cconj(w) : w);
+#pragma unroll
+  for (int r = 1; r < 8; ++r)
+    if (r & mask) u[r] = cmul(u[r], step_power<8>(make_float2(1.f, 0.f), b, r & mask));
+}
+
+template <bool INV>
+__device__ __forceinline__ void fft2048(cf (&u)[8], cf* smem, int j, cf t1, cf t2, cf t3) {
+  const int w = j >> 6, lane = j & 63;
+  if constexpr (!INV) {
+    dft<8, false>(u);
+    twiddle_powers<false>(u, t1, 7);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) smem[k * 256 + j] = u[k];
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) u[sl * 4 + v] = smem[(2 * w + sl) * 256 + v * 64 + lane];
+    dft4<false>(u[0], u[1], u[2], u[3]);
+    dft4<false>(u[4], u[5], u[6], u[7]);
+    twiddle_powers<false>(u, t2, 3);
+    transpose_high(u, lane);
+    dft<8, false>(u);
+    twiddle_powers<false>(u, t3, 7);
+    transpose_low(u, lane);
+    dft<8, false>(u);
+  } else {
+    dft<8, true>(u);
+    transpose_low(u, lane);
+    twiddle_powers<true>(u, t3, 7);
+    dft<8, true>(u);
+    transpose_high(u, lane);
+    twiddle_powers<true>(u, t2, 3);
+    dft4<true>(u[0], u[1], u[2], u[3]);
+    dft4<true>(u[4], u[5], u[6], u[7]);
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) smem[(2 * w + sl) * 256 + v * 64 + lane] = u[sl * 4 + v];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) u[k] = smem[k * 256 + j];
+    twiddle_powers<true>(u, t1, 7);
+    dft<8, true>(u);
+  }
+}
+
+}  // namespace xlane
+
+template <int IOT, bool EVEN, bool EXACT>
+__global__ void __launch_bounds__(256, HYENA_SINGLE_WAVES)
+k_single_forward_xl(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, void* __restrict__ y,
+                    int B, int D, int NORD, int L, int64_t spec_stride, int n_rows) {
+  constexpr int N = 2048, E = 8, S = N / E, NV = E / 2;
+  const auto ldp = [&](const void* p, int64_t o, int t) {
+    if constexpr (EXACT) return ld_pair_in<IOT>(p, o, t);
+    else return ld_pair<IOT, EVEN, true>(p, o, (int64_t)t, L);
+  };
+  __shared__ cf smem[N];
+  const int j = threadIdx.x, w = j >> 6, lane = j & 63;
+  const cf t1 = twiddle<false>((uint32_t)j, 2048u);
+  const cf t2 = twiddle<false>((uint32_t)lane, 256u);
+  const cf t3 = twiddle<false>((uint32_t)(lane & 7), 64u);
+  // bins of this thread: k(r) = kb + 256 r
+  const int kb = 2 * w + (lane >> 5) + 8 * ((lane >> 3) & 3) + 32 * (lane & 7);
+  const int64_t qs = spec_stride / 3;
+  for (int wg = blockIdx.x; wg < n_rows; wg += gridDim.x) {
+    const int r = row_of_workgroup(wg, B, D), d = r % D;
+    const int64_t off = (int64_t)r * L;
+    cf u[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) u[i] = (i < NV) ? ldp(v, off, 2 * (j + i * S)) : make_float2(0.f, 0.f);
+    for (int n = 0; n < NORD; ++n) {
+      const cf* g = spec + (int64_t)(n * D + d) * spec_stride;
+      xlane::fft2048<false>(u, smem, j, t1, t2, t3);
+      // spectral step: every bin meets its partner N - k through LDS
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < E; ++i) smem[kb + 256 * i] = u[i];
+      __syncthreads();
+      // every bin k: C'(k) = A C(k) + i Bq conj C(N - k), with (A, Bq) =
+      // (a1[k], bq[k]) below N/2, (a2[N-k], conj bq[N-k]) above, (a1[N/2], 0)
+      // at N/2 (bin 0 pairs with itself)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int k = kb + 256 * i;
+        const int p = k <= N / 2 ? k : N - k;
+        const cf A = g[(k <= N / 2 ? 0 : qs) + p];
+        cf Bq = g[2 * qs + p];
+        Bq = k < N / 2 ? Bq : (k == N / 2 ? make_float2(0.f, 0.f) : cconj(Bq));
+        const cf c = u[i], o = smem[(N - k) & (N - 1)];
+        u[i] = make_float2(fmaf(A.x, c.x, fmaf(-A.y, c.y, fmaf(Bq.x, o.y, -Bq.y * o.x))),
+                           fmaf(A.x, c.y, fmaf(A.y, c.x, fmaf(Bq.x, o.x, Bq.y * o.y))));
+      }
+      xlane::fft2048<true>(u, smem, j, t1, t2, t3);
+      const void* xn = x.p[0];   // uniform select: indexing the argument array would copy it to scratch
+#pragma unroll
+      for (int q = 1; q < kMaxOrder; ++q) xn = (n == q) ? x.p[q] : xn;
+      const bool last = (n == NORD - 1);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        cf z = make_float2(0.f, 0.f);
+        if (i < NV) {
+          const int t = 2 * (j + i * S);
+          const cf xv = ldp(xn, off, t);
+          z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+          if (last) {
+            if constexpr (EXACT) st_pair_in<IOT>(y, off, t, z);
+            else st_pair<IOT, EVEN>(y, off, (int64_t)t, L, z);
+          }
+        }
+        u[i] = z;
+      }
+    }
+  }
+}
+
+template <int IOT, bool EVEN, bool EXACT>
+static void launch_fwd_xl(const ForwardArgs& a, hipStream_t s) {
+  const auto k = k_single_forward_xl<IOT, EVEN, EXACT>;
+  int grid = a.n_rows;
+#if HYENA_SINGLE_PERSIST
+  static const int cap = resident_workgroups(k, 256) & ~7;
+  if (cap > 0 && grid > cap) grid = cap;
+#endif
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, a.v, a.x, (const cf*)a.spec, a.y, a.B, a.D, a.NORD, (int)a.L,
+                     a.spec_stride, a.n_rows);
+}
+
+template <int IOT>
+static hipError_t launch_fwd_xlane(const ForwardArgs& a, hipStream_t s) {
+  if (a.L == 2048) launch_fwd_xl<IOT, true, true>(a, s);
+  else if (a.L % 2 == 0) launch_fwd_xl<IOT, true, false>(a, s);
+  else launch_fwd_xl<IOT, false, false>(a, s);
+  return hipGetLastError();
+}
+
+#endif  // HYENA_SINGLE_XLANE
+
 template <int N, int IOT, bool EVEN, bool FULL, bool EXACT>
 static void launch_fwd_k(const ForwardArgs& a, hipStream_t s) {
   const auto k = k_single_forward<N, IOT, EVEN, FULL, EXACT>;
@@ -499,6 +740,9 @@ static hipError_t launch_spec(const SpectrumArgs& a, hipStream_t s) {
 }
 
 hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s) {
+#if HYENA_SINGLE_XLANE
+  if (N == 2048 && !a.circular) return a.io == 0 ? launch_fwd_xlane<0>(a, s) : launch_fwd_xlane<1>(a, s);
+#endif
 #define HY_CASE(NN)                                                       \
   case NN:                                                                \
     return a.io == 0 ? launch_fwd<NN, 0>(a, s) : launch_fwd<NN, 1>(a, s);
