@@ -418,13 +418,32 @@ struct RowArgs {
   int n_units;         // channel-major launch: (channel, row pair) units; the grid is padded to a multiple of 8
 };
 
+// LDS of the row pass.  HYENA_ROW_SW: 0 plain addressing; 1 XOR-swizzled
+// FFT stage buffers (RowLdsT<true>); 2 one padding slot after every 16
+// points, for every access (the first stage's stores, 16 points apart per
+// lane, then spread over the banks at the cost of a shift and an add).
+// Plain is the default: the pass keeps the VALU ~81% busy, and the other two
+// remove the bank conflicts (1.4 -> 0.02 / 0.3 per access) at the cost of
+// registers and address arithmetic, measured 14% and 1-2% slower.
+#ifndef HYENA_ROW_SW
+#define HYENA_ROW_SW 0
+#endif
+struct RowLdsPad16 {
+  cf* base;
+  static constexpr __host__ __device__ int padded(int npt) { return npt + npt / 16; }
+  template <int SH>
+  __device__ __forceinline__ cf& at(int i) const { return base[i + (i >> 4)]; }
+  __device__ __forceinline__ cf& operator()(int i) const { return base[i + (i >> 4)]; }
+};
+using RowPassLds = std::conditional<HYENA_ROW_SW == 2, RowLdsPad16, RowLdsT<HYENA_ROW_SW == 1>>::type;
+
 // Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
 // for k = k1 + n1*k2 < N, and S(N) at index N.
 template <int N2, int KIND>
 __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs a) {
   using C = RowCfg<N2>;
   constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E;
-  constexpr int PADN = RowLds::padded(N2);
+  constexpr int PADN = RowPassLds::padded(N2);
   __shared__ cf smem[2 * PADN];
   const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
   int g, w;
@@ -459,8 +478,8 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   const int k1m = (k1 == 0) ? 0 : n1 - k1;         // its k1
   const uint32_t N = (uint32_t)n1 * (uint32_t)N2;
   cf* row = a.work + (int64_t)g * N + (int64_t)k1 * N2;
-  const RowLds lds{smem + b * PADN};
-  const RowLds ldsm{smem + mb * PADN};
+  const RowPassLds lds{smem + b * PADN};
+  const RowPassLds ldsm{smem + mb * PADN};
   BlockFFT<N2, E, typename C::R> fft;
   fft.init(j);
   cf u[E];
