@@ -643,6 +643,9 @@ def main(argv=None):
                     help="time the whole block (in-projection + short convolutions, operator, out-projection)")
     ap.add_argument("--grid", default=None, metavar="NAME",
                     help="time the grid convolutions (HyenaND) on workload G1, G2, G3, GP, G4, GP2 or G5")
+    ap.add_argument("--work-mb", default=None, metavar="LIST",
+                    help="also time the main forward with four-step pass groups sized by each of these work "
+                         "budgets (MiB, comma-separated), reported under 'work_mb_sweep'")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for counter scaling)")
     args = ap.parse_args(argv)
@@ -836,9 +839,48 @@ def run_forward(args, cfg, torch, H, dev, copy_bps, steps, warmup):
         "setup": setup,
         "roofline": roof,
     }
+    if getattr(args, "work_mb", None):
+        out["work_mb_sweep"] = work_budget_sweep(args, cfg, torch, H, dev, data, sets, stream)
     v0, xs0, _, y0 = data[0]
     del data, calls, ws
     return out, (v0, xs0, y0)
+
+
+def work_budget_sweep(args, cfg, torch, H, dev, data, sets, stream):
+    """The same forward with the four-step pass groups sized by each work
+    budget of --work-mb (MiB; the library reads HYENA_WORK_MB at every call):
+    ms per forward from events around max(20, steps) forwards after 3 warm-up
+    forwards, and the HBM roofline fraction."""
+    budgets = [int(b) for b in str(args.work_mb).split(",") if b]
+    nc = H.plan(cfg.L)["M"] // 2
+    ws = torch.empty(max(max(budgets) << 20, nc * 8), dtype=torch.uint8, device=dev)
+    old = os.environ.get("HYENA_WORK_MB")
+    res = {}
+    try:
+        for mb in budgets:
+            os.environ["HYENA_WORK_MB"] = str(mb)
+            calls = [H.PreparedForward(v, xs, spec, out=y, workspace=ws) for v, xs, spec, y in data]
+            for i in range(3):
+                calls[i % sets]()
+            n = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(n):
+                calls[i % sets]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            rows = max(1, min(cfg.B * cfg.D, (mb << 20) // (nc * 8)))
+            res[str(mb)] = {"ms_per_step": ms, "rows_per_group_max": rows,
+                            "hbm_frac": min_bytes(cfg) / (ms / 1e3) / HBM_PEAK}
+    finally:
+        if old is None:
+            os.environ.pop("HYENA_WORK_MB", None)
+        else:
+            os.environ["HYENA_WORK_MB"] = old
+    del ws
+    return res
 
 
 if __name__ == "__main__":
