@@ -27,15 +27,14 @@ constexpr int64_t kMaxL = int64_t(1) << 22;
 #ifndef HYENA_SINGLE_MAX_N
 #define HYENA_SINGLE_MAX_N 16384
 #endif
-#ifndef HYENA_ROW_MAX
-#define HYENA_ROW_MAX 2048
-#endif
 #ifndef HYENA_WORK_MB
 #define HYENA_WORK_MB 256
 #endif
 constexpr int64_t kSingleMaxN = HYENA_SINGLE_MAX_N;
 constexpr int64_t kMinN = 64;
-constexpr int kRowMax = HYENA_ROW_MAX;   // largest row FFT (a row pair fills one workgroup's LDS)
+constexpr int kRowPref = 1024;           // preferred row length of power-of-two plans
+constexpr int kRowPrefMax = 4096;        // longest row a power-of-two plan takes below the 2^22 limit
+constexpr int kColPrefMin = 64, kColPrefMax = 512;
 constexpr int kRowMin = 64;
 constexpr int kRowLimit = 8192;  // largest row kernel compiled
 constexpr int kColMin = 16;
@@ -151,9 +150,18 @@ inline int make_plan(int64_t L, const char* force_path, const char* force_n1, Pl
       if (circular) return 3;
       N = (int64_t)kColMin * kRowMin;
     }
-    int64_t n1 = N / kRowMax;
+    // Rows of 1024 points with columns of 64..512 points: from timing sweeps
+    // over N = 2^15 .. 2^21 (orders 2-3, B = 1-4, fp32 and bf16), 1024-point
+    // rows beat 2048-point ones by 2-10% (the 64K shape 32 x 2048 -> 64 x 1024:
+    // -8%) as long as the columns stay at 512 points or fewer (1024-point
+    // columns run one workgroup per CU: the 1M shape keeps 512 x 2048;
+    // 2^21 takes 512 x 4096, 2.4% faster than 1024 x 2048).
+    int64_t n1 = N / kRowPref;
+    if (n1 < kColPrefMin) n1 = kColPrefMin;
+    if (n1 > kColPrefMax) n1 = kColPrefMax;
+    if (N / n1 < kRowMin) n1 = N / kRowMin;   // short (forced) lengths: rows of at least 64
     if (n1 < kColMin) n1 = kColMin;
-    if (n1 > kColMax) n1 = kColMax;   // longest rows (up to 8192) beyond that
+    if (N / n1 > kRowPrefMax) n1 = N / kRowPrefMax;   // 2^22: 1024 x 4096
     int64_t n2 = N / n1;
     const bool natural = (next_pow2(2 * L) / 2) > kSingleMaxN;
     if (force_n1 && *force_n1) {
