@@ -99,6 +99,7 @@ __all__ = [
     "filter_spectrum",
     "short_conv",
     "in_projection",
+    "in_projection_columns",
     "out_projection",
     "block_forward",
     "causal_conv_adjoint",
@@ -347,6 +348,20 @@ def in_projection(u: np.ndarray, W_in, b_in, w_short, N: int):
         Z = Z + np.asarray(b_in, np.float64)
     S = short_conv(np.transpose(Z, (0, 2, 1)), w_short)          # [B, (N+1)D, L]
     return S[:, :D], [S[:, n * D:(n + 1) * D] for n in range(1, N + 1)]
+
+
+def in_projection_columns(u: np.ndarray, W_in, b_in, w_short, cols) -> np.ndarray:
+    """The streams of in_projection at chosen projected columns only:
+    [B, len(cols), L], row i being column cols[i] of the (N+1)D-wide
+    projection (stream cols[i] // D, channel cols[i] % D), by the same
+    definition: the column's projection u W_in[c]^T (+ b_in[c]), then its
+    short causal FIR with w_short[c]."""
+    cols = np.asarray(cols, np.int64)
+    u = np.asarray(u, np.float64)
+    Z = u @ np.asarray(W_in, np.float64)[cols].T                   # [B, L, len(cols)]
+    if b_in is not None:
+        Z = Z + np.asarray(b_in, np.float64)[cols]
+    return short_conv(np.transpose(Z, (0, 2, 1)), np.asarray(w_short, np.float64)[cols])
 
 
 def out_projection(y: np.ndarray, W_out, b_out) -> np.ndarray:

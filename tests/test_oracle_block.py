@@ -71,6 +71,22 @@ def test_in_projection_matches_loops():
         assert np.allclose(xs[n], S[:, (n + 1) * D:(n + 2) * D], atol=1e-12)
 
 
+def test_in_projection_columns_match_loops():
+    """Column-sampled streams equal the loop definition at those columns (in
+    any order, repeats and both ends included), with and without bias."""
+    B, L, D, N, T = 2, 9, 4, 2, 4
+    u = rng.standard_normal((B, L, D))
+    W_in = rng.standard_normal(((N + 1) * D, D))
+    b_in = rng.standard_normal((N + 1) * D)
+    w = rng.standard_normal(((N + 1) * D, T))
+    cols = [11, 0, 5, 5, 3, 8]
+    for bias in (b_in, None):
+        got = O.in_projection_columns(u, W_in, bias, w, cols)
+        S = _loops_in_projection(u, W_in, np.zeros((N + 1) * D) if bias is None else bias, w, N)
+        assert got.shape == (B, len(cols), L)
+        assert np.allclose(got, S[:, cols], atol=1e-12)
+
+
 def test_out_projection_matches_loops():
     B, D, L = 2, 4, 5
     y = rng.standard_normal((B, D, L))
