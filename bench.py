@@ -310,7 +310,8 @@ def run_block(args, cfg, torch, H, dev):
     peak = MFMA_PEAK[cfg.io]
     roof = {"bound": "mfma", "achieved": fl_in / (ms_in / 1e3) / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
             "frac": fl_in / (ms_in / 1e3) / peak, "traffic": None,
-            "kernel": "k_inproj (in-projection GEMM + bias + short causal FIR + stream split)",
+            "kernel": (("k_inproj_wide" if cfg.io == "bf16" and D % 8 == 0 and bp["T"] <= 8 else "k_inproj")
+                       + " (in-projection GEMM + bias + short causal FIR + stream split)"),
             "algorithmic_flops_per_launch": fl_in,
             "out_projection": {"TFLOPs": fl_out / (ms_out / 1e3) / 1e12, "frac": fl_out / (ms_out / 1e3) / peak}}
     out = {

@@ -21,6 +21,8 @@
 // halo except at a strip's first tile.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "fft_engine.hpp"
 #include "launch.hpp"
 
@@ -386,6 +388,326 @@ __global__ void __launch_bounds__(TT, 2) k_inproj(InProjArgs a, int n_strips, in
   }
 }
 
+// ------------------------------------------- in-projection, bf16 wide tiles
+//
+// bf16 operands, D a multiple of 8, at most 8 short-filter taps.  Workgroup
+// = (batch b, time strip, 256-column block); the strip's tiles of 128 time
+// rows run in order.  Wave w owns columns [64w, 64w + 64) of the block at
+// all 128 rows of a tile: 4 x 2 accumulator blocks of 32 x 32
+// (v_mfma_f32_32x32x16_bf16), so each fragment read from LDS feeds 2 or 4
+// MFMAs.  Operand stages of 32 k go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: no registers, rows outside the data read as
+// zero) through a ring of three stage buffers: the loads of stage s + 2 are
+// issued as stage s is multiplied, so each has two stages' time to arrive,
+// with one barrier per stage.  A stage row is 64 B (4 chunks of 8 bf16);
+// chunk q of row r sits at chunk q ^ swz(r) of the row, which spreads both
+// the 16-lane and the 8-lane groups of a fragment read over all banks.
+//
+// The short convolution runs on the accumulators where they are.  Lane l of
+// a 32 x 32 block holds column l % 32 at rows 8g + 4(l / 32) + e (g, e < 4):
+// read in time order, the block's rows alternate between the two lane
+// halves in runs of 4.  One v_permlane32_swap per run position gives each
+// half the run before its own, so a lane has its 4 rows and the 4 (or 8)
+// before them; rows before a block come from the previous block, and rows
+// before a tile from the previous tile of the strip, all kept in registers
+// (a wave keeps its columns along the strip).  Each strip starts HALO rows
+// early: those rows give the first outputs their history and are not
+// stored.  Before t = 0 the rows are zero (no input, no bias).
+namespace wide {
+constexpr int TM = 128, TN = 256, BK = 32, HALO = 8, NBUF = 3;
+constexpr int A_BYTES = TM * BK * 2, B_BYTES = TN * BK * 2, STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr uint32_t OOB = 0x80000000u;            // a buffer offset past any record count: reads zero
+constexpr int EPI_CS = TM * 2 + 8;                // epilogue column stride in the ring (bytes)
+static_assert(4 * 64 * EPI_CS <= NBUF * STAGE_BYTES, "epilogue transpose fits the ring");
+// Chunk swizzle of stage row r: 2 bit 2 of r + (bit 1 xor bit 3).  For any
+// chunk q, 16 consecutive rows (and 8 consecutive rows) map to 16 (8)
+// distinct (r mod 4, q ^ swz) ((r mod 2, q ^ swz)) pairs: distinct banks.
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); }
+}  // namespace wide
+
+// Workgroup -> (row job, column block) map of the wide in-projection.  The
+// 8 XCDs form `groups` groups of 8 / groups; group g takes row jobs
+// [g * jpg, (g + 1) * jpg) with every column block, and splits those
+// (job, block) units, column block slowest, evenly over its XCDs.  An XCD
+// then streams the weights of about n_cb * groups / 8 + 1 column blocks
+// (few enough to stay in its L2) and shares each input tile among the
+// workgroups of its blocks; XCD loads differ by at most one unit.
+struct XcdSplit {
+  int groups, jpg, per_xcd;
+  __device__ __forceinline__ bool tile_of(int w, int jobs, int cbs, int& job, int& cb) const {
+    const int x = w & 7, k = w >> 3;
+    const int per = 8 / groups, g = x / per, xi = x - g * per;
+    const int j0 = g * jpg;
+    const int nj = (jobs - j0 < jpg) ? jobs - j0 : jpg;
+    if (nj <= 0) return false;
+    const int64_t n = (int64_t)nj * cbs;
+    const int64_t u = xi * n / per + k;
+    if (k >= per_xcd || u >= (xi + 1) * n / per) return false;
+    cb = (int)(u / nj);
+    job = j0 + (int)(u - (int64_t)cb * nj);
+    return true;
+  }
+};
+
+// The split for `jobs` row jobs x `cbs` column blocks of `block_bytes` of
+// weights each: the most groups (least input re-read across XCDs) whose
+// weight share per XCD stays within 2.5 MiB of its 4 MiB L2, unless
+// HYENA_INPROJ_GROUPS (1, 2, 4 or 8) says otherwise.
+static XcdSplit plan_split(int jobs, int cbs, int64_t block_bytes, int64_t& grid) {
+  int groups = 1;
+  for (int g = 8; g >= 1; g /= 2) {
+    const int64_t span = ((int64_t)cbs * g + 7) / 8 + 1;
+    if (span * block_bytes <= (int64_t)5 << 19 || g == 1) { groups = g; break; }
+  }
+  if (const char* e = getenv("HYENA_INPROJ_GROUPS")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4 || v == 8) groups = v;
+  }
+  const int per = 8 / groups;
+  const int jpg = ceil_div(jobs, groups);
+  const int per_xcd = ceil_div((int64_t)jpg * cbs, per);
+  grid = 8LL * per_xcd;
+  return XcdSplit{groups, jpg, per_xcd};
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Stage loads of one workgroup: A (128 time rows) is 8 instructions of 64
+// chunks, 2 per wave; B (256 columns) is 16, 4 per wave.  Instruction j of
+// wave w fills stage slots [64 (J w + j), +64) in lane order, so each lane
+// fetches the chunk that belongs in its slot: row s / 4, chunk (s % 4) ^
+// swz(row).  off: byte offset of (row, chunk) from the resource base, OOB
+// for rows outside the data; kq: the chunk's k offset (8 chunk).
+template <int J>
+struct WideLoads {
+  uint32_t off[J];
+  int kq[J];
+  // Stage at k0.  exact: D is a multiple of the stage depth, so every chunk
+  // of a row in the data is inside it and k0 goes in the scalar offset.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, unsigned char* dst, int w, int k0, int D,
+                                        bool exact) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      lds_ptr_t d = (lds_ptr_t)(dst + (J * w + j) * 1024);
+      if (exact) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, (int)off[j], 2 * k0, 0, 0);
+      } else {
+        const uint32_t o = (k0 + kq[j] < D && off[j] != wide::OOB) ? off[j] + 2u * (uint32_t)k0 : wide::OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, (int)o, 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int KT, bool AL8>
+__global__ void __launch_bounds__(256, 2) k_inproj_wide(InProjArgs a, int n_strips, int64_t strip_len, int n_cb,
+                                                       XcdSplit m) {
+  constexpr int TM = wide::TM, TN = wide::TN, BK = wide::BK, HALO = wide::HALO, NB = wide::NBUF;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * wide::STAGE_BYTES];
+  __shared__ uint16_t* colp[TN];                    // output row of each column of the block (null past C)
+  static_assert(HALO == 8, "the strip at t = 0 starts one run pair early");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  int job, cb;
+  if (!m.tile_of(blockIdx.x, a.B * n_strips, n_cb, job, cb)) return;   // idle slot (whole workgroup)
+  const int strip = job % n_strips, b = job / n_strips;
+  const int D = a.D, C = a.C, T = a.T, c0 = cb * TN;
+  const int64_t L = a.L;
+  const int64_t ts = (int64_t)strip * strip_len;
+  const int64_t te = (ts + strip_len < L) ? ts + strip_len : L;
+  const uint16_t* u = static_cast<const uint16_t*>(a.u) + (int64_t)b * L * D;
+
+  // This lane's two columns: taps, bias and bias * sum of taps; the
+  // block's output rows.
+  float tap[2][KT], bias[2], bsum[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int c = c0 + 64 * w + 32 * jb + l32;
+    const bool ok = c < C;
+    float ts_ = 0.f;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      tap[jb][j] = (ok && j < T) ? a.w[(int64_t)c * T + j] : 0.f;
+      ts_ += tap[jb][j];
+    }
+    bias[jb] = (ok && a.bias) ? a.bias[c] : 0.f;
+    bsum[jb] = bias[jb] * ts_;
+  }
+  {
+    const int c = c0 + tid;
+    colp[tid] = c < C ? static_cast<uint16_t*>(a.dst.p[c / D]) + ((int64_t)b * D + c % D) * L : nullptr;
+  }
+
+  // B (the block's weight rows) for the whole strip.
+  const int nb_rows = (C - c0 < TN) ? C - c0 : TN;
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.W) + (int64_t)c0 * D), (short)0, nb_rows * D * 2, 0x00020000);
+  WideLoads<4> lb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = (4 * w + j) * 64 + lane, r = sl >> 2, q = (sl & 3) ^ wide::swz(r);
+    lb.kq[j] = 8 * q;
+    lb.off[j] = r < nb_rows ? (uint32_t)(r * D + 8 * q) * 2u : wide::OOB;
+  }
+
+  // Fragment reads: row l32 of a 32-row block, chunk (2 kk + h) ^ swz(l32).
+  const int fsw = wide::swz(l32);
+  const int fo0 = l32 * 64 + 16 * (h ^ fsw), fo1 = l32 * 64 + 16 * ((2 + h) ^ fsw);
+
+  float xp[2][4];                                    // the run pair before the current one (Z, both halves)
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xp[jb][e] = 0.f;
+
+  const int nks = (D + BK - 1) / BK;
+  __amdgpu_buffer_rsrc_t rsa;
+  WideLoads<2> la;
+  // A of the tile at rows [t0, t0 + TM): resource from the first row >= 0.
+  auto tile_a = [&](int64_t t0) {
+    const int64_t tlo = t0 > 0 ? t0 : 0, thi = (t0 + TM < L) ? t0 + TM : L;
+    const int nrows = thi > tlo ? (int)(thi - tlo) : 0;
+    rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(u + tlo * D), (short)0, nrows * D * 2, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sl = (2 * w + j) * 64 + lane, r = sl >> 2, q = (sl & 3) ^ wide::swz(r);
+      const int64_t t = t0 + r;
+      la.kq[j] = 8 * q;
+      la.off[j] = (t >= tlo && t < thi) ? (uint32_t)((t - tlo) * D + 8 * q) * 2u : wide::OOB;
+    }
+  };
+  const bool exact = D % BK == 0;
+  auto issue = [&](int ks) {
+    unsigned char* st = lds + (ks % NB) * wide::STAGE_BYTES;
+    la.issue(rsa, st, w, ks * BK, D, exact);
+    lb.issue(rsb, st + wide::A_BYTES, w, ks * BK, D, exact);
+  };
+
+  int64_t t0 = ts - HALO;
+  tile_a(t0);
+  issue(0);
+  if (nks > 1) issue(1);
+  for (; t0 < te; t0 += TM) {
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jb][r] = 0.f;
+
+    for (int ks = 0; ks < nks; ++ks) {
+      // This wave's loads of stage ks are done once at most those of stage
+      // ks + 1 (6 instructions) are outstanding; its reads of the buffer
+      // refilled below are done; the barrier makes both hold for all waves.
+      if (ks + 1 < nks) __builtin_amdgcn_s_waitcnt(0x0076);     // vmcnt(6) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (ks + 2 < nks) issue(ks + 2);
+      const unsigned char* As = lds + (ks % NB) * wide::STAGE_BYTES;
+      const unsigned char* Bs = As + wide::A_BYTES + 64 * 64 * w;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = kk ? fo1 : fo0;
+        bf16x8 fa[4], fb[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(As + 32 * 64 * i + fo);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) fb[jb] = *reinterpret_cast<const bf16x8*>(Bs + 32 * 64 * jb + fo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+            acc[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+      }
+    }
+    // Every wave's reads of the ring are done: it is free for the epilogue.
+    __builtin_amdgcn_s_waitcnt(0xc07f);                         // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    // Short convolution, one run pair (8 rows) at a time, into this wave's
+    // part of the idle ring as [column][time] bf16 (column stride 264 B:
+    // the 32 columns of a half-wave write fall on distinct banks); then each
+    // 16 lanes store one column's 128 outputs, 256 B.  The bias enters once
+    // per output as bias * (sum of the taps): the convolution runs on the
+    // products alone, which are zero before t = 0, and the first KT - 1
+    // outputs (t < KT - 1) drop the taps that reach before t = 0.
+    unsigned char* ep = lds + w * 64 * wide::EPI_CS;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = k >> 2, g = k & 3;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        float x[4], y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[i][jb][4 * g + e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (KT <= 4 && e < 5 - KT) { y[e] = 0.f; continue; }   // not reached by KT taps
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(xp[jb][e]), __float_as_uint(x[e]), false,
+                                                           false);
+          y[e] = __uint_as_float(h ? sw[0] : sw[1]);
+        }
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = bsum[jb];
+#pragma unroll
+          for (int j = 0; j < KT; ++j) {
+            const int d = e - j;
+            const float z = d >= 0 ? x[d] : (d >= -4 ? y[d + 4] : xp[jb][d + 8]);
+            s = fmaf(tap[jb][j], z, s);
+          }
+          o[e] = s;
+        }
+        if (k == HALO / 8 && t0 < 0) {               // the strip at t = 0: rows t0 + 8k + 4h + e = 4h + e
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 1; j < KT; ++j)
+              if (4 * h + e < j) o[e] = fmaf(-bias[jb], tap[jb][j], o[e]);
+        }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(ep + (32 * jb + l32) * wide::EPI_CS + (8 * k + 4 * h) * 2) =
+            u32x2{bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[jb][e] = x[e];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      const int ch = lane & 15;                      // 8 outputs t0 + 8 ch .. + 7 of the column
+      const int64_t tc = t0 + 8 * ch;
+#pragma unroll 4
+      for (int q = 0; q < 16; ++q) {
+        const int col = 4 * q + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ep + col * wide::EPI_CS + 16 * ch);
+        uint16_t* p = colp[64 * w + col];
+        if (!p) continue;
+        if (AL8 && tc >= ts && tc + 8 <= te) {
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p + tc));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (tc + e >= ts && tc + e < te) p[tc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    // Every wave is done with the ring: the next tile's first stages may load.
+    __builtin_amdgcn_s_waitcnt(0xc07f);                         // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (t0 + TM < te) {
+      tile_a(t0 + TM);
+      issue(0);
+      if (nks > 1) issue(1);
+    }
+  }
+}
+
 // ----------------------------------------------------------- out-projection
 //
 // Workgroup = (batch b, 128 time rows, 128 output columns).  A = y^T: the
@@ -533,9 +855,49 @@ static hipError_t launch_inproj(const InProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Strips of whole tiles (the first HALO rows of each are history only), as
+// many as fit the GPU at once after the XCD map.
+template <int KT, bool AL8>
+static hipError_t launch_inproj_wide(const InProjArgs& a, hipStream_t s) {
+  const auto kern = k_inproj_wide<KT, AL8>;
+  const int n_cb = ceil_div(a.C, wide::TN);
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t cap = (int64_t)cus * per_cu;
+  const int64_t max_tiles = (a.L + wide::HALO + wide::TM - 1) / wide::TM;
+  const int64_t block_bytes = (int64_t)wide::TN * a.D * 2;
+  int64_t grid = 0, strip_len = 0;
+  int n_strips = 0;
+  XcdSplit m{};
+  int64_t per0 = max_tiles * a.B * n_cb / cap;   // fewer tiles per strip cannot fit
+  if (per0 < 1) per0 = 1;
+  for (int64_t per = per0;; ++per) {     // tiles per strip: the fewest whose grid fits at once
+    strip_len = per * wide::TM - wide::HALO;
+    const int64_t ns = (a.L + strip_len - 1) / strip_len;
+    if ((int64_t)a.B * ns > (1LL << 30)) continue;
+    n_strips = (int)ns;
+    m = plan_split(a.B * n_strips, n_cb, block_bytes, grid);
+    if (grid <= cap || per >= max_tiles) break;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a, n_strips, strip_len, n_cb, m);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t in_projection(const InProjArgs& a, hipStream_t s) {
+  if (a.io == 1 && a.D % 8 == 0 && a.T <= 8) {
+    const bool al8 = a.L % 8 == 0;
+    switch (a.T <= 2 ? 2 : a.T <= 4 ? a.T : 8) {
+      case 2: return al8 ? launch_inproj_wide<2, true>(a, s) : launch_inproj_wide<2, false>(a, s);
+      case 3: return al8 ? launch_inproj_wide<3, true>(a, s) : launch_inproj_wide<3, false>(a, s);
+      case 4: return al8 ? launch_inproj_wide<4, true>(a, s) : launch_inproj_wide<4, false>(a, s);
+      default: return al8 ? launch_inproj_wide<8, true>(a, s) : launch_inproj_wide<8, false>(a, s);
+    }
+  }
   const bool vec = a.D % (a.io == 0 ? 4 : 8) == 0;
   if (a.io == 0) return vec ? launch_inproj<0, true>(a, s) : launch_inproj<0, false>(a, s);
   return vec ? launch_inproj<1, true>(a, s) : launch_inproj<1, false>(a, s);

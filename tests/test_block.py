@@ -50,8 +50,15 @@ IN_CASES = [
     (1, 5, 3, 1, 1, "fp32"), (2, 130, 16, 2, 3, "fp32"), (1, 257, 37, 2, 3, "fp32"),
     (2, 1000, 128, 3, 3, "fp32"), (1, 700, 64, 2, 16, "fp32"), (2, 300, 48, 2, 3, "bf16"),
     (1, 200, 20, 2, 5, "bf16"), (1, 3, 8, 8, 2, "fp32"), (4, 2048, 768, 2, 3, "fp32"),
-    # bf16 widths that are multiples of 64 take the direct-to-LDS staging
+    # bf16 with D % 8 == 0 and T <= 8: 128 x 256 tiles, short convolution on the
+    # accumulators (strips of tiles; L % 4 != 0 stores element-wise; ragged k
+    # slices, column blocks and strips)
     (2, 1000, 128, 2, 3, "bf16"), (1, 777, 192, 3, 4, "bf16"), (1, 4096, 768, 2, 3, "bf16"),
+    (1, 129, 8, 1, 1, "bf16"), (1, 2050, 64, 2, 7, "bf16"), (2, 1500, 256, 1, 8, "bf16"),
+    (1, 20000, 64, 2, 3, "bf16"), (3, 5000, 256, 3, 6, "bf16"), (1, 1, 16, 2, 2, "bf16"),
+    (2, 6, 40, 2, 5, "bf16"), (1, 3001, 520, 2, 4, "bf16"),
+    # bf16 beyond the wide path: 16 taps, D % 8 != 0
+    (1, 700, 64, 2, 16, "bf16"), (1, 333, 36, 2, 3, "bf16"),
 ]
 
 
@@ -67,6 +74,28 @@ def test_in_projection_matches_oracle(B, L, D, N, T, io):
         err = channel_errors(_np(got), ref)
         assert np.all(np.isfinite(_np(got)))
         assert err.max() <= TOL_PROJ[io], (err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+def test_in_projection_full_width_sampled_columns():
+    """The 64K-token block shape (B=1, L=65536, D=768, order 2, 3 taps, bf16):
+    every time step of sampled projected columns against the oracle, among
+    them the first and last column of each stream and the columns on either
+    side of a 256-column block edge."""
+    B, L, D, N, T = 1, 65536, 768, 2, 3
+    cfg = _cfg(B, L, D, N, "bf16")
+    bp = make_block_params(cfg, T=T, bias_scale=0.3)
+    u = make_block_input(cfg, DEV)
+    v, xs = H.in_projection(u, _bp_device(bp, "bf16"))
+    torch.cuda.synchronize()
+    streams = [v] + xs
+    rs = np.random.default_rng(5)
+    cols = sorted({0, D - 1, D, 2 * D - 1, 2 * D, 3 * D - 1, 255, 256, 511, 512, 1279, 1280,
+                   *rs.integers(0, (N + 1) * D, 10).tolist()})
+    ref = O.in_projection_columns(_np(u), bp["W_in"], bp["b_in"], bp["w_short"], cols)
+    got = np.stack([_np(streams[c // D][:, c % D]) for c in cols], axis=1)
+    err = channel_errors(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= TOL_PROJ["bf16"], (err.max(), cols[int(np.argmax(err.max(axis=0)))])
 
 
 OUT_CASES = [(1, 5, 3, "fp32"), (2, 130, 16, "fp32"), (1, 257, 37, "fp32"), (2, 1000, 128, "fp32"),
