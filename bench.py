@@ -401,6 +401,8 @@ def run_backward(args, cfg, torch, H, dev):
     import numpy as np
     from workloads import make_activations, make_filter_params
 
+    if args.copy_calib:
+        measure_copy(torch, dev, reps=1)             # reference dispatch for counter scaling
     fp = make_filter_params(cfg)
     h = H.filter_gen({k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in fp.items()},
                      cfg.L)
