@@ -76,6 +76,12 @@ def source_hash(files=None) -> str:
     return h.hexdigest()[:16]
 
 
+def work_point_bytes(cfg) -> int:
+    """Bytes per point of the four-step intermediate: bf16 activations keep
+    it as bf16 pairs, fp32 ones as float2."""
+    return 4 if cfg.io == "bf16" else 8
+
+
 def measured_traffic(cfg_name: str):
     """HBM bytes per forward from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources (else None)."""
@@ -809,7 +815,7 @@ def run_forward(args, cfg, torch, H, dev, copy_bps, steps, warmup):
     single = plan["path"] == "single"
     nc = plan["M"] // 2
     rows = cfg.B * cfg.D
-    group = max(1, wsb // (nc * 8)) if not single else rows
+    group = max(1, wsb // (nc * work_point_bytes(cfg))) if not single else rows
     groups = -(-rows // group)
     # The metric's roofline is HBM bandwidth: algorithmic bytes (v, x_1..x_N,
     # y in the I/O dtype, the spectrum once) over the event-timed forward.
@@ -830,7 +836,8 @@ def run_forward(args, cfg, torch, H, dev, copy_bps, steps, warmup):
         "metric": "Hyena order-N fwd channel-tokens/sec (B*D*L/s) + % of HBM roofline",
         "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32" if cfg.io == "fp32" else "bf16 I/O, fp32 compute",
+        "dtype": ("fp32" if cfg.io == "fp32" else
+                  "bf16 I/O, fp32 compute" + ("" if single else ", bf16 four-step intermediate")),
         "data": "synthetic (seeded N(0,1) activations, DNA-token v for the 1M shape, random-init filter FFN)",
         "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D, "L": cfg.L,
                    "io": cfg.io, "ffn_hidden": cfg.H, "fft_len": plan["M"], "path": plan["path"],
@@ -856,7 +863,8 @@ def work_budget_sweep(args, cfg, torch, H, dev, data, sets, stream):
     forwards, and the HBM roofline fraction."""
     budgets = [int(b) for b in str(args.work_mb).split(",") if b]
     nc = H.plan(cfg.L)["M"] // 2
-    ws = torch.empty(max(max(budgets) << 20, nc * 8), dtype=torch.uint8, device=dev)
+    esz = work_point_bytes(cfg)
+    ws = torch.empty(max(max(budgets) << 20, nc * esz), dtype=torch.uint8, device=dev)
     old = os.environ.get("HYENA_WORK_MB")
     res = {}
     try:
@@ -874,7 +882,7 @@ def work_budget_sweep(args, cfg, torch, H, dev, data, sets, stream):
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / n
-            rows = max(1, min(cfg.B * cfg.D, (mb << 20) // (nc * 8)))
+            rows = max(1, min(cfg.B * cfg.D, (mb << 20) // (nc * esz)))
             res[str(mb)] = {"ms_per_step": ms, "rows_per_group_max": rows,
                             "hbm_frac": min_bytes(cfg) / (ms / 1e3) / HBM_PEAK}
     finally:

@@ -41,12 +41,13 @@ int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
 }
 
 // Rows per pass group of the four-step forward (equal-size groups under the
-// work budget, plan.hpp).
-int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows) { return rows_per_group(p.N, n_rows); }
+// work budget, plan.hpp), for intermediate points of esz bytes.
+int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows, int64_t esz) { return rows_per_group(p.N, n_rows, esz); }
 
-int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D) {
+int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D, hyena_dtype io) {
   if (p.path == PATH_SINGLE) return 0;
-  return forward_group_rows(p, B * D) * p.N * 8;
+  const int64_t esz = forward_work_esz(io == HYENA_BF16);
+  return forward_group_rows(p, B * D, esz) * p.N * esz;
 }
 
 // Grid convolutions: padded side P of the square/cube FFT grid.
@@ -294,7 +295,7 @@ int64_t hyena_forward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_
   if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
   PlanInfo p;
   if (plan_env(L, &p, mode)) return -1;
-  return forward_ws(p, B, D);
+  return forward_ws(p, B, D, io);
 }
 
 hyena_status hyena_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
@@ -352,18 +353,19 @@ hyena_status forward_impl(const void* v, const void* const* x, const void* spec,
   if (p.path == PATH_SINGLE) {
     e = single_forward(a, p.N, (hipStream_t)stream);
   } else {
+    const int64_t esz = forward_work_esz(a.io == 1), row_bytes = p.N * esz;
     if (static_ws) {
-      if (p.N * 8 > workspace_bytes) return HYENA_ERR_WORKSPACE;   // one row's intermediate must fit
+      if (row_bytes > workspace_bytes) return HYENA_ERR_WORKSPACE;   // one row's intermediate must fit
     } else {
-      if (!workspace || workspace_bytes < p.N * 8) return HYENA_ERR_WORKSPACE;
+      if (!workspace || workspace_bytes < row_bytes) return HYENA_ERR_WORKSPACE;
       if (overlap(workspace, workspace_bytes, y, act) || overlap(workspace, workspace_bytes, v, act) ||
           overlap(workspace, workspace_bytes, spec, sb))
         return HYENA_ERR_ALIAS;
       for (int n = 0; n < N; ++n)
         if (overlap(workspace, workspace_bytes, x[n], act)) return HYENA_ERR_ALIAS;
     }
-    int64_t g = forward_group_rows(p, B * D);
-    if (g * p.N * 8 > workspace_bytes) g = workspace_bytes / (p.N * 8);
+    int64_t g = forward_group_rows(p, B * D, esz);
+    if (g * row_bytes > workspace_bytes) g = workspace_bytes / row_bytes;
     a.work = workspace;
     a.rows_per_group = (int)g;
     e = fourstep_forward(a, p, (hipStream_t)stream);

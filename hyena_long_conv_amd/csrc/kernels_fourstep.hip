@@ -65,12 +65,23 @@ template <int N2> struct RowCfg {
 };
 
 // Intermediate accesses (each element is written by one pass and read back
-// by the next, long after it left the caches).
+// by the next, long after it left the caches).  An element is one complex
+// point: a float2, or with bf16 activations (WB) a pair of bf16 in 4 bytes
+// (real part in the low half, rounded to nearest even), which halves the
+// intermediate traffic of those forwards; the arithmetic stays fp32.
 #ifndef HYENA_WORK_NT
 #define HYENA_WORK_NT 0
 #endif
-__device__ __forceinline__ cf ld_work(const cf* p) {
-  if constexpr (HYENA_WORK_NT) {
+template <bool WB> struct WorkElem { using T = cf; };
+template <> struct WorkElem<true> { using T = uint32_t; };
+template <bool WB> using work_t = typename WorkElem<WB>::T;
+
+template <bool WB>
+__device__ __forceinline__ cf ld_work(const work_t<WB>* p) {
+  if constexpr (WB) {
+    const uint32_t w = *p;
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  } else if constexpr (HYENA_WORK_NT) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const f32x2 w = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
     return make_float2(w.x, w.y);
@@ -78,8 +89,11 @@ __device__ __forceinline__ cf ld_work(const cf* p) {
     return *p;
   }
 }
-__device__ __forceinline__ void st_work(cf* p, cf v) {
-  if constexpr (HYENA_WORK_NT) {
+template <bool WB>
+__device__ __forceinline__ void st_work(work_t<WB>* p, cf v) {
+  if constexpr (WB) {
+    *p = bf16x2_bits(v.x, v.y);
+  } else if constexpr (HYENA_WORK_NT) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(f32x2{v.x, v.y}, reinterpret_cast<f32x2*>(p));
   } else {
@@ -167,7 +181,8 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   const int col = cb * W + c;
   const bool valid = col < a.n2;
   const int64_t N = (int64_t)N1 * a.n2;
-  cf* buf = a.work + (int64_t)g * N;
+  constexpr bool WB = IOT == 1 && !GRID;             // bf16 activations: bf16 intermediate
+  work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * (GRID ? a.gL1 * a.gLm * a.gL2 : a.L);
   const int gi2 = col >> a.gNLs, gm = col & ((1 << a.gNLs) - 1);     // GRID: column -> (i2, packed m)
   const ColLds<W> lds{smem + c};
@@ -216,7 +231,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   } else {
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      u[i] = valid ? ld_work(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
+      u[i] = valid ? ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
     constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
     cf xp[PFX > 0 ? PFX : 1];
 #pragma unroll
@@ -246,7 +261,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
     fft.template run<false>(u, lds, j);
     if (valid) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) st_work(buf + (int64_t)(j + i * S1) * a.n2 + col, u[i]);
+      for (int i = 0; i < E; ++i) st_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + col, u[i]);
     }
   }
 }
@@ -261,10 +276,11 @@ constexpr int kColOddThreads = 128;
 // The same pointer, hidden from common-subexpression elimination: the stores
 // at the end of a column pass then recompute their addresses instead of
 // keeping the loads' (one 64-bit address per point) live through the DFTs.
-__device__ __forceinline__ cf* fresh_ptr(cf* p) {
+template <class T>
+__device__ __forceinline__ T* fresh_ptr(T* p) {
   uint64_t v = reinterpret_cast<uint64_t>(p);
   asm volatile("" : "+v"(v));
-  return reinterpret_cast<cf*>(v);
+  return reinterpret_cast<T*>(v);
 }
 
 template <int N1, int IOT, int KIND, bool EVEN>
@@ -273,7 +289,8 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   const int col = cb * kColOddThreads + (int)threadIdx.x;
   if (col >= a.n2) return;
   const int64_t N = (int64_t)N1 * a.n2;
-  cf* buf = a.work + (int64_t)g * N + col;
+  constexpr bool WB = IOT == 1;                      // bf16 activations: bf16 intermediate
+  work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   cf u[N1];
   if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
@@ -285,7 +302,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < N1; ++i) u[i] = ld_work(buf + (int64_t)i * a.n2);
+    for (int i = 0; i < N1; ++i) u[i] = ld_work<WB>(buf + (int64_t)i * a.n2);
     RegDft<N1, true>::run(u);
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
@@ -301,9 +318,9 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   }
   if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
     RegDft<N1, false>::run(u);
-    cf* dst = fresh_ptr(buf);
+    work_t<WB>* dst = fresh_ptr(buf);
 #pragma unroll
-    for (int i = 0; i < N1; ++i) st_work(dst + (int64_t)i * a.n2, u[i]);
+    for (int i = 0; i < N1; ++i) st_work<WB>(dst + (int64_t)i * a.n2, u[i]);
   }
 }
 
@@ -370,7 +387,8 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   const int col = cb * CPB + ((int)threadIdx.x >> 1);
   if (col >= a.n2) return;                  // both lanes of a pair leave together
   const int64_t N = (int64_t)(2 * Q) * a.n2;
-  cf* buf = a.work + (int64_t)g * N + col;
+  constexpr bool WB = IOT == 1;                      // bf16 activations: bf16 intermediate
+  work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   // time row of point m: lane_a + 2m;  spectrum row of point k: Q*lane_a + k
   const auto trow = [&](int m) { return 2 * ((int64_t)a.n2 * (lane_a + 2 * m) + col); };
@@ -383,7 +401,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < Q; ++k) u[k] = ld_work(buf + (int64_t)(Q * lane_a + k) * a.n2);
+    for (int k = 0; k < Q; ++k) u[k] = ld_work<WB>(buf + (int64_t)(Q * lane_a + k) * a.n2);
     pair_dft_inv<Q>(u, lane_a);
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
@@ -398,9 +416,9 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   }
   if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
     pair_dft_fwd<Q>(u, lane_a);
-    cf* dst = fresh_ptr(buf + (int64_t)Q * lane_a * a.n2);
+    work_t<WB>* dst = fresh_ptr(buf + (int64_t)Q * lane_a * a.n2);
 #pragma unroll
-    for (int k = 0; k < Q; ++k) st_work(dst + (int64_t)k * a.n2, u[k]);
+    for (int k = 0; k < Q; ++k) st_work<WB>(dst + (int64_t)k * a.n2, u[k]);
   }
 }
 
@@ -416,6 +434,7 @@ struct RowArgs {
   int n_row_pairs;     // workgroups per row: n1 / 2 (even n1) or (n1 + 1) / 2 (odd n1)
   int cmB;             // CONV, > 1: channel-major launch (r0 = first channel, cmB batch rows each)
   int n_units;         // channel-major launch: (channel, row pair) units; the grid is padded to a multiple of 8
+  int wb;              // CONV: the intermediate holds bf16 pairs (bf16 activations)
 };
 
 // LDS of the row pass.  HYENA_ROW_SW: 0 plain addressing; 1 XOR-swizzled
@@ -439,7 +458,7 @@ using RowPassLds = std::conditional<HYENA_ROW_SW == 2, RowLdsPad16, RowLdsT<HYEN
 
 // Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
 // for k = k1 + n1*k2 < N, and S(N) at index N.
-template <int N2, int KIND>
+template <int N2, int KIND, bool WB = false>
 __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs a) {
   using C = RowCfg<N2>;
   constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E;
@@ -477,7 +496,7 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   const int mb = self_mirror ? b : 1 - b;          // row holding the mirror bins
   const int k1m = (k1 == 0) ? 0 : n1 - k1;         // its k1
   const uint32_t N = (uint32_t)n1 * (uint32_t)N2;
-  cf* row = a.work + (int64_t)g * N + (int64_t)k1 * N2;
+  work_t<WB>* row = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + (int64_t)k1 * N2;
   const RowPassLds lds{smem + b * PADN};
   const RowPassLds ldsm{smem + mb * PADN};
   BlockFFT<N2, E, typename C::R> fft;
@@ -489,7 +508,7 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
   const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, N);
   const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, N);
 #pragma unroll
-  for (int i = 0; i < E; ++i) u[i] = cmul(ld_work(row + j + i * S2), step_power<E>(tb, ts, i));
+  for (int i = 0; i < E; ++i) u[i] = cmul(ld_work<WB>(row + j + i * S2), step_power<E>(tb, ts, i));
   fft.template run<false>(u, lds, j);
 
   // bins k = k1 + n1*k2 with k2 = j + i*S2; mirror N-k at (k1m, k2m)
@@ -550,7 +569,8 @@ __global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs 
     fft.template run<true>(u, lds, j);
     if (live) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) st_work(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
+      for (int i = 0; i < E; ++i)
+        st_work<WB>(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
     }
   }
 }
@@ -696,7 +716,8 @@ static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t
   const int blocks = (kind == ROW_CONV && r.cmB > 1) ? (r.n_units + 7) / 8 * 8 * r.cmB : groups * r.n_row_pairs;
   const dim3 grid(blocks), block(RowCfg<N2>::T);
   if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, block, 0, s, r);
-  else hipLaunchKernelGGL((k_row<N2, ROW_CONV>), grid, block, 0, s, r);
+  else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, block, 0, s, r);
+  else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, block, 0, s, r);
   return hipGetLastError();
 }
 
@@ -724,6 +745,7 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   RowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
   r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = (p.n1 + 1) / 2;
+  r.wb = a.io == 1;                                   // matches the column passes' intermediate
   // With B > 1 a launch covers whole channels (all their batch rows), so the
   // row pass reads each channel's spectrum once instead of once per batch row.
   const bool cm = a.B > 1 && a.n_rows == a.B * a.D && a.rows_per_group >= a.B;

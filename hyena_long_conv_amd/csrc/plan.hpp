@@ -229,7 +229,12 @@ inline int64_t group_rows(int64_t row_bytes, int64_t n_rows) {
   return (n_rows + groups - 1) / groups;
 }
 
-// The same for rows of an N-point complex intermediate.
-inline int rows_per_group(int64_t N, int64_t n_rows) { return (int)group_rows(N * 8, n_rows); }
+// The same for rows of an N-point complex intermediate of esz bytes per
+// point (8: float2; 4: a bf16 pair).
+inline int rows_per_group(int64_t N, int64_t n_rows, int64_t esz = 8) { return (int)group_rows(N * esz, n_rows); }
+
+// Bytes per intermediate point of the four-step forward: bf16 activations
+// keep the intermediate as bf16 pairs.
+inline int64_t forward_work_esz(bool bf16_io) { return bf16_io ? 4 : 8; }
 
 }  // namespace hyena
