@@ -28,6 +28,17 @@ namespace hyena {
 #ifndef HYENA_ROW_WAVES
 #define HYENA_ROW_WAVES 1
 #endif
+// Points per workgroup of the column pass for columns of up to 64 points
+// (its width W = HYENA_COL_POINTS / n1 columns).
+#ifndef HYENA_COL_POINTS
+#define HYENA_COL_POINTS 2048
+#endif
+// Gate loads of the middle and last column passes issued before the inverse
+// column FFT (PFX points per thread): for 256- and 512-point columns, or for
+// every length with HYENA_COL_PFX_ALL=1.
+#ifndef HYENA_COL_PFX_ALL
+#define HYENA_COL_PFX_ALL 0
+#endif
 #ifndef HYENA_COL_WAVES
 #define HYENA_COL_WAVES 1
 #endif
@@ -45,19 +56,28 @@ namespace hyena {
 template <int N1, bool GRID = false> struct ColCfg {
   static constexpr int E = 16;
   static constexpr int W = GRID ? (N1 == 16 ? 256 : N1 == 32 ? 128 : N1 == 64 ? 64 : N1 <= 512 ? 32 : 16)
-                                : (N1 <= 64 ? 2048 / N1 : N1 <= 256 ? 32 : 16);
+                                : (N1 <= 64 ? HYENA_COL_POINTS / N1 : N1 <= 256 ? 32 : 16);
   static constexpr int T = W * N1 / E;
   static constexpr bool LDS = N1 > E;
-  static constexpr int PFX = (!GRID && (N1 == 256 || N1 == 512)) ? E : 0;
+  static constexpr int PFX = (!GRID && (HYENA_COL_PFX_ALL || N1 == 256 || N1 == 512)) ? E : 0;
   using R = typename Plan16<N1>::R;
 };
 
+// Points per thread of the row pass: HYENA_ROW_E (16), except rows of up
+// to 1024 points with a bf16 intermediate: HYENA_ROW_E_BF16 (8).  Those
+// passes move half the bytes and are bound by VALU issue; at 8 points per
+// thread they ran 2% faster on the 64K and 1% on the 128K bf16 shapes, but
+// 4% slower with 2048-point rows (L = 100000) and, with an fp32
+// intermediate, 4% slower on the 1M shape.
 #ifndef HYENA_ROW_E
 #define HYENA_ROW_E 16
 #endif
+#ifndef HYENA_ROW_E_BF16
+#define HYENA_ROW_E_BF16 8
+#endif
 
-template <int N2> struct RowCfg {
-  static constexpr int E = HYENA_ROW_E;
+template <int N2, bool WB = false> struct RowCfg {
+  static constexpr int E = (WB && N2 <= 1024) ? HYENA_ROW_E_BF16 : HYENA_ROW_E;
   static constexpr int TPR = N2 / E;  // threads per row
   static constexpr int T = 2 * TPR;
   using R = typename std::conditional<E == 16, typename Plan16<N2>::R,
@@ -79,7 +99,7 @@ template <bool WB> using work_t = typename WorkElem<WB>::T;
 template <bool WB>
 __device__ __forceinline__ cf ld_work(const work_t<WB>* p) {
   if constexpr (WB) {
-    const uint32_t w = *p;
+    const uint32_t w = HYENA_WORK_NT ? __builtin_nontemporal_load(p) : *p;
     return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
   } else if constexpr (HYENA_WORK_NT) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -92,7 +112,8 @@ __device__ __forceinline__ cf ld_work(const work_t<WB>* p) {
 template <bool WB>
 __device__ __forceinline__ void st_work(work_t<WB>* p, cf v) {
   if constexpr (WB) {
-    *p = bf16x2_bits(v.x, v.y);
+    if constexpr (HYENA_WORK_NT) __builtin_nontemporal_store(bf16x2_bits(v.x, v.y), p);
+    else *p = bf16x2_bits(v.x, v.y);
   } else if constexpr (HYENA_WORK_NT) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(f32x2{v.x, v.y}, reinterpret_cast<f32x2*>(p));
@@ -459,8 +480,8 @@ using RowPassLds = std::conditional<HYENA_ROW_SW == 2, RowLdsPad16, RowLdsT<HYEN
 // Spectrum layout on this path: row f holds S(k) = H(k)/(2N) at k1*n2 + k2
 // for k = k1 + n1*k2 < N, and S(N) at index N.
 template <int N2, int KIND, bool WB = false>
-__global__ void __launch_bounds__(RowCfg<N2>::T, HYENA_ROW_WAVES) k_row(RowArgs a) {
-  using C = RowCfg<N2>;
+__global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(RowArgs a) {
+  using C = RowCfg<N2, WB>;
   constexpr int E = C::E, TPR = C::TPR, S2 = N2 / E;
   constexpr int PADN = RowPassLds::padded(N2);
   __shared__ cf smem[2 * PADN];
@@ -714,10 +735,10 @@ template <int N2>
 static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t s) {
   // channel-major: n_units (channel, row pair) units padded to a multiple of 8, cmB workgroups each
   const int blocks = (kind == ROW_CONV && r.cmB > 1) ? (r.n_units + 7) / 8 * 8 * r.cmB : groups * r.n_row_pairs;
-  const dim3 grid(blocks), block(RowCfg<N2>::T);
-  if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, block, 0, s, r);
-  else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, block, 0, s, r);
-  else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, block, 0, s, r);
+  const dim3 grid(blocks);
+  if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, dim3(RowCfg<N2>::T), 0, s, r);
+  else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, dim3(RowCfg<N2, true>::T), 0, s, r);
+  else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   return hipGetLastError();
 }
 
