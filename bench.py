@@ -77,9 +77,13 @@ def source_hash(files=None) -> str:
 
 
 def work_point_bytes(cfg) -> int:
-    """Bytes per point of the four-step intermediate: bf16 activations keep
-    it as bf16 pairs, fp32 ones as float2."""
-    return 4 if cfg.io == "bf16" else 8
+    """Bytes per point of the four-step intermediate: bf16 pairs for bf16
+    activations up to order 2, else float2."""
+    return 4 if bf16_work(cfg) else 8
+
+
+def bf16_work(cfg) -> bool:
+    return cfg.io == "bf16" and cfg.N <= 2
 
 
 def measured_traffic(cfg_name: str):
@@ -837,7 +841,8 @@ def run_forward(args, cfg, torch, H, dev, copy_bps, steps, warmup):
         "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("fp32" if cfg.io == "fp32" else
-                  "bf16 I/O, fp32 compute" + ("" if single else ", bf16 four-step intermediate")),
+                  "bf16 I/O, fp32 compute" + (", bf16 four-step intermediate" if bf16_work(cfg) and not single
+                                              else "")),
         "data": "synthetic (seeded N(0,1) activations, DNA-token v for the 1M shape, random-init filter FFN)",
         "config": {"workload": cfg.desc, "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D, "L": cfg.L,
                    "io": cfg.io, "ffn_hidden": cfg.H, "fft_len": plan["M"], "path": plan["path"],

@@ -44,9 +44,9 @@ int64_t spectrum_ws(const PlanInfo& p, int64_t NF) {
 // work budget, plan.hpp), for intermediate points of esz bytes.
 int64_t forward_group_rows(const PlanInfo& p, int64_t n_rows, int64_t esz) { return rows_per_group(p.N, n_rows, esz); }
 
-int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D, hyena_dtype io) {
+int64_t forward_ws(const PlanInfo& p, int64_t B, int64_t D, int N, hyena_dtype io) {
   if (p.path == PATH_SINGLE) return 0;
-  const int64_t esz = forward_work_esz(io == HYENA_BF16);
+  const int64_t esz = forward_work_esz(io == HYENA_BF16, N);
   return forward_group_rows(p, B * D, esz) * p.N * esz;
 }
 
@@ -295,7 +295,7 @@ int64_t hyena_forward_workspace_bytes_ex(int64_t B, int32_t D, int32_t N, int64_
   if (io != HYENA_FP32 && io != HYENA_BF16) return -1;
   PlanInfo p;
   if (plan_env(L, &p, mode)) return -1;
-  return forward_ws(p, B, D, io);
+  return forward_ws(p, B, D, N, io);
 }
 
 hyena_status hyena_forward(const void* v, const void* const* x, const void* spec, void* y, int64_t B,
@@ -353,7 +353,7 @@ hyena_status forward_impl(const void* v, const void* const* x, const void* spec,
   if (p.path == PATH_SINGLE) {
     e = single_forward(a, p.N, (hipStream_t)stream);
   } else {
-    const int64_t esz = forward_work_esz(a.io == 1), row_bytes = p.N * esz;
+    const int64_t esz = forward_work_esz(a.io == 1, N), row_bytes = p.N * esz;
     if (static_ws) {
       if (row_bytes > workspace_bytes) return HYENA_ERR_WORKSPACE;   // one row's intermediate must fit
     } else {

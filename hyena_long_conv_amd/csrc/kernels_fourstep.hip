@@ -192,6 +192,10 @@ __device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, in
 // n1 x 2*n2; the column FFT runs over the grid's first axis and no twiddle
 // follows (a 2-D DFT), the packed column index col covering grid columns
 // 2col, 2col+1.
+// Column-pass activation type: IOT 0 fp32, 1 bf16, 2 bf16 with the
+// intermediate kept as bf16 pairs.
+constexpr int io_of(int iot) { return iot == 2 ? 1 : iot; }
+
 template <int N1, int IOT, int KIND, bool EVEN, bool GRID = false>
 __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1, GRID>;
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   const int col = cb * W + c;
   const bool valid = col < a.n2;
   const int64_t N = (int64_t)N1 * a.n2;
-  constexpr bool WB = IOT == 1 && !GRID;             // bf16 activations: bf16 intermediate
+  constexpr bool WB = IOT == 2;                      // bf16 intermediate (bf16 activations, low orders)
   work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * (GRID ? a.gL1 * a.gLm * a.gL2 : a.L);
   const int gi2 = col >> a.gNLs, gm = col & ((1 << a.gNLs) - 1);     // GRID: column -> (i2, packed m)
@@ -246,7 +250,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       u[i] = make_float2(0.f, 0.f);
       if (ok) {
         if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, ro, t, len);
-        else u[i] = ld_pair<IOT, EVEN>(a.v, ro, t, len);
+        else u[i] = ld_pair<io_of(IOT), EVEN>(a.v, ro, t, len);
       }
     }
   } else {
@@ -258,7 +262,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
 #pragma unroll
     for (int i = 0; i < PFX; ++i) {
       int64_t ro, t, len;
-      xp[i] = at(j + i * S1, ro, t, len) ? ld_pair<IOT, EVEN>(a.xg, ro, t, len) : make_float2(0.f, 0.f);
+      xp[i] = at(j + i * S1, ro, t, len) ? ld_pair<io_of(IOT), EVEN>(a.xg, ro, t, len) : make_float2(0.f, 0.f);
     }
     fft.template run<true>(u, lds, j);
 #pragma unroll
@@ -270,10 +274,10 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
         if constexpr (KIND == COL_OUT) {
           z = u[i];
         } else {
-          const cf xv = i < PFX ? xp[i < PFX ? i : 0] : ld_pair<IOT, EVEN>(a.xg, ro, t, len);
+          const cf xv = i < PFX ? xp[i < PFX ? i : 0] : ld_pair<io_of(IOT), EVEN>(a.xg, ro, t, len);
           z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
         }
-        if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, ro, t, len, z);
+        if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
       }
       u[i] = z;
     }
@@ -310,7 +314,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   const int col = cb * kColOddThreads + (int)threadIdx.x;
   if (col >= a.n2) return;
   const int64_t N = (int64_t)N1 * a.n2;
-  constexpr bool WB = IOT == 1;                      // bf16 activations: bf16 intermediate
+  constexpr bool WB = IOT == 2;                      // bf16 intermediate (bf16 activations, low orders)
   work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   cf u[N1];
@@ -319,7 +323,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
       if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, off, t, a.L);
-      else u[i] = ld_pair<IOT, EVEN>(a.v, off, t, a.L);
+      else u[i] = ld_pair<io_of(IOT), EVEN>(a.v, off, t, a.L);
     }
   } else {
 #pragma unroll
@@ -330,10 +334,10 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
       cf z = u[i];
       if constexpr (KIND != COL_OUT) {
-        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, t, a.L);
+        const cf xv = ld_pair<io_of(IOT), EVEN>(a.xg, off, t, a.L);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
-      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, off, t, a.L, z);
+      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, t, a.L, z);
       u[i] = z;
     }
   }
@@ -408,7 +412,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   const int col = cb * CPB + ((int)threadIdx.x >> 1);
   if (col >= a.n2) return;                  // both lanes of a pair leave together
   const int64_t N = (int64_t)(2 * Q) * a.n2;
-  constexpr bool WB = IOT == 1;                      // bf16 activations: bf16 intermediate
+  constexpr bool WB = IOT == 2;                      // bf16 intermediate (bf16 activations, low orders)
   work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   // time row of point m: lane_a + 2m;  spectrum row of point k: Q*lane_a + k
@@ -418,7 +422,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
       if constexpr (KIND == COL_SPEC) u[m] = ld_pair<0, EVEN>(a.h, off, trow(m), a.L);
-      else u[m] = ld_pair<IOT, EVEN>(a.v, off, trow(m), a.L);
+      else u[m] = ld_pair<io_of(IOT), EVEN>(a.v, off, trow(m), a.L);
     }
   } else {
 #pragma unroll
@@ -428,10 +432,10 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
     for (int m = 0; m < Q; ++m) {
       cf z = u[m];
       if constexpr (KIND != COL_OUT) {
-        const cf xv = ld_pair<IOT, EVEN>(a.xg, off, trow(m), a.L);
+        const cf xv = ld_pair<io_of(IOT), EVEN>(a.xg, off, trow(m), a.L);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
-      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<IOT, EVEN>(a.y, off, trow(m), a.L, z);
+      if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, trow(m), a.L, z);
       u[m] = z;
     }
   }
@@ -608,27 +612,33 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
     if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
     else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
     else hipLaunchKernelGGL((k_col<N1, 0, COL_LAST, EVEN, GRID>), grid, block, 0, s, c);
-  } else {
+  } else if (io == 1 || GRID) {
     if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 1, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
     else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 1, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
     else hipLaunchKernelGGL((k_col<N1, 1, COL_LAST, EVEN, GRID>), grid, block, 0, s, c);
+  } else if constexpr (!GRID) {
+    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 2, COL_FIRST, EVEN, false>), grid, block, 0, s, c);
+    else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 2, COL_MID, EVEN, false>), grid, block, 0, s, c);
+    else hipLaunchKernelGGL((k_col<N1, 2, COL_LAST, EVEN, false>), grid, block, 0, s, c);
   }
 }
+
+// The kernel of one conv kind at one activation type (IOT as in k_col).
+#define HYENA_COL_KINDS(KERN, P, IOTV, EVENV)                                                        \
+  do {                                                                                               \
+    if (kind == COL_FIRST) hipLaunchKernelGGL((KERN<P, IOTV, COL_FIRST, EVENV>), grid, block, 0, s, c); \
+    else if (kind == COL_MID) hipLaunchKernelGGL((KERN<P, IOTV, COL_MID, EVENV>), grid, block, 0, s, c); \
+    else hipLaunchKernelGGL((KERN<P, IOTV, COL_LAST, EVENV>), grid, block, 0, s, c);                   \
+  } while (0)
 
 template <int N1, bool EVEN>
 static void launch_col_odd_t(int kind, int io, const ColArgs& c, dim3 grid, hipStream_t s) {
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
-  else if (io == 0) {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col_odd<N1, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
-  } else {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_odd<N1, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_odd<N1, 1, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col_odd<N1, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
-  }
+  else if (io == 0) HYENA_COL_KINDS(k_col_odd, N1, 0, EVEN);
+  else if (io == 1) HYENA_COL_KINDS(k_col_odd, N1, 1, EVEN);
+  else HYENA_COL_KINDS(k_col_odd, N1, 2, EVEN);
 }
 
 template <int Q, bool EVEN>
@@ -636,16 +646,11 @@ static void launch_col_pair_t(int kind, int io, const ColArgs& c, dim3 grid, hip
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
-  else if (io == 0) {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col_pair<Q, 0, COL_LAST, EVEN>), grid, block, 0, s, c);
-  } else {
-    if (kind == COL_FIRST) hipLaunchKernelGGL((k_col_pair<Q, 1, COL_FIRST, EVEN>), grid, block, 0, s, c);
-    else if (kind == COL_MID) hipLaunchKernelGGL((k_col_pair<Q, 1, COL_MID, EVEN>), grid, block, 0, s, c);
-    else hipLaunchKernelGGL((k_col_pair<Q, 1, COL_LAST, EVEN>), grid, block, 0, s, c);
-  }
+  else if (io == 0) HYENA_COL_KINDS(k_col_pair, Q, 0, EVEN);
+  else if (io == 1) HYENA_COL_KINDS(k_col_pair, Q, 1, EVEN);
+  else HYENA_COL_KINDS(k_col_pair, Q, 2, EVEN);
 }
+#undef HYENA_COL_KINDS
 
 template <int Q>
 static hipError_t launch_col_pair(int kind, int io, const ColArgs& c, int groups, hipStream_t s) {
@@ -766,7 +771,10 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   RowArgs r{};
   r.work = (cf*)a.work; r.spec = (const cf*)a.spec; r.spec_out = nullptr;
   r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = (p.n1 + 1) / 2;
-  r.wb = a.io == 1;                                   // matches the column passes' intermediate
+  // bf16 activations up to kBf16WorkMaxOrder: bf16 intermediate (column
+  // kernels IOT 2, row kernel WB), else float2.
+  const int cio = a.io == 0 ? 0 : (forward_bf16_work(true, a.NORD) ? 2 : 1);
+  r.wb = cio == 2;
   // With B > 1 a launch covers whole channels (all their batch rows), so the
   // row pass reads each channel's spectrum once instead of once per batch row.
   const bool cm = a.B > 1 && a.n_rows == a.B * a.D && a.rows_per_group >= a.B;
@@ -777,14 +785,14 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
     const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? a.B : 1);
     c.r0 = r0; r.r0 = r0;
     r.n_units = cm ? groups / a.B * r.n_row_pairs : 0;
-    hipError_t e = dispatch_col(p.n1, COL_FIRST, a.io, c, groups, s);
+    hipError_t e = dispatch_col(p.n1, COL_FIRST, cio, c, groups, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < a.NORD; ++n) {
       r.order = n;
       e = dispatch_row(p.n2, ROW_CONV, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
-      e = dispatch_col(p.n1, n < a.NORD - 1 ? COL_MID : (a.no_gate ? COL_OUT : COL_LAST), a.io, c, groups, s);
+      e = dispatch_col(p.n1, n < a.NORD - 1 ? COL_MID : (a.no_gate ? COL_OUT : COL_LAST), cio, c, groups, s);
       if (e != hipSuccess) return e;
     }
   }

@@ -233,8 +233,14 @@ inline int64_t group_rows(int64_t row_bytes, int64_t n_rows) {
 // point (8: float2; 4: a bf16 pair).
 inline int rows_per_group(int64_t N, int64_t n_rows, int64_t esz = 8) { return (int)group_rows(N * esz, n_rows); }
 
-// Bytes per intermediate point of the four-step forward: bf16 activations
-// keep the intermediate as bf16 pairs.
-inline int64_t forward_work_esz(bool bf16_io) { return bf16_io ? 4 : 8; }
+// The four-step forward keeps its intermediate as bf16 pairs for bf16
+// activations up to this order: each order rounds it twice and the rounding
+// compounds through the gates (max normalised error against the oracle,
+// bound 2e-2: 8.4e-3 at order 2 on the 64K shape, 1.8e-2 at order 3 on the
+// 128K and 100000 shapes, 3.6e-3 with an fp32 intermediate).
+constexpr int kBf16WorkMaxOrder = 2;
+inline bool forward_bf16_work(bool bf16_io, int order) { return bf16_io && order <= kBf16WorkMaxOrder; }
+// Bytes per intermediate point of the four-step forward.
+inline int64_t forward_work_esz(bool bf16_io, int order) { return forward_bf16_work(bf16_io, order) ? 4 : 8; }
 
 }  // namespace hyena

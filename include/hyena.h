@@ -147,9 +147,9 @@ int64_t hyena_forward_workspace_bytes(int64_t B, int32_t D, int32_t N, int64_t L
  *   y        device [B][D][L], I/O dtype; must not overlap v, any x_n or spec
  *   io       HYENA_FP32, or HYENA_BF16 (bf16 loads widened exactly, all
  *            arithmetic fp32, y rounded to nearest even; on the four-step
- *            path (long rows, see hyena_plan) the transform between its
- *            passes is also kept as bf16 pairs, rounded to nearest even:
- *            half the intermediate traffic and workspace)
+ *            path (long rows, see hyena_plan) with N <= 2 the transform
+ *            between its passes is also kept as bf16 pairs, rounded to
+ *            nearest even: half the intermediate traffic and workspace)
  *   workspace device scratch of hyena_forward_workspace_bytes() bytes
  * Errors: NULL -> NULL; sizes -> SHAPE; N > HYENA_MAX_ORDER -> UNSUPPORTED;
  * alignment -> ALIGN; workspace -> WORKSPACE; y overlapping an input -> ALIAS.

@@ -360,3 +360,15 @@ def test_nd_calls_reject_bad_arguments():
     assert sp(dims=big, ws=Dp + 64, wsb=1 << 24) == ALIAS
     assert H.nd_workspace_bytes(4, (200, 200)) >= 512 * 256 * 8
     assert H.nd_workspace_bytes(4, (8, 8)) == 0
+
+
+def test_forward_workspace_bf16_intermediate_up_to_order_2():
+    """Four-step lengths: bf16 activations keep the intermediate as 4-byte
+    bf16 pairs up to order 2 (half the fp32 workspace), float2 beyond."""
+    L, B, D = 65536, 1, 64
+    for N in (1, 2, 3):
+        f = H.forward_workspace_bytes(B, D, N, L, "fp32")
+        b = H.forward_workspace_bytes(B, D, N, L, "bf16")
+        assert f > 0
+        assert b == (f // 2 if N <= 2 else f), (N, f, b)
+    assert H.forward_workspace_bytes(B, D, 2, 2048, "bf16") == 0      # single path: no workspace
