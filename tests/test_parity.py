@@ -230,6 +230,20 @@ def test_spectrum_reused_across_batches():
     check_rows(y, p, cfg.L, v, xs, [(b, d) for b in range(4) for d in range(3)], TOL_FP32)
 
 
+def test_bf16_intermediate_every_row_order2():
+    """bf16 activations at order 2 keep the four-step intermediate as bf16
+    pairs: every row of a 64K-length shape (two channel groups of the
+    filter, batch rows sharing a channel) stays inside the bf16 bound; the
+    same shape at order 3 (fp32 intermediate) too."""
+    for N in (2, 3):
+        cfg = Config("w", N, 2, 24, 65536, "bf16", 32, 41 + N)
+        assert H.plan(cfg.L)["path"] == "fourstep"
+        p = make_filter_params(cfg, bias_scale=0.2)
+        v, xs = make_activations(cfg, DEV)
+        _, _, y = run_hip(p, cfg.L, v, xs)
+        check_rows(y, p, cfg.L, v, xs, [(b, d) for b in range(cfg.B) for d in range(cfg.D)], TOL_BF16)
+
+
 # ------------------------------------------------------------- configurations
 
 CFG_SAMPLES = {"C1": 16, "C2": 48, "C3": 6, "C4": 3, "C5a": 5, "C5b": 5}

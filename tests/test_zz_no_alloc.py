@@ -45,7 +45,8 @@ def _case(N, B, D, L, io, seed):
 
 
 def test_forward_static_two_calls_second_smaller():
-    # 1st: 80 rows of L = 100000, bf16 (FFT length 204800, 800 KiB of intermediate per row, one pass group)
+    # 1st: 80 rows of L = 100000, bf16 (FFT length 204800, the intermediate as bf16 pairs: 400 KiB per
+    # row, one pass group)
     p, v, xs, ref, y = _case(2, 2, 40, 100000, "bf16", 71)
     assert torch.equal(y, ref)
     check_rows(y, p, 100000, v, xs, [(0, 0), (1, 39), (1, 17)], 2e-2)
