@@ -426,7 +426,7 @@ __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 1) | (((r 
 }  // namespace wide
 
 // Workgroup -> (row job, column block) map of the wide in-projection.  The
-// 8 XCDs form `groups` groups of 8 / groups; group g takes row jobs
+// 8 XCDs form `groups` groups of 8 / groups XCDs each; group g takes row jobs
 // [g * jpg, (g + 1) * jpg) with every column block, and splits those
 // (job, block) units, column block slowest, evenly over its XCDs.  An XCD
 // then streams the weights of about n_cb * groups / 8 + 1 column blocks
