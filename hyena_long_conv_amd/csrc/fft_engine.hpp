@@ -53,12 +53,41 @@ __device__ __forceinline__ cf rot90(cf a) {
   return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x);
 }
 
-// exp(-2 pi i k / n) (forward) or its conjugate (inverse), for 0 <= k < n.
-// The argument 2k/n is formed exactly for power-of-two n.
+// exp(-2 pi i k / n) (forward) or its conjugate (inverse), for k, n < 2^24.
+// The angle is k/n turns.  Its nearest quarter turn q is taken out in exact
+// integer arithmetic (4k - q n fits a float exactly), leaving r = (4k - q n)
+// / 4n turns with |r| <= 1/8, i.e. |2 pi r| <= pi/4; cos and sin of 2 pi r
+// come from their Taylor series about 0 through the r^10 and r^9 terms
+// (truncation error below 2e-9 on that range), and the result is rotated by
+// q quarter turns.  Absolute error about 1.5 x 2^-24 for power-of-two n and
+// 2 x 2^-24 otherwise (checked on the CPU against double precision for n up
+// to 2^22); half the instructions of a general sincos, and no division:
+// 1/n is a reciprocal refined by one Newton step, folded when n is a
+// compile-time constant.
 template <bool INV>
 __device__ __forceinline__ cf twiddle(uint32_t k, uint32_t n) {
-  float s, c;
-  sincospif(2.0f * (float)k / (float)n, &s, &c);
+  const float fk4 = 4.0f * (float)k, fn = (float)n;
+  const float rn0 = __builtin_amdgcn_rcpf(fn);
+  const float rn = fmaf(fmaf(-fn, rn0, 1.0f), rn0, rn0);
+  const float q = __builtin_rintf(fk4 * rn);
+  const float r = fmaf(-q, fn, fk4) * (0.25f * rn);
+  const float r2 = r * r;
+  // (2 pi)^j / j! with alternating signs: sin(2 pi r) = r * S(r^2), cos = C(r^2)
+  float sp = fmaf(r2, 42.058693944897634f, -76.70585975306136f);
+  sp = fmaf(r2, sp, 81.60524927607504f);
+  sp = fmaf(r2, sp, -41.341702240399755f);
+  sp = fmaf(r2, sp, 6.283185307179586f);
+  const float sr = r * sp;
+  float cp = fmaf(r2, -26.426256783374388f, 60.24464137187664f);
+  cp = fmaf(r2, cp, -85.45681720669371f);
+  cp = fmaf(r2, cp, 64.93939402266828f);
+  cp = fmaf(r2, cp, -19.739208802178716f);
+  const float cr = fmaf(r2, cp, 1.0f);
+  // rotation by q quarter turns: (c, s) -> (-s, c) per quarter
+  const uint32_t qi = (uint32_t)(int)q;
+  const bool odd = (qi & 1u) != 0;
+  const float c = __uint_as_float(__float_as_uint(odd ? sr : cr) ^ (((qi + 1u) & 2u) << 30));
+  const float s = __uint_as_float(__float_as_uint(odd ? cr : sr) ^ ((qi & 2u) << 30));
   return INV ? make_float2(c, s) : make_float2(c, -s);
 }
 
