@@ -637,6 +637,57 @@ __device__ __forceinline__ cf ld_pair(const void* p, int64_t row_off, int64_t t,
   }
 }
 
+// The bf16 pair (x[t], x[t+1]) for even t as its raw 32-bit word (x[t] in
+// the low half), zero padding beyond L; bf16_pair_cf unpacks it.  One
+// register per pair instead of two while a load waits for its use.  The
+// load always runs, from a clamped in-row index (as ld_pair with CLAMP).
+template <bool EVEN>
+__device__ __forceinline__ uint32_t ld_pair_bits(const void* p, int64_t row_off, int64_t t, int64_t L) {
+  const uint16_t* q = static_cast<const uint16_t*>(p) + row_off;
+  if constexpr (EVEN) {
+    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + (t < L ? t : L - 2)));
+    return t < L ? w : 0u;
+  } else {
+    const uint32_t lo = __builtin_nontemporal_load(q + (t < L ? t : L - 1));
+    const uint32_t hi = __builtin_nontemporal_load(q + (t + 1 < L ? t + 1 : L - 1));
+    return (t < L ? lo : 0u) | (t + 1 < L ? hi << 16 : 0u);
+  }
+}
+__device__ __forceinline__ cf bf16_pair_cf(uint32_t w) {
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// An activation pair as loaded (a bf16 pair's 32-bit word, or two floats,
+// zero beyond L, from clamped indices), pinned, then unpacked.  pin() hands
+// the value to an empty asm statement, so the load has to complete there and
+// the compiler cannot sink it into a later branch (e.g. the mask of a
+// store): a load sunk into such a branch waits for its data before the next
+// one is issued.  Loading a batch, then pinning it, keeps the batch in flight
+// together; FENCE (a memory clobber) also keeps later loads after the pin,
+// which bounds the registers a batch holds.
+template <int IOT> struct RawPair { cf v; };
+template <> struct RawPair<1> { uint32_t w; };
+template <int IOT, bool EVEN>
+__device__ __forceinline__ RawPair<IOT> ld_pair_raw(const void* p, int64_t row_off, int64_t t, int64_t L) {
+  if constexpr (IOT == 0) return {ld_pair<0, EVEN, true>(p, row_off, t, L)};
+  else return {ld_pair_bits<EVEN>(p, row_off, t, L)};
+}
+template <int IOT, bool FENCE = false>
+__device__ __forceinline__ void pin(RawPair<IOT>& r) {
+  if constexpr (FENCE) {
+    if constexpr (IOT == 0) asm volatile("" : "+v"(r.v.x), "+v"(r.v.y) : : "memory");
+    else asm volatile("" : "+v"(r.w) : : "memory");
+  } else {
+    if constexpr (IOT == 0) asm volatile("" : "+v"(r.v.x), "+v"(r.v.y));
+    else asm volatile("" : "+v"(r.w));
+  }
+}
+template <int IOT>
+__device__ __forceinline__ cf unpack(RawPair<IOT> r) {
+  if constexpr (IOT == 0) return r.v;
+  else return bf16_pair_cf(r.w);
+}
+
 // (x[t], x[t+1]) of a row whose every requested pair is in range (t + 1 < L,
 // row offset and t even): one aligned access, no mask.
 template <int IOT>

@@ -39,6 +39,11 @@ namespace hyena {
 #ifndef HYENA_COL_PFX_ALL
 #define HYENA_COL_PFX_ALL 0
 #endif
+// bf16 gate inputs of the first half of each column requested before the
+// inverse column FFT where PFX does not apply.
+#ifndef HYENA_COL_PFB
+#define HYENA_COL_PFB 1
+#endif
 #ifndef HYENA_COL_WAVES
 #define HYENA_COL_WAVES 1
 #endif
@@ -214,6 +219,13 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   BlockFFT<N1, E, typename C::R> fft;
   fft.init(j);
   cf u[E];
+  // Loads of row passes (not GRID) run unconditionally, from in-range
+  // addresses: lanes past the last column work on column 0 (columns never
+  // mix, and those lanes store nothing) and positions past the row end read
+  // its last pair, masked to zero (CLAMP).  A branch around a load whose
+  // value is converted before the branch ends makes the wave wait for each
+  // load before it issues the next one.
+  const int colc = valid ? col : 0;
   // element pair of column point i1: row offset, first real index, row length
   const auto at = [&](int i1, int64_t& ro, int64_t& t, int64_t& len) {
     if constexpr (GRID) {
@@ -223,9 +235,20 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       return valid && i1 < a.gL1 && gi2 < a.gLm;
     } else {
       ro = off;
-      t = 2 * ((int64_t)a.n2 * i1 + col);
+      t = 2 * ((int64_t)a.n2 * i1 + colc);
       len = a.L;
       return valid;
+    }
+  };
+  // activation pair of column point i1 (zero where at() fails)
+  const auto act = [&](const void* p, int i1) {
+    int64_t ro, t, len;
+    const bool ok = at(i1, ro, t, len);
+    if constexpr (GRID) {
+      return ok ? ld_pair<io_of(IOT), EVEN>(p, ro, t, len) : make_float2(0.f, 0.f);
+    } else {
+      (void)ok;
+      return ld_pair<io_of(IOT), EVEN, true>(p, ro, t, len);
     }
   };
 
@@ -245,39 +268,70 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
   } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      int64_t ro, t, len;
-      const bool ok = at(j + i * S1, ro, t, len);
-      u[i] = make_float2(0.f, 0.f);
-      if (ok) {
-        if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, ro, t, len);
-        else u[i] = ld_pair<io_of(IOT), EVEN>(a.v, ro, t, len);
+      if constexpr (KIND == COL_SPEC) {
+        int64_t ro, t, len;
+        at(j + i * S1, ro, t, len);
+        u[i] = ld_pair<0, EVEN, true>(a.h, ro, t, len);
+      } else {
+        u[i] = act(a.v, j + i * S1);
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i)
-      u[i] = valid ? ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
+    for (int i = 0; i < E; ++i) u[i] = ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + colc);
     constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
     cf xp[PFX > 0 ? PFX : 1];
 #pragma unroll
-    for (int i = 0; i < PFX; ++i) {
+    for (int i = 0; i < PFX; ++i) xp[i] = act(a.xg, j + i * S1);
+    // bf16 gates of the first half of the column (on a zero-padded row the
+    // only points that hold samples) requested before the inverse FFT too,
+    // kept packed: one register per point.
+    constexpr int PFB = (KIND == COL_OUT || PFX > 0 || GRID || io_of(IOT) != 1 || !HYENA_COL_PFB) ? 0 : E / 2;
+    uint32_t xb[PFB > 0 ? PFB : 1];
+#pragma unroll
+    for (int i = 0; i < PFB; ++i) {
       int64_t ro, t, len;
-      xp[i] = at(j + i * S1, ro, t, len) ? ld_pair<io_of(IOT), EVEN>(a.xg, ro, t, len) : make_float2(0.f, 0.f);
+      at(j + i * S1, ro, t, len);
+      xb[i] = ld_pair_bits<EVEN>(a.xg, ro, t, len);
     }
     fft.template run<true>(u, lds, j);
+    // the other gates (not GRID): requested together, then pinned; points of
+    // the column's second half hold samples only on circular rows
+    constexpr int G0 = (GRID || KIND == COL_OUT) ? E : (PFX > PFB ? PFX : PFB);
+    RawPair<io_of(IOT)> xl[G0 < E ? E - G0 : 1];
+    if constexpr (G0 < E) {
+      const auto ld_gate = [&](int i) {
+        int64_t ro, t, len;
+        at(j + i * S1, ro, t, len);
+        xl[i - G0] = ld_pair_raw<io_of(IOT), EVEN>(a.xg, ro, t, len);
+      };
+#pragma unroll
+      for (int i = G0; i < E; ++i) {
+        if (i < E / 2) ld_gate(i);
+        else xl[i - G0] = RawPair<io_of(IOT)>{};
+      }
+      if (a.L > N) {
+#pragma unroll
+        for (int i = (G0 > E / 2 ? G0 : E / 2); i < E; ++i) ld_gate(i);
+      }
+#pragma unroll
+      for (int i = G0; i < E; ++i) pin(xl[i - G0]);
+    }
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       int64_t ro, t, len;
       const bool ok = at(j + i * S1, ro, t, len);
-      cf z = make_float2(0.f, 0.f);
-      if (ok) {
-        if constexpr (KIND == COL_OUT) {
-          z = u[i];
-        } else {
-          const cf xv = i < PFX ? xp[i < PFX ? i : 0] : ld_pair<io_of(IOT), EVEN>(a.xg, ro, t, len);
-          z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
-        }
-        if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
+      cf z = u[i];
+      if constexpr (KIND != COL_OUT) {
+        const cf xv = i < PFX   ? xp[i < PFX ? i : 0]
+                      : i < PFB ? bf16_pair_cf(xb[i < PFB ? i : 0])
+                      : GRID    ? act(a.xg, j + i * S1)
+                                : unpack(xl[i >= G0 && i - G0 < E ? i - G0 : 0]);
+        z = make_float2(xv.x * z.x, xv.y * z.y);
+      }
+      if constexpr (GRID) z = ok ? z : make_float2(0.f, 0.f);
+      if constexpr (KIND == COL_LAST || KIND == COL_OUT) {
+        if (ok) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
       }
       u[i] = z;
     }
@@ -297,6 +351,12 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
 // A wave covers 64 consecutive columns, i.e. 512-byte runs of every row of
 // the intermediate.  Same kinds and arguments as k_col (no grids).
 constexpr int kColOddThreads = 128;
+// Gate loads of these passes go out in batches of this many points: a batch
+// is in flight together, and the registers it holds stay bounded.
+#ifndef HYENA_GATE_BATCH
+#define HYENA_GATE_BATCH 8
+#endif
+constexpr int kGateBatch = HYENA_GATE_BATCH;
 
 // The same pointer, hidden from common-subexpression elimination: the stores
 // at the end of a column pass then recompute their addresses instead of
@@ -322,19 +382,29 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
-      if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN>(a.h, off, t, a.L);
-      else u[i] = ld_pair<io_of(IOT), EVEN>(a.v, off, t, a.L);
+      if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN, true>(a.h, off, t, a.L);
+      else u[i] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, t, a.L);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < N1; ++i) u[i] = ld_work<WB>(buf + (int64_t)i * a.n2);
     RegDft<N1, true>::run(u);
+    RawPair<io_of(IOT)> xl[N1];
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
+      if constexpr (KIND != COL_OUT) {
+        if (i % kGateBatch == 0) {   // the batch's gates requested together, then pinned
+#pragma unroll
+          for (int k = i; k < i + kGateBatch && k < N1; ++k)
+            xl[k] = ld_pair_raw<io_of(IOT), EVEN>(a.xg, off, 2 * ((int64_t)a.n2 * k + col), a.L);
+#pragma unroll
+          for (int k = i; k < i + kGateBatch && k < N1; ++k) pin<io_of(IOT), true>(xl[k]);
+        }
+      }
       cf z = u[i];
       if constexpr (KIND != COL_OUT) {
-        const cf xv = ld_pair<io_of(IOT), EVEN>(a.xg, off, t, a.L);
+        const cf xv = unpack(xl[i]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
       if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, t, a.L, z);
@@ -421,18 +491,27 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
-      if constexpr (KIND == COL_SPEC) u[m] = ld_pair<0, EVEN>(a.h, off, trow(m), a.L);
-      else u[m] = ld_pair<io_of(IOT), EVEN>(a.v, off, trow(m), a.L);
+      if constexpr (KIND == COL_SPEC) u[m] = ld_pair<0, EVEN, true>(a.h, off, trow(m), a.L);
+      else u[m] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, trow(m), a.L);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < Q; ++k) u[k] = ld_work<WB>(buf + (int64_t)(Q * lane_a + k) * a.n2);
     pair_dft_inv<Q>(u, lane_a);
+    RawPair<io_of(IOT)> xl[Q];
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
+      if constexpr (KIND != COL_OUT) {
+        if (m % kGateBatch == 0) {   // the batch's gates requested together, then pinned
+#pragma unroll
+          for (int k = m; k < m + kGateBatch && k < Q; ++k) xl[k] = ld_pair_raw<io_of(IOT), EVEN>(a.xg, off, trow(k), a.L);
+#pragma unroll
+          for (int k = m; k < m + kGateBatch && k < Q; ++k) pin<io_of(IOT), true>(xl[k]);
+        }
+      }
       cf z = u[m];
       if constexpr (KIND != COL_OUT) {
-        const cf xv = ld_pair<io_of(IOT), EVEN>(a.xg, off, trow(m), a.L);
+        const cf xv = unpack(xl[m]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
       if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, trow(m), a.L, z);
