@@ -281,8 +281,13 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
     for (int i = 0; i < E; ++i) u[i] = ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + colc);
     constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
     cf xp[PFX > 0 ? PFX : 1];
+    // (the column's second half holds samples only on circular rows)
 #pragma unroll
-    for (int i = 0; i < PFX; ++i) xp[i] = act(a.xg, j + i * S1);
+    for (int i = 0; i < PFX; ++i) xp[i] = (GRID || i < E / 2) ? act(a.xg, j + i * S1) : make_float2(0.f, 0.f);
+    if (!GRID && a.L > N) {
+#pragma unroll
+      for (int i = E / 2; i < PFX; ++i) xp[i] = act(a.xg, j + i * S1);
+    }
     // bf16 gates of the first half of the column (on a zero-padded row the
     // only points that hold samples) requested before the inverse FFT too,
     // kept packed: one register per point.

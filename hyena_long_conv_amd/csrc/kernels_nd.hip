@@ -284,11 +284,21 @@ k_nd_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, v
   ff.init(j);
   fi.init(j);
   cf u[E];
+  // Loads run unconditionally: points outside the grid (zero padding) read
+  // the grid's first pair and are masked afterwards.  A branch around a load
+  // whose value is converted inside it makes the wave wait for each load
+  // before issuing the next.
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     int off, tl;
-    const bool ok = nd_point<NDIM, P>(j + i * S, Lo, Lm, Ll, off, tl);
-    u[i] = (i < NV && (CIRC || ok)) ? ld_pair<IOT, EVEN>(vg, off, tl, Ll) : make_float2(0.f, 0.f);
+    const bool ok = CIRC || nd_point<NDIM, P>(j + i * S, Lo, Lm, Ll, off, tl);
+    if constexpr (CIRC) nd_point<NDIM, P>(j + i * S, Lo, Lm, Ll, off, tl);
+    if (i < NV) {
+      const cf w = ld_pair<IOT, EVEN, true>(vg, ok ? off : 0, ok ? tl : 0, Ll);
+      u[i] = ok ? w : make_float2(0.f, 0.f);
+    } else {
+      u[i] = make_float2(0.f, 0.f);
+    }
   }
   for (int n = 0; n < NORD; ++n) {
     const int jj = fresh(j);
@@ -330,17 +340,35 @@ k_nd_forward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ spec, v
     const void* xg = advance<IOT>(x.p[n], gbase);
     const bool last = (n == NORD - 1);
     const int jg = fresh(jj);
+    // gates requested in batches of 8 and pinned (not sunk into the stores'
+    // masks; the fence keeps the next batch's loads after the pins)
+    constexpr int GB = NV < 8 ? NV : 8;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      int off, tl;
-      const bool ok = nd_point<NDIM, P>(jg + i * S, Lo, Lm, Ll, off, tl);
-      cf z = make_float2(0.f, 0.f);
-      if (i < NV && (CIRC || ok)) {
-        const cf xv = ld_pair<IOT, EVEN>(xg, off, tl, Ll);
-        z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
-        if (last) st_pair<IOT, EVEN>(yg, off, tl, Ll, z);
+    for (int i0 = 0; i0 < E; i0 += GB) {
+      RawPair<IOT> xr[GB];
+      if (i0 < NV) {
+#pragma unroll
+        for (int c = 0; c < GB; ++c) {
+          int off, tl;
+          const bool ok = nd_point<NDIM, P>(jg + (i0 + c) * S, Lo, Lm, Ll, off, tl) || CIRC;
+          xr[c] = ld_pair_raw<IOT, EVEN>(xg, ok ? off : 0, ok ? tl : 0, Ll);
+        }
+#pragma unroll
+        for (int c = 0; c < GB; ++c) pin<IOT, true>(xr[c]);
       }
-      u[i] = z;
+#pragma unroll
+      for (int c = 0; c < GB; ++c) {
+        const int i = i0 + c;
+        int off, tl;
+        const bool ok = nd_point<NDIM, P>(jg + i * S, Lo, Lm, Ll, off, tl) || CIRC;
+        cf z = make_float2(0.f, 0.f);
+        if (i < NV && ok) {
+          const cf xv = unpack(xr[c]);
+          z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+          if (last) st_pair<IOT, EVEN>(yg, off, tl, Ll, z);
+        }
+        u[i] = z;
+      }
     }
   }
 }

@@ -246,7 +246,9 @@ __device__ __forceinline__ void fir_store(const InProjArgs& a, const float* Zs, 
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int c = c0 + 64 * h + n0 + g * (TT / 64);
+      // the column is the wave's own (uniform): the stream pointer is then a
+      // scalar load, not a per-lane one that each masked store waits for
+      const int c = __builtin_amdgcn_readfirstlane(c0 + 64 * h + n0 + g * (TT / 64));
       if (c >= C) break;
       const int s = c / D, d = c - (c / D) * D;
       void* dst = a.dst.p[s];
@@ -813,14 +815,18 @@ __global__ void __launch_bounds__(TT, 2) k_outproj(OutProjArgs a, int n_tt, int 
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = e0 + wn * 64 + j * 32 + (lane & 31);
-    if (e >= D) continue;
-    const float be = a.bias ? a.bias[e] : 0.f;
+    const bool ev = e < D;
+    // the bias is read outside the stores' lane masks and pinned: read
+    // inside them, every masked store would first wait for all earlier
+    // stores (the memory counter tracks both)
+    float be = a.bias ? a.bias[ev ? e : 0] : 0.f;
+    asm volatile("" : "+v"(be));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t t = t0 + wm * 64 + i * 32 + acc_row(r, lane);
-        if (t < L) st_f<IOT>(out, ((int64_t)b * L + t) * D + e, acc[i][j][r] + be);
+        if (ev && t < L) st_f<IOT>(out, ((int64_t)b * L + t) * D + e, acc[i][j][r] + be);
       }
   }
 }
