@@ -327,16 +327,32 @@ k_single_backward(const void* __restrict__ v, XPtrs x, const cf* __restrict__ sp
       PairCoeffs<N, E> pc;
       pc.load(spec + (int64_t)(n * D + d) * spec_stride, qs, j);
       cf zt[E], gt[E];
+      {
+        // every load of the step first (one branch on the order for z_n's
+        // inputs), then the products and the gx_n stores: loads and stores
+        // interleaved point by point waited for each other
+        cf cv[NV], xv[NV];
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        if (i < NV) {
+        for (int i = 0; i < NV; ++i) {
           const int64_t t = 2 * (int64_t)(j + i * S);
-          const cf c = cb[j + i * S];
-          st_pair<IOT, EVEN>(gx.p[n], off, t, L, had(g[i], c));                 // gx_n = g * c_n
-          gt[i] = had(g[i], ld_pair<IOT, EVEN, true>(xn, off, t, L));          // gc = g * x_n
-          zt[i] = (n == 0) ? ld_pair<IOT, EVEN, true>(v, off, t, L)
-                           : had(ld_pair<IOT, EVEN, true>(xp, off, t, L), cbp[j + i * S]);   // z_n
+          cv[i] = cb[j + i * S];
+          xv[i] = ld_pair<IOT, EVEN, true>(xn, off, t, L);
+        }
+        if (n == 0) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) zt[i] = ld_pair<IOT, EVEN, true>(v, off, 2 * (int64_t)(j + i * S), L);
         } else {
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            zt[i] = had(ld_pair<IOT, EVEN, true>(xp, off, 2 * (int64_t)(j + i * S), L), cbp[j + i * S]);   // z_n
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          st_pair<IOT, EVEN>(gx.p[n], off, 2 * (int64_t)(j + i * S), L, had(g[i], cv[i]));   // gx_n = g * c_n
+          gt[i] = had(g[i], xv[i]);                                                       // gc = g * x_n
+        }
+#pragma unroll
+        for (int i = NV; i < E; ++i) {
           zt[i] = make_float2(0.f, 0.f);
           gt[i] = make_float2(0.f, 0.f);
         }
