@@ -56,7 +56,7 @@ __global__ void k_filter_gen_mr(const float* __restrict__ hhat, const float* __r
 // read of four taps, 16 FMAs.  Taps are stored per order in rows of Lh4 =
 // Lh rounded up to 4 (zero beyond Lh), and each buffer has PAD zeroed
 // floats before it for the window reads left of the first output.
-constexpr int FIR_THREADS = 256, FR = 4, PAD = 8;
+constexpr int FIR_THREADS = 256, FR = 4, PAD = 8, FIR_UNROLL = 3, FIR_BATCH_TAPS = 32;
 typedef float fir_f4 __attribute__((ext_vector_type(4)));
 
 template <int IOT>
@@ -70,6 +70,40 @@ __device__ __forceinline__ void ld4(const void* p, int64_t i, float (&o)[4]) {  
     const u2 w = __builtin_nontemporal_load(reinterpret_cast<const u2*>(static_cast<const uint16_t*>(p) + i));
     o[0] = __uint_as_float(w.x << 16); o[1] = __uint_as_float(w.x & 0xffff0000u);
     o[2] = __uint_as_float(w.y << 16); o[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+}
+
+// Windows x[t_u .. t_u+3] (t_u = t + u * STEP, multiples of 4) for u <
+// FIR_UNROLL, zero outside [0, L).  Rows of a length that is a multiple of 4
+// (vec): every window is one aligned access from a clamped index (a window is
+// then all in or all out of the row), all issued before any is masked, so no
+// branch separates them: a load inside a lane-masked branch is waited for
+// before the next is issued.  Other rows go sample by sample.
+template <int IOT>
+__device__ __forceinline__ void ld4_batch(const void* p, int64_t off, int64_t t, int64_t L, bool vec,
+                                          float (&o)[FIR_UNROLL][4]) {
+  constexpr int STEP = 4 * FIR_THREADS;
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < FIR_UNROLL; ++u) {
+      const int64_t tu = t + u * STEP;
+      ld4<IOT>(p, off + (tu < 0 ? 0 : (tu >= L ? L - 4 : tu)), o[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < FIR_UNROLL; ++u) {
+      const int64_t tu = t + u * STEP;
+      const bool in = tu >= 0 && tu < L;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[u][q] = in ? o[u][q] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < FIR_UNROLL; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t tq = t + u * STEP + q;
+        o[u][q] = (tq >= 0 && tq < L) ? IO<IOT>::ld(p, off + tq) : 0.f;
+      }
   }
 }
 
@@ -95,20 +129,24 @@ __global__ void __launch_bounds__(FIR_THREADS) k_fir_forward(const void* __restr
     const int n = i / Lh4, k = i - n * Lh4;
     taps[i] = k < Lh ? h[((int64_t)n * D + d) * Lh + k] : 0.f;
   }
-  for (int i4 = 4 * tid; i4 < W; i4 += 4 * FIR_THREADS) {
-    const int64_t t = t0 - Hh + i4;
-    float o[4];
-    if (vec && t >= 0 && t + 3 < L) {
-      ld4<IOT>(v, off + t, o);
-    } else {
+  // Windows of 4 samples, FIR_UNROLL passes of the workgroup at a time: the
+  // loads of a batch are issued together (from in-row addresses, also on
+  // lanes past the end, which store nothing), then stored.
+  constexpr int STEP = 4 * FIR_THREADS;
+  for (int c0 = 0; c0 * STEP < W; c0 += FIR_UNROLL) {
+    float o[FIR_UNROLL][4];
+    ld4_batch<IOT>(v, off, t0 - Hh + 4 * tid + c0 * STEP, L, vec, o);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = (t + q >= 0 && t + q < L) ? IO<IOT>::ld(v, off + t + q) : 0.f;
+    for (int u = 0; u < FIR_UNROLL; ++u) {
+      const int i4 = 4 * tid + (c0 + u) * STEP;
+      if (i4 < W) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b0[i4 + q] = o[u][q];
+          b1[i4 + q] = 0.f;   // an order writes b1 from its first full-history output on; the
+        }                     // rest must hold finite values, since zero taps beyond Lh still read it
+      }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      b0[i4 + q] = o[q];
-      b1[i4 + q] = 0.f;   // an order writes b1 from its first full-history output on; the
-    }                     // rest must hold finite values, since zero taps beyond Lh still read it
   }
   __syncthreads();
   for (int n = 0; n < NORD; ++n) {
@@ -116,10 +154,10 @@ __global__ void __launch_bounds__(FIR_THREADS) k_fir_forward(const void* __restr
     const int lo4 = lo / 4 * 4;
     const float* tp = taps + n * Lh4;
     const void* xn = x.p[n];
-    for (int i0 = lo4 + FR * tid; i0 < W; i0 += FR * FIR_THREADS) {
-      // outputs i0 .. i0+3: acc[r] = sum_k h[k] b0[i0 + r - k].  For the taps
-      // k0 .. k0+3, cur = b0[i0-k0 .. i0-k0+3] and prv = the four before it
-      // (the lowest read is i0 - Lh4 >= -7, inside the pad).
+    // outputs i0 .. i0+3: acc[r] = sum_k h[k] b0[i0 + r - k].  For the taps
+    // k0 .. k0+3, cur = b0[i0-k0 .. i0-k0+3] and prv = the four before it
+    // (the lowest read is i0 - Lh4 >= -7, inside the pad).
+    const auto fir4 = [&](int i0, const float* xv) {
       float acc[FR] = {0.f, 0.f, 0.f, 0.f};
       fir_f4 cur = *reinterpret_cast<const fir_f4*>(b0 + i0);
       for (int k0 = 0; k0 < Lh4; k0 += 4) {
@@ -131,16 +169,33 @@ __global__ void __launch_bounds__(FIR_THREADS) k_fir_forward(const void* __restr
           for (int r = 0; r < FR; ++r) acc[r] = fmaf(hv[m], r >= m ? cur[r - m] : prv[4 + r - m], acc[r]);
         cur = prv;
       }
-      const int64_t t = t0 - Hh + i0;
-      float xv[4];
-      if (vec && t >= 0 && t + 3 < L) {
-        ld4<IOT>(xn, off + t, xv);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[q] = (t + q >= 0 && t + q < L) ? IO<IOT>::ld(xn, off + t + q) : 0.f;
-      }
 #pragma unroll
       for (int r = 0; r < FR; ++r) b1[i0 + r] = xv[r] * acc[r];
+    };
+    if (Lh4 <= FIR_BATCH_TAPS) {
+      // short filters: the sums are short next to a memory round trip, so the
+      // gates of FIR_UNROLL passes are requested together before them
+      for (int c0 = 0; lo4 + c0 * STEP < W; c0 += FIR_UNROLL) {
+        float xb[FIR_UNROLL][4];
+        ld4_batch<IOT>(xn, off, t0 - Hh + lo4 + FR * tid + c0 * STEP, L, vec, xb);
+#pragma unroll
+        for (int u = 0; u < FIR_UNROLL; ++u) {
+          const int i0 = lo4 + FR * tid + (c0 + u) * STEP;
+          if (i0 < W) fir4(i0, xb[u]);
+        }
+      }
+    } else {
+      for (int i0 = lo4 + FR * tid; i0 < W; i0 += STEP) {
+        const int64_t t = t0 - Hh + i0;
+        float xv[4];
+        if (vec && t >= 0 && t + 3 < L) {
+          ld4<IOT>(xn, off + t, xv);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xv[q] = (t + q >= 0 && t + q < L) ? IO<IOT>::ld(xn, off + t + q) : 0.f;
+        }
+        fir4(i0, xv);
+      }
     }
     __syncthreads();
     float* tmp = b0;

@@ -278,7 +278,13 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) u[i] = ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + colc);
+    for (int i = 0; i < E; ++i) {
+      if constexpr (GRID) {   // (unmasked, these loads held 40 more registers and spilled at n1 = 512)
+        u[i] = valid ? ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + col) : make_float2(0.f, 0.f);
+      } else {
+        u[i] = ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + colc);
+      }
+    }
     constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
     cf xp[PFX > 0 ? PFX : 1];
     // (the column's second half holds samples only on circular rows)
@@ -327,16 +333,27 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       int64_t ro, t, len;
       const bool ok = at(j + i * S1, ro, t, len);
       cf z = u[i];
-      if constexpr (KIND != COL_OUT) {
-        const cf xv = i < PFX   ? xp[i < PFX ? i : 0]
-                      : i < PFB ? bf16_pair_cf(xb[i < PFB ? i : 0])
-                      : GRID    ? act(a.xg, j + i * S1)
-                                : unpack(xl[i >= G0 && i - G0 < E ? i - G0 : 0]);
-        z = make_float2(xv.x * z.x, xv.y * z.y);
-      }
-      if constexpr (GRID) z = ok ? z : make_float2(0.f, 0.f);
-      if constexpr (KIND == COL_LAST || KIND == COL_OUT) {
-        if (ok) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
+      if constexpr (GRID) {   // grid passes: the gate and the store under the point's mask
+        z = make_float2(0.f, 0.f);
+        if (ok) {
+          if constexpr (KIND == COL_OUT) {
+            z = u[i];
+          } else {
+            const cf xv = ld_pair<io_of(IOT), EVEN>(a.xg, ro, t, len);
+            z = make_float2(xv.x * u[i].x, xv.y * u[i].y);
+          }
+          if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
+        }
+      } else {
+        if constexpr (KIND != COL_OUT) {
+          const cf xv = i < PFX   ? xp[i < PFX ? i : 0]
+                        : i < PFB ? bf16_pair_cf(xb[i < PFB ? i : 0])
+                                  : unpack(xl[i >= G0 && i - G0 < E ? i - G0 : 0]);
+          z = make_float2(xv.x * z.x, xv.y * z.y);
+        }
+        if constexpr (KIND == COL_LAST || KIND == COL_OUT) {
+          if (ok) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
+        }
       }
       u[i] = z;
     }
