@@ -226,10 +226,14 @@ hipError_t bw_ew(int io, int op, const void* a, const void* b, void* out, int64_
 // Causal convolution of every row of z with a filter spectrum: an order-1
 // four-step forward without the gate.  filters_per_row: the spectrum holds
 // one filter per row (else one per channel).
+// zspec: the rows are given by their spectra (filter-spectrum layout, one per
+// row) instead of z, which then goes unread; filters per channel only.
 hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* out, int B, int D,
-                   bool filters_per_row, void* work, int rows_per_group, hipStream_t s) {
+                   bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
+                   const void* zspec = nullptr) {
   ForwardArgs f{};
   f.v = z;
+  f.spec_in = zspec;
   f.no_gate = 1;
   f.spec = spec;
   f.y = out;
@@ -303,8 +307,9 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
       hipLaunchKernelGGL(k_bw_batch_sum_rev<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
                          a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
     BW_TRY(hipGetLastError());
-    // adjoint: g_n = R(h_n conv T2); kept reversed in T1
-    BW_TRY(bw_conv(p, spec_n(nn), T2, T1, (int)B, (int)D, false, work, w.rows_per_group, s));
+    // adjoint: g_n = R(h_n conv T2); kept reversed in T1.  T2's spectra are
+    // already in sg, so this convolution starts at its row pass.
+    BW_TRY(bw_conv(p, spec_n(nn), T2, T1, (int)B, (int)D, false, work, w.rows_per_group, s, sg));
     gcur = T1;
     grev = true;
   }

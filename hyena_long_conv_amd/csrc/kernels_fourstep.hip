@@ -144,8 +144,11 @@ __device__ __forceinline__ cf ld_spec(const cf* p) {
 }
 
 // COL_OUT: as COL_LAST without the gate (the plain causal convolution).
+// ROW_SMUL: the row pass of a convolution whose input rows are given by
+// their spectra (the ROW_SPEC layout) instead of a column-transformed
+// intermediate; no column pass precedes it.
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4 };
-enum { ROW_CONV = 0, ROW_SPEC = 1 };
+enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2 };
 
 struct ColArgs {
   const void* v;       // FIRST: z_1 rows
@@ -561,6 +564,7 @@ struct RowArgs {
   int cmB;             // CONV, > 1: channel-major launch (r0 = first channel, cmB batch rows each)
   int n_units;         // channel-major launch: (channel, row pair) units; the grid is padded to a multiple of 8
   int wb;              // CONV: the intermediate holds bf16 pairs (bf16 activations)
+  const cf* spec_in;   // SMUL: spectra of the input rows, one per activation row (ROW_SPEC layout)
 };
 
 // LDS of the row pass.  HYENA_ROW_SW: 0 plain addressing; 1 XOR-swizzled
@@ -593,7 +597,7 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
   const int b = threadIdx.x / TPR, j = threadIdx.x - b * TPR;
   int g, w;
   const int bid = blockIdx.x;
-  if (KIND == ROW_CONV && a.cmB > 1) {
+  if (KIND != ROW_SPEC && a.cmB > 1) {
     // Channel-major launch: the cmB workgroups of one (channel, row pair)
     // read the same spectrum slice, so they are placed on one XCD (workgroup
     // i runs on XCD i mod 8) one after another, and the slice is fetched
@@ -633,15 +637,56 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
   // powers of the step W_N^{k1 S2}
   const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, N);
   const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, N);
+  if constexpr (KIND != ROW_SMUL) {
 #pragma unroll
-  for (int i = 0; i < E; ++i) u[i] = cmul(ld_work<WB>(row + j + i * S2), step_power<E>(tb, ts, i));
-  fft.template run<false>(u, lds, j);
+    for (int i = 0; i < E; ++i) u[i] = cmul(ld_work<WB>(row + j + i * S2), step_power<E>(tb, ts, i));
+    fft.template run<false>(u, lds, j);
+  }
 
   // bins k = k1 + n1*k2 with k2 = j + i*S2; mirror N-k at (k1m, k2m)
   // W_{2N}^k = W_{2N}^{k1 + n1 j} * W_{2E}^i
   const cf wk = twiddle<false>((uint32_t)k1 + (uint32_t)n1 * (uint32_t)j, 2 * N);
 
-  if constexpr (KIND == ROW_SPEC) {
+  if constexpr (KIND == ROW_SMUL) {
+    // The input row's real-FFT bins X(k) are given as S(k) = X(k)/(2N), the
+    // filter's as G(k) = H(k)/(2N).  With Y = X H / (2N) = 2N S G, the
+    // half-length bins whose unnormalised inverse DFT is y[2m] + i y[2m+1]
+    // are C'(k) = Y(k) (1 + i conj W) + conj Y(N-k) (1 - i conj W),
+    // W = W_{2N}^k -- the even/odd re-packing that realconv_pair folds into
+    // its product.  Y(N-k) comes from the thread holding bin N-k (mirror row,
+    // through LDS); Y(N), the partner of bin 0, is loaded directly.
+    static_assert(!WB, "spectral-input rows use a float2 intermediate");
+    const int arow = launch_row_of(a.r0, g, a.cmB, a.D);
+    const int d = (a.cmB > 1) ? a.r0 + g / a.cmB : (a.r0 + g) % a.D;
+    const cf* xs = a.spec_in + (int64_t)arow * a.spec_stride;
+    const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
+    const float sc = 2.0f * (float)N;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t k = (int64_t)k1 * N2 + j + i * S2;
+      u[i] = cscale(cmul(ld_spec(xs + k), ld_spec(gs + k)), sc);
+    }
+    cf yn = make_float2(0.f, 0.f);
+    if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
+#pragma unroll
+    for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k2 = j + i * S2;
+      const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+      const cf ym = (k1 == 0 && k2 == 0) ? yn : ldsm(k2m);
+      const cf w = cmul(wk, w2e<E>(i));
+      const cf p = make_float2(1.f + w.y, w.x), q = make_float2(1.f - w.y, -w.x);
+      u[i] = cadd(cmul(u[i], p), cmul(cconj(ym), q));
+    }
+    __syncthreads();
+    fft.template run<true>(u, lds, j);
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) st_work<WB>(row + j + i * S2, cmulc(u[i], step_power<E>(tb, ts, i)));
+    }
+  } else if constexpr (KIND == ROW_SPEC) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
@@ -840,9 +885,10 @@ static hipError_t dispatch_col(int n1, int kind, int io, const ColArgs& c, int g
 template <int N2>
 static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t s) {
   // channel-major: n_units (channel, row pair) units padded to a multiple of 8, cmB workgroups each
-  const int blocks = (kind == ROW_CONV && r.cmB > 1) ? (r.n_units + 7) / 8 * 8 * r.cmB : groups * r.n_row_pairs;
+  const int blocks = (kind != ROW_SPEC && r.cmB > 1) ? (r.n_units + 7) / 8 * 8 * r.cmB : groups * r.n_row_pairs;
   const dim3 grid(blocks);
   if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, dim3(RowCfg<N2>::T), 0, s, r);
+  else if (kind == ROW_SMUL) hipLaunchKernelGGL((k_row<N2, ROW_SMUL>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, dim3(RowCfg<N2, true>::T), 0, s, r);
   else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   return hipGetLastError();
@@ -882,15 +928,20 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   const int units = cm ? a.D : a.n_rows, per = cm ? a.rows_per_group / a.B : a.rows_per_group;
   c.cmB = r.cmB = cm ? a.B : 1;
   c.cmD = a.D;
+  // Input rows given by their spectra: one order, no gate, fp32, and the
+  // first column pass and forward row FFT are skipped.
+  const bool smul = a.spec_in != nullptr;
+  if (smul && (a.NORD != 1 || !a.no_gate || cio != 0)) return hipErrorInvalidValue;
+  r.spec_in = static_cast<const cf*>(a.spec_in);
   for (int r0 = 0; r0 < units; r0 += per) {
     const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? a.B : 1);
     c.r0 = r0; r.r0 = r0;
     r.n_units = cm ? groups / a.B * r.n_row_pairs : 0;
-    hipError_t e = dispatch_col(p.n1, COL_FIRST, cio, c, groups, s);
+    hipError_t e = smul ? hipSuccess : dispatch_col(p.n1, COL_FIRST, cio, c, groups, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < a.NORD; ++n) {
       r.order = n;
-      e = dispatch_row(p.n2, ROW_CONV, r, groups, s);
+      e = dispatch_row(p.n2, smul ? ROW_SMUL : ROW_CONV, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
       e = dispatch_col(p.n1, n < a.NORD - 1 ? COL_MID : (a.no_gate ? COL_OUT : COL_LAST), cio, c, groups, s);

@@ -23,6 +23,8 @@ struct ForwardArgs {
   int rows_per_group;
   int circular;          // single path: rows fill the whole FFT length (no zero half)
   int no_gate;           // four-step, fp32 rows: the last order stores the convolution without a gate
+  const void* spec_in;   // four-step, one order, no gate: the input rows' spectra (filter-spectrum
+                         // layout, one per row b*D + d) in place of v; nullptr otherwise
 };
 
 struct SpectrumArgs {
