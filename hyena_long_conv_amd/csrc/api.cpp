@@ -135,7 +135,7 @@ bool sizes_ok(int64_t D, int64_t N, int64_t L) {
 
 namespace hyena {
 
-// Byte offsets of the long backward's workspace buffers: N saved c_n, z, g,
+// Byte offsets of the long backward's workspace buffers: N saved c_n, z,
 // two temporaries (fp32 rows), the per-row spectra and the four-step
 // intermediate of one pass group.
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
@@ -145,7 +145,6 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   int64_t o = 0;
   w.c = o;     o += NORD * act;
   w.z = o;     o += act;
-  w.g = o;     o += act;
   w.t1 = o;    o += act;
   w.t2 = o;    o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);

@@ -122,19 +122,21 @@ __device__ __forceinline__ int64_t mirror(int64_t t, int64_t L, bool circ) {
   return circ ? (t == 0 ? 0 : L - t) : L - 1 - t;
 }
 
+// Not REV (the first step) reads g straight from the caller's dloss/dy, in
+// the I/O dtype; a reversed g is an fp32 workspace row.
 template <int IOT, bool REV, bool V4, bool CIRC = false>
-__global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restrict__ c, const void* __restrict__ x,
+__global__ void k_bw_step(const void* __restrict__ gsrc, const float* __restrict__ c, const void* __restrict__ x,
                           void* __restrict__ gx, float* __restrict__ t2, int64_t rows, int64_t L) {
+  const float* gf = static_cast<const float*>(gsrc);
   if constexpr (V4) {
     ROW_LOOP4(rows, L) {
       const int64_t i = r * L + t, ri = r * L + (L - 4 - t);     // ri: mirror of t + 3
       float g[4], xv[4];
       if constexpr (REV) {
-        const float4 w = ld_f4(gsrc + ri);
+        const float4 w = ld_f4(gf + ri);
         g[0] = w.w; g[1] = w.z; g[2] = w.y; g[3] = w.x;
       } else {
-        const float4 w = ld_f4(gsrc + i);
-        g[0] = w.x; g[1] = w.y; g[2] = w.z; g[3] = w.w;
+        ld4_io<IOT>(gsrc, i, g);
       }
       const float4 cv = ld_f4(c + i);
       ld4_io<IOT>(x, i, xv);
@@ -144,7 +146,7 @@ __global__ void k_bw_step(const float* __restrict__ gsrc, const float* __restric
   } else {
     ROW_LOOP(rows, L) {
       const int64_t i = r * L + t, ri = r * L + mirror(t, L, CIRC);
-      const float g = gsrc[REV ? ri : i];
+      const float g = REV ? gf[ri] : IO<IOT>::ld(gsrc, i);
       IO<IOT>::st(gx, i, g * c[i]);
       t2[ri] = g * IO<IOT>::ld(x, i);
     }
@@ -199,7 +201,7 @@ hipError_t bw_elementwise_io(int op, const void* a, const void* b, void* out, in
 enum { BW_LOAD = 0, BW_GATE = 2 };
 
 template <int IOT>
-hipError_t bw_step_io(bool rev, const float* g, const float* c, const void* x, void* gx, float* t2, int64_t L,
+hipError_t bw_step_io(bool rev, const void* g, const float* c, const void* x, void* gx, float* t2, int64_t L,
                       int64_t n, bool circ, hipStream_t s) {
   const int64_t rows = n / L;
   const dim3 blk(EW_THREADS);
@@ -228,9 +230,10 @@ hipError_t bw_ew(int io, int op, const void* a, const void* b, void* out, int64_
 // one filter per row (else one per channel).
 // zspec: the rows are given by their spectra (filter-spectrum layout, one per
 // row) instead of z, which then goes unread; filters per channel only.
-hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* out, int B, int D,
+// zio: dtype of z (0 fp32, 1 bf16); the intermediate and out are fp32.
+hipError_t bw_conv(const PlanInfo& p, const void* spec, const void* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
-                   const void* zspec = nullptr) {
+                   const void* zspec = nullptr, int zio = 0) {
   ForwardArgs f{};
   f.v = z;
   f.spec_in = zspec;
@@ -241,7 +244,7 @@ hipError_t bw_conv(const PlanInfo& p, const void* spec, const float* z, float* o
   f.D = filters_per_row ? B * D : D;
   f.NORD = 1;
   f.L = p.L;
-  f.io = 0;
+  f.io = zio;
   f.spec_stride = p.spec_stride;
   f.n_rows = B * D;
   f.work = work;
@@ -262,7 +265,6 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   char* ws = static_cast<char*>(workspace);
   float* C = reinterpret_cast<float*>(ws + w.c);
   float* Z = reinterpret_cast<float*>(ws + w.z);
-  float* G = reinterpret_cast<float*>(ws + w.g);
   float* T1 = reinterpret_cast<float*>(ws + w.t1);
   float* T2 = reinterpret_cast<float*>(ws + w.t2);
   void* sg = ws + w.sg;
@@ -272,31 +274,37 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   const auto spec_n = [&](int nn) { return static_cast<const void*>(spec + (int64_t)nn * D * p.spec_stride); };
   hipError_t e;
 #define BW_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-  // forward: c_n = h_n conv z_n (kept), z_{n+1} = x_n * c_n
-  BW_TRY(bw_ew(a.io, BW_LOAD, a.v, nullptr, Z, n, s));
+  // forward: c_n = h_n conv z_n (kept), z_{n+1} = x_n * c_n; z_1 = v is
+  // read in the I/O dtype by the first convolution
   for (int nn = 0; nn < a.NORD; ++nn) {
     float* Cn = C + nn * cstride;
-    BW_TRY(bw_conv(p, spec_n(nn), Z, Cn, (int)B, (int)D, false, work, w.rows_per_group, s));
+    if (nn == 0)
+      BW_TRY(bw_conv(p, spec_n(nn), a.v, Cn, (int)B, (int)D, false, work, w.rows_per_group, s, nullptr, a.io));
+    else
+      BW_TRY(bw_conv(p, spec_n(nn), Z, Cn, (int)B, (int)D, false, work, w.rows_per_group, s));
     if (nn < a.NORD - 1) BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn], Cn, Z, n, s));
   }
-  // backward, g = dloss/dz_{n+1}; after each adjoint convolution g is left
-  // reversed in T1 and read through the reversal by the next step
-  BW_TRY(bw_ew(a.io, BW_LOAD, a.gy, nullptr, G, n, s));
-  const float* gcur = G;
+  // backward, g = dloss/dz_{n+1}: the first step reads dloss/dy itself; after
+  // each adjoint convolution g is left reversed in T1 and read through the
+  // reversal by the next step
+  const void* gcur = a.gy;
   bool grev = false;
   for (int nn = a.NORD - 1; nn >= 0; --nn) {
     const float* Cn = C + nn * cstride;
     // gx_n = g * c_n, T2 = R(g * x_n)
     BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s)
                      : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
-    if (nn == 0) BW_TRY(bw_ew(a.io, BW_LOAD, a.v, nullptr, Z, n, s));          // z_1 = v
-    else BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn - 1], C + (nn - 1) * cstride, Z, n, s));
-    // filter gradient: spectra of the rows of T2, then (T2 conv z) reversed and summed over the batch
+    if (nn > 0) BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn - 1], C + (nn - 1) * cstride, Z, n, s));
+    // filter gradient: spectra of the rows of T2, then (T2 conv z) reversed and
+    // summed over the batch (z_1 = v read in the I/O dtype)
     SpectrumArgs sa{};
     sa.h = T2; sa.spec = sg; sa.NF = (int)R; sa.L = L; sa.spec_stride = p.spec_stride;
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
     BW_TRY(fourstep_spectrum(sa, p, s));
-    BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
+    if (nn == 0)
+      BW_TRY(bw_conv(p, sg, a.v, T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io));
+    else
+      BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
     if (circ)
       hipLaunchKernelGGL((k_bw_batch_sum_rev<false, true>), row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
                          a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
@@ -313,16 +321,18 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     gcur = T1;
     grev = true;
   }
+  // (every order ran an adjoint, so g is the fp32 row buffer T1, reversed)
+  const float* gfin = T1;
   const dim3 rg = row_grid(R, L % 4 == 0 && !circ ? L / 4 : L);
   if (circ) {
-    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
-    else hipLaunchKernelGGL((k_bw_store_rev<1, false, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false, true>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, false, true>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
   } else if (L % 4 == 0) {
-    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
-    else hipLaunchKernelGGL((k_bw_store_rev<1, true>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, true>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, true>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
   } else {
-    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
-    else hipLaunchKernelGGL((k_bw_store_rev<1, false>), rg, dim3(EW_THREADS), 0, s, gcur, a.gv, R, L);
+    if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
+    else hipLaunchKernelGGL((k_bw_store_rev<1, false>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
   }
   BW_TRY(hipGetLastError());
 #undef BW_TRY

@@ -81,8 +81,11 @@ template <int N1, bool GRID = false> struct ColCfg {
 #define HYENA_ROW_E_BF16 8
 #endif
 
+#ifndef HYENA_ROW_E8_F32
+#define HYENA_ROW_E8_F32 0
+#endif
 template <int N2, bool WB = false> struct RowCfg {
-  static constexpr int E = (WB && N2 <= 1024) ? HYENA_ROW_E_BF16 : HYENA_ROW_E;
+  static constexpr int E = ((WB || HYENA_ROW_E8_F32) && N2 <= 1024) ? HYENA_ROW_E_BF16 : HYENA_ROW_E;
   static constexpr int TPR = N2 / E;  // threads per row
   static constexpr int T = 2 * TPR;
   using R = typename std::conditional<E == 16, typename Plan16<N2>::R,
@@ -920,7 +923,8 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   r.n1 = p.n1; r.spec_stride = a.spec_stride; r.D = a.D; r.n_row_pairs = (p.n1 + 1) / 2;
   // bf16 activations up to kBf16WorkMaxOrder: bf16 intermediate (column
   // kernels IOT 2, row kernel WB), else float2.
-  const int cio = a.io == 0 ? 0 : (forward_bf16_work(true, a.NORD) ? 2 : 1);
+  // The backward's convolutions (no gate) keep a float2 intermediate.
+  const int cio = a.io == 0 ? 0 : (!a.no_gate && forward_bf16_work(true, a.NORD) ? 2 : 1);
   r.wb = cio == 2;
   // With B > 1 a launch covers whole channels (all their batch rows), so the
   // row pass reads each channel's spectrum once instead of once per batch row.

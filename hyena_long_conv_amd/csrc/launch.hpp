@@ -102,7 +102,7 @@ hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 // workspace buffers (saved c_n, z, g, two temporaries, the per-row spectra
 // and the four-step intermediate).
 struct LongBackwardLayout {
-  int64_t c, z, g, t1, t2, sg, work, total;
+  int64_t c, z, t1, t2, sg, work, total;
   int rows_per_group;
 };
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD);
