@@ -135,8 +135,8 @@ bool sizes_ok(int64_t D, int64_t N, int64_t L) {
 
 namespace hyena {
 
-// Byte offsets of the long backward's workspace buffers: N saved c_n, z,
-// two temporaries (fp32 rows), the per-row spectra and the four-step
+// Byte offsets of the long backward's workspace buffers: N saved c_n, two
+// temporaries (fp32 rows), the per-row spectra and the four-step
 // intermediate of one pass group.
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
   const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -144,7 +144,6 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   LongBackwardLayout w{};
   int64_t o = 0;
   w.c = o;     o += NORD * act;
-  w.z = o;     o += act;
   w.t1 = o;    o += act;
   w.t2 = o;    o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);

@@ -25,18 +25,6 @@ namespace {
 
 constexpr int EW_THREADS = 256;
 
-inline dim3 ew_grid(int64_t n) {
-  int64_t b = (n / 4 + EW_THREADS - 1) / EW_THREADS;
-  if (b > 65536 * 8) b = 65536 * 8;
-  return dim3((unsigned)(b < 1 ? 1 : b));
-}
-
-// Four consecutive elements per thread (n4 = n / 4 groups), then a scalar
-// tail; every buffer here starts 16-byte aligned.
-#define EW_LOOP4(n)                                                                              \
-  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < (n) / 4;                   \
-       q += (int64_t)gridDim.x * blockDim.x)
-
 template <int IOT>
 __device__ __forceinline__ void ld4_io(const void* p, int64_t i, float (&o)[4]) {
   if constexpr (IOT == 0) {
@@ -46,34 +34,6 @@ __device__ __forceinline__ void ld4_io(const void* p, int64_t i, float (&o)[4]) 
     const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
     o[0] = __uint_as_float(w.x << 16); o[1] = __uint_as_float(w.x & 0xffff0000u);
     o[2] = __uint_as_float(w.y << 16); o[3] = __uint_as_float(w.y & 0xffff0000u);
-  }
-}
-
-template <int IOT>
-__global__ void k_bw_load(const void* __restrict__ src, float* __restrict__ dst, int64_t n) {
-  EW_LOOP4(n) {
-    float o[4];
-    ld4_io<IOT>(src, 4 * q, o);
-    *reinterpret_cast<float4*>(dst + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
-  }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-    const int64_t i = (n & ~int64_t(3)) + threadIdx.x;
-    dst[i] = IO<IOT>::ld(src, i);
-  }
-}
-
-// z = x * c  (x in the I/O dtype)
-template <int IOT>
-__global__ void k_bw_gate(const void* __restrict__ x, const float* __restrict__ c, float* __restrict__ z, int64_t n) {
-  EW_LOOP4(n) {
-    float o[4];
-    ld4_io<IOT>(x, 4 * q, o);
-    const float4 cv = *reinterpret_cast<const float4*>(c + 4 * q);
-    *reinterpret_cast<float4*>(z + 4 * q) = make_float4(o[0] * cv.x, o[1] * cv.y, o[2] * cv.z, o[3] * cv.w);
-  }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-    const int64_t i = (n & ~int64_t(3)) + threadIdx.x;
-    z[i] = IO<IOT>::ld(x, i) * c[i];
   }
 }
 
@@ -188,19 +148,6 @@ __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restri
 }
 
 template <int IOT>
-hipError_t bw_elementwise_io(int op, const void* a, const void* b, void* out, int64_t n, hipStream_t s) {
-  const dim3 g = ew_grid(n), blk(EW_THREADS);
-  switch (op) {
-    case 0: hipLaunchKernelGGL(k_bw_load<IOT>, g, blk, 0, s, a, (float*)out, n); break;
-    case 2: hipLaunchKernelGGL(k_bw_gate<IOT>, g, blk, 0, s, a, (const float*)b, (float*)out, n); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-enum { BW_LOAD = 0, BW_GATE = 2 };
-
-template <int IOT>
 hipError_t bw_step_io(bool rev, const void* g, const float* c, const void* x, void* gx, float* t2, int64_t L,
                       int64_t n, bool circ, hipStream_t s) {
   const int64_t rows = n / L;
@@ -221,22 +168,20 @@ hipError_t bw_step_io(bool rev, const void* g, const float* c, const void* x, vo
   return hipGetLastError();
 }
 
-hipError_t bw_ew(int io, int op, const void* a, const void* b, void* out, int64_t n, hipStream_t s) {
-  return io == 0 ? bw_elementwise_io<0>(op, a, b, out, n, s) : bw_elementwise_io<1>(op, a, b, out, n, s);
-}
-
 // Causal convolution of every row of z with a filter spectrum: an order-1
 // four-step forward without the gate.  filters_per_row: the spectrum holds
 // one filter per row (else one per channel).
 // zspec: the rows are given by their spectra (filter-spectrum layout, one per
 // row) instead of z, which then goes unread; filters per channel only.
 // zio: dtype of z (0 fp32, 1 bf16); the intermediate and out are fp32.
+// zc: the rows are z * zc (zc fp32), formed in the first column pass.
 hipError_t bw_conv(const PlanInfo& p, const void* spec, const void* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
-                   const void* zspec = nullptr, int zio = 0) {
+                   const void* zspec = nullptr, int zio = 0, const float* zc = nullptr) {
   ForwardArgs f{};
   f.v = z;
   f.spec_in = zspec;
+  f.vc = zc;
   f.no_gate = 1;
   f.spec = spec;
   f.y = out;
@@ -264,25 +209,23 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
   const LongBackwardLayout w = long_backward_layout(p, B, D, a.NORD);
   char* ws = static_cast<char*>(workspace);
   float* C = reinterpret_cast<float*>(ws + w.c);
-  float* Z = reinterpret_cast<float*>(ws + w.z);
   float* T1 = reinterpret_cast<float*>(ws + w.t1);
   float* T2 = reinterpret_cast<float*>(ws + w.t2);
   void* sg = ws + w.sg;
   void* work = ws + w.work;
-  const int64_t cstride = (w.z - w.c) / a.NORD / 4;   // floats between saved c_n
+  const int64_t cstride = (w.t1 - w.c) / a.NORD / 4;  // floats between saved c_n
   const cf* spec = static_cast<const cf*>(a.spec);
   const auto spec_n = [&](int nn) { return static_cast<const void*>(spec + (int64_t)nn * D * p.spec_stride); };
   hipError_t e;
 #define BW_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-  // forward: c_n = h_n conv z_n (kept), z_{n+1} = x_n * c_n; z_1 = v is
-  // read in the I/O dtype by the first convolution
-  for (int nn = 0; nn < a.NORD; ++nn) {
-    float* Cn = C + nn * cstride;
-    if (nn == 0)
-      BW_TRY(bw_conv(p, spec_n(nn), a.v, Cn, (int)B, (int)D, false, work, w.rows_per_group, s, nullptr, a.io));
-    else
-      BW_TRY(bw_conv(p, spec_n(nn), Z, Cn, (int)B, (int)D, false, work, w.rows_per_group, s));
-    if (nn < a.NORD - 1) BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn], Cn, Z, n, s));
+  // forward: c_n = h_n conv z_n (kept), z_{n+1} = x_n * c_n -- the forward's
+  // own passes, each order's column pass also storing c_n (fp32)
+  {
+    ForwardArgs f{};
+    f.v = a.v; f.x = a.x; f.spec = a.spec; f.B = (int)B; f.D = (int)D; f.NORD = a.NORD; f.L = L;
+    f.io = a.io; f.spec_stride = p.spec_stride; f.n_rows = (int)R; f.work = work;
+    f.rows_per_group = w.rows_per_group; f.no_gate = 1; f.csave = C; f.csave_stride = cstride;
+    BW_TRY(fourstep_forward(f, p, s));
   }
   // backward, g = dloss/dz_{n+1}: the first step reads dloss/dy itself; after
   // each adjoint convolution g is left reversed in T1 and read through the
@@ -294,9 +237,9 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     // gx_n = g * c_n, T2 = R(g * x_n)
     BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s)
                      : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
-    if (nn > 0) BW_TRY(bw_ew(a.io, BW_GATE, a.x.p[nn - 1], C + (nn - 1) * cstride, Z, n, s));
-    // filter gradient: spectra of the rows of T2, then (T2 conv z) reversed and
-    // summed over the batch (z_1 = v read in the I/O dtype)
+    // filter gradient: spectra of the rows of T2, then (T2 conv z_n) reversed
+    // and summed over the batch; z_1 = v, z_n = x_{n-1} * c_{n-1} formed by
+    // the convolution's first column pass
     SpectrumArgs sa{};
     sa.h = T2; sa.spec = sg; sa.NF = (int)R; sa.L = L; sa.spec_stride = p.spec_stride;
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
@@ -304,7 +247,8 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     if (nn == 0)
       BW_TRY(bw_conv(p, sg, a.v, T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io));
     else
-      BW_TRY(bw_conv(p, sg, Z, T1, (int)B, (int)D, true, work, w.rows_per_group, s));
+      BW_TRY(bw_conv(p, sg, a.x.p[nn - 1], T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io,
+                     C + (nn - 1) * cstride));
     if (circ)
       hipLaunchKernelGGL((k_bw_batch_sum_rev<false, true>), row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
                          a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);

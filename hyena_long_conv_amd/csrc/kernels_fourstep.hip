@@ -147,10 +147,13 @@ __device__ __forceinline__ cf ld_spec(const cf* p) {
 }
 
 // COL_OUT: as COL_LAST without the gate (the plain causal convolution).
+// COL_MIDSAVE: as COL_MID, and the ungated convolution is stored too (fp32,
+// to y).  COL_FIRSTG: as COL_FIRST with the input formed as x * c (x = xg
+// in the activation type, c = v in fp32).  Both serve the backward.
 // ROW_SMUL: the row pass of a convolution whose input rows are given by
 // their spectra (the ROW_SPEC layout) instead of a column-transformed
 // intermediate; no column pass precedes it.
-enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4 };
+enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4, COL_MIDSAVE = 5, COL_FIRSTG = 6 };
 enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2 };
 
 struct ColArgs {
@@ -271,13 +274,18 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc),
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm + 1, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc));
     }
-  } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+  } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       if constexpr (KIND == COL_SPEC) {
         int64_t ro, t, len;
         at(j + i * S1, ro, t, len);
         u[i] = ld_pair<0, EVEN, true>(a.h, ro, t, len);
+      } else if constexpr (KIND == COL_FIRSTG) {
+        int64_t ro, t, len;
+        at(j + i * S1, ro, t, len);
+        const cf cv = ld_pair<0, EVEN, true>(a.v, ro, t, len), xv = act(a.xg, j + i * S1);
+        u[i] = make_float2(xv.x * cv.x, xv.y * cv.y);
       } else {
         u[i] = act(a.v, j + i * S1);
       }
@@ -351,6 +359,9 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
           if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
         }
       } else {
+        if constexpr (KIND == COL_MIDSAVE) {
+          if (ok) st_pair<0, EVEN>(a.y, ro, t, len, z);
+        }
         if constexpr (KIND != COL_OUT) {
           const cf xv = i < PFX   ? xp[i < PFX ? i : 0]
                         : i < PFB ? bf16_pair_cf(xb[i < PFB ? i : 0])
@@ -406,12 +417,18 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   cf u[N1];
-  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
-      if constexpr (KIND == COL_SPEC) u[i] = ld_pair<0, EVEN, true>(a.h, off, t, a.L);
-      else u[i] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, t, a.L);
+      if constexpr (KIND == COL_SPEC) {
+        u[i] = ld_pair<0, EVEN, true>(a.h, off, t, a.L);
+      } else if constexpr (KIND == COL_FIRSTG) {
+        const cf cv = ld_pair<0, EVEN, true>(a.v, off, t, a.L), xv = ld_pair<io_of(IOT), EVEN, true>(a.xg, off, t, a.L);
+        u[i] = make_float2(xv.x * cv.x, xv.y * cv.y);
+      } else {
+        u[i] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, t, a.L);
+      }
     }
   } else {
 #pragma unroll
@@ -431,6 +448,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
         }
       }
       cf z = u[i];
+      if constexpr (KIND == COL_MIDSAVE) st_pair<0, EVEN>(a.y, off, t, a.L, z);
       if constexpr (KIND != COL_OUT) {
         const cf xv = unpack(xl[i]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
@@ -516,11 +534,18 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   // time row of point m: lane_a + 2m;  spectrum row of point k: Q*lane_a + k
   const auto trow = [&](int m) { return 2 * ((int64_t)a.n2 * (lane_a + 2 * m) + col); };
   cf u[Q];
-  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC) {
+  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
-      if constexpr (KIND == COL_SPEC) u[m] = ld_pair<0, EVEN, true>(a.h, off, trow(m), a.L);
-      else u[m] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, trow(m), a.L);
+      if constexpr (KIND == COL_SPEC) {
+        u[m] = ld_pair<0, EVEN, true>(a.h, off, trow(m), a.L);
+      } else if constexpr (KIND == COL_FIRSTG) {
+        const cf cv = ld_pair<0, EVEN, true>(a.v, off, trow(m), a.L);
+        const cf xv = ld_pair<io_of(IOT), EVEN, true>(a.xg, off, trow(m), a.L);
+        u[m] = make_float2(xv.x * cv.x, xv.y * cv.y);
+      } else {
+        u[m] = ld_pair<io_of(IOT), EVEN, true>(a.v, off, trow(m), a.L);
+      }
     }
   } else {
 #pragma unroll
@@ -538,6 +563,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
         }
       }
       cf z = u[m];
+      if constexpr (KIND == COL_MIDSAVE) st_pair<0, EVEN>(a.y, off, trow(m), a.L, z);
       if constexpr (KIND != COL_OUT) {
         const cf xv = unpack(xl[m]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
@@ -757,6 +783,13 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
     hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
   } else if (kind == COL_OUT) {
     if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+  } else if (kind == COL_MIDSAVE || kind == COL_FIRSTG) {
+    if constexpr (!GRID) {
+      if (kind == COL_MIDSAVE && io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_MIDSAVE, EVEN, false>), grid, block, 0, s, c);
+      else if (kind == COL_MIDSAVE) hipLaunchKernelGGL((k_col<N1, 1, COL_MIDSAVE, EVEN, false>), grid, block, 0, s, c);
+      else if (io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRSTG, EVEN, false>), grid, block, 0, s, c);
+      else hipLaunchKernelGGL((k_col<N1, 1, COL_FIRSTG, EVEN, false>), grid, block, 0, s, c);
+    }
   } else if (io == 0) {
     if (kind == COL_FIRST) hipLaunchKernelGGL((k_col<N1, 0, COL_FIRST, EVEN, GRID>), grid, block, 0, s, c);
     else if (kind == COL_MID) hipLaunchKernelGGL((k_col<N1, 0, COL_MID, EVEN, GRID>), grid, block, 0, s, c);
@@ -775,7 +808,11 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
 // The kernel of one conv kind at one activation type (IOT as in k_col).
 #define HYENA_COL_KINDS(KERN, P, IOTV, EVENV)                                                        \
   do {                                                                                               \
-    if (kind == COL_FIRST) hipLaunchKernelGGL((KERN<P, IOTV, COL_FIRST, EVENV>), grid, block, 0, s, c); \
+    if (IOTV != 2 && kind == COL_MIDSAVE)                                                            \
+      hipLaunchKernelGGL((KERN<P, (IOTV == 2 ? 0 : IOTV), COL_MIDSAVE, EVENV>), grid, block, 0, s, c); \
+    else if (IOTV != 2 && kind == COL_FIRSTG)                                                        \
+      hipLaunchKernelGGL((KERN<P, (IOTV == 2 ? 0 : IOTV), COL_FIRSTG, EVENV>), grid, block, 0, s, c); \
+    else if (kind == COL_FIRST) hipLaunchKernelGGL((KERN<P, IOTV, COL_FIRST, EVENV>), grid, block, 0, s, c); \
     else if (kind == COL_MID) hipLaunchKernelGGL((KERN<P, IOTV, COL_MID, EVENV>), grid, block, 0, s, c); \
     else hipLaunchKernelGGL((KERN<P, IOTV, COL_LAST, EVENV>), grid, block, 0, s, c);                   \
   } while (0)
@@ -937,18 +974,28 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   const bool smul = a.spec_in != nullptr;
   if (smul && (a.NORD != 1 || !a.no_gate || cio != 0)) return hipErrorInvalidValue;
   r.spec_in = static_cast<const cf*>(a.spec_in);
+  // csave: c_n of every order kept (fp32); vc: input rows x * c formed in the
+  // first column pass
+  const bool save = a.csave != nullptr;
+  if ((save || a.vc) && !a.no_gate) return hipErrorInvalidValue;
+  if (a.vc && (a.NORD != 1 || smul)) return hipErrorInvalidValue;
+  const int first = a.vc ? COL_FIRSTG : COL_FIRST;
+  if (a.vc) c.v = a.vc;
   for (int r0 = 0; r0 < units; r0 += per) {
     const int groups = ((units - r0 < per) ? units - r0 : per) * (cm ? a.B : 1);
     c.r0 = r0; r.r0 = r0;
     r.n_units = cm ? groups / a.B * r.n_row_pairs : 0;
-    hipError_t e = smul ? hipSuccess : dispatch_col(p.n1, COL_FIRST, cio, c, groups, s);
+    if (a.vc) c.xg = a.v;
+    hipError_t e = smul ? hipSuccess : dispatch_col(p.n1, first, cio, c, groups, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < a.NORD; ++n) {
       r.order = n;
       e = dispatch_row(p.n2, smul ? ROW_SMUL : ROW_CONV, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
-      e = dispatch_col(p.n1, n < a.NORD - 1 ? COL_MID : (a.no_gate ? COL_OUT : COL_LAST), cio, c, groups, s);
+      if (save) c.y = a.csave + n * a.csave_stride;
+      const int kind = n < a.NORD - 1 ? (save ? COL_MIDSAVE : COL_MID) : (a.no_gate ? COL_OUT : COL_LAST);
+      e = dispatch_col(p.n1, kind, cio, c, groups, s);
       if (e != hipSuccess) return e;
     }
   }

@@ -25,6 +25,10 @@ struct ForwardArgs {
   int no_gate;           // four-step, fp32 rows: the last order stores the convolution without a gate
   const void* spec_in;   // four-step, one order, no gate: the input rows' spectra (filter-spectrum
                          // layout, one per row b*D + d) in place of v; nullptr otherwise
+  float* csave;          // four-step, no gate: every order's convolution c_n (fp32 [B][D][L]) at
+                         // csave + n * csave_stride, the last order's being the only output (y unused)
+  int64_t csave_stride;
+  const float* vc;       // four-step, one order: the input is xv * vc (xv = v in the I/O dtype, vc fp32)
 };
 
 struct SpectrumArgs {
@@ -102,7 +106,7 @@ hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 // workspace buffers (saved c_n, z, g, two temporaries, the per-row spectra
 // and the four-step intermediate).
 struct LongBackwardLayout {
-  int64_t c, z, t1, t2, sg, work, total;
+  int64_t c, t1, t2, sg, work, total;
   int rows_per_group;
 };
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD);
