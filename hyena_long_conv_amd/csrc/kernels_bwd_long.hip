@@ -126,6 +126,19 @@ __global__ void k_bw_store_rev(const float* __restrict__ a, void* __restrict__ o
   }
 }
 
+// out = a in the I/O dtype (the final gradient of v, held in natural order)
+template <int IOT, bool V4>
+__global__ void k_bw_store(const float* __restrict__ a, void* __restrict__ out, int64_t rows, int64_t L) {
+  if constexpr (V4) {
+    ROW_LOOP4(rows, L) {
+      const float4 w = ld_f4(a + r * L + t);
+      st4_io<IOT>(out, r * L + t, w.x, w.y, w.z, w.w);
+    }
+  } else {
+    ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + t]);
+  }
+}
+
 // gh[d][k] = sum_b t[b*D + d][L-1-k]  (fixed batch order: deterministic)
 template <bool V4, bool CIRC = false>
 __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restrict__ gh, int B, int D, int64_t L) {
@@ -175,13 +188,16 @@ hipError_t bw_step_io(bool rev, const void* g, const float* c, const void* x, vo
 // row) instead of z, which then goes unread; filters per channel only.
 // zio: dtype of z (0 fp32, 1 bf16); the intermediate and out are fp32.
 // zc: the rows are z * zc (zc fp32), formed in the first column pass.
+// rev_c >= 0 (with zspec): the output row reversed, t -> (rev_c - t) mod M.
 hipError_t bw_conv(const PlanInfo& p, const void* spec, const void* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
-                   const void* zspec = nullptr, int zio = 0, const float* zc = nullptr) {
+                   const void* zspec = nullptr, int zio = 0, const float* zc = nullptr, int64_t rev_c = -1) {
   ForwardArgs f{};
   f.v = z;
   f.spec_in = zspec;
   f.vc = zc;
+  f.rev_out = rev_c >= 0;
+  f.rev_c = rev_c;
   f.no_gate = 1;
   f.spec = spec;
   f.y = out;
@@ -227,22 +243,33 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     f.rows_per_group = w.rows_per_group; f.no_gate = 1; f.csave = C; f.csave_stride = cstride;
     BW_TRY(fourstep_forward(f, p, s));
   }
-  // backward, g = dloss/dz_{n+1}: the first step reads dloss/dy itself; after
-  // each adjoint convolution g is left reversed in T1 and read through the
-  // reversal by the next step
+  // backward, g = dloss/dz_{n+1}; the first step reads dloss/dy itself.
+  // Power-of-two columns (fused): the spectrum pass forms g * x_n and stores
+  // gx_n = g * c_n itself, the reversal R enters as the spectral map
+  // X(k) -> W_M^(c k) conj X(k) (c = L - 1; periodic rows c = 0), and g stays
+  // in natural order in T1.  Otherwise an elementwise step writes gx_n and
+  // T2 = R(g * x_n), and each adjoint leaves g reversed in T1, read through
+  // the reversal by the next step.
+  const bool fused = fourstep_fused_spec_ok(p);
+  const int64_t rev_c = circ ? 0 : L - 1;
   const void* gcur = a.gy;
   bool grev = false;
   for (int nn = a.NORD - 1; nn >= 0; --nn) {
     const float* Cn = C + nn * cstride;
-    // gx_n = g * c_n, T2 = R(g * x_n)
-    BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s)
-                     : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
-    // filter gradient: spectra of the rows of T2, then (T2 conv z_n) reversed
-    // and summed over the batch; z_1 = v, z_n = x_{n-1} * c_{n-1} formed by
-    // the convolution's first column pass
+    // filter gradient: spectra of the rows of T2 = R(g * x_n), then (T2 conv
+    // z_n) reversed and summed over the batch; z_1 = v, z_n = x_{n-1} * c_{n-1}
+    // formed by the convolution's first column pass
     SpectrumArgs sa{};
     sa.h = T2; sa.spec = sg; sa.NF = (int)R; sa.L = L; sa.spec_stride = p.spec_stride;
     sa.work = work; sa.rows_per_group = w.rows_per_group; sa.circular = 0;
+    if (fused) {
+      sa.g = gcur; sa.g_f32 = nn != a.NORD - 1; sa.c = Cn; sa.x = a.x.p[nn]; sa.gx = a.gx.p[nn]; sa.io = a.io;
+      sa.rev = 1; sa.rev_c = rev_c;
+    } else {
+      // gx_n = g * c_n, T2 = R(g * x_n)
+      BW_TRY(a.io == 0 ? bw_step_io<0>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s)
+                       : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
+    }
     BW_TRY(fourstep_spectrum(sa, p, s));
     if (nn == 0)
       BW_TRY(bw_conv(p, sg, a.v, T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io));
@@ -259,14 +286,25 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
       hipLaunchKernelGGL(k_bw_batch_sum_rev<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
                          a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
     BW_TRY(hipGetLastError());
-    // adjoint: g_n = R(h_n conv T2); kept reversed in T1.  T2's spectra are
-    // already in sg, so this convolution starts at its row pass.
-    BW_TRY(bw_conv(p, spec_n(nn), T2, T1, (int)B, (int)D, false, work, w.rows_per_group, s, sg));
+    // adjoint: g_n = R(h_n conv T2).  T2's spectra are already in sg, so this
+    // convolution starts at its row pass; fused, it returns g_n itself (into gv
+    // directly for the last step with fp32 I/O), else R(g_n)
+    float* gout = (fused && nn == 0 && a.io == 0) ? static_cast<float*>(a.gv) : T1;
+    BW_TRY(bw_conv(p, spec_n(nn), T2, gout, (int)B, (int)D, false, work, w.rows_per_group, s, sg, 0, nullptr,
+                   fused ? rev_c : -1));
     gcur = T1;
-    grev = true;
+    grev = !fused;
   }
-  // (every order ran an adjoint, so g is the fp32 row buffer T1, reversed)
+  // (every order ran an adjoint, so g is the fp32 row buffer T1)
   const float* gfin = T1;
+  if (fused) {
+    if (a.io == 1) {
+      if (L % 4 == 0) hipLaunchKernelGGL((k_bw_store<1, true>), row_grid(R, L / 4), dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
+      else hipLaunchKernelGGL((k_bw_store<1, false>), row_grid(R, L), dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);
+    }
+    BW_TRY(hipGetLastError());
+    return hipSuccess;
+  }
   const dim3 rg = row_grid(R, L % 4 == 0 && !circ ? L / 4 : L);
   if (circ) {
     if (a.io == 0) hipLaunchKernelGGL((k_bw_store_rev<0, false, true>), rg, dim3(EW_THREADS), 0, s, gfin, a.gv, R, L);

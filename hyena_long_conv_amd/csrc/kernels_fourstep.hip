@@ -69,11 +69,13 @@ template <int N1, bool GRID = false> struct ColCfg {
 };
 
 // Points per thread of the row pass: HYENA_ROW_E (16), except rows of up
-// to 1024 points with a bf16 intermediate: HYENA_ROW_E_BF16 (8).  Those
+// to 1024 points: HYENA_ROW_E_BF16 (8).  With a bf16 intermediate those
 // passes move half the bytes and are bound by VALU issue; at 8 points per
 // thread they ran 2% faster on the 64K and 1% on the 128K bf16 shapes, but
 // 4% slower with 2048-point rows (L = 100000) and, with an fp32
-// intermediate, 4% slower on the 1M shape.
+// intermediate, 4% slower on the 1M shape (2048-point rows).  fp32 rows of
+// up to 1024 points (HYENA_ROW_E8_F32) take 8 as well: the order-3 128K
+// forward 2.7% and the 64K backward 2.2% faster.
 #ifndef HYENA_ROW_E
 #define HYENA_ROW_E 16
 #endif
@@ -82,7 +84,7 @@ template <int N1, bool GRID = false> struct ColCfg {
 #endif
 
 #ifndef HYENA_ROW_E8_F32
-#define HYENA_ROW_E8_F32 0
+#define HYENA_ROW_E8_F32 1
 #endif
 template <int N2, bool WB = false> struct RowCfg {
   static constexpr int E = ((WB || HYENA_ROW_E8_F32) && N2 <= 1024) ? HYENA_ROW_E_BF16 : HYENA_ROW_E;
@@ -149,11 +151,15 @@ __device__ __forceinline__ cf ld_spec(const cf* p) {
 // COL_OUT: as COL_LAST without the gate (the plain causal convolution).
 // COL_MIDSAVE: as COL_MID, and the ungated convolution is stored too (fp32,
 // to y).  COL_FIRSTG: as COL_FIRST with the input formed as x * c (x = xg
-// in the activation type, c = v in fp32).  Both serve the backward.
+// in the activation type, c = v in fp32).  COL_SPECG / COL_SPECGF: a
+// spectrum's first pass whose rows are g * x (g = v in the activation type /
+// in fp32, x = xg), also storing g * c to y (c = h, fp32; y in the
+// activation type).  These serve the backward.
 // ROW_SMUL: the row pass of a convolution whose input rows are given by
 // their spectra (the ROW_SPEC layout) instead of a column-transformed
 // intermediate; no column pass precedes it.
-enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4, COL_MIDSAVE = 5, COL_FIRSTG = 6 };
+enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4, COL_MIDSAVE = 5, COL_FIRSTG = 6,
+       COL_SPECG = 7, COL_SPECGF = 8 };
 enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2 };
 
 struct ColArgs {
@@ -273,6 +279,24 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
         u[i] = make_float2(
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc),
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm + 1, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc));
+    }
+  } else if constexpr (KIND == COL_SPECG || KIND == COL_SPECGF) {
+    // all loads of the column first, then the stores of g * c
+    constexpr int GT = KIND == COL_SPECGF ? 0 : io_of(IOT);
+    cf gc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      int64_t ro, t, len;
+      at(j + i * S1, ro, t, len);
+      const cf gv = ld_pair<GT, EVEN, true>(a.v, ro, t, len), cv = ld_pair<0, EVEN, true>(a.h, ro, t, len);
+      const cf xv = act(a.xg, j + i * S1);
+      gc[i] = make_float2(gv.x * cv.x, gv.y * cv.y);
+      u[i] = make_float2(gv.x * xv.x, gv.y * xv.y);
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      int64_t ro, t, len;
+      if (at(j + i * S1, ro, t, len)) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, gc[i]);
     }
   } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
@@ -594,6 +618,21 @@ struct RowArgs {
   int n_units;         // channel-major launch: (channel, row pair) units; the grid is padded to a multiple of 8
   int wb;              // CONV: the intermediate holds bf16 pairs (bf16 activations)
   const cf* spec_in;   // SMUL: spectra of the input rows, one per activation row (ROW_SPEC layout)
+  int rev;             // SPEC: spectrum of the row reversal t -> (rev_c - t) mod 2N; SMUL: output reversed so
+  int64_t rev_c;
+};
+
+// W_{2N}^(c k) for the thread's bins k = k1 + n1 (j + i S2), i < E: the
+// spectrum of a row reversal t -> (c - t) mod 2N is W^(c k) conj X(k).
+template <int E>
+struct RevTwiddle {
+  cf b, st;
+  __device__ __forceinline__ RevTwiddle(int64_t c, int k1, int n1, int j, int S2, uint32_t M) {
+    const uint64_t kb = (uint64_t)k1 + (uint64_t)n1 * (uint64_t)j, ks = (uint64_t)n1 * (uint64_t)S2;
+    b = twiddle<false>((uint32_t)(((uint64_t)c * kb) % M), M);
+    st = twiddle<false>((uint32_t)(((uint64_t)c * ks) % M), M);
+  }
+  __device__ __forceinline__ cf apply(cf v, int i) const { return cmul(step_power<E>(b, st, i), cconj(v)); }
 };
 
 // LDS of the row pass.  HYENA_ROW_SW: 0 plain addressing; 1 XOR-swizzled
@@ -697,6 +736,12 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     }
     cf yn = make_float2(0.f, 0.f);
     if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
+    if (a.rev) {   // the reversed output row: Y'(k) = W^(c k) conj Y(k), Y'(N) = (-1)^c conj Y(N)
+      const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
+#pragma unroll
+      for (int i = 0; i < E; ++i) u[i] = rt.apply(u[i], i);
+      yn = cscale(cconj(yn), a.rev_c & 1 ? -1.f : 1.f);
+    }
 #pragma unroll
     for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
     __syncthreads();
@@ -723,13 +768,26 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     cf* out = a.spec_out + (int64_t)(a.r0 + g) * a.spec_stride;
     const float sc = 1.0f / (float)(2 * N);
     if (live) {
+      if (a.rev) {
+        const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int k2 = j + i * S2;
-        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-        const cf am = ldsm(k2m);
-        out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc);
-        if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
+        for (int i = 0; i < E; ++i) {
+          const int k2 = j + i * S2;
+          const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+          const cf am = ldsm(k2m);
+          out[(int64_t)k1 * N2 + k2] = rt.apply(realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc), i);
+          if (k1 == 0 && k2 == 0)   // Nyquist bin, W^(c N) = (-1)^c
+            out[N] = make_float2((a.rev_c & 1 ? -1.f : 1.f) * (u[i].x - u[i].y) * sc, 0.f);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int k2 = j + i * S2;
+          const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+          const cf am = ldsm(k2m);
+          out[(int64_t)k1 * N2 + k2] = realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc);
+          if (k1 == 0 && k2 == 0) out[N] = make_float2((u[i].x - u[i].y) * sc, 0.f);   // Nyquist bin
+        }
       }
     }
   } else {
@@ -783,6 +841,13 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
     hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
   } else if (kind == COL_OUT) {
     if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+  } else if (kind == COL_SPECG || kind == COL_SPECGF) {
+    if constexpr (!GRID) {
+      if (kind == COL_SPECGF && io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_SPECGF, EVEN, false>), grid, block, 0, s, c);
+      else if (kind == COL_SPECGF) hipLaunchKernelGGL((k_col<N1, 1, COL_SPECGF, EVEN, false>), grid, block, 0, s, c);
+      else if (io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_SPECG, EVEN, false>), grid, block, 0, s, c);
+      else hipLaunchKernelGGL((k_col<N1, 1, COL_SPECG, EVEN, false>), grid, block, 0, s, c);
+    }
   } else if (kind == COL_MIDSAVE || kind == COL_FIRSTG) {
     if constexpr (!GRID) {
       if (kind == COL_MIDSAVE && io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_MIDSAVE, EVEN, false>), grid, block, 0, s, c);
@@ -974,6 +1039,8 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   const bool smul = a.spec_in != nullptr;
   if (smul && (a.NORD != 1 || !a.no_gate || cio != 0)) return hipErrorInvalidValue;
   r.spec_in = static_cast<const cf*>(a.spec_in);
+  r.rev = smul && a.rev_out;
+  r.rev_c = a.rev_c;
   // csave: c_n of every order kept (fp32); vc: input rows x * c formed in the
   // first column pass
   const bool save = a.csave != nullptr;
@@ -1011,10 +1078,16 @@ hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream
   RowArgs r{};
   r.work = (cf*)a.work; r.spec_out = (cf*)a.spec; r.n1 = p.n1; r.spec_stride = a.spec_stride;
   r.n_row_pairs = (p.n1 + 1) / 2;
+  r.rev = a.rev; r.rev_c = a.rev_c;
+  // rows g * x formed in the column pass (power-of-two columns only)
+  const bool fused = a.g != nullptr;
+  if (fused && !fourstep_fused_spec_ok(p)) return hipErrorInvalidValue;
+  const int kind = fused ? (a.g_f32 ? COL_SPECGF : COL_SPECG) : COL_SPEC;
+  if (fused) { c.v = a.g; c.h = a.c; c.xg = a.x; c.y = a.gx; }
   for (int r0 = 0; r0 < a.NF; r0 += a.rows_per_group) {
     const int groups = (a.NF - r0 < a.rows_per_group) ? a.NF - r0 : a.rows_per_group;
     c.r0 = r0; r.r0 = r0;
-    hipError_t e = dispatch_col(p.n1, COL_SPEC, 0, c, groups, s);
+    hipError_t e = dispatch_col(p.n1, kind, fused ? a.io : 0, c, groups, s);
     if (e != hipSuccess) return e;
     e = dispatch_row(p.n2, ROW_SPEC, r, groups, s);
     if (e != hipSuccess) return e;

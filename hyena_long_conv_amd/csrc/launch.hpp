@@ -29,6 +29,8 @@ struct ForwardArgs {
                          // csave + n * csave_stride, the last order's being the only output (y unused)
   int64_t csave_stride;
   const float* vc;       // four-step, one order: the input is xv * vc (xv = v in the I/O dtype, vc fp32)
+  int rev_out;           // with spec_in: the output row reversed, t -> (rev_c - t) mod M
+  int64_t rev_c;
 };
 
 struct SpectrumArgs {
@@ -40,6 +42,18 @@ struct SpectrumArgs {
   void* work;
   int rows_per_group;
   int circular;
+  // four-step, backward: rows h = g * x formed in the column pass, which also
+  // stores gx = g * c (g: the I/O dtype, or fp32 with g_f32; c fp32; x, gx
+  // the I/O dtype io); used when g is set
+  const void* g;
+  const float* c;
+  const void* x;
+  void* gx;
+  int g_f32, io;
+  // rev: the spectrum of the reversed row t -> (rev_c - t) mod M instead,
+  // i.e. bins W_M^(rev_c k) conj X(k)
+  int rev;
+  int64_t rev_c;
 };
 
 struct FilterGenArgs {
@@ -156,6 +170,8 @@ hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);
 hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s);
+// The fused spectrum pass (SpectrumArgs.g) exists for power-of-two column lengths.
+inline bool fourstep_fused_spec_ok(const PlanInfo& p) { return p.n1 >= 16 && (p.n1 & (p.n1 - 1)) == 0; }
 hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s);
 hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s);
 hipError_t spectrum_to_fourstep(const void* spec, int NF, const PlanInfo& single, const PlanInfo& fs, void* out,
