@@ -139,6 +139,27 @@ __global__ void k_bw_store(const float* __restrict__ a, void* __restrict__ out, 
   }
 }
 
+// gh[d][k] = sum_b t[b*D + d][k]  (fixed batch order: deterministic)
+template <bool V4>
+__global__ void k_bw_batch_sum(const float* __restrict__ tt, float* __restrict__ gh, int B, int D, int64_t L) {
+  if constexpr (V4) {
+    ROW_LOOP4(D, L) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int b = 0; b < B; ++b) {
+        const float4 w = ld_f4(tt + ((int64_t)b * D + r) * L + t);
+        acc.x += w.x; acc.y += w.y; acc.z += w.z; acc.w += w.w;
+      }
+      st_f4(gh + r * L + t, acc.x, acc.y, acc.z, acc.w);
+    }
+  } else {
+    ROW_LOOP(D, L) {
+      float acc = 0.f;
+      for (int b = 0; b < B; ++b) acc += tt[((int64_t)b * D + r) * L + t];
+      gh[r * L + t] = acc;
+    }
+  }
+}
+
 // gh[d][k] = sum_b t[b*D + d][L-1-k]  (fixed batch order: deterministic)
 template <bool V4, bool CIRC = false>
 __global__ void k_bw_batch_sum_rev(const float* __restrict__ tt, float* __restrict__ gh, int B, int D, int64_t L) {
@@ -188,7 +209,7 @@ hipError_t bw_step_io(bool rev, const void* g, const float* c, const void* x, vo
 // row) instead of z, which then goes unread; filters per channel only.
 // zio: dtype of z (0 fp32, 1 bf16); the intermediate and out are fp32.
 // zc: the rows are z * zc (zc fp32), formed in the first column pass.
-// rev_c >= 0 (with zspec): the output row reversed, t -> (rev_c - t) mod M.
+// rev_c >= 0: the output row reversed, t -> (rev_c - t) mod M.
 hipError_t bw_conv(const PlanInfo& p, const void* spec, const void* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
                    const void* zspec = nullptr, int zio = 0, const float* zc = nullptr, int64_t rev_c = -1) {
@@ -271,20 +292,29 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
                        : bw_step_io<1>(grev, gcur, Cn, a.x.p[nn], a.gx.p[nn], T2, L, n, circ, s));
     }
     BW_TRY(fourstep_spectrum(sa, p, s));
+    // (fused: the convolution returns the reversed row itself, for B = 1
+    // straight into gh)
+    float* gh_n = a.gh + (int64_t)nn * D * L;
+    float* fout = (fused && B == 1) ? gh_n : T1;
+    const int64_t frev = fused ? rev_c : -1;
     if (nn == 0)
-      BW_TRY(bw_conv(p, sg, a.v, T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io));
+      BW_TRY(bw_conv(p, sg, a.v, fout, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io, nullptr, frev));
     else
-      BW_TRY(bw_conv(p, sg, a.x.p[nn - 1], T1, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io,
-                     C + (nn - 1) * cstride));
-    if (circ)
-      hipLaunchKernelGGL((k_bw_batch_sum_rev<false, true>), row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
-                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
-    else if (L % 4 == 0)
-      hipLaunchKernelGGL(k_bw_batch_sum_rev<true>, row_grid(D, L / 4), dim3(EW_THREADS), 0, s, T1,
-                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
-    else
-      hipLaunchKernelGGL(k_bw_batch_sum_rev<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1,
-                         a.gh + (int64_t)nn * D * L, (int)B, (int)D, L);
+      BW_TRY(bw_conv(p, sg, a.x.p[nn - 1], fout, (int)B, (int)D, true, work, w.rows_per_group, s, nullptr, a.io,
+                     C + (nn - 1) * cstride, frev));
+    if (fused) {
+      if (B > 1) {
+        if (L % 4 == 0) hipLaunchKernelGGL(k_bw_batch_sum<true>, row_grid(D, L / 4), dim3(EW_THREADS), 0, s, T1, gh_n, (int)B, (int)D, L);
+        else hipLaunchKernelGGL(k_bw_batch_sum<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1, gh_n, (int)B, (int)D, L);
+      }
+    } else if (circ) {
+      hipLaunchKernelGGL((k_bw_batch_sum_rev<false, true>), row_grid(D, L), dim3(EW_THREADS), 0, s, T1, gh_n,
+                         (int)B, (int)D, L);
+    } else if (L % 4 == 0) {
+      hipLaunchKernelGGL(k_bw_batch_sum_rev<true>, row_grid(D, L / 4), dim3(EW_THREADS), 0, s, T1, gh_n, (int)B, (int)D, L);
+    } else {
+      hipLaunchKernelGGL(k_bw_batch_sum_rev<false>, row_grid(D, L), dim3(EW_THREADS), 0, s, T1, gh_n, (int)B, (int)D, L);
+    }
     BW_TRY(hipGetLastError());
     // adjoint: g_n = R(h_n conv T2).  T2's spectra are already in sg, so this
     // convolution starts at its row pass; fused, it returns g_n itself (into gv

@@ -160,7 +160,9 @@ __device__ __forceinline__ cf ld_spec(const cf* p) {
 // intermediate; no column pass precedes it.
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4, COL_MIDSAVE = 5, COL_FIRSTG = 6,
        COL_SPECG = 7, COL_SPECGF = 8 };
-enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2 };
+// ROW_CONVREV: ROW_CONV (float2 intermediate) whose output row is reversed,
+// t -> (rev_c - t) mod 2N, by the spectral map of RevTwiddle.
+enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2, ROW_CONVREV = 3 };
 
 struct ColArgs {
   const void* v;       // FIRST: z_1 rows
@@ -715,27 +717,44 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
   // W_{2N}^k = W_{2N}^{k1 + n1 j} * W_{2E}^i
   const cf wk = twiddle<false>((uint32_t)k1 + (uint32_t)n1 * (uint32_t)j, 2 * N);
 
-  if constexpr (KIND == ROW_SMUL) {
-    // The input row's real-FFT bins X(k) are given as S(k) = X(k)/(2N), the
-    // filter's as G(k) = H(k)/(2N).  With Y = X H / (2N) = 2N S G, the
+  if constexpr (KIND == ROW_SMUL || KIND == ROW_CONVREV) {
+    // The input row's real-FFT bins X(k) are given as S(k) = X(k)/(2N)
+    // (SMUL), or formed from the row FFT as ROW_SPEC does (CONVREV); the
+    // filter's as G(k) = H(k)/(2N).  With Y = X H / (2N) = X G, the
     // half-length bins whose unnormalised inverse DFT is y[2m] + i y[2m+1]
     // are C'(k) = Y(k) (1 + i conj W) + conj Y(N-k) (1 - i conj W),
     // W = W_{2N}^k -- the even/odd re-packing that realconv_pair folds into
     // its product.  Y(N-k) comes from the thread holding bin N-k (mirror row,
-    // through LDS); Y(N), the partner of bin 0, is loaded directly.
-    static_assert(!WB, "spectral-input rows use a float2 intermediate");
-    const int arow = launch_row_of(a.r0, g, a.cmB, a.D);
+    // through LDS); Y(N), the partner of bin 0, is formed by that thread.
+    static_assert(!WB, "these row passes use a float2 intermediate");
     const int d = (a.cmB > 1) ? a.r0 + g / a.cmB : (a.r0 + g) % a.D;
-    const cf* xs = a.spec_in + (int64_t)arow * a.spec_stride;
     const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
-    const float sc = 2.0f * (float)N;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const int64_t k = (int64_t)k1 * N2 + j + i * S2;
-      u[i] = cscale(cmul(ld_spec(xs + k), ld_spec(gs + k)), sc);
-    }
     cf yn = make_float2(0.f, 0.f);
-    if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
+    if constexpr (KIND == ROW_SMUL) {
+      const int arow = launch_row_of(a.r0, g, a.cmB, a.D);
+      const cf* xs = a.spec_in + (int64_t)arow * a.spec_stride;
+      const float sc = 2.0f * (float)N;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int64_t k = (int64_t)k1 * N2 + j + i * S2;
+        u[i] = cscale(cmul(ld_spec(xs + k), ld_spec(gs + k)), sc);
+      }
+      if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
+    } else {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
+      __syncthreads();
+      if (k1 == 0 && j == 0) yn = cscale(ld_spec(gs + N), u[0].x - u[0].y);   // X(N) G(N)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int k2 = j + i * S2;
+        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
+        const cf am = ldsm(k2m);
+        u[i] = cmul(realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), 1.0f), ld_spec(gs + (int64_t)k1 * N2 + k2));
+      }
+      __syncthreads();
+    }
     if (a.rev) {   // the reversed output row: Y'(k) = W^(c k) conj Y(k), Y'(N) = (-1)^c conj Y(N)
       const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
 #pragma unroll
@@ -994,6 +1013,7 @@ static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t
   const dim3 grid(blocks);
   if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   else if (kind == ROW_SMUL) hipLaunchKernelGGL((k_row<N2, ROW_SMUL>), grid, dim3(RowCfg<N2>::T), 0, s, r);
+  else if (kind == ROW_CONVREV) hipLaunchKernelGGL((k_row<N2, ROW_CONVREV>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, dim3(RowCfg<N2, true>::T), 0, s, r);
   else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   return hipGetLastError();
@@ -1039,8 +1059,11 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   const bool smul = a.spec_in != nullptr;
   if (smul && (a.NORD != 1 || !a.no_gate || cio != 0)) return hipErrorInvalidValue;
   r.spec_in = static_cast<const cf*>(a.spec_in);
-  r.rev = smul && a.rev_out;
+  // rev_out: the output row reversed (one order, no gate, float2 intermediate)
+  if (a.rev_out && (a.NORD != 1 || !a.no_gate || cio == 2)) return hipErrorInvalidValue;
+  r.rev = a.rev_out;
   r.rev_c = a.rev_c;
+  const int rkind = smul ? ROW_SMUL : (a.rev_out ? ROW_CONVREV : ROW_CONV);
   // csave: c_n of every order kept (fp32); vc: input rows x * c formed in the
   // first column pass
   const bool save = a.csave != nullptr;
@@ -1057,7 +1080,7 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
     if (e != hipSuccess) return e;
     for (int n = 0; n < a.NORD; ++n) {
       r.order = n;
-      e = dispatch_row(p.n2, smul ? ROW_SMUL : ROW_CONV, r, groups, s);
+      e = dispatch_row(p.n2, rkind, r, groups, s);
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
       if (save) c.y = a.csave + n * a.csave_stride;
