@@ -154,15 +154,14 @@ __device__ __forceinline__ cf ld_spec(const cf* p) {
 // in the activation type, c = v in fp32).  COL_SPECG / COL_SPECGF: a
 // spectrum's first pass whose rows are g * x (g = v in the activation type /
 // in fp32, x = xg), also storing g * c to y (c = h, fp32; y in the
-// activation type).  These serve the backward.
+// activation type).  COL_OUTREV: as COL_OUT, the row stored reversed,
+// t -> (rev_c - t) mod L.  These serve the backward.
 // ROW_SMUL: the row pass of a convolution whose input rows are given by
 // their spectra (the ROW_SPEC layout) instead of a column-transformed
 // intermediate; no column pass precedes it.
 enum { COL_FIRST = 0, COL_MID = 1, COL_LAST = 2, COL_SPEC = 3, COL_OUT = 4, COL_MIDSAVE = 5, COL_FIRSTG = 6,
-       COL_SPECG = 7, COL_SPECGF = 8 };
-// ROW_CONVREV: ROW_CONV (float2 intermediate) whose output row is reversed,
-// t -> (rev_c - t) mod 2N, by the spectral map of RevTwiddle.
-enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2, ROW_CONVREV = 3 };
+       COL_SPECG = 7, COL_SPECGF = 8, COL_OUTREV = 9 };
+enum { ROW_CONV = 0, ROW_SPEC = 1, ROW_SMUL = 2 };
 
 struct ColArgs {
   const void* v;       // FIRST: z_1 rows
@@ -180,6 +179,7 @@ struct ColArgs {
   int gNLs;            // log2 NL
   int gcirc;           // SPEC: kernel of the grid's shape (else extent 2L-1 per axis)
   int cmB, cmD;        // > 1: channel-major launch, see launch_row_of
+  int64_t rev_c;       // OUTREV: position t is stored at (rev_c - t) mod L
 };
 
 // Activation row (b*D + d) of the launch's local row g.  Natural launches
@@ -221,6 +221,7 @@ constexpr int io_of(int iot) { return iot == 2 ? 1 : iot; }
 template <int N1, int IOT, int KIND, bool EVEN, bool GRID = false>
 __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1, GRID>;
+  constexpr bool OUTK = KIND == COL_OUT || KIND == COL_OUTREV;   // ungated output passes
   constexpr int E = C::E, W = C::W, S1 = N1 / E;
   __shared__ cf smem[C::LDS ? N1 * W : 1];
   const int c = threadIdx.x % W, j = threadIdx.x / W;
@@ -325,7 +326,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
         u[i] = ld_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + colc);
       }
     }
-    constexpr int PFX = KIND == COL_OUT ? 0 : C::PFX;
+    constexpr int PFX = OUTK ? 0 : C::PFX;
     cf xp[PFX > 0 ? PFX : 1];
     // (the column's second half holds samples only on circular rows)
 #pragma unroll
@@ -337,7 +338,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
     // bf16 gates of the first half of the column (on a zero-padded row the
     // only points that hold samples) requested before the inverse FFT too,
     // kept packed: one register per point.
-    constexpr int PFB = (KIND == COL_OUT || PFX > 0 || GRID || io_of(IOT) != 1 || !HYENA_COL_PFB) ? 0 : E / 2;
+    constexpr int PFB = (OUTK || PFX > 0 || GRID || io_of(IOT) != 1 || !HYENA_COL_PFB) ? 0 : E / 2;
     uint32_t xb[PFB > 0 ? PFB : 1];
 #pragma unroll
     for (int i = 0; i < PFB; ++i) {
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
     fft.template run<true>(u, lds, j);
     // the other gates (not GRID): requested together, then pinned; points of
     // the column's second half hold samples only on circular rows
-    constexpr int G0 = (GRID || KIND == COL_OUT) ? E : (PFX > PFB ? PFX : PFB);
+    constexpr int G0 = (GRID || OUTK) ? E : (PFX > PFB ? PFX : PFB);
     RawPair<io_of(IOT)> xl[G0 < E ? E - G0 : 1];
     if constexpr (G0 < E) {
       const auto ld_gate = [&](int i) {
@@ -388,7 +389,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
         if constexpr (KIND == COL_MIDSAVE) {
           if (ok) st_pair<0, EVEN>(a.y, ro, t, len, z);
         }
-        if constexpr (KIND != COL_OUT) {
+        if constexpr (!OUTK) {
           const cf xv = i < PFX   ? xp[i < PFX ? i : 0]
                         : i < PFB ? bf16_pair_cf(xb[i < PFB ? i : 0])
                                   : unpack(xl[i >= G0 && i - G0 < E ? i - G0 : 0]);
@@ -397,11 +398,20 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
         if constexpr (KIND == COL_LAST || KIND == COL_OUT) {
           if (ok) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
         }
+        if constexpr (KIND == COL_OUTREV) {   // fp32 rows, t -> (rev_c - t) mod L
+          if (ok) {
+            int64_t q0 = a.rev_c - t, q1 = q0 - 1;
+            if (q0 < 0) q0 += len;
+            if (q1 < 0) q1 += len;
+            if (t < len) IO<0>::st(a.y, ro + q0, z.x);
+            if (t + 1 < len) IO<0>::st(a.y, ro + q1, z.y);
+          }
+        }
       }
       u[i] = z;
     }
   }
-  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
+  if constexpr (KIND != COL_LAST && !OUTK) {
     fft.template run<false>(u, lds, j);
     if (valid) {
 #pragma unroll
@@ -717,44 +727,27 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
   // W_{2N}^k = W_{2N}^{k1 + n1 j} * W_{2E}^i
   const cf wk = twiddle<false>((uint32_t)k1 + (uint32_t)n1 * (uint32_t)j, 2 * N);
 
-  if constexpr (KIND == ROW_SMUL || KIND == ROW_CONVREV) {
-    // The input row's real-FFT bins X(k) are given as S(k) = X(k)/(2N)
-    // (SMUL), or formed from the row FFT as ROW_SPEC does (CONVREV); the
-    // filter's as G(k) = H(k)/(2N).  With Y = X H / (2N) = X G, the
+  if constexpr (KIND == ROW_SMUL) {
+    // The input row's real-FFT bins X(k) are given as S(k) = X(k)/(2N), the
+    // filter's as G(k) = H(k)/(2N).  With Y = X H / (2N) = 2N S G, the
     // half-length bins whose unnormalised inverse DFT is y[2m] + i y[2m+1]
     // are C'(k) = Y(k) (1 + i conj W) + conj Y(N-k) (1 - i conj W),
     // W = W_{2N}^k -- the even/odd re-packing that realconv_pair folds into
     // its product.  Y(N-k) comes from the thread holding bin N-k (mirror row,
-    // through LDS); Y(N), the partner of bin 0, is formed by that thread.
-    static_assert(!WB, "these row passes use a float2 intermediate");
+    // through LDS); Y(N), the partner of bin 0, is loaded directly.
+    static_assert(!WB, "spectral-input rows use a float2 intermediate");
+    const int arow = launch_row_of(a.r0, g, a.cmB, a.D);
     const int d = (a.cmB > 1) ? a.r0 + g / a.cmB : (a.r0 + g) % a.D;
+    const cf* xs = a.spec_in + (int64_t)arow * a.spec_stride;
     const cf* gs = a.spec + (int64_t)(a.order * a.D + d) * a.spec_stride;
-    cf yn = make_float2(0.f, 0.f);
-    if constexpr (KIND == ROW_SMUL) {
-      const int arow = launch_row_of(a.r0, g, a.cmB, a.D);
-      const cf* xs = a.spec_in + (int64_t)arow * a.spec_stride;
-      const float sc = 2.0f * (float)N;
+    const float sc = 2.0f * (float)N;
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int64_t k = (int64_t)k1 * N2 + j + i * S2;
-        u[i] = cscale(cmul(ld_spec(xs + k), ld_spec(gs + k)), sc);
-      }
-      if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
-    } else {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < E; ++i) lds(j + i * S2) = u[i];
-      __syncthreads();
-      if (k1 == 0 && j == 0) yn = cscale(ld_spec(gs + N), u[0].x - u[0].y);   // X(N) G(N)
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int k2 = j + i * S2;
-        const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
-        const cf am = ldsm(k2m);
-        u[i] = cmul(realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), 1.0f), ld_spec(gs + (int64_t)k1 * N2 + k2));
-      }
-      __syncthreads();
+    for (int i = 0; i < E; ++i) {
+      const int64_t k = (int64_t)k1 * N2 + j + i * S2;
+      u[i] = cscale(cmul(ld_spec(xs + k), ld_spec(gs + k)), sc);
     }
+    cf yn = make_float2(0.f, 0.f);
+    if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
     if (a.rev) {   // the reversed output row: Y'(k) = W^(c k) conj Y(k), Y'(N) = (-1)^c conj Y(N)
       const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
 #pragma unroll
@@ -860,6 +853,8 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
     hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
   } else if (kind == COL_OUT) {
     if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+  } else if (kind == COL_OUTREV) {
+    if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUTREV, EVEN, false>), grid, block, 0, s, c);
   } else if (kind == COL_SPECG || kind == COL_SPECGF) {
     if constexpr (!GRID) {
       if (kind == COL_SPECGF && io == 0) hipLaunchKernelGGL((k_col<N1, 0, COL_SPECGF, EVEN, false>), grid, block, 0, s, c);
@@ -1013,7 +1008,6 @@ static hipError_t launch_row(int kind, const RowArgs& r, int groups, hipStream_t
   const dim3 grid(blocks);
   if (kind == ROW_SPEC) hipLaunchKernelGGL((k_row<N2, ROW_SPEC>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   else if (kind == ROW_SMUL) hipLaunchKernelGGL((k_row<N2, ROW_SMUL>), grid, dim3(RowCfg<N2>::T), 0, s, r);
-  else if (kind == ROW_CONVREV) hipLaunchKernelGGL((k_row<N2, ROW_CONVREV>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   else if (r.wb) hipLaunchKernelGGL((k_row<N2, ROW_CONV, true>), grid, dim3(RowCfg<N2, true>::T), 0, s, r);
   else hipLaunchKernelGGL((k_row<N2, ROW_CONV, false>), grid, dim3(RowCfg<N2>::T), 0, s, r);
   return hipGetLastError();
@@ -1059,11 +1053,15 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
   const bool smul = a.spec_in != nullptr;
   if (smul && (a.NORD != 1 || !a.no_gate || cio != 0)) return hipErrorInvalidValue;
   r.spec_in = static_cast<const cf*>(a.spec_in);
-  // rev_out: the output row reversed (one order, no gate, float2 intermediate)
+  // rev_out: the output row reversed (one order, no gate, float2 intermediate):
+  // by the spectral map in the row pass from a spectral input, else by the
+  // output column pass's addressing (COL_OUTREV, power-of-two columns)
   if (a.rev_out && (a.NORD != 1 || !a.no_gate || cio == 2)) return hipErrorInvalidValue;
-  r.rev = a.rev_out;
+  if (a.rev_out && !smul && !fourstep_fused_spec_ok(p)) return hipErrorInvalidValue;
+  r.rev = smul && a.rev_out;
   r.rev_c = a.rev_c;
-  const int rkind = smul ? ROW_SMUL : (a.rev_out ? ROW_CONVREV : ROW_CONV);
+  c.rev_c = a.rev_c;
+  const int rkind = smul ? ROW_SMUL : ROW_CONV;
   // csave: c_n of every order kept (fp32); vc: input rows x * c formed in the
   // first column pass
   const bool save = a.csave != nullptr;
@@ -1084,7 +1082,8 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
       if (e != hipSuccess) return e;
       c.xg = a.x.p[n];
       if (save) c.y = a.csave + n * a.csave_stride;
-      const int kind = n < a.NORD - 1 ? (save ? COL_MIDSAVE : COL_MID) : (a.no_gate ? COL_OUT : COL_LAST);
+      const int kind = n < a.NORD - 1 ? (save ? COL_MIDSAVE : COL_MID)
+                                      : (a.no_gate ? (a.rev_out && !smul ? COL_OUTREV : COL_OUT) : COL_LAST);
       e = dispatch_col(p.n1, kind, cio, c, groups, s);
       if (e != hipSuccess) return e;
     }
