@@ -135,9 +135,9 @@ bool sizes_ok(int64_t D, int64_t N, int64_t L) {
 
 namespace hyena {
 
-// Byte offsets of the long backward's workspace buffers: N saved c_n, two
-// temporaries (fp32 rows), the per-row spectra and the four-step
-// intermediate of one pass group.
+// Byte offsets of the long backward's workspace buffers: N saved c_n, one
+// temporary (fp32 rows), the per-row spectra and the four-step intermediate
+// of one pass group.
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD) {
   const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t R = B * D, act = al(R * p.L * 4);
@@ -145,7 +145,6 @@ LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D,
   int64_t o = 0;
   w.c = o;     o += NORD * act;
   w.t1 = o;    o += act;
-  w.t2 = o;    o += act;
   w.sg = o;    o += al(R * p.spec_stride * 8);
   // as many pass groups as the work budget needs, of equal size (plan.hpp)
   w.rows_per_group = rows_per_group(p.N, R);

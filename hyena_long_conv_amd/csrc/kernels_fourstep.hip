@@ -218,6 +218,26 @@ __device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, in
 // intermediate kept as bf16 pairs.
 constexpr int io_of(int iot) { return iot == 2 ? 1 : iot; }
 
+// COL_OUTREV store of the pair at position t (even) of a row of length L:
+// t -> (rev_c - t) mod L.  With L even and rev_c = L - 1 the mirrored pair
+// (L-2-t, L-1-t) is one aligned 8-byte store; otherwise (odd L, periodic
+// rows) two 4-byte stores.
+template <bool EVEN>
+__device__ __forceinline__ void st_pair_rev(void* y, int64_t off, int64_t t, int64_t L, int64_t rev_c, cf z) {
+  if (EVEN && (rev_c & 1) && rev_c == L - 1) {
+    if (t < L) {
+      const f32x2 w = {z.y, z.x};
+      __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(static_cast<float*>(y) + off + (L - 2 - t)));
+    }
+    return;
+  }
+  int64_t q0 = rev_c - t, q1 = q0 - 1;
+  if (q0 < 0) q0 += L;
+  if (q1 < 0) q1 += L;
+  if (t < L) IO<0>::st(y, off + q0, z.x);
+  if (t + 1 < L) IO<0>::st(y, off + q1, z.y);
+}
+
 template <int N1, int IOT, int KIND, bool EVEN, bool GRID = false>
 __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(ColArgs a) {
   using C = ColCfg<N1, GRID>;
@@ -399,13 +419,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
           if (ok) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, z);
         }
         if constexpr (KIND == COL_OUTREV) {   // fp32 rows, t -> (rev_c - t) mod L
-          if (ok) {
-            int64_t q0 = a.rev_c - t, q1 = q0 - 1;
-            if (q0 < 0) q0 += len;
-            if (q1 < 0) q1 += len;
-            if (t < len) IO<0>::st(a.y, ro + q0, z.x);
-            if (t + 1 < len) IO<0>::st(a.y, ro + q1, z.y);
-          }
+          if (ok) st_pair_rev<EVEN>(a.y, ro, t, len, a.rev_c, z);
         }
       }
       u[i] = z;
@@ -443,6 +457,41 @@ __device__ __forceinline__ T* fresh_ptr(T* p) {
   return reinterpret_cast<T*>(v);
 }
 
+// First pass of the backward's fused spectrum (COL_SPECG/F) on one lane's
+// points: u[m] = g x, and g c stored to y, for the pair positions pos(m) of
+// row offset off.  Loads go out in batches of kGateBatch points, pinned
+// before the batch's stores, so a batch stays in flight together.
+template <int NP, int IOT, int KIND, bool EVEN, class Pos>
+__device__ __forceinline__ void specg_points(const ColArgs& a, int64_t off, cf (&u)[NP], Pos pos) {
+  constexpr int GT = KIND == COL_SPECGF ? 0 : io_of(IOT);
+#pragma unroll
+  for (int m0 = 0; m0 < NP; m0 += kGateBatch) {
+    RawPair<GT> gr[kGateBatch];
+    RawPair<0> cr[kGateBatch];
+    RawPair<io_of(IOT)> xr[kGateBatch];
+#pragma unroll
+    for (int k = 0; k < kGateBatch; ++k) {
+      if (m0 + k < NP) {
+        gr[k] = ld_pair_raw<GT, EVEN>(a.v, off, pos(m0 + k), a.L);
+        cr[k] = ld_pair_raw<0, EVEN>(a.h, off, pos(m0 + k), a.L);
+        xr[k] = ld_pair_raw<io_of(IOT), EVEN>(a.xg, off, pos(m0 + k), a.L);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGateBatch; ++k) {
+      if (m0 + k < NP) { pin<GT, true>(gr[k]); pin<0, true>(cr[k]); pin<io_of(IOT), true>(xr[k]); }
+    }
+#pragma unroll
+    for (int k = 0; k < kGateBatch; ++k) {
+      if (m0 + k < NP) {
+        const cf gv = unpack(gr[k]), cv = unpack(cr[k]), xv = unpack(xr[k]);
+        u[m0 + k] = make_float2(gv.x * xv.x, gv.y * xv.y);
+        st_pair<io_of(IOT), EVEN>(a.y, off, pos(m0 + k), a.L, make_float2(gv.x * cv.x, gv.y * cv.y));
+      }
+    }
+  }
+}
+
 template <int N1, int IOT, int KIND, bool EVEN>
 __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   const int g = blockIdx.x / a.n_col_blocks, cb = blockIdx.x - g * a.n_col_blocks;
@@ -453,7 +502,10 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
   work_t<WB>* buf = reinterpret_cast<work_t<WB>*>(a.work) + (int64_t)g * N + col;
   const int64_t off = (int64_t)launch_row_of(a.r0, g, a.cmB, a.cmD) * a.L;
   cf u[N1];
-  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
+  constexpr bool OUTK = KIND == COL_OUT || KIND == COL_OUTREV;   // ungated output passes
+  if constexpr (KIND == COL_SPECG || KIND == COL_SPECGF) {
+    specg_points<N1, IOT, KIND, EVEN>(a, off, u, [&](int i) { return 2 * ((int64_t)a.n2 * i + col); });
+  } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
@@ -474,7 +526,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       const int64_t t = 2 * ((int64_t)a.n2 * i + col);
-      if constexpr (KIND != COL_OUT) {
+      if constexpr (!OUTK) {
         if (i % kGateBatch == 0) {   // the batch's gates requested together, then pinned
 #pragma unroll
           for (int k = i; k < i + kGateBatch && k < N1; ++k)
@@ -485,15 +537,16 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_odd(ColArgs a) {
       }
       cf z = u[i];
       if constexpr (KIND == COL_MIDSAVE) st_pair<0, EVEN>(a.y, off, t, a.L, z);
-      if constexpr (KIND != COL_OUT) {
+      if constexpr (!OUTK) {
         const cf xv = unpack(xl[i]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
       if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, t, a.L, z);
+      if constexpr (KIND == COL_OUTREV) st_pair_rev<EVEN>(a.y, off, t, a.L, a.rev_c, z);
       u[i] = z;
     }
   }
-  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
+  if constexpr (KIND != COL_LAST && !OUTK) {
     RegDft<N1, false>::run(u);
     work_t<WB>* dst = fresh_ptr(buf);
 #pragma unroll
@@ -570,7 +623,10 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
   // time row of point m: lane_a + 2m;  spectrum row of point k: Q*lane_a + k
   const auto trow = [&](int m) { return 2 * ((int64_t)a.n2 * (lane_a + 2 * m) + col); };
   cf u[Q];
-  if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
+  constexpr bool OUTK = KIND == COL_OUT || KIND == COL_OUTREV;   // ungated output passes
+  if constexpr (KIND == COL_SPECG || KIND == COL_SPECGF) {
+    specg_points<Q, IOT, KIND, EVEN>(a, off, u, trow);
+  } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
       if constexpr (KIND == COL_SPEC) {
@@ -590,7 +646,7 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
     RawPair<io_of(IOT)> xl[Q];
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
-      if constexpr (KIND != COL_OUT) {
+      if constexpr (!OUTK) {
         if (m % kGateBatch == 0) {   // the batch's gates requested together, then pinned
 #pragma unroll
           for (int k = m; k < m + kGateBatch && k < Q; ++k) xl[k] = ld_pair_raw<io_of(IOT), EVEN>(a.xg, off, trow(k), a.L);
@@ -600,15 +656,16 @@ __global__ void __launch_bounds__(kColOddThreads) k_col_pair(ColArgs a) {
       }
       cf z = u[m];
       if constexpr (KIND == COL_MIDSAVE) st_pair<0, EVEN>(a.y, off, trow(m), a.L, z);
-      if constexpr (KIND != COL_OUT) {
+      if constexpr (!OUTK) {
         const cf xv = unpack(xl[m]);
         z = make_float2(xv.x * z.x, xv.y * z.y);
       }
       if constexpr (KIND == COL_LAST || KIND == COL_OUT) st_pair<io_of(IOT), EVEN>(a.y, off, trow(m), a.L, z);
+      if constexpr (KIND == COL_OUTREV) st_pair_rev<EVEN>(a.y, off, trow(m), a.L, a.rev_c, z);
       u[m] = z;
     }
   }
-  if constexpr (KIND != COL_LAST && KIND != COL_OUT) {
+  if constexpr (KIND != COL_LAST && !OUTK) {
     pair_dft_fwd<Q>(u, lane_a);
     work_t<WB>* dst = fresh_ptr(buf + (int64_t)Q * lane_a * a.n2);
 #pragma unroll
@@ -887,10 +944,15 @@ static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 blo
 // The kernel of one conv kind at one activation type (IOT as in k_col).
 #define HYENA_COL_KINDS(KERN, P, IOTV, EVENV)                                                        \
   do {                                                                                               \
+    constexpr int IOF = IOTV == 2 ? 0 : IOTV;   /* backward kinds: float2 intermediate */            \
     if (IOTV != 2 && kind == COL_MIDSAVE)                                                            \
-      hipLaunchKernelGGL((KERN<P, (IOTV == 2 ? 0 : IOTV), COL_MIDSAVE, EVENV>), grid, block, 0, s, c); \
+      hipLaunchKernelGGL((KERN<P, IOF, COL_MIDSAVE, EVENV>), grid, block, 0, s, c);                  \
     else if (IOTV != 2 && kind == COL_FIRSTG)                                                        \
-      hipLaunchKernelGGL((KERN<P, (IOTV == 2 ? 0 : IOTV), COL_FIRSTG, EVENV>), grid, block, 0, s, c); \
+      hipLaunchKernelGGL((KERN<P, IOF, COL_FIRSTG, EVENV>), grid, block, 0, s, c);                   \
+    else if (IOTV != 2 && kind == COL_SPECG)                                                         \
+      hipLaunchKernelGGL((KERN<P, IOF, COL_SPECG, EVENV>), grid, block, 0, s, c);                    \
+    else if (IOTV != 2 && kind == COL_SPECGF)                                                        \
+      hipLaunchKernelGGL((KERN<P, IOF, COL_SPECGF, EVENV>), grid, block, 0, s, c);                   \
     else if (kind == COL_FIRST) hipLaunchKernelGGL((KERN<P, IOTV, COL_FIRST, EVENV>), grid, block, 0, s, c); \
     else if (kind == COL_MID) hipLaunchKernelGGL((KERN<P, IOTV, COL_MID, EVENV>), grid, block, 0, s, c); \
     else hipLaunchKernelGGL((KERN<P, IOTV, COL_LAST, EVENV>), grid, block, 0, s, c);                   \
@@ -901,6 +963,7 @@ static void launch_col_odd_t(int kind, int io, const ColArgs& c, dim3 grid, hipS
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUTREV) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUTREV, EVEN>), grid, block, 0, s, c);
   else if (io == 0) HYENA_COL_KINDS(k_col_odd, N1, 0, EVEN);
   else if (io == 1) HYENA_COL_KINDS(k_col_odd, N1, 1, EVEN);
   else HYENA_COL_KINDS(k_col_odd, N1, 2, EVEN);
@@ -911,6 +974,7 @@ static void launch_col_pair_t(int kind, int io, const ColArgs& c, dim3 grid, hip
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUTREV) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUTREV, EVEN>), grid, block, 0, s, c);
   else if (io == 0) HYENA_COL_KINDS(k_col_pair, Q, 0, EVEN);
   else if (io == 1) HYENA_COL_KINDS(k_col_pair, Q, 1, EVEN);
   else HYENA_COL_KINDS(k_col_pair, Q, 2, EVEN);

@@ -120,7 +120,7 @@ hipError_t single_backward(const BackwardArgs& a, int64_t N, hipStream_t s);
 // workspace buffers (saved c_n, z, g, two temporaries, the per-row spectra
 // and the four-step intermediate).
 struct LongBackwardLayout {
-  int64_t c, t1, t2, sg, work, total;
+  int64_t c, t1, sg, work, total;
   int rows_per_group;
 };
 LongBackwardLayout long_backward_layout(const PlanInfo& p, int64_t B, int64_t D, int64_t NORD);
@@ -170,8 +170,14 @@ hipError_t single_forward(const ForwardArgs& a, int64_t N, hipStream_t s);
 hipError_t single_spectrum(const SpectrumArgs& a, int64_t N, hipStream_t s);
 hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t s);
 hipError_t fourstep_spectrum(const SpectrumArgs& a, const PlanInfo& p, hipStream_t s);
-// The fused spectrum pass (SpectrumArgs.g) exists for power-of-two column lengths.
-inline bool fourstep_fused_spec_ok(const PlanInfo& p) { return p.n1 >= 16 && (p.n1 & (p.n1 - 1)) == 0; }
+// The backward's fused passes (SpectrumArgs.g, reversed outputs) exist for
+// every column kernel of the four-step forward: power-of-two columns, odd
+// columns in registers and 2q columns on lane pairs.
+inline bool fourstep_fused_spec_ok(const PlanInfo& p) {
+  const int n1 = p.n1, q = n1 % 2 == 0 ? n1 / 2 : n1;
+  const bool odd = q == 3 || q == 5 || q == 9 || q == 15 || q == 25 || q == 27;
+  return (n1 >= 16 && (n1 & (n1 - 1)) == 0) || odd;
+}
 hipError_t filter_gen(const FilterGenArgs& a, hipStream_t s);
 hipError_t spectrum_export(const void* spec, int NF, const PlanInfo& p, float* out, hipStream_t s);
 hipError_t spectrum_to_fourstep(const void* spec, int NF, const PlanInfo& single, const PlanInfo& fs, void* out,

@@ -241,9 +241,9 @@ def test_backward_rejects_bad_arguments():
     assert bw(gh=Y) == ALIAS                                    # gh over gv
     assert bw(gx=(vp * 2)(Y + 0x100000, Bp)) == ALIAS           # gx_2 over x_1
     assert H.backward_workspace_bytes(4, 768, 2, 2048) > 0
-    # four-step lengths: saved c_n, two temporary row buffers, per-row spectra, the pass intermediate
+    # four-step lengths: saved c_n, one temporary row buffer, per-row spectra, the pass intermediate
     R, L = 4, 20000
-    assert H.backward_workspace_bytes(1, 4, 2, L) >= (2 + 2) * R * L * 4 + R * (32768 + 1) * 8
+    assert H.backward_workspace_bytes(1, 4, 2, L) >= (2 + 1) * R * L * 4 + R * (32768 + 1) * 8
     # 8192 < L <= 16384: the single-path spectrum is rewritten into the four-step layout (extra N*D rows)
     assert H.backward_workspace_bytes(1, 4, 2, 12000) > H.backward_workspace_bytes(1, 4, 2, 8192)
 
