@@ -461,7 +461,8 @@ def run_backward(args, cfg, torch, H, dev):
         "metric": "Hyena order-N backward channel-tokens/sec (B*D*L/s)",
         "value": cfg.B * cfg.D * cfg.L / t, "unit": "channel-tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32", "data": "synthetic (seeded N(0,1) activations and output gradient, random-init filter FFN)",
+        "dtype": "fp32" if cfg.io == "fp32" else "bf16 I/O, fp32 compute",
+        "data": "synthetic (seeded N(0,1) activations and output gradient, random-init filter FFN)",
         "config": {"workload": cfg.desc + ", backward", "name": cfg.name, "N": cfg.N, "B": cfg.B, "D": cfg.D,
                    "L": cfg.L, "io": cfg.io, "input_sets": sets},
         "roofline": roof,
