@@ -704,6 +704,15 @@ struct RevTwiddle {
   __device__ __forceinline__ cf apply(cf v, int i) const { return cmul(step_power<E>(b, st, i), cconj(v)); }
 };
 
+// Four-step twiddles of the row pass, W_N^{k1 i2} for the thread's points
+// i2 = j + i*S2: the base W_N^{k1 j} times the i-th power of the step
+// W_N^{k1 S2}, the powers by repeated multiplication (HYENA_ROW_TW_SEQ = 1:
+// E - 1 products, rounding growing with i up to ~E ulp) or by binary
+// powers (0: about twice the products for E = 16).
+#ifndef HYENA_ROW_TW_SEQ
+#define HYENA_ROW_TW_SEQ 1
+#endif
+
 // LDS of the row pass.  HYENA_ROW_SW: 0 plain addressing; 1 XOR-swizzled
 // FFT stage buffers (RowLdsT<true>); 2 one padding slot after every 16
 // points, for every access (the first stage's stores, 16 points apart per
@@ -775,8 +784,17 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
   const cf tb = twiddle<false>((uint32_t)k1 * (uint32_t)j, N);
   const cf ts = twiddle<false>((uint32_t)k1 * (uint32_t)S2, N);
   if constexpr (KIND != ROW_SMUL) {
+    if constexpr (HYENA_ROW_TW_SEQ) {
+      cf p = tb;
 #pragma unroll
-    for (int i = 0; i < E; ++i) u[i] = cmul(ld_work<WB>(row + j + i * S2), step_power<E>(tb, ts, i));
+      for (int i = 0; i < E; ++i) {
+        u[i] = cmul(ld_work<WB>(row + j + i * S2), p);
+        if (i + 1 < E) p = cmul(p, ts);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) u[i] = cmul(ld_work<WB>(row + j + i * S2), step_power<E>(tb, ts, i));
+    }
     fft.template run<false>(u, lds, j);
   }
 
@@ -826,8 +844,12 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     __syncthreads();
     fft.template run<true>(u, lds, j);
     if (live) {
+      cf p = tb;
 #pragma unroll
-      for (int i = 0; i < E; ++i) st_work<WB>(row + j + i * S2, cmulc(u[i], step_power<E>(tb, ts, i)));
+      for (int i = 0; i < E; ++i) {
+        st_work<WB>(row + j + i * S2, cmulc(u[i], HYENA_ROW_TW_SEQ ? p : step_power<E>(tb, ts, i)));
+        if (HYENA_ROW_TW_SEQ && i + 1 < E) p = cmul(p, ts);
+      }
     }
   } else if constexpr (KIND == ROW_SPEC) {
     __syncthreads();
@@ -895,9 +917,19 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     for (int i = E / 2; i < E; ++i) u[i] = lds(j + i * S2);
     fft.template run<true>(u, lds, j);
     if (live) {
+      if constexpr (HYENA_ROW_TW_SEQ) {
+        cf p = opaque(tb);
+        const cf sq = opaque(ts);
 #pragma unroll
-      for (int i = 0; i < E; ++i)
-        st_work<WB>(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
+        for (int i = 0; i < E; ++i) {
+          st_work<WB>(row + j + i * S2, cmulc(u[i], p));
+          if (i + 1 < E) p = cmul(p, sq);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+          st_work<WB>(row + j + i * S2, cmulc(u[i], step_power<E>(opaque(tb), opaque(ts), i)));
+      }
     }
   }
 }
