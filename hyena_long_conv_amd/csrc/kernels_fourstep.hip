@@ -695,13 +695,20 @@ struct RowArgs {
 // spectrum of a row reversal t -> (c - t) mod 2N is W^(c k) conj X(k).
 template <int E>
 struct RevTwiddle {
-  cf b, st;
+  cf st, p;   // step W^(c n1 S2); the running power W^(c k_i)
   __device__ __forceinline__ RevTwiddle(int64_t c, int k1, int n1, int j, int S2, uint32_t M) {
     const uint64_t kb = (uint64_t)k1 + (uint64_t)n1 * (uint64_t)j, ks = (uint64_t)n1 * (uint64_t)S2;
-    b = twiddle<false>((uint32_t)(((uint64_t)c * kb) % M), M);
+    p = twiddle<false>((uint32_t)(((uint64_t)c * kb) % M), M);
     st = twiddle<false>((uint32_t)(((uint64_t)c * ks) % M), M);
   }
-  __device__ __forceinline__ cf apply(cf v, int i) const { return cmul(step_power<E>(b, st, i), cconj(v)); }
+  // W^(c k_i) conj v for the thread's points in order i = 0, 1, ...: the
+  // power by a running product, as the four-step twiddles with
+  // HYENA_ROW_TW_SEQ
+  __device__ __forceinline__ cf apply_next(cf v) {
+    const cf r = cmul(p, cconj(v));
+    p = cmul(p, st);
+    return r;
+  }
 };
 
 // Four-step twiddles of the row pass, W_N^{k1 i2} for the thread's points
@@ -824,9 +831,9 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     cf yn = make_float2(0.f, 0.f);
     if (k1 == 0 && j == 0) yn = cscale(cmul(ld_spec(xs + N), ld_spec(gs + N)), sc);
     if (a.rev) {   // the reversed output row: Y'(k) = W^(c k) conj Y(k), Y'(N) = (-1)^c conj Y(N)
-      const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
+      RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
 #pragma unroll
-      for (int i = 0; i < E; ++i) u[i] = rt.apply(u[i], i);
+      for (int i = 0; i < E; ++i) u[i] = rt.apply_next(u[i]);
       yn = cscale(cconj(yn), a.rev_c & 1 ? -1.f : 1.f);
     }
 #pragma unroll
@@ -860,13 +867,13 @@ __global__ void __launch_bounds__((RowCfg<N2, WB>::T), HYENA_ROW_WAVES) k_row(Ro
     const float sc = 1.0f / (float)(2 * N);
     if (live) {
       if (a.rev) {
-        const RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
+        RevTwiddle<E> rt(a.rev_c, k1, n1, j, S2, 2 * N);
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           const int k2 = j + i * S2;
           const int k2m = (k1 == 0) ? ((N2 - k2) & (N2 - 1)) : (N2 - 1 - k2);
           const cf am = ldsm(k2m);
-          out[(int64_t)k1 * N2 + k2] = rt.apply(realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc), i);
+          out[(int64_t)k1 * N2 + k2] = rt.apply_next(realfft_bin(u[i], am, cmul(wk, w2e<E>(i)), sc));
           if (k1 == 0 && k2 == 0)   // Nyquist bin, W^(c N) = (-1)^c
             out[N] = make_float2((a.rev_c & 1 ? -1.f : 1.f) * (u[i].x - u[i].y) * sc, 0.f);
         }
