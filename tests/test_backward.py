@@ -151,3 +151,36 @@ def test_backward_long_deterministic(monkeypatch):
     a, _ = _run(2, 3, 2, 600, "fp32", channels=[1])
     b, _ = _run(2, 3, 2, 600, "fp32", channels=[1])
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("name,channels", [("C3", 3), ("C4", 2), ("C5b", 2)])
+def test_backward_config_full_size_sampled(name, channels):
+    """The backward on the full configuration shapes (the pass groups and
+    column kernels the benchmark times: 64 x 1024 rows in two groups, 512 x
+    2048 rows in eight, 50-point columns on lane pairs), checked on channels
+    0, D - 1 and a seeded sample against the oracle's backward on the same
+    inputs.  fp32 gradients beyond L = 64K against 5e-4, as the forward."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[name]
+    p = make_filter_params(cfg)
+    v, xs = make_activations(cfg, DEV)
+    g = torch.Generator(device=DEV); g.manual_seed(cfg.seed + 7)
+    gy = torch.randn(v.shape, generator=g, device=DEV).to(v.dtype)
+    h = H.filter_gen(params_to_device(p), cfg.L)
+    spec = H.filter_spectrum(h)
+    del h
+    gv, gxs, gh = H.backward(v, xs, spec, gy)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.seed)
+    ds = sorted({0, cfg.D - 1} | set(rng.choice(np.arange(1, cfg.D - 1), channels - 2, replace=False).tolist()
+                                      if channels > 2 else set()))
+    hn = O.filter_gen(p, cfg.L, channels=ds)
+    sel = lambda t: t[:, ds].float().cpu().numpy().astype(np.float64)
+    rv, rxs, rgh = O.hyena_backward(sel(v), [sel(x) for x in xs], hn, sel(gy))
+    tol = TOL[cfg.io] if (cfg.io == "bf16" or cfg.L <= 65536) else 5e-4
+    tol_gh = TOL_GH if cfg.L <= 65536 else 5e-4
+    errs = [channel_errors(sel(gv), rv).max()] + [channel_errors(sel(a), r).max() for a, r in zip(gxs, rxs)]
+    egh = channel_errors(gh[:, ds].cpu().numpy().astype(np.float64), rgh).max()
+    print(f"{name} backward: channels {ds}, gv/gx max normalised error {max(errs):.3e}, gh {egh:.3e}")
+    assert all(np.isfinite(errs)) and max(errs) <= tol, errs
+    assert np.isfinite(egh) and egh <= tol_gh, egh
