@@ -218,6 +218,12 @@ __device__ __forceinline__ float grid_kernel_at(const float* k, int64_t koff, in
 // intermediate kept as bf16 pairs.
 constexpr int io_of(int iot) { return iot == 2 ? 1 : iot; }
 
+// COL_SPECG/F: the g * c stores after the column FFT's stores (1) or before
+// the FFT (0; 1M backward 16.83 against 16.96 ms, 64K 2.776 against 2.789).
+#ifndef HYENA_SPECG_LATE
+#define HYENA_SPECG_LATE 1
+#endif
+
 // COL_OUTREV store of the pair at position t (even) of a row of length L:
 // t -> (rev_c - t) mod L.  With L even and rev_c = L - 1 the mirrored pair
 // (L-2-t, L-1-t) is one aligned 8-byte store; otherwise (odd L, periodic
@@ -289,6 +295,15 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       return ld_pair<io_of(IOT), EVEN, true>(p, ro, t, len);
     }
   };
+  constexpr bool SPECG = KIND == COL_SPECG || KIND == COL_SPECGF;
+  cf gc[SPECG ? E : 1];   // SPECG: g * c of the column's points
+  const auto store_gc = [&]() {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      int64_t ro, t, len;
+      if (at(j + i * S1, ro, t, len)) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, gc[SPECG ? i : 0]);
+    }
+  };
 
   if constexpr (KIND == COL_SPEC && GRID) {
     const int64_t e = a.gcirc ? a.gL1 * a.gLm * a.gL2 : (2 * a.gL1 - 1) * (2 * a.gLm - 1) * (2 * a.gL2 - 1);
@@ -303,10 +318,10 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc),
             grid_kernel_at(a.h, koff, i1, gi2, 2 * gm + 1, N1, Pm, P3, a.gL1, a.gLm, a.gL2, a.gcirc));
     }
-  } else if constexpr (KIND == COL_SPECG || KIND == COL_SPECGF) {
-    // all loads of the column first, then the stores of g * c
+  } else if constexpr (SPECG) {
+    // all loads of the column first, then the stores of g * c (after the
+    // column FFT's stores with HYENA_SPECG_LATE)
     constexpr int GT = KIND == COL_SPECGF ? 0 : io_of(IOT);
-    cf gc[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       int64_t ro, t, len;
@@ -316,11 +331,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       gc[i] = make_float2(gv.x * cv.x, gv.y * cv.y);
       u[i] = make_float2(gv.x * xv.x, gv.y * xv.y);
     }
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      int64_t ro, t, len;
-      if (at(j + i * S1, ro, t, len)) st_pair<io_of(IOT), EVEN>(a.y, ro, t, len, gc[i]);
-    }
+    if constexpr (!HYENA_SPECG_LATE) store_gc();
   } else if constexpr (KIND == COL_FIRST || KIND == COL_SPEC || KIND == COL_FIRSTG) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
@@ -432,6 +443,7 @@ __global__ void __launch_bounds__((ColCfg<N1, GRID>::T), HYENA_COL_WAVES) k_col(
       for (int i = 0; i < E; ++i) st_work<WB>(buf + (int64_t)(j + i * S1) * a.n2 + col, u[i]);
     }
   }
+  if constexpr (SPECG && HYENA_SPECG_LATE) store_gc();
 }
 
 // Column pass for odd column lengths (n1 in 3, 5, 9, 15, 25, 27: FFT
