@@ -49,7 +49,7 @@ typedef enum {
   HYENA_OK = 0,
   HYENA_ERR_NULL = 1,        /* a required pointer is NULL                       */
   HYENA_ERR_SHAPE = 2,       /* a size is <= 0 or out of the supported range     */
-  HYENA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement    */
+  HYENA_ERR_UNSUPPORTED = 3, /* a valid request the library does not implement   */
   HYENA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned          */
   HYENA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
   HYENA_ERR_ALIAS = 6,       /* the output overlaps an input                     */
@@ -60,7 +60,7 @@ typedef enum { HYENA_FP32 = 0, HYENA_BF16 = 1 } hyena_dtype;
 
 typedef enum { HYENA_PATH_SINGLE = 1, HYENA_PATH_FOURSTEP = 2 } hyena_path;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define HYENA_MAX_ORDER 8          /* N in 1..8                                 */
 #define HYENA_MAX_L (1LL << 22)    /* L in 1..2^22                              */
 #define HYENA_MAX_FREQ 16          /* K in 0..16 (positional features 1+2K)     */
