@@ -52,27 +52,6 @@ __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_ca
 __device__ __forceinline__ void st_f4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
-template <int IOT>
-__device__ __forceinline__ void st4_io(void* p, int64_t i, float a, float b, float c, float d) {
-  if constexpr (IOT == 0) {
-    st_f4(static_cast<float*>(p) + i, a, b, c, d);
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
-  }
-}
-
-// out = a in the I/O dtype (the final gradient of v, held in natural order)
-template <int IOT, bool V4>
-__global__ void k_bw_store(const float* __restrict__ a, void* __restrict__ out, int64_t rows, int64_t L) {
-  if constexpr (V4) {
-    ROW_LOOP4(rows, L) {
-      const float4 w = ld_f4(a + r * L + t);
-      st4_io<IOT>(out, r * L + t, w.x, w.y, w.z, w.w);
-    }
-  } else {
-    ROW_LOOP(rows, L) IO<IOT>::st(out, r * L + t, a[r * L + t]);
-  }
-}
 
 // gh[d][k] = sum_b t[b*D + d][k]  (fixed batch order: deterministic)
 template <bool V4>
@@ -105,8 +84,10 @@ __global__ void k_bw_batch_sum(const float* __restrict__ tt, float* __restrict__
 // rev_c >= 0: the output row reversed, t -> (rev_c - t) mod M.
 hipError_t bw_conv(const PlanInfo& p, const void* spec, const void* z, float* out, int B, int D,
                    bool filters_per_row, void* work, int rows_per_group, hipStream_t s,
-                   const void* zspec = nullptr, int zio = 0, const float* zc = nullptr, int64_t rev_c = -1) {
+                   const void* zspec = nullptr, int zio = 0, const float* zc = nullptr, int64_t rev_c = -1,
+                   bool out_bf16 = false) {
   ForwardArgs f{};
+  f.out_bf16 = out_bf16;
   f.v = z;
   f.spec_in = zspec;
   f.vc = zc;
@@ -187,17 +168,11 @@ hipError_t long_backward(const BackwardArgs& a, const PlanInfo& p, void* workspa
     }
     // adjoint: g_n = R(h_n conv R(g * x_n)).  Those spectra are already in sg,
     // so it starts at its row pass, whose reversal map returns g_n itself
-    // (into gv directly for the last step with fp32 I/O)
-    float* gout = (nn == 0 && a.io == 0) ? static_cast<float*>(a.gv) : T1;
+    // (into gv directly for the last step, in the I/O dtype)
+    float* gout = nn == 0 ? static_cast<float*>(a.gv) : T1;
     BW_TRY(bw_conv(p, spec_n(nn), nullptr, gout, (int)B, (int)D, false, work, w.rows_per_group, s, sg, 0, nullptr,
-                   rev_c));
+                   rev_c, nn == 0 && a.io == 1));
     gcur = T1;
-  }
-  // bf16 I/O: gv from the fp32 row buffer T1
-  if (a.io == 1) {
-    if (L % 4 == 0) hipLaunchKernelGGL((k_bw_store<1, true>), row_grid(R, L / 4), dim3(EW_THREADS), 0, s, T1, a.gv, R, L);
-    else hipLaunchKernelGGL((k_bw_store<1, false>), row_grid(R, L), dim3(EW_THREADS), 0, s, T1, a.gv, R, L);
-    BW_TRY(hipGetLastError());
   }
 #undef BW_TRY
   return hipSuccess;

@@ -959,8 +959,11 @@ template <int N1, bool EVEN, bool GRID>
 static void launch_col_t(int kind, int io, const ColArgs& c, dim3 grid, dim3 block, hipStream_t s) {
   if (kind == COL_SPEC) {
     hipLaunchKernelGGL((k_col<N1, 0, COL_SPEC, EVEN, GRID>), grid, block, 0, s, c);
-  } else if (kind == COL_OUT) {
-    if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+  } else if (kind == COL_OUT) {   // io: the output's dtype (the intermediate is float2)
+    if constexpr (!GRID) {
+      if (io == 1) hipLaunchKernelGGL((k_col<N1, 1, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+      else hipLaunchKernelGGL((k_col<N1, 0, COL_OUT, EVEN, false>), grid, block, 0, s, c);
+    }
   } else if (kind == COL_OUTREV) {
     if constexpr (!GRID) hipLaunchKernelGGL((k_col<N1, 0, COL_OUTREV, EVEN, false>), grid, block, 0, s, c);
   } else if (kind == COL_SPECG || kind == COL_SPECGF) {
@@ -1013,6 +1016,7 @@ template <int N1, bool EVEN>
 static void launch_col_odd_t(int kind, int io, const ColArgs& c, dim3 grid, hipStream_t s) {
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUT && io == 1) hipLaunchKernelGGL((k_col_odd<N1, 1, COL_OUT, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUTREV) hipLaunchKernelGGL((k_col_odd<N1, 0, COL_OUTREV, EVEN>), grid, block, 0, s, c);
   else if (io == 0) HYENA_COL_KINDS(k_col_odd, N1, 0, EVEN);
@@ -1024,6 +1028,7 @@ template <int Q, bool EVEN>
 static void launch_col_pair_t(int kind, int io, const ColArgs& c, dim3 grid, hipStream_t s) {
   const dim3 block(kColOddThreads);
   if (kind == COL_SPEC) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_SPEC, EVEN>), grid, block, 0, s, c);
+  else if (kind == COL_OUT && io == 1) hipLaunchKernelGGL((k_col_pair<Q, 1, COL_OUT, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUT) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUT, EVEN>), grid, block, 0, s, c);
   else if (kind == COL_OUTREV) hipLaunchKernelGGL((k_col_pair<Q, 0, COL_OUTREV, EVEN>), grid, block, 0, s, c);
   else if (io == 0) HYENA_COL_KINDS(k_col_pair, Q, 0, EVEN);
@@ -1199,7 +1204,8 @@ hipError_t fourstep_forward(const ForwardArgs& a, const PlanInfo& p, hipStream_t
       if (save) c.y = a.csave + n * a.csave_stride;
       const int kind = n < a.NORD - 1 ? (save ? COL_MIDSAVE : COL_MID)
                                       : (a.no_gate ? (a.rev_out && !smul ? COL_OUTREV : COL_OUT) : COL_LAST);
-      e = dispatch_col(p.n1, kind, cio, c, groups, s);
+      // ungated outputs: fp32 rows, bf16 with out_bf16 (float2 intermediate either way)
+      e = dispatch_col(p.n1, kind, kind == COL_OUT ? (a.out_bf16 ? 1 : 0) : cio, c, groups, s);
       if (e != hipSuccess) return e;
     }
   }

@@ -29,7 +29,9 @@ struct ForwardArgs {
                          // csave + n * csave_stride, the last order's being the only output (y unused)
   int64_t csave_stride;
   const float* vc;       // four-step, one order: the input is xv * vc (xv = v in the I/O dtype, vc fp32)
-  int rev_out;           // with spec_in: the output row reversed, t -> (rev_c - t) mod M
+  int rev_out;           // four-step, one order, no gate: the output row reversed, t -> (rev_c - t) mod L
+                         // (by the spectral map with spec_in, else by the output pass's addressing)
+  int out_bf16;          // four-step, no gate: unreversed output rows in bf16 instead of fp32
   int64_t rev_c;
 };
 
