@@ -221,7 +221,7 @@ hyena_status hyena_forward_fir(const void* v, const void* const* x, const float*
  * L <= 8192 runs in one launch, one workgroup per channel; longer rows (up
  * to the forward's limit) express every convolution of the chain through
  * the forward's four-step causal convolution and a row reversal, with the
- * forward's c_n kept in the workspace (about (N + 1) * B * D * L * 4 bytes
+ * forward's c_n kept in the workspace (about (N + 1) * B * D * L * 4 bytes, N + 2 rows with B > 1,
  * plus per-row spectra; a spectrum built on the single path is rewritten
  * into the four-step layout there).  Errors as hyena_forward, plus ALIAS for an output overlapping an
  * input or another output.  hyena_backward_ex takes the convolution mode (see the circular mode below):
